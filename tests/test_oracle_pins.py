@@ -1,0 +1,349 @@
+"""Pins for the CPU oracle: each test ties it to something other than itself
+(printed worked examples, closed forms, invariants, a library routine and an
+independent brute force), so that a dropped term, a wrong sign or index, or a
+transposed operand anywhere in it fails at least one of them."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import attention as orc
+from oracle import blockwise
+from tests.brute import attention_loops
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _golden_case(g):
+    B, Hq, Hkv, Lq, Lk, D, Dv = (g[x] for x in ("B", "Hq", "Hkv", "Lq", "Lk", "D", "Dv"))
+    q = np.array(g["q"], float).reshape(B, Hq, Lq, D)
+    k = np.array(g["k"], float).reshape(B, Hkv, Lk, D)
+    v = np.array(g["v"], float).reshape(B, Hkv, Lk, Dv)
+    mask = np.array(g["mask"], bool)
+    return q, k, v, mask
+
+
+# --- pin 1 and 2: worked examples printed on the lattice-inference page --------------------
+
+@pytest.mark.parametrize("name", ["masked_key_sentinel.json", "all_masked_single_tile.json",
+                                  "all_masked_multi_tile.json"])
+def test_printed_worked_examples(name):
+    g = _load(name)
+    q, k, v, mask = _golden_case(g)
+    out = orc.sdpa(q, k, v, g["scale"], orc.MASK_BOOL, mask)
+    want = np.array(g["expected"]).reshape(out.shape)
+    assert np.all(np.isfinite(out))
+    if g["tolerance"] == 0:
+        assert np.array_equal(out, want)
+    else:
+        assert np.max(np.abs(out - want)) < g["tolerance"]
+
+
+@pytest.mark.parametrize("name", ["masked_key_sentinel.json", "all_masked_single_tile.json",
+                                  "all_masked_multi_tile.json"])
+def test_printed_examples_through_the_online_recurrence(name):
+    g = _load(name)
+    q, k, v, mask = _golden_case(g)
+    out = blockwise.online_head(q[0, 0], k[0, 0], v[0, 0], mask, g["scale"],
+                                g.get("tile_q", 1), g.get("tile_kv", 1))
+    want = np.array(g["expected"]).reshape(out.shape)
+    assert np.all(np.isfinite(out))
+    assert np.max(np.abs(out - want)) <= g["tolerance"]
+
+
+# --- pin 3: the direct formula of the nuvec-core fused-op test (causal, Lq=3, Lk=5, D=4) ---
+
+def test_direct_formula_causal_3x5():
+    rng = np.random.default_rng(0x65)
+    lq, lk, d = 3, 5, 4
+    q = rng.random((1, 1, lq, d)) / 4
+    k = rng.random((1, 1, lk, d)) / 4
+    v = rng.random((1, 1, lk, d)) / 4
+    got = orc.sdpa(q, k, v, 0.5, orc.MASK_CAUSAL)[0, 0]
+    for i in range(lq):
+        visible = i + lk - lq + 1
+        s = [0.5 * sum(q[0, 0, i, c] * k[0, 0, j, c] for c in range(d)) for j in range(visible)]
+        m = max(s)
+        z = sum(math.exp(x - m) for x in s)
+        for c in range(d):
+            want = sum(math.exp(s[j] - m) / z * v[0, 0, j, c] for j in range(visible))
+            assert abs(got[i, c] - want) < 1e-12
+
+
+# --- pin 4: hand-computed exact cases ------------------------------------------------------
+
+def _one(q, k, v, scale=1.0, mask_kind=0, mask=None, sinks=None, Hq=1, Hkv=1):
+    q = np.array(q, float)
+    k = np.array(k, float)
+    v = np.array(v, float)
+    return orc.sdpa(q, k, v, scale, mask_kind, mask, sinks)
+
+
+def test_hand_cases():
+    # (i) equal scores: the mean of the values
+    out = _one([[[[1.0]]]], [[[[0.0], [0.0]]]], [[[[1.0], [3.0]]]])
+    assert out[0, 0, 0, 0] == 2.0
+    # (ii) the same with a zero sink logit: (1 + 3) / 3
+    out = _one([[[[1.0]]]], [[[[0.0], [0.0]]]], [[[[1.0], [3.0]]]], sinks=np.array([0.0]))
+    assert abs(out[0, 0, 0, 0] - 4.0 / 3.0) < 1e-15
+    # (iii) causal, Lq = Lk = 2: row 0 sees key 0 only
+    q = [[[[0.3], [-0.7]]]]
+    k = [[[[1.5], [-2.0]]]]
+    v = [[[[5.0], [9.0]]]]
+    out = _one(q, k, v, mask_kind=orc.MASK_CAUSAL)
+    assert out[0, 0, 0, 0] == 5.0
+    # (iv) boolean identity mask: each row sees its own key
+    out = _one(q, k, v, mask_kind=orc.MASK_BOOL, mask=np.eye(2, dtype=bool))
+    assert out[0, 0, 0, 0] == 5.0 and out[0, 0, 1, 0] == 9.0
+    # (v) scores 0 and ln 3: weights 1/4 and 3/4 (a sign error in the max subtraction
+    #     or a swapped operand would move these)
+    out = _one([[[[1.0]]]], [[[[0.0], [math.log(3.0)]]]], [[[[4.0], [8.0]]]])
+    assert abs(out[0, 0, 0, 0] - 7.0) < 1e-14
+    # (vi) D != Dv and a two-key row whose weights are fixed by a 2-d dot product
+    q = [[[[1.0, 2.0]]]]
+    k = [[[[0.5, 0.0], [0.0, 0.5]]]]           # scores 0.5 and 1.0
+    v = [[[[1.0, 0.0, 2.0], [0.0, 1.0, -2.0]]]]
+    out = _one(q, k, v)
+    w1 = 1.0 / (1.0 + math.exp(0.5))
+    want = [w1, 1 - w1, 2 * w1 - 2 * (1 - w1)]
+    assert np.allclose(out[0, 0, 0], want, atol=1e-15, rtol=0)
+
+
+# --- pin 5: closed-form invariants ---------------------------------------------------------
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+@pytest.mark.parametrize("mask_kind", [0, 1, 2])
+def test_single_key_returns_its_value(mask_kind):
+    rng = np.random.default_rng(1)
+    q, k, v = _rand(rng, 2, 4, 1, 8), _rand(rng, 2, 2, 1, 8), _rand(rng, 2, 2, 1, 5)
+    mask = np.ones((1, 1), bool)
+    out = orc.sdpa(q, k, v, 0.3, mask_kind, mask)
+    for h in range(4):
+        assert np.array_equal(out[:, h, 0], v[:, h // 2, 0])
+    sinks = _rand(rng, 4)
+    out = orc.sdpa(q, k, v, 0.3, mask_kind, mask, sinks)
+    for b in range(2):
+        for h in range(4):
+            s0 = 0.3 * q[b, h, 0] @ k[b, h // 2, 0]
+            want = v[b, h // 2, 0] / (1.0 + math.exp(sinks[h] - s0))
+            assert np.allclose(out[b, h, 0], want, rtol=1e-14, atol=1e-15)
+
+
+def test_constant_values_are_returned():
+    rng = np.random.default_rng(2)
+    q, k = _rand(rng, 1, 4, 7, 16), _rand(rng, 1, 4, 11, 16)
+    v = np.full((1, 4, 11, 3), 2.5)
+    out = orc.sdpa(q, k, v, 0.25, orc.MASK_NONE)
+    assert np.allclose(out, 2.5, rtol=0, atol=1e-14)
+    sinks = _rand(rng, 4)
+    out = orc.sdpa(q, k, v, 0.25, orc.MASK_NONE, None, sinks)
+    _, ps = orc.probabilities(q, k, 0.25, orc.MASK_NONE, None, sinks)
+    assert np.allclose(out, 2.5 * (1 - ps)[..., None], rtol=0, atol=1e-14)
+    assert np.all(ps > 0) and np.all(ps < 1)
+
+
+@pytest.mark.parametrize("lq,lk", [(5, 5), (3, 8), (6, 4)])
+def test_zero_scale_averages_the_visible_values(lq, lk):
+    rng = np.random.default_rng(3)
+    q, k, v = _rand(rng, 1, 2, lq, 4), _rand(rng, 1, 2, lk, 4), _rand(rng, 1, 2, lk, 6)
+    bmask = rng.random((lq, lk)) < 0.6
+    for kind in (0, 1, 2):
+        out = orc.sdpa(q, k, v, 0.0, kind, bmask)
+        for h in range(2):
+            for i in range(lq):
+                if kind == 0:
+                    cols = list(range(lk))
+                elif kind == 1:
+                    cols = [j for j in range(lk) if j - i <= lk - lq]
+                else:
+                    cols = [j for j in range(lk) if bmask[i, j]]
+                want = v[0, h, cols].mean(axis=0) if cols else np.zeros(6)
+                assert np.allclose(out[0, h, i], want, rtol=0, atol=1e-14), (kind, h, i)
+
+
+def test_rows_sum_to_one_or_leave_the_sink_share():
+    rng = np.random.default_rng(4)
+    q, k = _rand(rng, 2, 6, 9, 8), _rand(rng, 2, 3, 13, 8)
+    bmask = rng.random((9, 13)) < 0.7
+    bmask[:, 4] = True
+    for kind in (0, 1, 2):
+        p, ps = orc.probabilities(q, k, 0.4, kind, bmask)
+        assert np.allclose(p.sum(-1), 1.0, rtol=0, atol=1e-14)
+        assert np.all(p >= 0)
+        sinks = _rand(rng, 6)
+        p, ps = orc.probabilities(q, k, 0.4, kind, bmask, sinks)
+        assert np.allclose(p.sum(-1) + ps, 1.0, rtol=0, atol=1e-14)
+        if kind == 1:
+            # causal, Lq <= Lk: key j > i + Lk - Lq never receives weight
+            for i in range(9):
+                assert np.all(p[:, :, i, i + 13 - 9 + 1:] == 0)
+
+
+# --- pin 6: grouped-query heads equal explicitly repeated key/value heads -----------------
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (8, 1), (6, 3)])
+def test_gqa_equals_repeated_heads(hq, hkv):
+    rng = np.random.default_rng(5)
+    q, k, v = _rand(rng, 2, hq, 5, 8), _rand(rng, 2, hkv, 7, 8), _rand(rng, 2, hkv, 7, 4)
+    sinks = _rand(rng, hq)
+    g = hq // hkv
+    k_rep = np.repeat(k, g, axis=1)   # head h of the repeated tensor is head h // g
+    v_rep = np.repeat(v, g, axis=1)
+    for kind in (0, 1):
+        a = orc.sdpa(q, k, v, 0.35, kind, None, sinks)
+        b = orc.sdpa(q, k_rep, v_rep, 0.35, kind, None, sinks)
+        assert np.array_equal(a, b)
+    # the mapping is h // g, not h % Hkv: distinct heads must give distinct rows
+    if hkv > 1:
+        k_mod = k[:, [h % hkv for h in range(hq)]]
+        v_mod = v[:, [h % hkv for h in range(hq)]]
+        c = orc.sdpa(q, k_mod, v_mod, 0.35, 0)
+        assert not np.allclose(orc.sdpa(q, k, v, 0.35, 0), c)
+
+
+# --- pin 7: mask plumbing, sinks at -inf, batch independence ------------------------------
+
+@pytest.mark.parametrize("lq,lk", [(4, 4), (3, 9), (7, 5)])
+def test_causal_equals_its_boolean_pattern(lq, lk):
+    rng = np.random.default_rng(6)
+    q, k, v = _rand(rng, 1, 2, lq, 8), _rand(rng, 1, 2, lk, 8), _rand(rng, 1, 2, lk, 8)
+    pattern = np.array([[j <= i + lk - lq for j in range(lk)] for i in range(lq)])
+    a = orc.sdpa(q, k, v, 0.2, orc.MASK_CAUSAL)
+    b = orc.sdpa(q, k, v, 0.2, orc.MASK_BOOL, pattern)
+    assert np.array_equal(a, b)
+    if lq > lk:
+        # rows with no visible key are zero
+        assert np.all(a[:, :, : lq - lk] == 0)
+
+
+def test_very_negative_sink_is_no_sink():
+    rng = np.random.default_rng(7)
+    q, k, v = _rand(rng, 1, 4, 6, 8), _rand(rng, 1, 2, 6, 8), _rand(rng, 1, 2, 6, 8)
+    a = orc.sdpa(q, k, v, 0.3, 1)
+    b = orc.sdpa(q, k, v, 0.3, 1, None, np.full(4, -1e30))
+    assert np.array_equal(a, b)
+
+
+def test_batch_item_alone_equals_in_batch():
+    rng = np.random.default_rng(8)
+    q, k, v = _rand(rng, 3, 4, 6, 8), _rand(rng, 3, 2, 9, 8), _rand(rng, 3, 2, 9, 8)
+    full = orc.sdpa(q, k, v, 0.3, 1)
+    for b in range(3):
+        alone = orc.sdpa(q[b:b + 1], k[b:b + 1], v[b:b + 1], 0.3, 1)
+        assert np.array_equal(full[b:b + 1], alone)
+
+
+def test_no_keys_gives_zeros_and_no_queries_gives_empty():
+    rng = np.random.default_rng(9)
+    q = _rand(rng, 1, 2, 3, 8)
+    k, v = np.zeros((1, 2, 0, 8)), np.zeros((1, 2, 0, 8))
+    for kind, sinks in ((0, None), (1, None), (1, _rand(rng, 2))):
+        out = orc.sdpa(q, k, v, 0.125, kind, None, sinks)
+        assert out.shape == (1, 2, 3, 8) and np.array_equal(out, np.zeros_like(out))
+    out = orc.sdpa(np.zeros((1, 2, 0, 8)), _rand(rng, 1, 2, 4, 8), _rand(rng, 1, 2, 4, 8), 0.1, 1)
+    assert out.shape == (1, 2, 0, 8)
+
+
+def test_row_subset_matches_full_evaluation():
+    rng = np.random.default_rng(10)
+    q, k, v = _rand(rng, 2, 4, 9, 8), _rand(rng, 2, 2, 12, 8), _rand(rng, 2, 2, 12, 5)
+    bmask = rng.random((9, 12)) < 0.5
+    sinks = _rand(rng, 4)
+    full = orc.sdpa(q, k, v, 0.3, 2, bmask, sinks)
+    rows = [(1, 3, 8), (0, 0, 0), (1, 1, 4), (0, 2, 8)]
+    sub = orc.sdpa(q, k, v, 0.3, 2, bmask, sinks, rows=rows)
+    for n, (b, h, i) in enumerate(rows):
+        # same arithmetic; only the matrix-product blocking may differ in the last bit
+        assert np.allclose(sub[n], full[b, h, i], rtol=0, atol=1e-14)
+
+
+# --- pin 8: library special case (torch CPU float64 with an explicit boolean mask) --------
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_torch_cpu_float64_sdpa(kind):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, Lq, Lk, D, Dv = 2, 8, 2, 7, 11, 16, 12
+    q, k, v = _rand(rng, B, Hq, Lq, D), _rand(rng, B, Hkv, Lk, D), _rand(rng, B, Hkv, Lk, Dv)
+    bmask = rng.random((Lq, Lk)) < 0.6
+    bmask[np.arange(Lq), np.arange(Lq) + Lk - Lq] = True   # every row sees a key
+    out = orc.sdpa(q, k, v, 0.27, kind, bmask)
+    if kind == 0:
+        allowed = np.ones((Lq, Lk), bool)
+    elif kind == 1:   # bottom-right alignment; torch's own causal flag is top-left
+        allowed = np.array([[j <= i + Lk - Lq for j in range(Lk)] for i in range(Lq)])
+    else:
+        allowed = bmask
+    g = Hq // Hkv
+    tq = torch.from_numpy(q)
+    tk = torch.from_numpy(k).repeat_interleave(g, dim=1)
+    tv = torch.from_numpy(v).repeat_interleave(g, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=torch.from_numpy(allowed), scale=0.27).numpy()
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
+
+
+# --- pin 9: the split-key schedule reaches the definition -------------------------------
+
+@pytest.mark.parametrize("block", [1, 3, 16, 64])
+def test_split_key_combine_equals_definition(block):
+    rng = np.random.default_rng(12)
+    Lk, D, Dv = 53, 16, 9
+    q, k, v = _rand(rng, 1, 2, 1, D), _rand(rng, 1, 1, Lk, D), _rand(rng, 1, 1, Lk, Dv)
+    bmask = rng.random((1, Lk)) < 0.5
+    bmask[0, :block] = False            # at least one block sees nothing
+    bmask[0, -1] = True
+    sinks = _rand(rng, 2)
+    for kind, m in ((0, None), (2, bmask)):
+        for s in (None, sinks):
+            want = orc.sdpa(q, k, v, 0.25, kind, m, s)
+            for h in range(2):
+                vis = orc.visible_keys(0, 1, Lk, kind, m)
+                parts = blockwise.split_partials(q[0, h, 0], k[0, 0], v[0, 0], vis, 0.25, block)
+                got = blockwise.combine_partials(parts, Dv, None if s is None else float(s[h]))
+                assert np.allclose(got, want[0, h, 0], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("tq,tk", [(1, 1), (2, 3), (4, 16), (32, 8)])
+def test_online_recurrence_equals_definition(tq, tk):
+    rng = np.random.default_rng(13)
+    Lq, Lk = 13, 29
+    q, k, v = _rand(rng, Lq, 8), _rand(rng, Lk, 8), _rand(rng, Lk, 6)
+    for kind in (0, 1, 2):
+        bmask = rng.random((Lq, Lk)) < 0.3
+        vis = np.stack([orc.visible_keys(i, Lq, Lk, kind, bmask) for i in range(Lq)])
+        want = orc.sdpa(q[None, None], k[None, None], v[None, None], 0.5, kind, bmask)[0, 0]
+        got = blockwise.online_head(q, k, v, vis, 0.5, tq, tk)
+        assert np.allclose(got, want, rtol=0, atol=1e-13)
+
+
+# --- pin 10: independent loop-by-loop brute force on random tiny shapes --------------------
+
+@pytest.mark.parametrize("seed", range(12))
+def test_brute_force_tiny(seed):
+    rng = np.random.default_rng(100 + seed)
+    hkv = int(rng.integers(1, 3))
+    hq = hkv * int(rng.integers(1, 4))
+    B = int(rng.integers(1, 3))
+    lq, lk = int(rng.integers(1, 10)), int(rng.integers(1, 10))
+    d, dv = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+    kind = seed % 3
+    q, k, v = _rand(rng, B, hq, lq, d), _rand(rng, B, hkv, lk, d), _rand(rng, B, hkv, lk, dv)
+    bmask = rng.random((lq, lk)) < 0.5
+    sinks = _rand(rng, hq) if seed % 2 else None
+    scale = float(rng.uniform(0.1, 1.0))
+    got = orc.sdpa(q, k, v, scale, kind, bmask, sinks)
+    want = np.array(attention_loops(q.tolist(), k.tolist(), v.tolist(), B, hq, hkv, lq, lk, d, dv,
+                                    scale, kind, bmask.astype(int).tolist(),
+                                    None if sinks is None else sinks.tolist()))
+    assert np.allclose(got, want.reshape(got.shape), rtol=0, atol=1e-12)

@@ -1,0 +1,137 @@
+/*
+ * sdpa.h - C ABI of the MI355X (gfx950) fused scaled-dot-product attention
+ * forward library, libsdpa.so.
+ *
+ *   out = softmax(scale * Q K^T + mask) V
+ *
+ * The operation is the one tested by nuvec-core "tests/fast.rs"
+ * (attention_fallback_matches_a_direct_formula: scores scale * q.k, the row
+ * maximum subtracted before exp, weights divided by their sum, applied to v),
+ * with the masking and all-masked-row semantics of lattice-inference
+ * "src/attention/flash.rs" (run_tiled_attention_head: masked keys get zero
+ * weight; a row that sees no key outputs zeros) and its grouped-query head
+ * mapping (kv_head_index: query head h reads key/value head h / (Hq/Hkv)).
+ *
+ * Every tensor pointer is a DEVICE pointer to a contiguous row-major array
+ * and must be 16-byte aligned (the mask and sinks excepted). The caller owns
+ * every buffer. `out` must not overlap any input.
+ *
+ * Errors are return codes; nothing aborts, throws or prints. After an error,
+ * sdpa_last_error() returns a message naming the offending argument.
+ */
+#ifndef SDPA_H
+#define SDPA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of q, k, v, out and sinks (all the same type). */
+enum { SDPA_F32 = 0, SDPA_F16 = 1, SDPA_BF16 = 2 };
+
+/* Mask kinds.
+ * SDPA_MASK_NONE   every key is visible.
+ * SDPA_MASK_CAUSAL bottom-right aligned: query i sees key j iff j <= i + Lk - Lq
+ *                  (nuvec-core tests/fast.rs, direct-formula test). With Lq > Lk
+ *                  the first Lq - Lk rows see nothing and output zeros.
+ * SDPA_MASK_BOOL   a device uint8 matrix [Lq, Lk], nonzero = visible, shared by
+ *                  every batch item and head (nuvec-core tests/attention_plan.rs,
+ *                  attention(); tests/fast.rs, window_mask). */
+enum { SDPA_MASK_NONE = 0, SDPA_MASK_CAUSAL = 1, SDPA_MASK_BOOL = 2 };
+
+/* Return codes. */
+enum {
+  SDPA_OK = 0,
+  SDPA_ERR_INVALID = -1,     /* an argument is malformed (shape, pointer, dtype, overflow) */
+  SDPA_ERR_UNSUPPORTED = -2, /* well-formed but not built: a head-size pair outside the list below */
+  SDPA_ERR_HIP = -3          /* the HIP runtime reported an error while enqueuing */
+};
+
+/* Routes a call can take (sdpa_plan_t.route). */
+enum {
+  SDPA_ROUTE_EMPTY = 0,     /* B*Hq*Lq*Dv == 0: nothing to do, no launch */
+  SDPA_ROUTE_ZERO_FILL = 1, /* Lk == 0: out is filled with zeros by one small kernel */
+  SDPA_ROUTE_PREFILL = 2,   /* tiled online-softmax kernel over query blocks */
+  SDPA_ROUTE_DECODE = 3     /* split-key first pass over key blocks, then a log-sum-exp reduce */
+};
+
+/* The plan of one call: a pure function of the shapes, mask kind, sinks flag and dtype. */
+typedef struct sdpa_plan_t {
+  int32_t route;          /* SDPA_ROUTE_* */
+  int32_t kernels;        /* kernel launches the call enqueues */
+  int32_t rows_per_wave;  /* query rows one wavefront carries (MFMA tile height) */
+  int32_t waves;          /* wavefronts per workgroup of the first kernel */
+  int32_t block_n;        /* keys per tile */
+  int32_t heads_per_group;/* prefill: query heads sharing one workgroup's K/V tiles;
+                             decode: query heads packed into one wavefront (Hq/Hkv) */
+  int64_t keys_per_split; /* decode: keys per first-pass workgroup */
+  int64_t splits;         /* decode: key blocks per (batch, kv head) */
+  int64_t grid[3];        /* workgroups of the first kernel (x, y, z) */
+  int64_t scratch_bytes;  /* device scratch the call uses, 0 for prefill; decode: per (batch, kv head,
+                             split, packed row) a 16-byte {max, sum} slot and Dv f32 partial outputs */
+} sdpa_plan_t;
+
+/*
+ * sdpa_forward - enqueue one attention forward on `stream`.
+ *
+ *   q     [B, Hq,  Lq, D ]   device, dtype
+ *   k     [B, Hkv, Lk, D ]   device, dtype
+ *   v     [B, Hkv, Lk, Dv]   device, dtype
+ *   out   [B, Hq,  Lq, Dv]   device, dtype, written in full
+ *   Hq must be a multiple of Hkv; query head h reads kv head h / (Hq / Hkv).
+ *   scale  any finite float, applied to q.k as given (1/sqrt(D) is usual).
+ *   mask_kind  SDPA_MASK_*; `mask` is required (device [Lq, Lk] uint8) iff
+ *          mask_kind == SDPA_MASK_BOOL and ignored otherwise. A raw pointer
+ *          carries no shape: the caller guarantees Lq*Lk readable bytes.
+ *   sinks  NULL, or device [Hq] in dtype: one logit per query head that joins
+ *          the softmax denominator only (no value row) and is not multiplied
+ *          by `scale`.
+ *   Head sizes (D, Dv): (64,64) (80,80) (96,96) (128,128) (192,192) (256,256)
+ *          (512,512) (96,64) (192,128); others -> SDPA_ERR_UNSUPPORTED.
+ *   stream a hipStream_t (NULL = the default stream).
+ *
+ * Computation is float32 inside the kernels (f32 MFMA for SDPA_F32, bf16/f16
+ * MFMA with f32 accumulation otherwise); the output is rounded once to dtype.
+ * Empty cases: B*Hq*Lq == 0 or Dv == 0 enqueue nothing; Lk == 0 writes zeros.
+ * The call is asynchronous: validation errors return before anything is
+ * enqueued; a launch failure returns SDPA_ERR_HIP. A given plan gives the
+ * same bits run to run, and each batch item's bits do not depend on B.
+ * The decode route takes its scratch from a per-(device, stream) buffer that
+ * the library allocates on first use and keeps (sdpa_release_workspace frees).
+ */
+int sdpa_forward(const void* q, const void* k, const void* v, void* out,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                 int64_t D, int64_t Dv, float scale,
+                 int mask_kind, const uint8_t* mask, const void* sinks,
+                 int dtype, void* stream);
+
+/*
+ * sdpa_plan - the route, launch geometry and scratch size sdpa_forward would
+ * use for these arguments, validated exactly as sdpa_forward validates them
+ * (has_mask / has_sinks stand for non-NULL mask / sinks pointers). Pure: no
+ * device work and no allocation. `plan` must be non-NULL; it is written only
+ * on SDPA_OK. Mirrors nuvec-core tests/attention_plan.rs (plan_attention: a
+ * pure host plan naming the kernels that run and the scratch they hold).
+ */
+int sdpa_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+              int64_t D, int64_t Dv, int mask_kind, int has_mask, int has_sinks,
+              int dtype, sdpa_plan_t* plan);
+
+/* Message of the last error on the calling thread ("" if none). The pointer
+ * stays valid until the thread's next sdpa_* call. */
+const char* sdpa_last_error(void);
+
+/* Wait for the streams that used cached decode scratch, then free it.
+ * Returns SDPA_OK or SDPA_ERR_HIP. */
+int sdpa_release_workspace(void);
+
+/* ABI version of this header: 1. */
+int sdpa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_H */

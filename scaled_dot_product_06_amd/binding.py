@@ -1,0 +1,177 @@
+"""ctypes binding of libsdpa.so (include/sdpa.h): the same entry points under
+the same names, plus `attention`, which only marshals torch tensors into an
+sdpa_forward call. Every step of the computation runs in the library's HIP
+kernels; there is no Python or CPU fallback."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
+
+SDPA_F32, SDPA_F16, SDPA_BF16 = 0, 1, 2
+SDPA_MASK_NONE, SDPA_MASK_CAUSAL, SDPA_MASK_BOOL = 0, 1, 2
+SDPA_OK, SDPA_ERR_INVALID, SDPA_ERR_UNSUPPORTED, SDPA_ERR_HIP = 0, -1, -2, -3
+SDPA_ROUTE_EMPTY, SDPA_ROUTE_ZERO_FILL, SDPA_ROUTE_PREFILL, SDPA_ROUTE_DECODE = 0, 1, 2, 3
+ROUTE_NAMES = {0: "empty", 1: "zero_fill", 2: "prefill", 3: "decode"}
+
+EXPORTED = ("sdpa_forward", "sdpa_plan", "sdpa_last_error", "sdpa_release_workspace", "sdpa_abi_version")
+
+
+class SdpaPlan(ctypes.Structure):
+    _fields_ = [
+        ("route", ctypes.c_int32),
+        ("kernels", ctypes.c_int32),
+        ("rows_per_wave", ctypes.c_int32),
+        ("waves", ctypes.c_int32),
+        ("block_n", ctypes.c_int32),
+        ("heads_per_group", ctypes.c_int32),
+        ("keys_per_split", ctypes.c_int64),
+        ("splits", ctypes.c_int64),
+        ("grid", ctypes.c_int64 * 3),
+        ("scratch_bytes", ctypes.c_int64),
+    ]
+
+    def as_dict(self):
+        return {
+            "route": ROUTE_NAMES.get(self.route, self.route),
+            "kernels": self.kernels,
+            "rows_per_wave": self.rows_per_wave,
+            "waves": self.waves,
+            "block_n": self.block_n,
+            "heads_per_group": self.heads_per_group,
+            "keys_per_split": self.keys_per_split,
+            "splits": self.splits,
+            "grid": tuple(self.grid),
+            "scratch_bytes": self.scratch_bytes,
+        }
+
+
+class SdpaError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"sdpa error {code}: {message}")
+        self.code = code
+        self.message = message
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libsdpa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m scaled_dot_product_06_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, c_int, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.sdpa_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                 c_int, vp, vp, c_int, vp]
+    lib.sdpa_forward.restype = c_int
+    lib.sdpa_plan.argtypes = [i64, i64, i64, i64, i64, i64, i64, c_int, c_int, c_int, c_int,
+                              ctypes.POINTER(SdpaPlan)]
+    lib.sdpa_plan.restype = c_int
+    lib.sdpa_last_error.argtypes = []
+    lib.sdpa_last_error.restype = ctypes.c_char_p
+    lib.sdpa_release_workspace.argtypes = []
+    lib.sdpa_release_workspace.restype = c_int
+    lib.sdpa_abi_version.argtypes = []
+    lib.sdpa_abi_version.restype = c_int
+    _lib = lib
+    return lib
+
+
+def sdpa_last_error() -> str:
+    return load().sdpa_last_error().decode()
+
+
+def _check(rc: int) -> int:
+    if rc != SDPA_OK:
+        raise SdpaError(rc, sdpa_last_error())
+    return rc
+
+
+def sdpa_forward(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, Dv, scale, mask_kind, mask, sinks, dtype, stream,
+                 check: bool = True) -> int:
+    """Raw call: pointers are integers (device addresses) or None."""
+    rc = load().sdpa_forward(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, Dv, ctypes.c_float(scale), mask_kind,
+                             mask, sinks, dtype, stream)
+    return _check(rc) if check else rc
+
+
+def sdpa_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, has_mask, has_sinks, dtype, check: bool = True):
+    """Returns the plan as a dict (or the return code when check=False and it fails)."""
+    p = SdpaPlan()
+    rc = load().sdpa_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, int(bool(has_mask)), int(bool(has_sinks)),
+                          dtype, ctypes.byref(p))
+    if rc != SDPA_OK:
+        if check:
+            _check(rc)
+        return rc
+    return p.as_dict()
+
+
+def sdpa_release_workspace() -> int:
+    return _check(load().sdpa_release_workspace())
+
+
+def sdpa_abi_version() -> int:
+    return load().sdpa_abi_version()
+
+
+# ---- torch marshalling -------------------------------------------------------------------
+
+def _dtype_code(t):
+    import torch
+    codes = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16}
+    if t.dtype not in codes:
+        raise SdpaError(SDPA_ERR_INVALID, f"unsupported tensor dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def attention(q, k, v, scale: float, mask_kind: int = SDPA_MASK_NONE, mask=None, sinks=None, out=None,
+              stream=None):
+    """softmax(scale * q k^T + mask) v on the GPU through sdpa_forward.
+
+    q [B,Hq,Lq,D], k [B,Hkv,Lk,D], v [B,Hkv,Lk,Dv] contiguous CUDA tensors of one
+    dtype; mask a contiguous uint8/bool CUDA tensor [Lq,Lk] (mask_kind 2);
+    sinks a CUDA tensor [Hq] of q's dtype. Returns out [B,Hq,Lq,Dv].
+    """
+    import torch
+    B, Hq, Lq, D = q.shape
+    _, Hkv, Lk, _ = k.shape
+    Dv = v.shape[3]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise SdpaError(SDPA_ERR_INVALID, f"{name} must be a contiguous GPU tensor")
+        if t.dtype != q.dtype:
+            raise SdpaError(SDPA_ERR_INVALID, f"{name} has dtype {t.dtype}, q has {q.dtype}")
+    if tuple(k.shape) != (B, Hkv, Lk, D) or tuple(v.shape[:3]) != (B, Hkv, Lk):
+        raise SdpaError(SDPA_ERR_INVALID, f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    mptr = None
+    if mask_kind == SDPA_MASK_BOOL:
+        if mask is None or tuple(mask.shape) != (Lq, Lk) or not mask.is_contiguous() or not mask.is_cuda:
+            raise SdpaError(SDPA_ERR_INVALID, f"mask must be a contiguous GPU tensor of shape ({Lq}, {Lk})")
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        if mask.dtype != torch.uint8:
+            raise SdpaError(SDPA_ERR_INVALID, "mask must be uint8 or bool")
+        mptr = mask.data_ptr()
+    sptr = None
+    if sinks is not None:
+        if tuple(sinks.shape) != (Hq,) or sinks.dtype != q.dtype or not sinks.is_cuda:
+            raise SdpaError(SDPA_ERR_INVALID, f"sinks must be a GPU tensor of shape ({Hq},) and dtype {q.dtype}")
+        sinks = sinks.contiguous()
+        sptr = sinks.data_ptr()
+    if out is None:
+        out = torch.empty((B, Hq, Lq, Dv), dtype=q.dtype, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, Lq, Lk, D, Dv,
+                 float(scale), mask_kind, mptr, sptr, _dtype_code(q), stream)
+    return out

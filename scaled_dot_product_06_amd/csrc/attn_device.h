@@ -1,0 +1,169 @@
+// Device-side building blocks for the gfx950 attention kernels: vector types,
+// MFMA wrappers and their lane layouts, LDS transpose reads, cross-lane row
+// reductions and the online-softmax state update.
+//
+// The online-softmax recurrence follows lattice-inference
+// "src/attention/flash.rs" (run_tiled_attention_head): per key tile, a new row
+// maximum, a rescale factor for the running sum and output, tile weights, and
+// a final division by the running sum (zero rows when it is zero). Masked keys
+// carry no weight at all. Here the arithmetic is base 2 (scores are multiplied
+// by scale*log2(e) and exponentiated with exp2), which is the same softmax.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+// A row's reference maximum is moved only when a tile's maximum exceeds it by
+// more than this many powers of two, so most tiles skip the output rescale.
+// Softmax is invariant to the reference, and weights stay below 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
+struct ElemBF16 {};
+struct ElemF16 {};
+
+// ---- MFMA tile traits ------------------------------------------------------
+// MF x MF output tile; every lane holds 8 consecutive k-elements of A and B.
+// Lane l: column/row index l % MF, k-group l / MF (KG groups of 8 k's).
+// Accumulator element i of lane l sits at row acc_row(i, l / MF), column l % MF.
+template <int MF> struct Mfma;
+template <> struct Mfma<32> {
+  static constexpr int KW = 16;   // k per instruction (16-bit inputs)
+  static constexpr int ACC = 16;  // accumulators per lane
+  static constexpr int KG = 2;
+  static constexpr int KWF = 2;   // k per instruction for f32 inputs
+  typedef f32x16 acc_t;
+};
+template <> struct Mfma<16> {
+  static constexpr int KW = 32;
+  static constexpr int ACC = 4;
+  static constexpr int KG = 4;
+  static constexpr int KWF = 4;
+  typedef f32x4 acc_t;
+};
+
+template <int MF>
+__device__ __forceinline__ constexpr int acc_row(int i, int kg) {
+  return (i / 4) * (4 * Mfma<MF>::KG) + kg * 4 + (i % 4);
+}
+
+template <class E, int MF>
+__device__ __forceinline__ typename Mfma<MF>::acc_t mma16(u32x4 a, u32x4 b, typename Mfma<MF>::acc_t c);
+
+template <> __device__ __forceinline__ f32x16 mma16<ElemBF16, 32>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x16 mma16<ElemF16, 32>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4 mma16<ElemBF16, 16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4 mma16<ElemF16, 16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <int MF>
+__device__ __forceinline__ typename Mfma<MF>::acc_t mma_f32(float a, float b, typename Mfma<MF>::acc_t c);
+template <> __device__ __forceinline__ f32x16 mma_f32<32>(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4 mma_f32<16>(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---- 16-bit element helpers -------------------------------------------------
+template <class E> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack2<ElemBF16>(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+template <> __device__ __forceinline__ uint32_t pack2<ElemF16>(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+}
+template <class E> __device__ __forceinline__ float half_to_f32(uint16_t h);
+template <> __device__ __forceinline__ float half_to_f32<ElemBF16>(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+template <> __device__ __forceinline__ float half_to_f32<ElemF16>(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+template <class E> __device__ __forceinline__ uint16_t f32_to_half(float x) {
+  return (uint16_t)(pack2<E>(x, 0.0f) & 0xFFFFu);
+}
+
+// ---- memory helpers ----------------------------------------------------------
+__device__ __forceinline__ u32x4 ld_global16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st_global8(void* p, u32x2 v) {
+  *reinterpret_cast<u32x2*>(p) = v;
+}
+
+#define SDPA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Transposed 4 x 16-bit LDS read (gfx950 ds_read_b64_tr_b16). Within each
+// group of 16 lanes, lane j receives element (j % 4) of the 8-byte chunks that
+// lanes 4e + j/4 (e = 0..3) point at, in element order e.  If provider lane
+// 4e + c points at row (r0 + e), column (c0 + 4c) of a row-major 16-bit
+// matrix, lane j receives rows r0..r0+3 of column c0 + j.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SDPA_LDS(i16x4, p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// ---- cross-lane reductions over the lanes that hold one row ---------------------
+// permlane32_swap(x, x) returns {x[l], x[l-32]} above lane 31 and {x[l], x[l+32]}
+// (as {first, second} = {x[l] or x[l-32], x[l+32] or x[l]}) so the pair holds
+// both halves' values in every lane.
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <int MF> __device__ __forceinline__ float row_max(float x) {
+  x = max_xor32(x);
+  if constexpr (MF == 16) x = fmaxf(x, __shfl_xor(x, 16));
+  return x;
+}
+template <int MF> __device__ __forceinline__ float row_sum(float x) {
+  x = sum_xor32(x);
+  if constexpr (MF == 16) x = x + __shfl_xor(x, 16);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online-softmax reference update for one wave. `tile_max` is the row's
+// largest scaled score in the new tile (-inf if it sees none). When any row's
+// tile maximum passes its reference by more than kRescaleSlack, every row moves
+// its reference to max(old, tile) and rescales its running sum and output.
+template <int NACC, class Acc>
+__device__ __forceinline__ void softmax_rebase(float tile_max, float& m, float& l, Acc* o) {
+  const bool need = tile_max > m + kRescaleSlack;
+  if (__any(need)) {
+    const float m_new = fmaxf(m, tile_max);
+    const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int d = 0; d < NACC; ++d) o[d] *= alpha;
+    m = m_new;
+  }
+}
+
+}  // namespace sdpa

@@ -1,0 +1,83 @@
+// Kernel argument block and the launcher entry points the host router calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+enum Elem { kF32 = 0, kF16 = 1, kBF16 = 2 };
+enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskBool = 2 };
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const uint8_t* mask;   // [Lq, Lk] bytes when mask_kind == kMaskBool
+  const void* sinks;     // [Hq] in the element type, or null
+  int B, Hq, Hkv, Lq, Lk;
+  int group;             // Hq / Hkv
+  int mask_kind;
+  float c;               // |scale| * log2(e): scores are taken as c * q.k in base 2
+  uint32_t qsign;        // XOR applied to q bits (flips q's sign when scale < 0)
+  // prefill
+  int nqb;               // query blocks per head
+  int head_blocks;       // B * Hq / heads_per_group
+  // decode
+  int rows;              // group * Lq: query rows packed into one wavefront
+  int kps;               // keys per split (one wavefront's key range)
+  int nsplit;            // splits per (batch, kv head)
+  float* part;           // scratch: per split and row, {m, l} then Dv floats of output
+};
+
+// Geometry chosen by the host for a prefill launch.
+struct PrefillShape {
+  int mf;         // MFMA tile (rows per wave): 32 or 16
+  int waves;      // waves per workgroup
+  int heads;      // query heads per workgroup (share the K/V tiles)
+  int block_n;    // keys per tile
+  int block_m;    // query rows per head per workgroup
+};
+
+struct DecodeShape {
+  int mf;         // 16 or 32 (>= group * Lq)
+  int waves;      // waves (splits) per workgroup
+  int block_n;    // keys per tile
+};
+
+// Each launcher returns hipSuccess or the launch error; `ok` is false when no
+// kernel is built for the (dtype, D, Dv) combination.
+hipError_t launch_prefill(int elem, int D, int Dv, const PrefillShape& s, const FwdArgs& a,
+                          hipStream_t stream, bool* ok);
+hipError_t launch_decode(int elem, int D, int Dv, const DecodeShape& s, const FwdArgs& a,
+                         hipStream_t stream, bool* ok);
+hipError_t launch_zero_fill(void* out, int64_t bytes, hipStream_t stream);
+
+// Geometry rules shared by the launchers (template arguments) and the planner.
+constexpr int kPrefillWaves = 4;
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeBN = 32;       // keys per decode tile
+constexpr int head_max(int D, int Dv) { return D > Dv ? D : Dv; }
+// 32x32 MFMA tiles (32 query rows per wavefront) up to 128-wide heads; 16x16
+// tiles above, where a 32-row output accumulator would not fit in registers.
+constexpr int prefill_mf(int elem, int D, int Dv) { return head_max(D, Dv) <= 128 ? 32 : 16; }
+constexpr int prefill_bn(int elem, int D, int Dv) {
+  return elem == kF32 ? (head_max(D, Dv) <= 128 ? 32 : 16) : (head_max(D, Dv) <= 256 ? 64 : 32);
+}
+// 16x16 tiles when the packed query rows fit (and the head is a whole number
+// of 32-wide k-steps), else 32x32.
+constexpr int decode_mf(int D, int rows) { return rows <= 16 && D % 32 == 0 ? 16 : 32; }
+
+// The (D, Dv) pairs kernels are built for.
+#define SDPA_HEAD_PAIRS(X) \
+  X(64, 64) X(80, 80) X(96, 96) X(128, 128) X(192, 192) X(256, 256) X(512, 512) X(96, 64) X(192, 128)
+
+inline bool head_pair_supported(long long D, long long Dv) {
+#define SDPA_CHECK_PAIR(d, dv) if (D == d && Dv == dv) return true;
+  SDPA_HEAD_PAIRS(SDPA_CHECK_PAIR)
+#undef SDPA_CHECK_PAIR
+  return false;
+}
+
+}  // namespace sdpa

@@ -1,0 +1,30 @@
+// Prefill kernel instantiations for 16-bit inputs (bf16 and f16).
+#include "prefill_impl.h"
+
+namespace sdpa {
+
+template <class E, int D, int DV>
+static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_t stream) {
+  constexpr int elem = std::is_same<E, ElemBF16>::value ? kBF16 : kF16;
+  constexpr int MF = prefill_mf(elem, D, DV);
+  constexpr int BN = prefill_bn(elem, D, DV);
+  dim3 grid(a.head_blocks, a.nqb, 1);
+  hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves>), grid, dim3(kPrefillWaves * 64), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_16(int elem, int D, int Dv, const PrefillShape& s, const FwdArgs& a,
+                             hipStream_t stream, bool* ok) {
+  *ok = true;
+#define SDPA_PAIR(d, dv)                                                   \
+  if (D == d && Dv == dv)                                                  \
+    return elem == kBF16 ? launch_one<ElemBF16, d, dv>(s, a, stream)      \
+                         : launch_one<ElemF16, d, dv>(s, a, stream);
+  SDPA_HEAD_PAIRS(SDPA_PAIR)
+#undef SDPA_PAIR
+  *ok = false;
+  return hipSuccess;
+}
+
+}  // namespace sdpa

@@ -1,0 +1,27 @@
+// Prefill kernel instantiations for float32 inputs (f32 MFMA).
+#include "prefill_impl.h"
+
+namespace sdpa {
+
+template <int D, int DV>
+static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_t stream) {
+  constexpr int MF = prefill_mf(kF32, D, DV);
+  constexpr int BN = prefill_bn(kF32, D, DV);
+  dim3 grid(a.head_blocks, a.nqb, 1);
+  hipLaunchKernelGGL((prefill_f32_kernel<MF, D, DV, BN, kPrefillWaves>), grid, dim3(kPrefillWaves * 64), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_f32(int D, int Dv, const PrefillShape& s, const FwdArgs& a, hipStream_t stream,
+                              bool* ok) {
+  *ok = true;
+#define SDPA_PAIR(d, dv) \
+  if (D == d && Dv == dv) return launch_one<d, dv>(s, a, stream);
+  SDPA_HEAD_PAIRS(SDPA_PAIR)
+#undef SDPA_PAIR
+  *ok = false;
+  return hipSuccess;
+}
+
+}  // namespace sdpa

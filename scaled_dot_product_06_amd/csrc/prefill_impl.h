@@ -1,0 +1,473 @@
+// Prefill: tiled online-softmax attention over query blocks (gfx950 MFMA).
+//
+// One workgroup = NW wavefronts = `heads` query heads of one key/value group x
+// (NW / heads) x MF consecutive query rows. The workgroup walks the key axis in
+// tiles of BN keys, staging each K and V tile once in LDS for all its
+// wavefronts. Each wavefront keeps its MF query rows' Q fragment, running
+// maximum, running sum and output accumulator in registers for the whole walk
+// (the per-tile recurrence of lattice-inference "src/attention/flash.rs",
+// run_tiled_attention_head). Scores are computed transposed, S^T = K Q^T, so a
+// lane's accumulators all belong to one query row: the row maximum needs one
+// cross-lane exchange and the output rescale is a per-lane scalar. P goes back
+// into the MFMA as the B operand of O^T = V^T P^T; the V^T operand is read
+// from the row-major V tile with LDS transpose reads.
+//
+// Causal masking is bottom-right aligned (nuvec-core "tests/fast.rs", direct
+// formula test): row i sees keys j <= i + Lk - Lq. Workgroups stop at their
+// last visible key; only tiles that cross a row's last key are masked per
+// element. Late (long) query blocks are dispatched first.
+#pragma once
+
+#include "attn_device.h"
+#include "kernels.h"
+
+namespace sdpa {
+
+template <int MF, int D, int DV, int BN, int NW>
+struct PrefillCfg {
+  static constexpr int KW = Mfma<MF>::KW, ACC = Mfma<MF>::ACC, KG = Mfma<MF>::KG;
+  static constexpr int DVP = (DV + MF - 1) / MF * MF;  // V columns padded to whole MFMA tiles
+  static constexpr int KST = D + 8;                      // LDS row strides (elements)
+  static constexpr int VST = DVP + 16;
+  static constexpr int NQC = D / KW;
+  static constexpr int NSB = BN / MF;
+  static constexpr int NPV = BN / KW;
+  static constexpr int NDB = DVP / MF;
+  static constexpr int NT = NW * 64;
+  static constexpr int KCH = BN * D / 8, VCH = BN * DV / 8;  // 16-byte chunks per tile
+  static constexpr int KPT = (KCH + NT - 1) / NT, VPT = (VCH + NT - 1) / NT;
+  static constexpr int LDS_ELEMS = BN * KST + BN * VST;
+  static_assert(D % KW == 0, "head size must be a whole number of MFMA k-steps");
+  static_assert(BN % MF == 0 && BN % KW == 0, "tile must hold whole MFMA blocks");
+};
+
+template <class E, int MF, int D, int DV, int BN, int NW>
+__global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
+  using C = PrefillCfg<MF, D, DV, BN, NW>;
+  using acc_t = typename Mfma<MF>::acc_t;
+  constexpr int ACC = C::ACC;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  uint16_t* Ks = lds;
+  uint16_t* Vs = lds + BN * C::KST;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int col = lane % MF;
+  const int kg = lane / MF;
+
+  const int heads = a.Hq * a.B / a.head_blocks;   // query heads per workgroup
+  const int wph = NW / heads;                      // wavefronts per head
+  const int bm = wph * MF;                         // query rows per head per workgroup
+  const int qb = a.nqb - 1 - (int)blockIdx.y;      // late query blocks first
+  const int groups_per_b = a.Hq / heads;
+  const int b = (int)blockIdx.x / groups_per_b;
+  const int h0 = ((int)blockIdx.x % groups_per_b) * heads;
+  const int hkv = h0 / a.group;
+  const int h = h0 + w / wph;
+  const int wi0 = qb * bm + (w % wph) * MF;
+  const int iq = wi0 + col;
+  const int shift = a.Lk - a.Lq;
+
+  int kend = a.Lk;
+  if (a.mask_kind == kMaskCausal) kend = min(a.Lk, min(qb * bm + bm, a.Lq) - 1 + shift + 1);
+  if (kend < 0) kend = 0;
+  const int ntiles = (kend + BN - 1) / BN;
+
+  const bool wave_live = wi0 < a.Lq;
+  const int w_last = min(wi0 + MF, a.Lq) - 1;
+  int w_kend = a.Lk, w_kfull = a.Lk;
+  if (a.mask_kind == kMaskCausal) {
+    w_kend = min(a.Lk, w_last + shift + 1);
+    w_kfull = min(a.Lk, wi0 + shift + 1);
+  } else if (a.mask_kind == kMaskBool) {
+    w_kfull = 0;
+  }
+
+  // Q fragment (B operand of S^T = K Q^T): row iq, k-elements kg*8.. of each KW chunk.
+  const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(b * a.Hq + h) * a.Lq + iq) * D;
+  u32x4 qop[C::NQC];
+#pragma unroll
+  for (int c = 0; c < C::NQC; ++c) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (iq < a.Lq) x = ld_global16(qp + c * C::KW + kg * 8);
+    qop[c] = x ^ a.qsign;
+  }
+
+  if constexpr (C::DVP > DV) {
+    for (int e = tid; e < BN * (C::DVP - DV); e += C::NT) {
+      const int r = e / (C::DVP - DV), cc = DV + e % (C::DVP - DV);
+      Vs[r * C::VST + cc] = 0;
+    }
+  }
+
+  acc_t o[C::NDB];
+#pragma unroll
+  for (int d = 0; d < C::NDB; ++d) o[d] = acc_t{};
+  float m = -INFINITY, l = 0.0f, sink2 = 0.0f;
+  const bool has_sink = a.sinks != nullptr;
+  if (has_sink) {
+    sink2 = half_to_f32<E>(((const uint16_t*)a.sinks)[h]) * kLog2e;
+    m = sink2;
+  }
+
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * D;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * DV;
+  const uint8_t* mrow = a.mask + (size_t)iq * a.Lk;
+
+  u32x4 kr[C::KPT], vr[C::VPT];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < C::KPT; ++it) {
+      const int c = tid + it * C::NT;
+      if (C::KCH % C::NT == 0 || c < C::KCH) {
+        const int r = c / (D / 8), cc = c % (D / 8);
+        const int key = k0 + r;
+        kr[it] = key < a.Lk ? ld_global16(kp + (size_t)key * D + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < C::VPT; ++it) {
+      const int c = tid + it * C::NT;
+      if (C::VCH % C::NT == 0 || c < C::VCH) {
+        const int r = c / (DV / 8), cc = c % (DV / 8);
+        const int key = k0 + r;
+        vr[it] = key < a.Lk ? ld_global16(vp + (size_t)key * DV + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < C::KPT; ++it) {
+      const int c = tid + it * C::NT;
+      if (C::KCH % C::NT == 0 || c < C::KCH) {
+        const int r = c / (D / 8), cc = c % (D / 8);
+        *reinterpret_cast<u32x4*>(&Ks[r * C::KST + cc * 8]) = kr[it];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < C::VPT; ++it) {
+      const int c = tid + it * C::NT;
+      if (C::VCH % C::NT == 0 || c < C::VCH) {
+        const int r = c / (DV / 8), cc = c % (DV / 8);
+        *reinterpret_cast<u32x4*>(&Vs[r * C::VST + cc * 8]) = vr[it];
+      }
+    }
+  };
+
+  // transpose-read provider coordinates (see lds_read_tr16)
+  const int tr_e = (lane & 15) >> 2;
+  const int tr_c = lane & 3;
+  const int tr_dv = ((lane >> 4) * 16) % MF + 4 * tr_c;
+
+  if (ntiles > 0) load_tile(0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * BN;
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (t + 1 < ntiles) load_tile(k0 + BN);
+    if (!wave_live || k0 >= w_kend) continue;
+    const bool full = k0 + BN <= w_kfull;
+
+    // S^T = K Q^T
+    acc_t s[C::NSB];
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb) {
+      acc_t acc = acc_t{};
+#pragma unroll
+      for (int c = 0; c < C::NQC; ++c) {
+        const u32x4 kop = *reinterpret_cast<const u32x4*>(&Ks[(nb * MF + col) * C::KST + c * C::KW + kg * 8]);
+        acc = mma16<E, MF>(kop, qop[c], acc);
+      }
+      s[nb] = acc;
+    }
+
+    float mx = -INFINITY;
+    if (full) {
+#pragma unroll
+      for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+        for (int i = 0; i < ACC; ++i) mx = fmaxf(mx, s[nb][i]);
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+        for (int i = 0; i < ACC; ++i) {
+          const int key = k0 + nb * MF + acc_row<MF>(i, kg);
+          bool vis = key < a.Lk && iq < a.Lq;
+          if (a.mask_kind == kMaskCausal) vis = vis && key <= iq + shift;
+          else if (a.mask_kind == kMaskBool) vis = vis && mrow[key] != 0;
+          if (!vis) s[nb][i] = -INFINITY;
+          mx = fmaxf(mx, s[nb][i]);
+        }
+    }
+    mx = row_max<MF>(mx);
+    const float tmax = (mx == -INFINITY) ? -INFINITY : mx * a.c;
+    softmax_rebase<C::NDB>(tmax, m, l, o);
+    const float mu = (m == -INFINITY) ? 0.0f : m;
+
+    uint32_t pk[C::NSB * ACC / 2];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+      for (int i = 0; i < ACC; i += 2) {
+        const float p0 = fast_exp2(fmaf(s[nb][i], a.c, -mu));
+        const float p1 = fast_exp2(fmaf(s[nb][i + 1], a.c, -mu));
+        lsum += p0 + p1;
+        pk[(nb * ACC + i) / 2] = pack2<E>(p0, p1);
+      }
+    l += lsum;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int t8 = 0; t8 < C::NPV; ++t8) {
+      const u32x4 pb = {pk[4 * t8], pk[4 * t8 + 1], pk[4 * t8 + 2], pk[4 * t8 + 3]};
+      const int keyA = ((8 * t8) / ACC) * MF + acc_row<MF>((8 * t8) % ACC, kg);
+      const int keyB = ((8 * t8 + 4) / ACC) * MF + acc_row<MF>((8 * t8 + 4) % ACC, kg);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const u32x2 ra = lds_read_tr16(&Vs[(keyA + tr_e) * C::VST + db * MF + tr_dv]);
+        const u32x2 rb = lds_read_tr16(&Vs[(keyB + tr_e) * C::VST + db * MF + tr_dv]);
+        const u32x4 va = {ra[0], ra[1], rb[0], rb[1]};
+        o[db] = mma16<E, MF>(va, pb, o[db]);
+      }
+    }
+  }
+
+  if (!wave_live) return;
+  float lt = row_sum<MF>(l);
+  if (has_sink) lt += fast_exp2(sink2 - m);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (iq >= a.Lq) return;
+  uint16_t* op = (uint16_t*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq) * DV;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < ACC / 4; ++g4) {
+      const int dv = db * MF + g4 * 4 * C::KG + kg * 4;
+      if (dv < DV) {
+        const u32x2 st = {pack2<E>(o[db][g4 * 4 + 0] * inv, o[db][g4 * 4 + 1] * inv),
+                          pack2<E>(o[db][g4 * 4 + 2] * inv, o[db][g4 * 4 + 3] * inv)};
+        st_global8(op + dv, st);
+      }
+    }
+}
+
+// float32 inputs: the same walk on f32 MFMA (32x32x2 / 16x16x4), one k-element per lane.
+template <int MF, int D, int DV, int BN, int NW>
+struct PrefillCfgF32 {
+  static constexpr int KWF = Mfma<MF>::KWF, ACC = Mfma<MF>::ACC, KG = Mfma<MF>::KG;
+  static constexpr int DVP = (DV + MF - 1) / MF * MF;
+  static constexpr int KST = D + 1;
+  static constexpr int VST = DVP + MF;
+  static constexpr int NQS = D / KWF;
+  static constexpr int NSB = BN / MF;
+  static constexpr int NDB = DVP / MF;
+  static constexpr int NT = NW * 64;
+  static constexpr int KCH = BN * D / 4, VCH = BN * DV / 4;
+  static constexpr int KPT = (KCH + NT - 1) / NT, VPT = (VCH + NT - 1) / NT;
+  static constexpr int LDS_ELEMS = BN * KST + BN * VST;
+  static_assert(D % KWF == 0 && BN % MF == 0, "shape");
+};
+
+template <int MF, int D, int DV, int BN, int NW>
+__global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
+  using C = PrefillCfgF32<MF, D, DV, BN, NW>;
+  using acc_t = typename Mfma<MF>::acc_t;
+  constexpr int ACC = C::ACC;
+  __shared__ __attribute__((aligned(16))) float lds[C::LDS_ELEMS];
+  float* Ks = lds;
+  float* Vs = lds + BN * C::KST;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int col = lane % MF;
+  const int kg = lane / MF;
+
+  const int heads = a.Hq * a.B / a.head_blocks;
+  const int wph = NW / heads;
+  const int bm = wph * MF;
+  const int qb = a.nqb - 1 - (int)blockIdx.y;
+  const int groups_per_b = a.Hq / heads;
+  const int b = (int)blockIdx.x / groups_per_b;
+  const int h0 = ((int)blockIdx.x % groups_per_b) * heads;
+  const int hkv = h0 / a.group;
+  const int h = h0 + w / wph;
+  const int wi0 = qb * bm + (w % wph) * MF;
+  const int iq = wi0 + col;
+  const int shift = a.Lk - a.Lq;
+
+  int kend = a.Lk;
+  if (a.mask_kind == kMaskCausal) kend = min(a.Lk, min(qb * bm + bm, a.Lq) - 1 + shift + 1);
+  if (kend < 0) kend = 0;
+  const int ntiles = (kend + BN - 1) / BN;
+
+  const bool wave_live = wi0 < a.Lq;
+  const int w_last = min(wi0 + MF, a.Lq) - 1;
+  int w_kend = a.Lk, w_kfull = a.Lk;
+  if (a.mask_kind == kMaskCausal) {
+    w_kend = min(a.Lk, w_last + shift + 1);
+    w_kfull = min(a.Lk, wi0 + shift + 1);
+  } else if (a.mask_kind == kMaskBool) {
+    w_kfull = 0;
+  }
+
+  const float* qp = (const float*)a.q + ((size_t)(b * a.Hq + h) * a.Lq + iq) * D;
+  float qop[C::NQS];
+#pragma unroll
+  for (int s = 0; s < C::NQS; ++s) {
+    uint32_t x = 0u;
+    if (iq < a.Lq) x = __float_as_uint(qp[s * C::KWF + kg]);
+    qop[s] = __uint_as_float(x ^ a.qsign);
+  }
+
+  if constexpr (C::DVP > DV) {
+    for (int e = tid; e < BN * (C::DVP - DV); e += C::NT) {
+      const int r = e / (C::DVP - DV), cc = DV + e % (C::DVP - DV);
+      Vs[r * C::VST + cc] = 0.0f;
+    }
+  }
+
+  acc_t o[C::NDB];
+#pragma unroll
+  for (int d = 0; d < C::NDB; ++d) o[d] = acc_t{};
+  float m = -INFINITY, l = 0.0f, sink2 = 0.0f;
+  const bool has_sink = a.sinks != nullptr;
+  if (has_sink) {
+    sink2 = ((const float*)a.sinks)[h] * kLog2e;
+    m = sink2;
+  }
+
+  const float* kp = (const float*)a.k + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * D;
+  const float* vp = (const float*)a.v + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * DV;
+  const uint8_t* mrow = a.mask + (size_t)iq * a.Lk;
+
+  u32x4 kr[C::KPT], vr[C::VPT];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < C::KPT; ++it) {
+      const int c = tid + it * C::NT;
+      if (C::KCH % C::NT == 0 || c < C::KCH) {
+        const int r = c / (D / 4), cc = c % (D / 4);
+        const int key = k0 + r;
+        kr[it] = key < a.Lk ? ld_global16(kp + (size_t)key * D + cc * 4) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < C::VPT; ++it) {
+      const int c = tid + it * C::NT;
+      if (C::VCH % C::NT == 0 || c < C::VCH) {
+        const int r = c / (DV / 4), cc = c % (DV / 4);
+        const int key = k0 + r;
+        vr[it] = key < a.Lk ? ld_global16(vp + (size_t)key * DV + cc * 4) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < C::KPT; ++it) {
+      const int c = tid + it * C::NT;
+      if (C::KCH % C::NT == 0 || c < C::KCH) {
+        const int r = c / (D / 4), cc = c % (D / 4);
+        float* dst = &Ks[r * C::KST + cc * 4];   // odd row stride: scalar stores
+        dst[0] = __uint_as_float(kr[it][0]);
+        dst[1] = __uint_as_float(kr[it][1]);
+        dst[2] = __uint_as_float(kr[it][2]);
+        dst[3] = __uint_as_float(kr[it][3]);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < C::VPT; ++it) {
+      const int c = tid + it * C::NT;
+      if (C::VCH % C::NT == 0 || c < C::VCH) {
+        const int r = c / (DV / 4), cc = c % (DV / 4);
+        *reinterpret_cast<u32x4*>(&Vs[r * C::VST + cc * 4]) = vr[it];
+      }
+    }
+  };
+
+  if (ntiles > 0) load_tile(0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * BN;
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (t + 1 < ntiles) load_tile(k0 + BN);
+    if (!wave_live || k0 >= w_kend) continue;
+    const bool full = k0 + BN <= w_kfull;
+
+    acc_t s[C::NSB];
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb) {
+      acc_t acc = acc_t{};
+#pragma unroll
+      for (int st = 0; st < C::NQS; ++st)
+        acc = mma_f32<MF>(Ks[(nb * MF + col) * C::KST + st * C::KWF + kg], qop[st], acc);
+      s[nb] = acc;
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+      for (int i = 0; i < ACC; ++i) {
+        if (!full) {
+          const int key = k0 + nb * MF + acc_row<MF>(i, kg);
+          bool vis = key < a.Lk && iq < a.Lq;
+          if (a.mask_kind == kMaskCausal) vis = vis && key <= iq + shift;
+          else if (a.mask_kind == kMaskBool) vis = vis && mrow[key] != 0;
+          if (!vis) s[nb][i] = -INFINITY;
+        }
+        mx = fmaxf(mx, s[nb][i]);
+      }
+    mx = row_max<MF>(mx);
+    const float tmax = (mx == -INFINITY) ? -INFINITY : mx * a.c;
+    softmax_rebase<C::NDB>(tmax, m, l, o);
+    const float mu = (m == -INFINITY) ? 0.0f : m;
+
+    float lsum = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+      for (int i = 0; i < ACC; ++i) {
+        const float p = fast_exp2(fmaf(s[nb][i], a.c, -mu));
+        s[nb][i] = p;
+        lsum += p;
+      }
+    l += lsum;
+
+    // O^T += V^T P^T, one key per lane k-group and instruction
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+      for (int i = 0; i < ACC; ++i) {
+        const int key = nb * MF + acc_row<MF>(i, kg);
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+          o[db] = mma_f32<MF>(Vs[key * C::VST + db * MF + col], s[nb][i], o[db]);
+      }
+  }
+
+  if (!wave_live) return;
+  float lt = row_sum<MF>(l);
+  if (has_sink) lt += fast_exp2(sink2 - m);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (iq >= a.Lq) return;
+  float* op = (float*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq) * DV;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < ACC / 4; ++g4) {
+      const int dv = db * MF + g4 * 4 * C::KG + kg * 4;
+      if (dv < DV) {
+        const f32x4 st = {o[db][g4 * 4 + 0] * inv, o[db][g4 * 4 + 1] * inv,
+                          o[db][g4 * 4 + 2] * inv, o[db][g4 * 4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(op + dv) = st;
+      }
+    }
+}
+
+}  // namespace sdpa

@@ -1,0 +1,348 @@
+// The C ABI (include/sdpa.h): argument validation, the router between the
+// prefill and decode kernels, decode scratch, and the launches.
+//
+// The router keeps the shape of the rules in nuvec-core
+// "tests/attention_plan.rs" (a fused tiled kernel for many queries; for few
+// queries a vector kernel split over key partitions in two passes, with more
+// partitions as the key count grows), with thresholds set for gfx950: one
+// wavefront carries one MFMA tile of query rows, so the decode route applies
+// while Lq <= 8 and the (Hq/Hkv) x Lq rows that read one kv head fit in a
+// 32-row tile.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/sdpa.h"
+#include "kernels.h"
+
+namespace sdpa {
+
+hipError_t launch_prefill_16(int elem, int D, int Dv, const PrefillShape& s, const FwdArgs& a,
+                             hipStream_t stream, bool* ok);
+hipError_t launch_prefill_f32(int D, int Dv, const PrefillShape& s, const FwdArgs& a, hipStream_t stream,
+                              bool* ok);
+
+hipError_t launch_prefill(int elem, int D, int Dv, const PrefillShape& s, const FwdArgs& a,
+                          hipStream_t stream, bool* ok) {
+  if (elem == kF32) return launch_prefill_f32(D, Dv, s, a, stream, ok);
+  return launch_prefill_16(elem, D, Dv, s, a, stream, ok);
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(256) zero_fill_kernel(u32x4_t* out, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    out[i] = u32x4_t{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_zero_fill(void* out, int64_t bytes, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > (1 << 20)) blocks = 1 << 20;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (u32x4_t*)out, n16);
+  return hipGetLastError();
+}
+
+}  // namespace sdpa
+
+using namespace sdpa;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+bool mul3(int64_t a, int64_t b, int64_t c, int64_t* r) {
+  int64_t t;
+  if (__builtin_mul_overflow(a, b, &t)) return false;
+  return !__builtin_mul_overflow(t, c, r);
+}
+bool mul4(int64_t a, int64_t b, int64_t c, int64_t d, int64_t* r) {
+  int64_t t;
+  if (!mul3(a, b, c, &t)) return false;
+  return !__builtin_mul_overflow(t, d, r);
+}
+
+int64_t gcd64(int64_t a, int64_t b) {
+  while (b) {
+    int64_t t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+int64_t pow2_floor(int64_t x) {
+  int64_t p = 1;
+  while (p * 2 <= x) p *= 2;
+  return p;
+}
+
+const int64_t kMaxLen = INT_MAX - 4096;  // positions are 32-bit inside the kernels
+const int64_t kMaxGridYZ = 65535;
+
+int elem_size(int dtype) { return dtype == SDPA_F32 ? 4 : 2; }
+
+// Validation shared by sdpa_plan and sdpa_forward; fills `plan` on success.
+int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D, int64_t Dv,
+                      int mask_kind, bool has_mask, bool has_sinks, int dtype, sdpa_plan_t* plan) {
+  (void)has_sinks;
+  if (B < 0) return fail(SDPA_ERR_INVALID, "B must be >= 0 (got %lld)", (long long)B);
+  if (Hq < 0) return fail(SDPA_ERR_INVALID, "Hq must be >= 0 (got %lld)", (long long)Hq);
+  if (Hkv < 0) return fail(SDPA_ERR_INVALID, "Hkv must be >= 0 (got %lld)", (long long)Hkv);
+  if (Lq < 0) return fail(SDPA_ERR_INVALID, "Lq must be >= 0 (got %lld)", (long long)Lq);
+  if (Lk < 0) return fail(SDPA_ERR_INVALID, "Lk must be >= 0 (got %lld)", (long long)Lk);
+  if (D < 0) return fail(SDPA_ERR_INVALID, "D must be >= 0 (got %lld)", (long long)D);
+  if (Dv < 0) return fail(SDPA_ERR_INVALID, "Dv must be >= 0 (got %lld)", (long long)Dv);
+  if (dtype != SDPA_F32 && dtype != SDPA_F16 && dtype != SDPA_BF16)
+    return fail(SDPA_ERR_INVALID, "dtype must be SDPA_F32, SDPA_F16 or SDPA_BF16 (got %d)", dtype);
+  if (mask_kind != SDPA_MASK_NONE && mask_kind != SDPA_MASK_CAUSAL && mask_kind != SDPA_MASK_BOOL)
+    return fail(SDPA_ERR_INVALID, "mask_kind must be 0 (none), 1 (causal) or 2 (bool) (got %d)", mask_kind);
+  if (mask_kind == SDPA_MASK_BOOL && !has_mask)
+    return fail(SDPA_ERR_INVALID, "mask_kind is SDPA_MASK_BOOL but mask is NULL");
+  if (Hkv == 0 && Hq != 0) return fail(SDPA_ERR_INVALID, "Hkv must be positive when Hq (%lld) is", (long long)Hq);
+  if (Hkv != 0 && Hq % Hkv != 0)
+    return fail(SDPA_ERR_INVALID, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+  int64_t n;
+  const int64_t es = elem_size(dtype);
+  if (!mul4(B, Hq, Lq, D, &n) || __builtin_mul_overflow(n, es, &n))
+    return fail(SDPA_ERR_INVALID, "shape overflow: B*Hq*Lq*D bytes do not fit in 64 bits");
+  if (!mul4(B, Hkv, Lk, D, &n) || __builtin_mul_overflow(n, es, &n))
+    return fail(SDPA_ERR_INVALID, "shape overflow: B*Hkv*Lk*D bytes do not fit in 64 bits");
+  if (!mul4(B, Hkv, Lk, Dv, &n) || __builtin_mul_overflow(n, es, &n))
+    return fail(SDPA_ERR_INVALID, "shape overflow: B*Hkv*Lk*Dv bytes do not fit in 64 bits");
+  if (!mul4(B, Hq, Lq, Dv, &n) || __builtin_mul_overflow(n, es, &n))
+    return fail(SDPA_ERR_INVALID, "shape overflow: B*Hq*Lq*Dv bytes do not fit in 64 bits");
+  if (!mul3(Lq, Lk, 1, &n)) return fail(SDPA_ERR_INVALID, "shape overflow: Lq*Lk mask bytes do not fit in 64 bits");
+  if (!head_pair_supported(D, Dv))
+    return fail(SDPA_ERR_UNSUPPORTED,
+                "head sizes (D=%lld, Dv=%lld) are not built; supported: (64,64) (80,80) (96,96) (128,128) "
+                "(192,192) (256,256) (512,512) (96,64) (192,128)",
+                (long long)D, (long long)Dv);
+
+  sdpa_plan_t p;
+  memset(&p, 0, sizeof p);
+  if (B == 0 || Hq == 0 || Lq == 0) {
+    p.route = SDPA_ROUTE_EMPTY;
+    *plan = p;
+    return SDPA_OK;
+  }
+  if (Lq > kMaxLen) return fail(SDPA_ERR_UNSUPPORTED, "Lq (%lld) exceeds %lld", (long long)Lq, (long long)kMaxLen);
+  if (Lk > kMaxLen) return fail(SDPA_ERR_UNSUPPORTED, "Lk (%lld) exceeds %lld", (long long)Lk, (long long)kMaxLen);
+  if (B * Hq > INT_MAX) return fail(SDPA_ERR_UNSUPPORTED, "B*Hq (%lld) exceeds INT_MAX", (long long)(B * Hq));
+  if (Lk == 0) {
+    p.route = SDPA_ROUTE_ZERO_FILL;
+    p.kernels = 1;
+    int64_t n16 = B * Hq * Lq * Dv * elem_size(dtype) / 16;
+    int64_t blocks = (n16 + 255) / 256;
+    p.grid[0] = blocks < 1 ? 1 : (blocks > (1 << 20) ? (1 << 20) : blocks);
+    p.grid[1] = p.grid[2] = 1;
+    *plan = p;
+    return SDPA_OK;
+  }
+  const int64_t group = Hq / Hkv;
+  if (dtype != SDPA_F32 && Lq <= 8 && group * Lq <= 32) {
+    const int64_t rows = group * Lq;
+    int64_t kps = pow2_floor(Lk / 64 > 0 ? Lk / 64 : 1);
+    if (kps < 64) kps = 64;
+    if (kps > 256) kps = 256;
+    const int64_t nsplit = (Lk + kps - 1) / kps;
+    p.route = SDPA_ROUTE_DECODE;
+    p.kernels = 2;
+    p.rows_per_wave = decode_mf((int)D, (int)rows);
+    p.waves = kDecodeWaves;
+    p.block_n = kDecodeBN;
+    p.heads_per_group = (int32_t)group;
+    p.keys_per_split = kps;
+    p.splits = nsplit;
+    p.grid[0] = (nsplit + kDecodeWaves - 1) / kDecodeWaves;
+    p.grid[1] = Hkv;
+    p.grid[2] = B;
+    if (Hkv > kMaxGridYZ || B > kMaxGridYZ)
+      return fail(SDPA_ERR_UNSUPPORTED, "decode grid: Hkv (%lld) and B (%lld) must be <= 65535", (long long)Hkv,
+                  (long long)B);
+    int64_t sb;
+    if (!mul4(B * Hkv, nsplit, rows, (Dv + 4) * 4, &sb))
+      return fail(SDPA_ERR_INVALID, "decode scratch size overflows");
+    p.scratch_bytes = sb;
+    *plan = p;
+    return SDPA_OK;
+  }
+  const int mf = prefill_mf(dtype, (int)D, (int)Dv);
+  const int64_t heads = gcd64(group, kPrefillWaves);
+  const int64_t bm = (kPrefillWaves / heads) * mf;
+  const int64_t nqb = (Lq + bm - 1) / bm;
+  if (nqb > kMaxGridYZ)
+    return fail(SDPA_ERR_UNSUPPORTED, "Lq (%lld) needs %lld query blocks; at most 65535 are supported", (long long)Lq,
+                (long long)nqb);
+  p.route = SDPA_ROUTE_PREFILL;
+  p.kernels = 1;
+  p.rows_per_wave = mf;
+  p.waves = kPrefillWaves;
+  p.block_n = prefill_bn(dtype, (int)D, (int)Dv);
+  p.heads_per_group = (int32_t)heads;
+  p.grid[0] = B * Hq / heads;
+  p.grid[1] = nqb;
+  p.grid[2] = 1;
+  *plan = p;
+  return SDPA_OK;
+}
+
+struct ScratchEntry {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, ScratchEntry> g_scratch;
+
+hipError_t get_scratch(hipStream_t stream, size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_mu);
+  ScratchEntry& s = g_scratch[std::make_pair(dev, stream)];
+  if (s.bytes < bytes) {
+    if (s.ptr) {
+      e = hipFreeAsync(s.ptr, stream);
+      s.ptr = nullptr;
+      s.bytes = 0;
+      if (e != hipSuccess) return e;
+    }
+    const size_t want = (bytes + (size_t(1) << 20) - 1) & ~((size_t(1) << 20) - 1);
+    e = hipMallocAsync(&s.ptr, want, stream);
+    if (e != hipSuccess) {
+      s.ptr = nullptr;
+      return e;
+    }
+    s.bytes = want;
+  }
+  *out = s.ptr;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_abi_version(void) { return 1; }
+
+const char* sdpa_last_error(void) { return g_err.c_str(); }
+
+int sdpa_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D, int64_t Dv, int mask_kind,
+              int has_mask, int has_sinks, int dtype, sdpa_plan_t* plan) {
+  g_err.clear();
+  if (!plan) return fail(SDPA_ERR_INVALID, "plan must not be NULL");
+  sdpa_plan_t p;
+  const int rc = validate_and_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, has_mask != 0, has_sinks != 0, dtype, &p);
+  if (rc == SDPA_OK) *plan = p;
+  return rc;
+}
+
+int sdpa_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t Hq, int64_t Hkv,
+                 int64_t Lq, int64_t Lk, int64_t D, int64_t Dv, float scale, int mask_kind, const uint8_t* mask,
+                 const void* sinks, int dtype, void* stream_v) {
+  g_err.clear();
+  sdpa_plan_t p;
+  int rc = validate_and_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, mask != nullptr, sinks != nullptr, dtype, &p);
+  if (rc != SDPA_OK) return rc;
+  if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID, "scale must be finite (got %g)", (double)scale);
+  if (p.route == SDPA_ROUTE_EMPTY) return SDPA_OK;
+  if (!out) return fail(SDPA_ERR_INVALID, "out must not be NULL");
+  if (!q) return fail(SDPA_ERR_INVALID, "q must not be NULL");
+  if (((uintptr_t)out | (uintptr_t)q) & 15)
+    return fail(SDPA_ERR_INVALID, "q and out must be 16-byte aligned");
+  hipStream_t stream = (hipStream_t)stream_v;
+  hipError_t e;
+  if (p.route == SDPA_ROUTE_ZERO_FILL) {
+    e = launch_zero_fill(out, B * Hq * Lq * Dv * elem_size(dtype), stream);
+    if (e != hipSuccess) return fail(SDPA_ERR_HIP, "zero-fill launch failed: %s", hipGetErrorString(e));
+    return SDPA_OK;
+  }
+  if (!k || !v) return fail(SDPA_ERR_INVALID, "k and v must not be NULL");
+  if (((uintptr_t)k | (uintptr_t)v) & 15) return fail(SDPA_ERR_INVALID, "k and v must be 16-byte aligned");
+
+  FwdArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.mask = mask_kind == SDPA_MASK_BOOL ? mask : nullptr;
+  a.sinks = sinks;
+  a.B = (int)B;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.Lq = (int)Lq;
+  a.Lk = (int)Lk;
+  a.group = (int)(Hq / Hkv);
+  a.mask_kind = mask_kind;
+  // scores are used in base 2; a zero scale becomes the smallest normal float,
+  // which leaves every finite score's weight at exactly exp2(0) = 1
+  a.c = fmaxf(fabsf(scale) * 1.4426950408889634f, FLT_MIN);
+  a.qsign = scale < 0.0f ? (dtype == SDPA_F32 ? 0x80000000u : 0x80008000u) : 0u;
+
+  bool ok = false;
+  if (p.route == SDPA_ROUTE_DECODE) {
+    a.rows = (int)(a.group * Lq);
+    a.kps = (int)p.keys_per_split;
+    a.nsplit = (int)p.splits;
+    void* part = nullptr;
+    e = get_scratch(stream, (size_t)p.scratch_bytes, &part);
+    if (e != hipSuccess) return fail(SDPA_ERR_HIP, "decode scratch allocation failed: %s", hipGetErrorString(e));
+    a.part = (float*)part;
+    DecodeShape s{p.rows_per_wave, p.waves, p.block_n};
+    e = launch_decode(dtype, (int)D, (int)Dv, s, a, stream, &ok);
+  } else {
+    a.nqb = (int)p.grid[1];
+    a.head_blocks = (int)p.grid[0];
+    PrefillShape s{p.rows_per_wave, p.waves, p.heads_per_group, p.block_n,
+                   (int)((p.waves / p.heads_per_group) * p.rows_per_wave)};
+    e = launch_prefill(dtype, (int)D, (int)Dv, s, a, stream, &ok);
+  }
+  if (!ok) return fail(SDPA_ERR_UNSUPPORTED, "no kernel built for dtype %d, D=%lld, Dv=%lld", dtype, (long long)D,
+                       (long long)Dv);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SDPA_OK;
+}
+
+int sdpa_release_workspace(void) {
+  g_err.clear();
+  std::lock_guard<std::mutex> lock(g_mu);
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  int rc = SDPA_OK;
+  for (auto& kv : g_scratch) {
+    if (!kv.second.ptr) continue;
+    hipError_t e = hipSetDevice(kv.first.first);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipFree(kv.second.ptr);
+    if (e != hipSuccess && rc == SDPA_OK) rc = fail(SDPA_ERR_HIP, "releasing scratch: %s", hipGetErrorString(e));
+    kv.second.ptr = nullptr;
+    kv.second.bytes = 0;
+  }
+  g_scratch.clear();
+  (void)hipSetDevice(cur);
+  return rc;
+}
+
+}  // extern "C"

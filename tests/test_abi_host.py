@@ -1,0 +1,153 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/sdpa.h declares, and sdpa_plan validates and routes as
+documented (errors are return codes with a message naming the argument)."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+import threading
+
+import pytest
+
+import scaled_dot_product_06_amd as sd
+from scaled_dot_product_06_amd import inputs as gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdpa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(sdpa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert _declared_functions() == sorted(sd.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(sd.library_path())
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert sd.sdpa_abi_version() == 1
+    out = subprocess.run(["nm", "-D", "--defined-only", sd.library_path()], capture_output=True, text=True).stdout
+    for name in _declared_functions():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), f"{name} not exported with C linkage"
+
+
+def _plan(B=1, Hq=8, Hkv=2, Lq=128, Lk=128, D=128, Dv=128, mask=0, has_mask=None, sinks=0, dtype=2):
+    if has_mask is None:
+        has_mask = mask == 2
+    return sd.sdpa_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask, has_mask, sinks, dtype, check=False)
+
+
+@pytest.mark.parametrize("number,route", [(1, "prefill"), (2, "decode"), (3, "prefill"), (4, "prefill"),
+                                          (5, "decode")])
+def test_workload_routes(number, route):
+    w = gen.WORKLOADS[number]
+    p = sd.sdpa_plan(w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], w["D"], w["Dv"], w["mask_kind"],
+                     w["mask_kind"] == 2, w["sinks"], w["dtype"])
+    assert p["route"] == route
+    if route == "decode":
+        assert p["kernels"] == 2
+        rows = w["Hq"] // w["Hkv"] * w["Lq"]
+        assert p["splits"] * p["keys_per_split"] >= w["Lk"] > (p["splits"] - 1) * p["keys_per_split"]
+        assert p["scratch_bytes"] == w["B"] * w["Hkv"] * p["splits"] * rows * (w["Dv"] + 4) * 4
+        assert p["grid"] == ((p["splits"] + p["waves"] - 1) // p["waves"], w["Hkv"], w["B"])
+    else:
+        assert p["kernels"] == 1 and p["scratch_bytes"] == 0
+        rows_per_block = p["waves"] // p["heads_per_group"] * p["rows_per_wave"]
+        assert p["grid"][1] == -(-w["Lq"] // rows_per_block)
+        assert p["grid"][0] * p["heads_per_group"] == w["B"] * w["Hq"]
+
+
+def test_decode_split_size_depends_on_keys_not_batch():
+    a = _plan(B=1, Hq=32, Hkv=4, Lq=1, Lk=20000)
+    b = _plan(B=7, Hq=32, Hkv=4, Lq=1, Lk=20000)
+    assert a["keys_per_split"] == b["keys_per_split"] and a["splits"] == b["splits"]
+
+
+def test_routing_thresholds():
+    assert _plan(Lq=8, Hq=4, Hkv=1)["route"] == "decode"        # 32 rows
+    assert _plan(Lq=9, Hq=4, Hkv=1)["route"] == "prefill"       # more than 8 queries
+    assert _plan(Lq=5, Hq=8, Hkv=1)["route"] == "prefill"       # 40 rows do not fit a tile
+    assert _plan(Lq=1, dtype=0)["route"] == "prefill"           # f32 always tiles
+
+
+def test_empty_and_keyless_routes():
+    assert _plan(Lq=0)["route"] == "empty"
+    assert _plan(B=0)["route"] == "empty"
+    assert _plan(Hq=0, Hkv=0)["route"] == "empty"
+    p = _plan(Lk=0, mask=1, sinks=1)
+    assert p["route"] == "zero_fill" and p["kernels"] == 1
+
+
+@pytest.mark.parametrize("kwargs,code,needle", [
+    (dict(Hq=3, Hkv=2), -1, "multiple of Hkv"),
+    (dict(Hq=4, Hkv=0), -1, "Hkv"),
+    (dict(B=-1), -1, "B must be"),
+    (dict(Lk=-5), -1, "Lk must be"),
+    (dict(dtype=3), -1, "dtype"),
+    (dict(mask=3), -1, "mask_kind"),
+    (dict(mask=2, has_mask=False), -1, "mask is NULL"),
+    (dict(D=100, Dv=100), -2, "head sizes"),
+    (dict(D=128, Dv=64), -2, "head sizes"),
+    (dict(B=1 << 40, Hq=1 << 20, Hkv=1 << 20, Lq=1 << 20), -1, "overflow"),
+])
+def test_invalid_arguments_are_rejected(kwargs, code, needle):
+    rc = _plan(**kwargs)
+    assert rc == code
+    assert needle in sd.sdpa_last_error()
+
+
+def test_forward_validates_before_touching_memory():
+    # No GPU needed: every one of these fails validation before any HIP call.
+    f = sd.sdpa_forward
+    assert f(None, None, None, None, 1, 3, 2, 4, 4, 64, 64, 0.1, 0, None, None, 2, None, check=False) == -1
+    assert "multiple" in sd.sdpa_last_error()
+    assert f(None, None, None, None, 1, 2, 2, 4, 4, 64, 64, float("nan"), 0, None, None, 2, None,
+             check=False) == -1
+    assert "scale" in sd.sdpa_last_error()
+    assert f(None, None, None, None, 1, 2, 2, 4, 4, 64, 64, 0.1, 2, None, None, 2, None, check=False) == -1
+    assert "mask" in sd.sdpa_last_error()
+    assert f(None, None, None, None, 1, 2, 2, 4, 4, 64, 64, 0.1, 0, None, None, 2, None, check=False) == -1
+    assert "NULL" in sd.sdpa_last_error()
+    assert f(16, 16, 16, 8, 1, 2, 2, 4, 4, 64, 64, 0.1, 0, None, None, 2, None, check=False) == -1
+    assert "aligned" in sd.sdpa_last_error()
+    # an empty call is a successful no-op, even with null pointers
+    assert f(None, None, None, None, 1, 2, 2, 0, 4, 64, 64, 0.1, 0, None, None, 2, None, check=False) == 0
+
+
+def test_plans_are_pure_across_repeats_and_threads():
+    cases = [dict(Lq=1, Lk=65537, Hq=16, Hkv=2, D=256, Dv=256), dict(Lq=4096, Lk=4096, Hq=32, Hkv=8),
+             dict(Lq=1024, Lk=1801, Hq=16, Hkv=2, D=256, Dv=256, mask=2, sinks=1, dtype=1)]
+    first = [_plan(**c) for c in cases]
+    for _ in range(100):
+        assert [_plan(**c) for c in cases] == first
+    got = []
+    t = threading.Thread(target=lambda: got.extend(_plan(**c) for c in cases))
+    t.start()
+    t.join()
+    assert got == first
+    code = ("import scaled_dot_product_06_amd as sd, json; "
+            f"print(json.dumps([sd.sdpa_plan(*a) for a in {[(1, c.get('Hq', 8), c.get('Hkv', 2), c.get('Lq', 128), c.get('Lk', 128), c.get('D', 128), c.get('Dv', 128), c.get('mask', 0), c.get('mask', 0) == 2, c.get('sinks', 0), c.get('dtype', 2)) for c in cases]}]))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert out.returncode == 0, out.stderr
+    import json
+    other = json.loads(out.stdout)
+    for a, b in zip(other, first):
+        b = dict(b)
+        b["grid"] = list(b["grid"])
+        assert a == b
+
+
+def test_errors_are_per_thread():
+    assert _plan(Hq=3, Hkv=2) == -1
+    msgs = []
+    t = threading.Thread(target=lambda: msgs.append(sd.sdpa_last_error()))
+    t.start()
+    t.join()
+    assert msgs == [""]
+    assert "multiple" in sd.sdpa_last_error()

@@ -1,0 +1,55 @@
+"""The seeded input generator: reproducible, counter-based, correctly rounded."""
+import numpy as np
+
+from scaled_dot_product_06_amd import inputs as gen
+
+
+def test_words_are_counter_based():
+    a = gen.words(3, 1, 0, 1000)
+    b = gen.words(3, 1, 500, 500)
+    assert np.array_equal(a[500:], b)
+    assert not np.array_equal(gen.words(3, 2, 0, 10), gen.words(3, 1, 0, 10))
+    assert not np.array_equal(gen.words(4, 1, 0, 10), gen.words(3, 1, 0, 10))
+
+
+def test_splitmix_finaliser_reference_value():
+    # splitmix64 finaliser of 0 and of 1 (Steele, Lea, Flood): mix(1) = 0x5692161d100b05e5
+    z = gen._mix64(np.array([0, 1], dtype=np.uint64))
+    assert int(z[0]) == 0
+    assert int(z[1]) == 0x5692161D100B05E5
+
+
+def test_uniform_range_and_moments():
+    x = gen.uniform_pm1(1, 1, 200000)
+    assert x.dtype == np.float32 and x.min() >= -1.0 and x.max() < 1.0
+    assert abs(x.mean()) < 0.01 and abs(x.var() - 1 / 3) < 0.01
+
+
+def test_normal_moments():
+    x = gen.normal(2, 3, 200000)
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 1) < 0.01
+    assert abs(np.mean(x ** 4) - 3) < 0.1
+
+
+def test_bernoulli_rate_and_forced_diagonal():
+    m = gen.diagonal_bool_mask(4, 1024, 1801)
+    assert m.shape == (1024, 1801)
+    assert abs(m.mean() - 0.9) < 0.005
+    assert np.all(m[np.arange(1024), np.arange(1024) + 777] == 1)
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -8 + 2 ** -20], np.float32)
+    b = gen.f32_to_bf16_bits(x)
+    back = gen.bf16_bits_to_f32(b)
+    # halfway cases go to even, others to nearest
+    assert back.tolist() == [1.0, 1.0, 1.0 + 2 ** -6, -2.5, 1.0 + 2 ** -7]
+
+
+def test_workload_shapes():
+    p = gen.workload(1)
+    assert p.q.shape == (1, 8, 128, 64) and p.q.dtype == np.float32
+    p = gen.workload(4)
+    assert p.q.dtype == np.float16 and p.sinks.shape == (16,) and p.mask.shape == (1024, 1801)
+    q, k, v, m, s = p.widened()
+    assert q.dtype == np.float64 and m.dtype == bool

@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward hot path on one MI355X.
+
+One step = one pass over the whole path on one batch of synthetic input:
+  * prefill: bf16 GQA causal prefill, B=2, Hq=32, Hkv=8, Lq=Lk=4096, D=Dv=128
+    (one sdpa_forward call, routed to the tiled MFMA kernel);
+  * decode:  bf16 GQA decode, B=4, Hq=16, Hkv=2, Lq=1, Lk=65537, D=Dv=256
+    (one sdpa_forward call, routed to the split-key kernel and its reduce).
+Inputs are resident in HBM before timing starts. The decode K/V alternates
+between two copies (1.07 GB together, over four times the 256 MB MALL) so that
+every decode step streams its K/V from HBM; prefill runs warm.
+
+`value` is prefill TFLOP/s (causal pairs only, 2 FLOP per multiply-add over
+QK^T and PV); the decode K/V GB/s sits in `decode`. Per-call kernel time is
+taken with HIP events on the stream the library launches on. The printed JSON
+line also carries the roofline fraction of the dominant kernel and the CPU
+float64 oracle timed on a bounded sample of the same prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PREFILL_WORKLOAD, DECODE_WORKLOAD = 3, 5
+
+
+def causal_pairs(Lq: int, Lk: int) -> int:
+    """Visible (query, key) pairs of a bottom-right aligned causal mask."""
+    total = 0
+    for i in range(Lq):
+        total += max(0, min(Lk, i + Lk - Lq + 1))
+    return total
+
+
+def prefill_flop(p) -> int:
+    pairs = causal_pairs(p.Lq, p.Lk) if p.mask_kind == 1 else p.Lq * p.Lk
+    return p.B * p.Hq * pairs * 2 * (p.D + p.Dv)
+
+
+def decode_bytes(p) -> int:
+    esize = 4 if p.dtype == 0 else 2
+    return p.B * p.Hkv * p.Lk * (p.D + p.Dv) * esize
+
+
+def _traffic_for(kernel_tag: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_tag)
+    except Exception:
+        return None
+    if not rec or rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "scaled_dot_product_06_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def cpu_baseline(p, seconds: float):
+    """Time the float64 oracle on whole heads of the prefill workload until
+    about `seconds` of CPU work; report algorithmic TFLOP/s."""
+    import numpy as np
+    from oracle import attention as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    q, k, v, m, s = p.widened()
+    group = p.Hq // p.Hkv
+    per_head = causal_pairs(p.Lq, p.Lk) * 2 * (p.D + p.Dv)
+    done = 0
+    t0 = time.perf_counter()
+    for h in range(p.Hq):
+        orc.sdpa(q[:1, h:h + 1], k[:1, h // group:h // group + 1], v[:1, h // group:h // group + 1],
+                 p.scale, p.mask_kind, m, None if s is None else s[h:h + 1])
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done * per_head / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {p.B * p.Hq} (batch, head) slices of the prefill workload, all {p.Lq} rows "
+                      f"each; numpy float64, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
+              f"multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import scaled_dot_product_06_amd as sd
+    from scaled_dot_product_06_amd import inputs as gen
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    def to_dev(a, dtype):
+        import numpy as np
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if dtype == gen.BF16 else torch.from_numpy(a)
+        return t.to(dev)
+
+    t0 = time.perf_counter()
+    pre = gen.workload(PREFILL_WORKLOAD)
+    dec = gen.workload(DECODE_WORKLOAD)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    pq, pk, pv = (to_dev(a, pre.dtype) for a in (pre.q, pre.k, pre.v))
+    pout = torch.empty((pre.B, pre.Hq, pre.Lq, pre.Dv), dtype=pq.dtype, device=dev)
+    dq = to_dev(dec.q, dec.dtype)
+    dk = [to_dev(dec.k, dec.dtype)]
+    dv = [to_dev(dec.v, dec.dtype)]
+    dk.append(dk[0].clone())
+    dv.append(dv[0].clone())
+    dout = torch.empty((dec.B, dec.Hq, dec.Lq, dec.Dv), dtype=dq.dtype, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        sd.attention(pq, pk, pv, pre.scale, pre.mask_kind, out=pout, stream=stream.cuda_stream)
+        sd.attention(dq, dk[i % 2], dv[i % 2], dec.scale, dec.mask_kind, out=dout, stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(K):
+            ev[i][0].record(stream)
+            sd.attention(pq, pk, pv, pre.scale, pre.mask_kind, out=pout, stream=stream.cuda_stream)
+            ev[i][1].record(stream)
+            sd.attention(dq, dk[i % 2], dv[i % 2], dec.scale, dec.mask_kind, out=dout,
+                         stream=stream.cuda_stream)
+            ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / K
+
+    flop = prefill_flop(pre)
+    nbytes = decode_bytes(dec)
+    tflops = flop / (pre_ms * 1e-3) / 1e12
+    gbps = nbytes / (dec_ms * 1e-3) / 1e9
+    log(f"prefill {pre_ms * 1e3:.1f} us/call = {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of "
+        f"bf16 MFMA peak); decode {dec_ms * 1e3:.1f} us/call = {gbps:.0f} GB/s "
+        f"({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM peak); step {step_ms:.3f} ms; wall {wall:.2f} s")
+
+    pre_plan = sd.sdpa_plan(pre.B, pre.Hq, pre.Hkv, pre.Lq, pre.Lk, pre.D, pre.Dv, pre.mask_kind, False, False,
+                            pre.dtype)
+    dec_plan = sd.sdpa_plan(dec.B, dec.Hq, dec.Hkv, dec.Lq, dec.Lk, dec.D, dec.Dv, dec.mask_kind, False, False,
+                            dec.dtype)
+    traffic_pre = _traffic_for("prefill")
+    traffic_dec = _traffic_for("decode")
+
+    result = {
+        "metric": "prefill TFLOP/s (% MFMA peak) + decode K/V GB/s (% HBM peak), 1 GPU",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based N(0,1) inputs, no dataset)",
+        "config": {
+            "workload": "bf16 GQA causal prefill B=2 Hq=32 Hkv=8 Lq=Lk=4096 D=Dv=128 + "
+                        "bf16 GQA decode B=4 Hq=16 Hkv=2 Lq=1 Lk=65537 D=Dv=256",
+            "prefill_flop_per_call": flop,
+            "decode_kv_bytes_per_call": nbytes,
+            "prefill_plan": pre_plan,
+            "decode_plan": dec_plan,
+        },
+        "decode": {
+            "value": round(gbps, 1), "unit": "GB/s", "us_per_call": round(dec_ms * 1e3, 2),
+            "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+        },
+        "roofline": {
+            "kernel": "prefill_kernel (bf16, 32x32x16 MFMA, D=128)",
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_pre,
+        },
+        "roofline_decode": {
+            "kernel": "decode_split_kernel + decode_reduce_kernel (bf16, D=256)",
+            "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "traffic": traffic_dec,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample of the prefill workload ...")
+        result["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

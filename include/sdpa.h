@@ -66,7 +66,8 @@ typedef struct sdpa_plan_t {
   int32_t block_n;        /* keys per tile */
   int32_t heads_per_group;/* prefill: query heads sharing one workgroup's K/V tiles;
                              decode: query heads packed into one wavefront (Hq/Hkv) */
-  int64_t keys_per_split; /* decode: keys per first-pass workgroup */
+  int64_t keys_per_split; /* decode: keys per first-pass workgroup (a power of two, 64..1024,
+                             from Lk alone so that batch items never change it) */
   int64_t splits;         /* decode: key blocks per (batch, kv head) */
   int64_t grid[3];        /* workgroups of the first kernel (x, y, z) */
   int64_t scratch_bytes;  /* device scratch the call uses, 0 for prefill; decode: per (batch, kv head,

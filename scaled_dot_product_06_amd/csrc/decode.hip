@@ -5,7 +5,7 @@ namespace sdpa {
 
 template <class E, int D, int DV>
 static hipError_t launch_one(const DecodeShape& s, const FwdArgs& a, hipStream_t stream) {
-  dim3 grid1((a.nsplit + kDecodeWaves - 1) / kDecodeWaves, a.Hkv, a.B);
+  dim3 grid1(a.nsplit, a.Hkv, a.B);
   if constexpr (D % 32 == 0) {
     if (s.mf == 16) {
       hipLaunchKernelGGL((decode_split_kernel<E, 16, D, DV, kDecodeWaves>), grid1, dim3(kDecodeWaves * 64), 0,
@@ -13,7 +13,7 @@ static hipError_t launch_one(const DecodeShape& s, const FwdArgs& a, hipStream_t
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       dim3 grid2(a.rows, a.Hkv, a.B);
-      hipLaunchKernelGGL((decode_reduce_kernel<E, DV>), grid2, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL((decode_reduce_kernel<E, DV>), grid2, dim3(256), 0, stream, a);
       return hipGetLastError();
     }
   }
@@ -22,7 +22,7 @@ static hipError_t launch_one(const DecodeShape& s, const FwdArgs& a, hipStream_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid2(a.rows, a.Hkv, a.B);
-  hipLaunchKernelGGL((decode_reduce_kernel<E, DV>), grid2, dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((decode_reduce_kernel<E, DV>), grid2, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -1,20 +1,23 @@
 // Decode: split-key two-pass attention for few query rows per key/value head.
 //
-// First pass (decode_split_kernel): one wavefront per (batch, kv head, key
-// split). The wavefront packs all Hq/Hkv x Lq query rows that read this kv head
-// into one MFMA tile, so each K/V byte is fetched once for the whole group.
-// K fragments go straight from global memory into MFMA operands (16-byte
-// loads); each 32-key V tile passes through a wavefront-private LDS buffer so
-// that transpose reads can form the V^T operand. The wavefront leaves, per
-// query row, its running maximum m (base 2), its sum of weights l and its
-// unnormalised output in the scratch buffer (per row: a 16-byte {m, l}
-// slot, then Dv floats in a second region).
+// First pass (decode_split_kernel): one workgroup of NW wavefronts per (batch,
+// kv head, key split). All Hq/Hkv x Lq query rows that read this kv head are
+// packed into one MFMA tile, so every K/V byte is fetched once for the whole
+// group. The workgroup streams its keys in tiles of BN: each tile's K and V
+// rows are loaded by all threads with 16-byte loads (the next tile's loads are
+// in flight while the current tile is computed) and staged once in LDS. Every
+// wavefront forms the scores and softmax weights of the tile (S^T = K Q^T on
+// MFMA; this redundant work is small), then accumulates its own share of the
+// value columns (O^T += V^T P^T, V^T via LDS transpose reads). The workgroup
+// leaves, per query row, its maximum m (base 2), its sum of weights l and its
+// unnormalised output in the scratch buffer: per row a 16-byte {m, l} slot in
+// a first region, and Dv floats in a second.
 //
 // Second pass (decode_reduce_kernel): per query row, the log-sum-exp combine
-// of the splits, plus the sink logit as one more term of the denominator, one
-// division, and the single rounding to the output type. The two passes are
-// the split/reduce pair named by nuvec-core "tests/attention_plan.rs"
-// (first-pass dispatches over key partitions, then a second pass).
+// of the splits with the sink logit as one more term of the denominator, one
+// division and the single rounding to the output type. The two passes are the
+// split/reduce pair named by nuvec-core "tests/attention_plan.rs" (first-pass
+// dispatches over key partitions, then a second pass).
 #pragma once
 
 #include "attn_device.h"
@@ -22,41 +25,47 @@
 
 namespace sdpa {
 
-template <int MF, int D, int DV>
+template <int MF, int D, int DV, int NW>
 struct DecodeCfg {
   static constexpr int KW = Mfma<MF>::KW, ACC = Mfma<MF>::ACC, KG = Mfma<MF>::KG;
   static constexpr int BN = kDecodeBN;
   static constexpr int DVP = (DV + MF - 1) / MF * MF;
+  static constexpr int KST = D + 8;        // LDS row strides (elements)
   static constexpr int VST = DVP + 16;
   static constexpr int NQC = D / KW;
   static constexpr int NSB = BN / MF;
   static constexpr int NPV = BN / KW;
-  static constexpr int NDB = DVP / MF;
-  static constexpr int VCH = BN * DV / 8;
-  static constexpr int VPT = (VCH + 63) / 64;
+  static constexpr int NDB = DVP / MF;            // value-column blocks in all
+  static constexpr int NDBW = (NDB + NW - 1) / NW; // blocks per wavefront (at most)
+  static constexpr int NT = NW * 64;
+  static constexpr int KCH = BN * D / 8, VCH = BN * DV / 8;
+  static constexpr int KPT = (KCH + NT - 1) / NT, VPT = (VCH + NT - 1) / NT;
+  static constexpr int LDS_ELEMS = BN * KST + BN * VST;
   static_assert(D % KW == 0, "head size must be a whole number of MFMA k-steps");
 };
 
 template <class E, int MF, int D, int DV, int NW>
 __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
-  using C = DecodeCfg<MF, D, DV>;
+  using C = DecodeCfg<MF, D, DV, NW>;
   using acc_t = typename Mfma<MF>::acc_t;
   constexpr int ACC = C::ACC;
   constexpr int BN = C::BN;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[NW * BN * C::VST];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  uint16_t* Ks = lds;
+  uint16_t* Vs = lds + BN * C::KST;
 
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const int col = lane % MF;
   const int kg = lane / MF;
-  uint16_t* Vs = lds + w * BN * C::VST;
 
-  const int split = (int)blockIdx.x * NW + w;
+  const int split = blockIdx.x;
   const int hkv = blockIdx.y;
   const int b = blockIdx.z;
-  if (split >= a.nsplit) return;
   const int ks = split * a.kps;
   const int ke = min(ks + a.kps, a.Lk);
+  const int ntiles = (ke - ks + BN - 1) / BN;
 
   // packed query rows: row r -> head hkv*group + r / Lq, position r % Lq
   const int r = col;
@@ -75,15 +84,15 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   }
 
   if constexpr (C::DVP > DV) {
-    for (int e = lane; e < BN * (C::DVP - DV); e += 64) {
+    for (int e = tid; e < BN * (C::DVP - DV); e += C::NT) {
       const int rr = e / (C::DVP - DV), cc = DV + e % (C::DVP - DV);
       Vs[rr * C::VST + cc] = 0;
     }
   }
 
-  acc_t o[C::NDB];
+  acc_t o[C::NDBW];
 #pragma unroll
-  for (int d = 0; d < C::NDB; ++d) o[d] = acc_t{};
+  for (int d = 0; d < C::NDBW; ++d) o[d] = acc_t{};
   float m = -INFINITY, l = 0.0f;
 
   const uint16_t* kp = (const uint16_t*)a.k + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * D;
@@ -91,37 +100,67 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   const uint8_t* mrow = a.mask + (size_t)iq * a.Lk;
   const bool causal_cut = a.mask_kind == kMaskCausal && a.Lq > 1;
 
-  const int tr_e = (lane & 15) >> 2;
-  const int tr_c = lane & 3;
-  const int tr_dv = ((lane >> 4) * 16) % MF + 4 * tr_c;
-
-  for (int k0 = ks; k0 < ke; k0 += BN) {
-    u32x4 kop[C::NSB][C::NQC];
+  u32x4 kr[C::KPT], vr[C::VPT];
+  auto load_tile = [&](int k0) {
 #pragma unroll
-    for (int nb = 0; nb < C::NSB; ++nb) {
-      const int key = k0 + nb * MF + col;
-#pragma unroll
-      for (int c = 0; c < C::NQC; ++c)
-        kop[nb][c] = key < ke ? ld_global16(kp + (size_t)key * D + c * C::KW + kg * 8)
-                              : u32x4{0u, 0u, 0u, 0u};
+    for (int it = 0; it < C::KPT; ++it) {
+      const int c = tid + it * C::NT;
+      if (C::KCH % C::NT == 0 || c < C::KCH) {
+        const int rr = c / (D / 8), cc = c % (D / 8);
+        const int key = k0 + rr;
+        kr[it] = key < ke ? ld_global16(kp + (size_t)key * D + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
     }
-    u32x4 vr[C::VPT];
 #pragma unroll
     for (int it = 0; it < C::VPT; ++it) {
-      const int c = lane + it * 64;
-      if (C::VCH % 64 == 0 || c < C::VCH) {
+      const int c = tid + it * C::NT;
+      if (C::VCH % C::NT == 0 || c < C::VCH) {
         const int rr = c / (DV / 8), cc = c % (DV / 8);
         const int key = k0 + rr;
         vr[it] = key < ke ? ld_global16(vp + (size_t)key * DV + cc * 8) : u32x4{0u, 0u, 0u, 0u};
       }
     }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < C::KPT; ++it) {
+      const int c = tid + it * C::NT;
+      if (C::KCH % C::NT == 0 || c < C::KCH) {
+        const int rr = c / (D / 8), cc = c % (D / 8);
+        *reinterpret_cast<u32x4*>(&Ks[rr * C::KST + cc * 8]) = kr[it];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < C::VPT; ++it) {
+      const int c = tid + it * C::NT;
+      if (C::VCH % C::NT == 0 || c < C::VCH) {
+        const int rr = c / (DV / 8), cc = c % (DV / 8);
+        *reinterpret_cast<u32x4*>(&Vs[rr * C::VST + cc * 8]) = vr[it];
+      }
+    }
+  };
+
+  const int tr_e = (lane & 15) >> 2;
+  const int tr_c = lane & 3;
+  const int tr_dv = ((lane >> 4) * 16) % MF + 4 * tr_c;
+
+  if (ntiles > 0) load_tile(ks);
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = ks + t * BN;
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (t + 1 < ntiles) load_tile(k0 + BN);
 
     acc_t s[C::NSB];
 #pragma unroll
     for (int nb = 0; nb < C::NSB; ++nb) {
       acc_t acc = acc_t{};
 #pragma unroll
-      for (int c = 0; c < C::NQC; ++c) acc = mma16<E, MF>(kop[nb][c], qop[c], acc);
+      for (int c = 0; c < C::NQC; ++c) {
+        const u32x4 kop = *reinterpret_cast<const u32x4*>(&Ks[(nb * MF + col) * C::KST + c * C::KW + kg * 8]);
+        acc = mma16<E, MF>(kop, qop[c], acc);
+      }
       s[nb] = acc;
     }
 
@@ -142,7 +181,7 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
       }
     mx = row_max<MF>(mx);
     const float tmax = (mx == -INFINITY) ? -INFINITY : mx * a.c;
-    softmax_rebase<C::NDB>(tmax, m, l, o);
+    softmax_rebase<C::NDBW>(tmax, m, l, o);
     const float mu = (m == -INFINITY) ? 0.0f : m;
 
     uint32_t pk[C::NSB * ACC / 2];
@@ -158,62 +197,60 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
       }
     l += lsum;
 
-    // V tile into this wavefront's LDS buffer, then O^T += V^T P^T
-#pragma unroll
-    for (int it = 0; it < C::VPT; ++it) {
-      const int c = lane + it * 64;
-      if (C::VCH % 64 == 0 || c < C::VCH) {
-        const int rr = c / (DV / 8), cc = c % (DV / 8);
-        *reinterpret_cast<u32x4*>(&Vs[rr * C::VST + cc * 8]) = vr[it];
-      }
-    }
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int t8 = 0; t8 < C::NPV; ++t8) {
       const u32x4 pb = {pk[4 * t8], pk[4 * t8 + 1], pk[4 * t8 + 2], pk[4 * t8 + 3]};
       const int keyA = ((8 * t8) / ACC) * MF + acc_row<MF>((8 * t8) % ACC, kg);
       const int keyB = ((8 * t8 + 4) / ACC) * MF + acc_row<MF>((8 * t8 + 4) % ACC, kg);
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        const u32x2 ra = lds_read_tr16(&Vs[(keyA + tr_e) * C::VST + db * MF + tr_dv]);
-        const u32x2 rb = lds_read_tr16(&Vs[(keyB + tr_e) * C::VST + db * MF + tr_dv]);
-        const u32x4 va = {ra[0], ra[1], rb[0], rb[1]};
-        o[db] = mma16<E, MF>(va, pb, o[db]);
+      for (int j = 0; j < C::NDBW; ++j) {
+        const int db = w + NW * j;
+        if (C::NDB % NW == 0 || db < C::NDB) {
+          const u32x2 ra = lds_read_tr16(&Vs[(keyA + tr_e) * C::VST + db * MF + tr_dv]);
+          const u32x2 rb = lds_read_tr16(&Vs[(keyB + tr_e) * C::VST + db * MF + tr_dv]);
+          const u32x4 va = {ra[0], ra[1], rb[0], rb[1]};
+          o[j] = mma16<E, MF>(va, pb, o[j]);
+        }
       }
     }
-    // every lane's transpose reads must land before the next tile overwrites the buffer
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 
-  // partial results: {m, l} per row, then the unnormalised output row
   const float lt = row_sum<MF>(l);
   if (!row_ok) return;
   const size_t prow = ((size_t)(b * a.Hkv + hkv) * a.nsplit + split) * a.rows + r;
   const size_t total_rows = (size_t)a.B * a.Hkv * a.nsplit * a.rows;
-  float* pml = a.part + prow * 4;                 // {m, l} in a 16-byte slot
+  float* pml = a.part + prow * 4;
   float* po = a.part + total_rows * 4 + prow * DV;
-  if (kg == 0) {
+  if (w == 0 && kg == 0) {
     pml[0] = m;
     pml[1] = lt;
   }
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
+  for (int j = 0; j < C::NDBW; ++j) {
+    const int db = w + NW * j;
 #pragma unroll
     for (int g4 = 0; g4 < ACC / 4; ++g4) {
       const int dv = db * MF + g4 * 4 * C::KG + kg * 4;
-      if (dv < DV) {
-        const f32x4 st = {o[db][g4 * 4 + 0], o[db][g4 * 4 + 1], o[db][g4 * 4 + 2], o[db][g4 * 4 + 3]};
+      if ((C::NDB % NW == 0 || db < C::NDB) && dv < DV) {
+        const f32x4 st = {o[j][g4 * 4 + 0], o[j][g4 * 4 + 1], o[j][g4 * 4 + 2], o[j][g4 * 4 + 3]};
         *reinterpret_cast<f32x4*>(po + dv) = st;
       }
     }
+  }
 }
 
-// One workgroup (64 lanes) per (query row, kv head, batch item); lanes stride
-// over the value columns in groups of four.
+// One workgroup (4 wavefronts) per (query row, kv head, batch item). The
+// workgroup first finds the largest split maximum (and the sink); then each
+// wavefront folds every fourth split into its own running sums for four value
+// columns per lane, and the four wavefronts' sums are added in LDS.
 template <class E, int DV>
-__global__ void __launch_bounds__(64) decode_reduce_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(256) decode_reduce_kernel(FwdArgs a) {
+  constexpr int NCH = (DV + 255) / 256;   // 4-column chunks per lane
+  __shared__ float red[4];
+  __shared__ f32x4 accs[4][NCH][64];
+  __shared__ float Ls[4];
   const int r = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x, sg = t >> 6, j = t & 63;
   const int h = hkv * a.group + r / a.Lq;
   const int iq = r % a.Lq;
   const size_t pair = (size_t)(b * a.Hkv + hkv);
@@ -223,28 +260,49 @@ __global__ void __launch_bounds__(64) decode_reduce_kernel(FwdArgs a) {
 
   const bool has_sink = a.sinks != nullptr;
   const float sink2 = has_sink ? half_to_f32<E>(((const uint16_t*)a.sinks)[h]) * kLog2e : -INFINITY;
-  float M = sink2;
-  for (int sp = 0; sp < a.nsplit; ++sp) M = fmaxf(M, pml[((pair * a.nsplit + sp) * a.rows + r) * 4]);
+  float M = -INFINITY;
+  for (int sp = t; sp < a.nsplit; sp += 256) M = fmaxf(M, pml[((pair * a.nsplit + sp) * a.rows + r) * 4]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (j == 0) red[sg] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), sink2);
 
-  uint16_t* op = (uint16_t*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq) * DV;
-  for (int dv = lane * 4; dv < DV; dv += 256) {
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    float L = 0.0f;
-    if (M != -INFINITY) {
-      if (has_sink) L = fast_exp2(sink2 - M);
-      for (int sp = 0; sp < a.nsplit; ++sp) {
-        const size_t prow = (pair * a.nsplit + sp) * a.rows + r;
-        const float ms = pml[prow * 4];
-        if (ms == -INFINITY) continue;
-        const float f = fast_exp2(ms - M);
-        L += pml[prow * 4 + 1] * f;
-        const f32x4 x = *reinterpret_cast<const f32x4*>(po + prow * DV + dv);
-        acc += x * f;
+  f32x4 acc[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float L = 0.0f;
+  if (M != -INFINITY) {
+    for (int sp = sg; sp < a.nsplit; sp += 4) {
+      const size_t prow = (pair * a.nsplit + sp) * a.rows + r;
+      const float ms = pml[prow * 4];
+      if (ms == -INFINITY) continue;
+      const float f = fast_exp2(ms - M);
+      L += pml[prow * 4 + 1] * f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int dv = c * 256 + j * 4;
+        if (dv < DV) acc[c] += *reinterpret_cast<const f32x4*>(po + prow * DV + dv) * f;
       }
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    const u32x2 st = {pack2<E>(acc[0] * inv, acc[1] * inv), pack2<E>(acc[2] * inv, acc[3] * inv)};
-    st_global8(op + dv, st);
+  }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) accs[sg][c][j] = acc[c];
+  if (j == 0) Ls[sg] = L;
+  __syncthreads();
+  if (sg != 0) return;
+  float Lt = Ls[0] + Ls[1] + Ls[2] + Ls[3];
+  if (has_sink && M != -INFINITY) Lt += fast_exp2(sink2 - M);
+  const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+  uint16_t* op = (uint16_t*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq) * DV;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int dv = c * 256 + j * 4;
+    if (dv < DV) {
+      const f32x4 x = (accs[0][c][j] + accs[1][c][j] + accs[2][c][j] + accs[3][c][j]) * inv;
+      const u32x2 st = {pack2<E>(x[0], x[1]), pack2<E>(x[2], x[3])};
+      st_global8(op + dv, st);
+    }
   }
 }
 

@@ -1,4 +1,5 @@
 // Prefill kernel instantiations for 16-bit inputs (bf16 and f16).
+#include "prefill_fast.h"
 #include "prefill_impl.h"
 
 namespace sdpa {
@@ -9,8 +10,14 @@ static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_
   constexpr int MF = prefill_mf(elem, D, DV);
   constexpr int BN = prefill_bn(elem, D, DV);
   dim3 grid(a.head_blocks, a.nqb, 1);
-  hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves>), grid, dim3(kPrefillWaves * 64), 0,
-                     stream, a);
+  if constexpr (D == DV && (D == 64 || D == 128)) {
+    static_assert(MF == FastCfg<D>::MF && BN == FastCfg<D>::BN && kPrefillWaves == FastCfg<D>::NW,
+                  "planner geometry must match the kernel");
+    hipLaunchKernelGGL((prefill_fast_kernel<E, D>), grid, dim3(kPrefillWaves * 64), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves>), grid, dim3(kPrefillWaves * 64), 0,
+                       stream, a);
+  }
   return hipGetLastError();
 }
 

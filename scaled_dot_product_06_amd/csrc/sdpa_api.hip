@@ -165,7 +165,7 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
     const int64_t rows = group * Lq;
     int64_t kps = pow2_floor(Lk / 64 > 0 ? Lk / 64 : 1);
     if (kps < 64) kps = 64;
-    if (kps > 256) kps = 256;
+    if (kps > 1024) kps = 1024;
     const int64_t nsplit = (Lk + kps - 1) / kps;
     p.route = SDPA_ROUTE_DECODE;
     p.kernels = 2;
@@ -175,10 +175,10 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
     p.heads_per_group = (int32_t)group;
     p.keys_per_split = kps;
     p.splits = nsplit;
-    p.grid[0] = (nsplit + kDecodeWaves - 1) / kDecodeWaves;
+    p.grid[0] = nsplit;
     p.grid[1] = Hkv;
     p.grid[2] = B;
-    if (Hkv > kMaxGridYZ || B > kMaxGridYZ)
+    if (Hkv > kMaxGridYZ || B > kMaxGridYZ || rows > kMaxGridYZ)
       return fail(SDPA_ERR_UNSUPPORTED, "decode grid: Hkv (%lld) and B (%lld) must be <= 65535", (long long)Hkv,
                   (long long)B);
     int64_t sb;

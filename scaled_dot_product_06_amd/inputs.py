@@ -21,6 +21,9 @@ pattern. Tensor ids: q=1, k=2, v=3, mask=4, sinks=5.
 """
 from __future__ import annotations
 
+import concurrent.futures as _cf
+import os
+
 import numpy as np
 
 F32, F16, BF16 = 0, 1, 2
@@ -58,36 +61,50 @@ def words(seed: int, tensor: int, start: int, count: int) -> np.ndarray:
         return _mix64(n ^ key)
 
 
+def _chunked(count: int, dtype, fill) -> np.ndarray:
+    """Fill out[s:s+c] = fill(s, c) over fixed chunks, on a few threads (numpy
+    releases the GIL); the values do not depend on the thread count."""
+    out = np.empty(count, dtype=dtype)
+    starts = list(range(0, count, _CHUNK))
+
+    def work(s):
+        c = min(_CHUNK, count - s)
+        out[s:s + c] = fill(s, c)
+
+    workers = min(16, os.cpu_count() or 1, max(1, len(starts)))
+    if workers <= 1:
+        for s in starts:
+            work(s)
+    else:
+        with _cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(work, starts))
+    return out
+
+
 def uniform_pm1(seed: int, tensor: int, count: int) -> np.ndarray:
     """float32 draws on [-1, 1), exact."""
-    out = np.empty(count, dtype=np.float32)
-    for s in range(0, count, _CHUNK):
-        c = min(_CHUNK, count - s)
+    def fill(s, c):
         u = (words(seed, tensor, s, c) >> np.uint64(40)).astype(np.float64)
-        out[s:s + c] = (u * 2.0 ** -23 - 1.0).astype(np.float32)
-    return out
+        return (u * 2.0 ** -23 - 1.0).astype(np.float32)
+    return _chunked(count, np.float32, fill)
 
 
 def normal(seed: int, tensor: int, count: int) -> np.ndarray:
     """float64 standard-normal draws (Box-Muller)."""
-    out = np.empty(count, dtype=np.float64)
-    for s in range(0, count, _CHUNK):
-        c = min(_CHUNK, count - s)
+    def fill(s, c):
         a = words(seed, tensor, s, c) >> np.uint64(11)
         b = words(seed, tensor, s + (1 << 55), c) >> np.uint64(11)
         u1 = (a.astype(np.float64) + 1.0) * 2.0 ** -53  # (0, 1]
         u2 = b.astype(np.float64) * 2.0 ** -53          # [0, 1)
-        out[s:s + c] = np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)
-    return out
+        return np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)
+    return _chunked(count, np.float64, fill)
 
 
 def bernoulli(seed: int, tensor: int, count: int, threshold: int = 15099494) -> np.ndarray:
     """uint8 draws, 1 with probability threshold / 2**24."""
-    out = np.empty(count, dtype=np.uint8)
-    for s in range(0, count, _CHUNK):
-        c = min(_CHUNK, count - s)
-        out[s:s + c] = (words(seed, tensor, s, c) >> np.uint64(40)) < np.uint64(threshold)
-    return out
+    def fill(s, c):
+        return (words(seed, tensor, s, c) >> np.uint64(40)) < np.uint64(threshold)
+    return _chunked(count, np.uint8, fill)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:

@@ -55,7 +55,7 @@ def test_workload_routes(number, route):
         rows = w["Hq"] // w["Hkv"] * w["Lq"]
         assert p["splits"] * p["keys_per_split"] >= w["Lk"] > (p["splits"] - 1) * p["keys_per_split"]
         assert p["scratch_bytes"] == w["B"] * w["Hkv"] * p["splits"] * rows * (w["Dv"] + 4) * 4
-        assert p["grid"] == ((p["splits"] + p["waves"] - 1) // p["waves"], w["Hkv"], w["B"])
+        assert p["grid"] == (p["splits"], w["Hkv"], w["B"])
     else:
         assert p["kernels"] == 1 and p["scratch_bytes"] == 0
         rows_per_block = p["waves"] // p["heads_per_group"] * p["rows_per_wave"]

@@ -91,10 +91,14 @@ def cpu_baseline(p, seconds: float):
     per_head = causal_pairs(p.Lq, p.Lk) * 2 * (p.D + p.Dv)
     done = 0
     t0 = time.perf_counter()
-    for h in range(p.Hq):
-        orc.sdpa(q[:1, h:h + 1], k[:1, h // group:h // group + 1], v[:1, h // group:h // group + 1],
-                 p.scale, p.mask_kind, m, None if s is None else s[h:h + 1])
-        done += 1
+    for b in range(p.B):
+        for h in range(p.Hq):
+            hk = h // group
+            orc.sdpa(q[b:b + 1, h:h + 1], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1],
+                     p.scale, p.mask_kind, m, None if s is None else s[h:h + 1])
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
@@ -106,8 +110,10 @@ def cpu_baseline(p, seconds: float):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle", type=float, default=2.0,
+                    help="extra untimed stepping (seconds) after the warmup steps, so GPU clocks settle")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -154,6 +160,15 @@ def main() -> int:
 
     for i in range(args.warmup):
         step(i)
+    torch.cuda.synchronize()
+    # let the clocks settle: keep stepping (untimed) for at least --settle seconds
+    t_settle = time.perf_counter() + args.settle
+    i = args.warmup
+    while time.perf_counter() < t_settle:
+        step(i)
+        i += 1
+        if i % 50 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     K = args.steps

@@ -104,6 +104,16 @@ template <class E> __device__ __forceinline__ uint16_t f32_to_half(float x) {
   return (uint16_t)(pack2<E>(x, 0.0f) & 0xFFFFu);
 }
 
+// acc + lo + hi of a packed pair of 16-bit values (one v_dot2 against (1, 1)).
+template <class E> __device__ __forceinline__ float pair_sum(uint32_t packed, float acc);
+template <> __device__ __forceinline__ float pair_sum<ElemBF16>(uint32_t packed, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                         acc, false);
+}
+template <> __device__ __forceinline__ float pair_sum<ElemF16>(uint32_t packed, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
+}
+
 // ---- memory helpers ----------------------------------------------------------
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -113,6 +123,7 @@ __device__ __forceinline__ void st_global8(void* p, u32x2 v) {
 }
 
 #define SDPA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
 
 // Transposed 4 x 16-bit LDS read (gfx950 ds_read_b64_tr_b16). Within each
 // group of 16 lanes, lane j receives element (j % 4) of the 8-byte chunks that
@@ -148,6 +159,28 @@ template <int MF> __device__ __forceinline__ float row_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Work item (head block hb, query block qb) of prefill workgroup n, for a 1-D
+// grid of head_blocks * nqb workgroups. The dispatcher deals workgroups to the
+// 8 XCDs round-robin; this order makes each XCD walk the head blocks of one
+// (batch, kv head) pair at a time, longest (latest) query blocks first, so the
+// pair's K/V stays resident in that XCD's L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void prefill_item(int n, int head_blocks, int nqb, int hb_per_pair, int& hb, int& qb) {
+  const int pairs = head_blocks / hb_per_pair;
+  const int per_pair = hb_per_pair * nqb;
+  int pair, r;
+  if (pairs % kXcds == 0) {
+    const int xcd = n % kXcds, s = n / kXcds;
+    pair = (s / per_pair) * kXcds + xcd;
+    r = s % per_pair;
+  } else {
+    pair = n / per_pair;
+    r = n % per_pair;
+  }
+  qb = nqb - 1 - r / hb_per_pair;
+  hb = pair * hb_per_pair + r % hb_per_pair;
+}
 
 // Online-softmax reference update for one wave. `tile_max` is the row's
 // largest scaled score in the new tile (-inf if it sees none). When any row's

@@ -65,6 +65,9 @@ constexpr int prefill_mf(int elem, int D, int Dv) { return head_max(D, Dv) <= 12
 constexpr int prefill_bn(int elem, int D, int Dv) {
   return elem == kF32 ? (head_max(D, Dv) <= 128 ? 32 : 16) : (head_max(D, Dv) <= 256 ? 64 : 32);
 }
+// The 64/128-wide 16-bit prefill shapes run the double-buffered direct-load kernel.
+constexpr bool prefill_is_fast(int elem, int D, int Dv) { return elem != kF32 && D == Dv && (D == 64 || D == 128); }
+constexpr int prefill_waves(int elem, int D, int Dv) { return kPrefillWaves; }
 // 16x16 tiles when the packed query rows fit (and the head is a whole number
 // of 32-wide k-steps), else 32x32.
 constexpr int decode_mf(int D, int rows) { return rows <= 16 && D % 32 == 0 ? 16 : 32; }

@@ -9,11 +9,11 @@ static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_
   constexpr int elem = std::is_same<E, ElemBF16>::value ? kBF16 : kF16;
   constexpr int MF = prefill_mf(elem, D, DV);
   constexpr int BN = prefill_bn(elem, D, DV);
-  dim3 grid(a.head_blocks, a.nqb, 1);
-  if constexpr (D == DV && (D == 64 || D == 128)) {
-    static_assert(MF == FastCfg<D>::MF && BN == FastCfg<D>::BN && kPrefillWaves == FastCfg<D>::NW,
+  dim3 grid(a.head_blocks * a.nqb, 1, 1);
+  if constexpr (prefill_is_fast(elem, D, DV)) {
+    static_assert(MF == FastCfg<D>::MF && BN == FastCfg<D>::BN && prefill_waves(elem, D, DV) == FastCfg<D>::NW,
                   "planner geometry must match the kernel");
-    hipLaunchKernelGGL((prefill_fast_kernel<E, D>), grid, dim3(kPrefillWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL((prefill_fast_kernel<E, D>), grid, dim3(FastCfg<D>::NW * 64), 0, stream, a);
   } else {
     hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves>), grid, dim3(kPrefillWaves * 64), 0,
                        stream, a);

@@ -7,7 +7,7 @@ template <int D, int DV>
 static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_t stream) {
   constexpr int MF = prefill_mf(kF32, D, DV);
   constexpr int BN = prefill_bn(kF32, D, DV);
-  dim3 grid(a.head_blocks, a.nqb, 1);
+  dim3 grid(a.head_blocks * a.nqb, 1, 1);
   hipLaunchKernelGGL((prefill_f32_kernel<MF, D, DV, BN, kPrefillWaves>), grid, dim3(kPrefillWaves * 64), 0,
                      stream, a);
   return hipGetLastError();

@@ -7,7 +7,8 @@
 //    (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16 * lane),
 //    so no registers hold tile data and no LDS store instructions are issued;
 //  * two LDS stages: tile t+1 streams in while tile t is computed, with one
-//    workgroup barrier per tile;
+//    workgroup barrier per tile; the stages are distinct LDS objects so the
+//    compiler can tell the loads into one from the reads of the other;
 //  * each LDS row is stored with its 16-byte chunks permuted by an XOR of the
 //    row index (different for K and V), chosen so that the K-operand reads
 //    (16 consecutive rows, one chunk each) and the V transpose reads (8
@@ -54,21 +55,26 @@ prefill_fast_kernel(FwdArgs a) {
   using C = FastCfg<D>;
   constexpr int MF = C::MF, ACC = C::ACC, BN = C::BN;
   using acc_t = f32x16;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE_BYTES];
+  // Two stages as two distinct LDS objects: the compiler can then prove that
+  // the direct loads into one stage never alias the reads of the other, and
+  // does not make the reads of tile t wait for the loads of tile t+1.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::STAGE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps control flow scalar
   const int col = lane % MF;
   const int kg = lane / MF;
 
   const int heads = a.Hq * a.B / a.head_blocks;
   const int wph = C::NW / heads;
   const int bm = wph * MF;
-  const int qb = a.nqb - 1 - (int)blockIdx.y;
+  int hb, qb;
+  prefill_item((int)blockIdx.x, a.head_blocks, a.nqb, a.group / heads, hb, qb);
   const int groups_per_b = a.Hq / heads;
-  const int b = (int)blockIdx.x / groups_per_b;
-  const int h0 = ((int)blockIdx.x % groups_per_b) * heads;
+  const int b = hb / groups_per_b;
+  const int h0 = (hb % groups_per_b) * heads;
   const int hkv = h0 / a.group;
   const int h = h0 + w / wph;
   const int wi0 = qb * bm + (w % wph) * MF;
@@ -113,24 +119,38 @@ prefill_fast_kernel(FwdArgs a) {
   const uint8_t* vbase = (const uint8_t*)a.v + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * C::RB;
   const uint8_t* mrow = a.mask + (size_t)iq * a.Lk;
 
-  // direct loads: this lane's row within a 1 KB block and its LDS slot
+  // direct loads: per lane, byte offsets of its 16-byte chunk within the tile
+  // (row blk*ROWS_PER_KB + lane/CPR, global chunk permuted by the row's XOR)
   const int ld_row = lane / C::CPR;
   const int ld_slot = lane % C::CPR;
-  auto issue_tile = [&](int k0, int stage) {
-    uint8_t* sbase = lds + stage * C::STAGE_BYTES;
+  uint32_t offk[C::LOADS_PER_WAVE], offv[C::LOADS_PER_WAVE];
+  int ldrow[C::LOADS_PER_WAVE];
+#pragma unroll
+  for (int it = 0; it < C::LOADS_PER_WAVE; ++it) {
+    const int row = (w + C::NW * it) * C::ROWS_PER_KB + ld_row;
+    ldrow[it] = row;
+    offk[it] = row * C::RB + (ld_slot ^ swz_k<D>(row)) * 16;
+    offv[it] = row * C::RB + (ld_slot ^ swz_v<D>(row)) * 16;
+  }
+  auto issue_tile = [&](int k0, uint8_t* sbase) {
+    const uint8_t* kt = kbase + (size_t)k0 * C::RB;
+    const uint8_t* vt = vbase + (size_t)k0 * C::RB;
+    const bool tail = k0 + BN > a.Lk;
 #pragma unroll
     for (int it = 0; it < C::LOADS_PER_WAVE; ++it) {
+      uint32_t ok = offk[it], ov = offv[it];
+      if (tail) {
+        // rows past the end read the last real row instead; those keys get weight 0
+        const int over = max(k0 + ldrow[it] - (a.Lk - 1), 0) * C::RB;
+        ok -= over;
+        ov -= over;
+      }
       const int blk = w + C::NW * it;
-      const int row = blk * C::ROWS_PER_KB + ld_row;
-      const int key = min(k0 + row, a.Lk - 1);   // rows past the end repeat a real row; their weight is 0
-      const int ck = ld_slot ^ swz_k<D>(row);
-      const int cv = ld_slot ^ swz_v<D>(row);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(kbase + (size_t)key * C::RB + ck * 16),
-          (__attribute__((address_space(3))) void*)(sbase + blk * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(vbase + (size_t)key * C::RB + cv * 16),
-          (__attribute__((address_space(3))) void*)(sbase + C::TILE_BYTES + blk * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + ok),
+                                       (__attribute__((address_space(3))) void*)(sbase + blk * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt + ov),
+                                       (__attribute__((address_space(3))) void*)(sbase + C::TILE_BYTES + blk * 1024),
+                                       16, 0, 0);
     }
   };
 
@@ -140,30 +160,23 @@ prefill_fast_kernel(FwdArgs a) {
   const int tr_chunk = ((lane >> 4) & 1) * 2 + (tr_c >> 1);  // chunk within a 32-column block
   const int tr_half = (tr_c & 1) * 8;
 
-  if (ntiles > 0) issue_tile(0, 0);
-  for (int t = 0; t < ntiles; ++t) {
+  auto compute = [&](int t, const uint8_t* Ks) {
     const int k0 = t * BN;
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 1 < ntiles) issue_tile(k0 + BN, (t + 1) & 1);
-    if (!wave_live || k0 >= w_kend) continue;
     const bool full = k0 + BN <= w_kfull;
-    const uint8_t* Ks = lds + (t & 1) * C::STAGE_BYTES;
     const uint8_t* Vs = Ks + C::TILE_BYTES;
 
     acc_t s[C::NSB];
 #pragma unroll
-    for (int nb = 0; nb < C::NSB; ++nb) {
-      const int row = nb * MF + col;
-      const uint8_t* krow = Ks + row * C::RB;
-      const int sw = swz_k<D>(row);
-      acc_t acc = acc_t{};
+    for (int nb = 0; nb < C::NSB; ++nb) s[nb] = acc_t{};
 #pragma unroll
-      for (int c = 0; c < C::NQC; ++c) {
-        const u32x4 kop = *reinterpret_cast<const u32x4*>(krow + (((2 * c + kg) ^ sw) * 16));
-        acc = mma16<E, MF>(kop, qop[c], acc);
+    for (int c = 0; c < C::NQC; ++c) {
+#pragma unroll
+      for (int nb = 0; nb < C::NSB; ++nb) {
+        const int row = nb * MF + col;
+        const u32x4 kop =
+            *reinterpret_cast<const u32x4*>(Ks + row * C::RB + (((2 * c + kg) ^ swz_k<D>(row)) * 16));
+        s[nb] = mma16<E, MF>(kop, qop[c], s[nb]);
       }
-      s[nb] = acc;
     }
 
     float mx = -INFINITY;
@@ -190,18 +203,24 @@ prefill_fast_kernel(FwdArgs a) {
     softmax_rebase<C::NDB>(tmax, m, l, o);
     const float mu = (m == -INFINITY) ? 0.0f : m;
 
+    // weights, rounded to 16 bits for the MFMA; the running sum adds the same
+    // rounded weights (two per v_dot2), so numerator and denominator agree
     uint32_t pk[C::NSB * ACC / 2];
-    float lsum = 0.0f;
 #pragma unroll
     for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
       for (int i = 0; i < ACC; i += 2) {
         const float p0 = fast_exp2(fmaf(s[nb][i], a.c, -mu));
         const float p1 = fast_exp2(fmaf(s[nb][i + 1], a.c, -mu));
-        lsum += p0 + p1;
         pk[(nb * ACC + i) / 2] = pack2<E>(p0, p1);
       }
-    l += lsum;
+    float lsum0 = 0.0f, lsum1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < C::NSB * ACC / 2; j += 2) {
+      lsum0 = pair_sum<E>(pk[j], lsum0);
+      lsum1 = pair_sum<E>(pk[j + 1], lsum1);
+    }
+    l += lsum0 + lsum1;
 
 #pragma unroll
     for (int t8 = 0; t8 < C::NPV; ++t8) {
@@ -220,6 +239,21 @@ prefill_fast_kernel(FwdArgs a) {
         o[db] = mma16<E, MF>(va, pb, o[db]);
       }
     }
+  };
+
+  // one barrier per tile: tile t's loads have landed (own wait + barrier) and
+  // every wavefront has finished tile t-1, whose stage the next loads reuse
+  if (ntiles > 0) issue_tile(0, lds0);
+  for (int t = 0; t < ntiles; t += 2) {
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < ntiles) issue_tile((t + 1) * BN, lds1);
+    if (wave_live && t * BN < w_kend) compute(t, lds0);
+    if (t + 1 >= ntiles) break;
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 2 < ntiles) issue_tile((t + 2) * BN, lds0);
+    if (wave_live && (t + 1) * BN < w_kend) compute(t + 1, lds1);
   }
 
   if (!wave_live) return;

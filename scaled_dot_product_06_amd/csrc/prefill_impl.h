@@ -59,10 +59,11 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
   const int heads = a.Hq * a.B / a.head_blocks;   // query heads per workgroup
   const int wph = NW / heads;                      // wavefronts per head
   const int bm = wph * MF;                         // query rows per head per workgroup
-  const int qb = a.nqb - 1 - (int)blockIdx.y;      // late query blocks first
+  int hb, qb;
+  prefill_item((int)blockIdx.x, a.head_blocks, a.nqb, a.group / heads, hb, qb);
   const int groups_per_b = a.Hq / heads;
-  const int b = (int)blockIdx.x / groups_per_b;
-  const int h0 = ((int)blockIdx.x % groups_per_b) * heads;
+  const int b = hb / groups_per_b;
+  const int h0 = (hb % groups_per_b) * heads;
   const int hkv = h0 / a.group;
   const int h = h0 + w / wph;
   const int wi0 = qb * bm + (w % wph) * MF;
@@ -290,10 +291,11 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
   const int heads = a.Hq * a.B / a.head_blocks;
   const int wph = NW / heads;
   const int bm = wph * MF;
-  const int qb = a.nqb - 1 - (int)blockIdx.y;
+  int hb, qb;
+  prefill_item((int)blockIdx.x, a.head_blocks, a.nqb, a.group / heads, hb, qb);
   const int groups_per_b = a.Hq / heads;
-  const int b = (int)blockIdx.x / groups_per_b;
-  const int h0 = ((int)blockIdx.x % groups_per_b) * heads;
+  const int b = hb / groups_per_b;
+  const int h0 = (hb % groups_per_b) * heads;
   const int hkv = h0 / a.group;
   const int h = h0 + w / wph;
   const int wi0 = qb * bm + (w % wph) * MF;

@@ -189,20 +189,21 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
     return SDPA_OK;
   }
   const int mf = prefill_mf(dtype, (int)D, (int)Dv);
-  const int64_t heads = gcd64(group, kPrefillWaves);
-  const int64_t bm = (kPrefillWaves / heads) * mf;
+  const int nw = prefill_waves(dtype, (int)D, (int)Dv);
+  const int64_t heads = gcd64(group, nw);
+  const int64_t bm = (nw / heads) * mf;
   const int64_t nqb = (Lq + bm - 1) / bm;
-  if (nqb > kMaxGridYZ)
-    return fail(SDPA_ERR_UNSUPPORTED, "Lq (%lld) needs %lld query blocks; at most 65535 are supported", (long long)Lq,
-                (long long)nqb);
+  if ((B * Hq / heads) * nqb > INT_MAX)
+    return fail(SDPA_ERR_UNSUPPORTED, "Lq (%lld) needs %lld query blocks per head block; more than INT_MAX "
+                "workgroups in all", (long long)Lq, (long long)nqb);
   p.route = SDPA_ROUTE_PREFILL;
   p.kernels = 1;
   p.rows_per_wave = mf;
-  p.waves = kPrefillWaves;
+  p.waves = nw;
   p.block_n = prefill_bn(dtype, (int)D, (int)Dv);
   p.heads_per_group = (int32_t)heads;
-  p.grid[0] = B * Hq / heads;
-  p.grid[1] = nqb;
+  p.grid[0] = (B * Hq / heads) * nqb;   // one workgroup per (head block, query block)
+  p.grid[1] = 1;
   p.grid[2] = 1;
   *plan = p;
   return SDPA_OK;
@@ -313,8 +314,8 @@ int sdpa_forward(const void* q, const void* k, const void* v, void* out, int64_t
     DecodeShape s{p.rows_per_wave, p.waves, p.block_n};
     e = launch_decode(dtype, (int)D, (int)Dv, s, a, stream, &ok);
   } else {
-    a.nqb = (int)p.grid[1];
-    a.head_blocks = (int)p.grid[0];
+    a.head_blocks = (int)(B * Hq / p.heads_per_group);
+    a.nqb = (int)(p.grid[0] / a.head_blocks);
     PrefillShape s{p.rows_per_wave, p.waves, p.heads_per_group, p.block_n,
                    (int)((p.waves / p.heads_per_group) * p.rows_per_wave)};
     e = launch_prefill(dtype, (int)D, (int)Dv, s, a, stream, &ok);

@@ -59,8 +59,8 @@ def test_workload_routes(number, route):
     else:
         assert p["kernels"] == 1 and p["scratch_bytes"] == 0
         rows_per_block = p["waves"] // p["heads_per_group"] * p["rows_per_wave"]
-        assert p["grid"][1] == -(-w["Lq"] // rows_per_block)
-        assert p["grid"][0] * p["heads_per_group"] == w["B"] * w["Hq"]
+        head_blocks = w["B"] * w["Hq"] // p["heads_per_group"]
+        assert p["grid"] == (head_blocks * -(-w["Lq"] // rows_per_block), 1, 1)
 
 
 def test_decode_split_size_depends_on_keys_not_batch():

@@ -118,6 +118,10 @@ template <> __device__ __forceinline__ float pair_sum<ElemF16>(uint32_t packed, 
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+// Streaming (non-temporal) 16-byte load, for data read exactly once.
+__device__ __forceinline__ u32x4 ld_global16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ void st_global8(void* p, u32x2 v) {
   *reinterpret_cast<u32x2*>(p) = v;
 }

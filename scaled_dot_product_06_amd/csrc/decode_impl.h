@@ -4,8 +4,9 @@
 // kv head, key split). All Hq/Hkv x Lq query rows that read this kv head are
 // packed into one MFMA tile, so every K/V byte is fetched once for the whole
 // group. The workgroup streams its keys in tiles of BN: each tile's K and V
-// rows are loaded by all threads with 16-byte loads (the next tile's loads are
-// in flight while the current tile is computed) and staged once in LDS. Every
+// rows are loaded by all threads with 16-byte streaming loads (the next two
+// tiles' loads are in flight while the current tile is computed; each
+// workgroup reads one contiguous stretch of K and of V) and staged once in LDS. Every
 // wavefront forms the scores and softmax weights of the tile (S^T = K Q^T on
 // MFMA; this redundant work is small), then accumulates its own share of the
 // value columns (O^T += V^T P^T, V^T via LDS transpose reads). The workgroup
@@ -100,15 +101,17 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   const uint8_t* mrow = a.mask + (size_t)iq * a.Lk;
   const bool causal_cut = a.mask_kind == kMaskCausal && a.Lq > 1;
 
-  u32x4 kr[C::KPT], vr[C::VPT];
-  auto load_tile = [&](int k0) {
+  // Two register tiles (A and B) cycle so that two tiles of K/V loads are in
+  // flight while the LDS copy of a third is being computed.
+  u32x4 kra[C::KPT], vra[C::VPT], krb[C::KPT], vrb[C::VPT];
+  auto load_tile = [&](int k0, u32x4* kr, u32x4* vr) {
 #pragma unroll
     for (int it = 0; it < C::KPT; ++it) {
       const int c = tid + it * C::NT;
       if (C::KCH % C::NT == 0 || c < C::KCH) {
         const int rr = c / (D / 8), cc = c % (D / 8);
         const int key = k0 + rr;
-        kr[it] = key < ke ? ld_global16(kp + (size_t)key * D + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+        kr[it] = key < ke ? ld_global16_nt(kp + (size_t)key * D + cc * 8) : u32x4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
@@ -117,11 +120,11 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
       if (C::VCH % C::NT == 0 || c < C::VCH) {
         const int rr = c / (DV / 8), cc = c % (DV / 8);
         const int key = k0 + rr;
-        vr[it] = key < ke ? ld_global16(vp + (size_t)key * DV + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+        vr[it] = key < ke ? ld_global16_nt(vp + (size_t)key * DV + cc * 8) : u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](const u32x4* kr, const u32x4* vr) {
 #pragma unroll
     for (int it = 0; it < C::KPT; ++it) {
       const int c = tid + it * C::NT;
@@ -144,14 +147,7 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   const int tr_c = lane & 3;
   const int tr_dv = ((lane >> 4) * 16) % MF + 4 * tr_c;
 
-  if (ntiles > 0) load_tile(ks);
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = ks + t * BN;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(k0 + BN);
-
+  auto compute = [&](int k0) {
     acc_t s[C::NSB];
 #pragma unroll
     for (int nb = 0; nb < C::NSB; ++nb) {
@@ -213,6 +209,22 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
         }
       }
     }
+  };
+
+  if (ntiles > 0) load_tile(ks, kra, vra);
+  if (ntiles > 1) load_tile(ks + BN, krb, vrb);
+  for (int t = 0; t < ntiles; t += 2) {
+    __syncthreads();
+    store_tile(kra, vra);
+    __syncthreads();
+    if (t + 2 < ntiles) load_tile(ks + (t + 2) * BN, kra, vra);
+    compute(ks + t * BN);
+    if (t + 1 >= ntiles) break;
+    __syncthreads();
+    store_tile(krb, vrb);
+    __syncthreads();
+    if (t + 3 < ntiles) load_tile(ks + (t + 3) * BN, krb, vrb);
+    compute(ks + (t + 1) * BN);
   }
 
   const float lt = row_sum<MF>(l);
@@ -239,71 +251,78 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   }
 }
 
-// One workgroup (4 wavefronts) per (query row, kv head, batch item). The
-// workgroup first finds the largest split maximum (and the sink); then each
-// wavefront folds every fourth split into its own running sums for four value
-// columns per lane, and the four wavefronts' sums are added in LDS.
+// One 256-thread workgroup per (query row, kv head, batch item). Pass 1 finds
+// the largest split maximum (with the sink). Pass 2 walks the splits in chunks
+// of 256: each thread turns one split's maximum into its weight in LDS and adds
+// that split's share of the sum; then SG groups of threads, each lane owning
+// four value columns, add the weighted partial outputs of every SG-th split
+// (independent loads, many in flight). The groups' sums meet in LDS.
 template <class E, int DV>
 __global__ void __launch_bounds__(256) decode_reduce_kernel(FwdArgs a) {
-  constexpr int NCH = (DV + 255) / 256;   // 4-column chunks per lane
+  constexpr int NCG = (DV + 3) / 4;  // four-column groups
+  constexpr int SG = 256 / NCG;      // split lanes
+  __shared__ float fw[256];
   __shared__ float red[4];
-  __shared__ f32x4 accs[4][NCH][64];
-  __shared__ float Ls[4];
+  __shared__ f32x4 accs[SG][NCG];
   const int r = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
-  const int t = threadIdx.x, sg = t >> 6, j = t & 63;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int h = hkv * a.group + r / a.Lq;
   const int iq = r % a.Lq;
   const size_t pair = (size_t)(b * a.Hkv + hkv);
   const size_t total_rows = (size_t)a.B * a.Hkv * a.nsplit * a.rows;
-  const float* pml = a.part;
-  const float* po = a.part + total_rows * 4;
+  const size_t row0 = pair * a.nsplit * a.rows + r;        // split sp's row: row0 + sp * rows
+  const float* pml = a.part + row0 * 4;
+  const float* po = a.part + total_rows * 4 + row0 * DV;
+  const size_t ml_step = (size_t)a.rows * 4, o_step = (size_t)a.rows * DV;
 
   const bool has_sink = a.sinks != nullptr;
   const float sink2 = has_sink ? half_to_f32<E>(((const uint16_t*)a.sinks)[h]) * kLog2e : -INFINITY;
   float M = -INFINITY;
-  for (int sp = t; sp < a.nsplit; sp += 256) M = fmaxf(M, pml[((pair * a.nsplit + sp) * a.rows + r) * 4]);
+  for (int sp = t; sp < a.nsplit; sp += 256) M = fmaxf(M, pml[sp * ml_step]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (j == 0) red[sg] = M;
+  if (lane == 0) red[wv] = M;
   __syncthreads();
   M = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), sink2);
 
-  f32x4 acc[NCH];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float L = 0.0f;
+  const int cg = t % NCG, sg = t / NCG;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float lpart = 0.0f;
   if (M != -INFINITY) {
-    for (int sp = sg; sp < a.nsplit; sp += 4) {
-      const size_t prow = (pair * a.nsplit + sp) * a.rows + r;
-      const float ms = pml[prow * 4];
-      if (ms == -INFINITY) continue;
-      const float f = fast_exp2(ms - M);
-      L += pml[prow * 4 + 1] * f;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int dv = c * 256 + j * 4;
-        if (dv < DV) acc[c] += *reinterpret_cast<const f32x4*>(po + prow * DV + dv) * f;
+    for (int base = 0; base < a.nsplit; base += 256) {
+      const int n = min(256, a.nsplit - base);
+      __syncthreads();
+      if (t < n) {
+        const float ms = pml[(base + t) * ml_step];
+        const float f = ms == -INFINITY ? 0.0f : fast_exp2(ms - M);  // empty splits hold zeros
+        fw[t] = f;
+        lpart += pml[(base + t) * ml_step + 1] * f;
+      }
+      __syncthreads();
+      if (sg < SG) {
+#pragma unroll 8
+        for (int j = sg; j < n; j += SG)
+          acc += *reinterpret_cast<const f32x4*>(po + (base + j) * o_step + cg * 4) * fw[j];
       }
     }
   }
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) accs[sg][c][j] = acc[c];
-  if (j == 0) Ls[sg] = L;
   __syncthreads();
-  if (sg != 0) return;
-  float Lt = Ls[0] + Ls[1] + Ls[2] + Ls[3];
-  if (has_sink && M != -INFINITY) Lt += fast_exp2(sink2 - M);
-  const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
-  uint16_t* op = (uint16_t*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq) * DV;
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int dv = c * 256 + j * 4;
-    if (dv < DV) {
-      const f32x4 x = (accs[0][c][j] + accs[1][c][j] + accs[2][c][j] + accs[3][c][j]) * inv;
-      const u32x2 st = {pack2<E>(x[0], x[1]), pack2<E>(x[2], x[3])};
-      st_global8(op + dv, st);
-    }
-  }
+  for (int off = 32; off >= 1; off >>= 1) lpart += __shfl_xor(lpart, off);
+  if (lane == 0) red[wv] = lpart;
+  if (sg < SG) accs[sg][cg] = acc;
+  __syncthreads();
+  if (t >= NCG) return;
+  float L = red[0] + red[1] + red[2] + red[3];
+  if (has_sink && M != -INFINITY) L += fast_exp2(sink2 - M);
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  f32x4 x = accs[0][t];
+#pragma unroll
+  for (int g = 1; g < SG; ++g) x += accs[g][t];
+  x *= inv;
+  uint16_t* op = (uint16_t*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq) * DV;
+  const u32x2 st = {pack2<E>(x[0], x[1]), pack2<E>(x[2], x[3])};
+  st_global8(op + t * 4, st);
 }
 
 }  // namespace sdpa

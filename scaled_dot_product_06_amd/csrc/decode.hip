@@ -12,7 +12,7 @@ static hipError_t launch_one(const DecodeShape& s, const FwdArgs& a, hipStream_t
                          stream, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      dim3 grid2(a.rows, a.Hkv, a.B);
+      dim3 grid2(a.rows, a.Hkv, a.B * (DV / kReduceCols));
       hipLaunchKernelGGL((decode_reduce_kernel<E, DV>), grid2, dim3(256), 0, stream, a);
       return hipGetLastError();
     }
@@ -21,7 +21,7 @@ static hipError_t launch_one(const DecodeShape& s, const FwdArgs& a, hipStream_t
                        stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid2(a.rows, a.Hkv, a.B);
+  dim3 grid2(a.rows, a.Hkv, a.B * (DV / kReduceCols));
   hipLaunchKernelGGL((decode_reduce_kernel<E, DV>), grid2, dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -251,7 +251,8 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   }
 }
 
-// One 256-thread workgroup per (query row, kv head, batch item). Pass 1 finds
+// One 256-thread workgroup per (16-column slice, query row, kv head, batch
+// item). Pass 1 finds
 // the largest split maximum (with the sink). Pass 2 walks the splits in chunks
 // of 256: each thread turns one split's maximum into its weight in LDS and adds
 // that split's share of the sum; then SG groups of threads, each lane owning
@@ -259,12 +260,15 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
 // (independent loads, many in flight). The groups' sums meet in LDS.
 template <class E, int DV>
 __global__ void __launch_bounds__(256) decode_reduce_kernel(FwdArgs a) {
-  constexpr int NCG = (DV + 3) / 4;  // four-column groups
+  constexpr int CS = kReduceCols;    // value columns per workgroup
+  constexpr int NCG = CS / 4;        // four-column groups
   constexpr int SG = 256 / NCG;      // split lanes
+  static_assert(DV % CS == 0, "value columns split into whole slices");
   __shared__ float fw[256];
   __shared__ float red[4];
   __shared__ f32x4 accs[SG][NCG];
-  const int r = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  const int r = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z / (DV / CS);
+  const int c0 = (blockIdx.z % (DV / CS)) * CS;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int h = hkv * a.group + r / a.Lq;
   const int iq = r % a.Lq;
@@ -272,7 +276,7 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(FwdArgs a) {
   const size_t total_rows = (size_t)a.B * a.Hkv * a.nsplit * a.rows;
   const size_t row0 = pair * a.nsplit * a.rows + r;        // split sp's row: row0 + sp * rows
   const float* pml = a.part + row0 * 4;
-  const float* po = a.part + total_rows * 4 + row0 * DV;
+  const float* po = a.part + total_rows * 4 + row0 * DV + c0;
   const size_t ml_step = (size_t)a.rows * 4, o_step = (size_t)a.rows * DV;
 
   const bool has_sink = a.sinks != nullptr;
@@ -320,7 +324,7 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(FwdArgs a) {
 #pragma unroll
   for (int g = 1; g < SG; ++g) x += accs[g][t];
   x *= inv;
-  uint16_t* op = (uint16_t*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq) * DV;
+  uint16_t* op = (uint16_t*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq) * DV + c0;
   const u32x2 st = {pack2<E>(x[0], x[1]), pack2<E>(x[2], x[3])};
   st_global8(op + t * 4, st);
 }

@@ -58,6 +58,7 @@ hipError_t launch_zero_fill(void* out, int64_t bytes, hipStream_t stream);
 constexpr int kPrefillWaves = 4;
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeBN = 32;       // keys per decode tile
+constexpr int kReduceCols = 16;     // value columns per decode-reduce workgroup
 constexpr int head_max(int D, int Dv) { return D > Dv ? D : Dv; }
 // 32x32 MFMA tiles (32 query rows per wavefront) up to 128-wide heads; 16x16
 // tiles above, where a 32-row output accumulator would not fit in registers.

@@ -230,7 +230,7 @@ def main() -> int:
             "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
         },
         "roofline": {
-            "kernel": "prefill_kernel (bf16, 32x32x16 MFMA, D=128)",
+            "kernel": "prefill_fast_kernel (bf16, 32x32x16 MFMA, D=Dv=128)",
             "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_pre,

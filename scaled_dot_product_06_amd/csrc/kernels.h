@@ -63,11 +63,13 @@ constexpr int head_max(int D, int Dv) { return D > Dv ? D : Dv; }
 // 32x32 MFMA tiles (32 query rows per wavefront) up to 128-wide heads; 16x16
 // tiles above, where a 32-row output accumulator would not fit in registers.
 constexpr int prefill_mf(int elem, int D, int Dv) { return head_max(D, Dv) <= 128 ? 32 : 16; }
-constexpr int prefill_bn(int elem, int D, int Dv) {
-  return elem == kF32 ? (head_max(D, Dv) <= 128 ? 32 : 16) : (head_max(D, Dv) <= 256 ? 64 : 32);
-}
-// The 64/128-wide 16-bit prefill shapes run the double-buffered direct-load kernel.
+// The 64/128-wide 16-bit prefill shapes run the pipelined direct-load kernel.
 constexpr bool prefill_is_fast(int elem, int D, int Dv) { return elem != kF32 && D == Dv && (D == 64 || D == 128); }
+constexpr int prefill_bn(int elem, int D, int Dv) {
+  return elem == kF32 ? (head_max(D, Dv) <= 128 ? 32 : 16)
+                      : (prefill_is_fast(elem, D, Dv) || head_max(D, Dv) > 256 ? 32 : 64);
+}
+constexpr int prefill_rows(int elem, int D, int Dv) { return prefill_mf(elem, D, Dv); }
 constexpr int prefill_waves(int elem, int D, int Dv) { return kPrefillWaves; }
 // 16x16 tiles when the packed query rows fit (and the head is a whole number
 // of 32-wide k-steps), else 32x32.

@@ -11,9 +11,11 @@ static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_
   constexpr int BN = prefill_bn(elem, D, DV);
   dim3 grid(a.head_blocks * a.nqb, 1, 1);
   if constexpr (prefill_is_fast(elem, D, DV)) {
-    static_assert(MF == FastCfg<D>::MF && BN == FastCfg<D>::BN && prefill_waves(elem, D, DV) == FastCfg<D>::NW,
+    using C = FastCfg<D>;
+    static_assert(MF == C::MF && BN == C::BN && prefill_waves(elem, D, DV) == C::NW &&
+                      prefill_rows(elem, D, DV) == C::ROWS,
                   "planner geometry must match the kernel");
-    hipLaunchKernelGGL((prefill_fast_kernel<E, D>), grid, dim3(FastCfg<D>::NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((prefill_fast_kernel<E, D>), grid, dim3(C::NW * 64), 0, stream, a);
   } else {
     hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves>), grid, dim3(kPrefillWaves * 64), 0,
                        stream, a);

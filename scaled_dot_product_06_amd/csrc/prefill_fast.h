@@ -1,20 +1,29 @@
-// Prefill for 16-bit inputs with D = Dv in {64, 128}: the same tiled
-// online-softmax walk as prefill_kernel (lattice-inference
-// "src/attention/flash.rs", run_tiled_attention_head; causal alignment of
-// nuvec-core "tests/fast.rs"), laid out for gfx950 occupancy:
+// Prefill for 16-bit inputs with D = Dv in {64, 128}: the tiled online-softmax
+// walk of lattice-inference "src/attention/flash.rs" (run_tiled_attention_head)
+// with the bottom-right causal alignment of nuvec-core "tests/fast.rs"
+// (attention_fallback_matches_a_direct_formula), laid out for gfx950:
 //
+//  * each wavefront owns one 32-row MFMA block of query rows and the
+//    workgroup's four wavefronts share every K/V tile (one head each under
+//    grouped queries); the register budget leaves room for two wavefronts
+//    per SIMD, which hide each other's latencies;
 //  * K and V tiles go from global memory straight into LDS
 //    (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16 * lane),
-//    so no registers hold tile data and no LDS store instructions are issued;
-//  * two LDS stages: tile t+1 streams in while tile t is computed, with one
-//    workgroup barrier per tile; the stages are distinct LDS objects so the
-//    compiler can tell the loads into one from the reads of the other;
-//  * each LDS row is stored with its 16-byte chunks permuted by an XOR of the
-//    row index (different for K and V), chosen so that the K-operand reads
-//    (16 consecutive rows, one chunk each) and the V transpose reads (8
-//    consecutive rows, four chunks each) touch every bank equally;
-//  * the register budget is held to two wavefronts per SIMD, so one
-//    wavefront's softmax arithmetic overlaps the other's MFMA work.
+//    four stages, three tiles ahead of the compute, one barrier per tile;
+//    the stages are distinct LDS objects so the compiler can tell the loads
+//    into one stage from the reads of another;
+//  * the loop is software-pipelined inside each wavefront: the QK^T MFMAs of
+//    tile t+1 are issued among the exponentials of tile t, and the PV MFMAs
+//    of tile t among the row maxima of tile t+1, so the matrix cores and the
+//    vector ALUs work at the same time;
+//  * a tile some row sees only in part (the causal diagonal, a ragged end,
+//    every tile under a boolean mask) has its hidden scores set to -inf and
+//    its row maxima taken again at the top of its step; other tiles skip
+//    that branch, so the pipelined body has a single path;
+//  * each LDS row holds its 16-byte chunks permuted by an XOR of the row index
+//    (different for K and V), so the K-operand reads (16 consecutive rows, one
+//    chunk each) and the V transpose reads (8 consecutive rows, four chunks
+//    each) touch every bank equally.
 #pragma once
 
 #include "attn_device.h"
@@ -25,7 +34,9 @@ namespace sdpa {
 template <int D>
 struct FastCfg {
   static constexpr int MF = 32, KW = 16, ACC = 16, KG = 2;
-  static constexpr int BN = 64;                 // keys per tile
+  static constexpr int QB = 1;                  // 32-row query blocks per wavefront
+  static constexpr int ROWS = QB * MF;          // query rows per wavefront
+  static constexpr int BN = 32;                 // keys per tile
   static constexpr int NW = 4;                  // wavefronts per workgroup
   static constexpr int NT = NW * 64;
   static constexpr int RB = D * 2;              // bytes per row
@@ -35,10 +46,12 @@ struct FastCfg {
   static constexpr int LOADS = TILE_BYTES / 1024;  // direct-load instructions per tile and tensor
   static constexpr int LOADS_PER_WAVE = LOADS / NW;
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K then V
-  static constexpr int NQC = D / KW;
-  static constexpr int NSB = BN / MF;
-  static constexpr int NPV = BN / KW;
-  static constexpr int NDB = D / MF;
+  static constexpr int LOADS_PER_TILE = 2 * LOADS_PER_WAVE;  // per wavefront, K and V
+  static constexpr int NQC = D / KW;            // k-steps of QK^T
+  static constexpr int NSB = BN / MF;           // 32-key blocks per tile
+  static constexpr int NPV = BN / KW;           // k-steps of PV
+  static constexpr int NDB = D / MF;            // 32-column output blocks
+  static constexpr int NPK = NSB * ACC / 2;     // packed weight pairs per query block
   static_assert(D == 64 || D == 128, "fast prefill covers 64- and 128-wide heads");
   static_assert(LOADS % NW == 0, "loads divide among wavefronts");
 };
@@ -49,17 +62,22 @@ template <int D> __device__ __forceinline__ int swz_v(int row) {
   return 4 * ((row / (256 / FastCfg<D>::RB)) % (FastCfg<D>::CPR / 4));
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding and leaves the other counters alone (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8). Given as the builtin so that
+// the compiler's own wait tracking sees it.
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 template <class E, int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_fast_kernel(FwdArgs a) {
   using C = FastCfg<D>;
-  constexpr int MF = C::MF, ACC = C::ACC, BN = C::BN;
+  constexpr int MF = C::MF, ACC = C::ACC, BN = C::BN, QB = C::QB;
   using acc_t = f32x16;
-  // Two stages as two distinct LDS objects: the compiler can then prove that
-  // the direct loads into one stage never alias the reads of the other, and
-  // does not make the reads of tile t wait for the loads of tile t+1.
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds3[C::STAGE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -69,7 +87,7 @@ prefill_fast_kernel(FwdArgs a) {
 
   const int heads = a.Hq * a.B / a.head_blocks;
   const int wph = C::NW / heads;
-  const int bm = wph * MF;
+  const int bm = wph * C::ROWS;
   int hb, qb;
   prefill_item((int)blockIdx.x, a.head_blocks, a.nqb, a.group / heads, hb, qb);
   const int groups_per_b = a.Hq / heads;
@@ -77,47 +95,51 @@ prefill_fast_kernel(FwdArgs a) {
   const int h0 = (hb % groups_per_b) * heads;
   const int hkv = h0 / a.group;
   const int h = h0 + w / wph;
-  const int wi0 = qb * bm + (w % wph) * MF;
-  const int iq = wi0 + col;
+  const int wi0 = qb * bm + (w % wph) * C::ROWS;
   const int shift = a.Lk - a.Lq;
 
+  // keys the workgroup needs (its last row's causal limit)
   int kend = a.Lk;
   if (a.mask_kind == kMaskCausal) kend = min(a.Lk, min(qb * bm + bm, a.Lq) - 1 + shift + 1);
   if (kend < 0) kend = 0;
   const int ntiles = (kend + BN - 1) / BN;
-
+  // keys every row of this wavefront sees
+  int w_kfull = a.mask_kind == kMaskBool ? 0 : a.Lk;
+  if (a.mask_kind == kMaskCausal) w_kfull = min(a.Lk, wi0 + shift + 1);
   const bool wave_live = wi0 < a.Lq;
-  const int w_last = min(wi0 + MF, a.Lq) - 1;
-  int w_kend = a.Lk, w_kfull = a.Lk;
-  if (a.mask_kind == kMaskCausal) {
-    w_kend = min(a.Lk, w_last + shift + 1);
-    w_kfull = min(a.Lk, wi0 + shift + 1);
-  } else if (a.mask_kind == kMaskBool) {
-    w_kfull = 0;
+
+  int iq[QB];
+  u32x4 qop[QB][C::NQC];
+#pragma unroll
+  for (int r = 0; r < QB; ++r) {
+    iq[r] = wi0 + r * MF + col;
+    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(b * a.Hq + h) * a.Lq + iq[r]) * D;
+#pragma unroll
+    for (int c = 0; c < C::NQC; ++c) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (iq[r] < a.Lq) x = ld_global16(qp + c * C::KW + kg * 8);
+      qop[r][c] = x ^ a.qsign;
+    }
   }
 
-  const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(b * a.Hq + h) * a.Lq + iq) * D;
-  u32x4 qop[C::NQC];
+  acc_t o[QB][C::NDB];
 #pragma unroll
-  for (int c = 0; c < C::NQC; ++c) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (iq < a.Lq) x = ld_global16(qp + c * C::KW + kg * 8);
-    qop[c] = x ^ a.qsign;
-  }
-
-  acc_t o[C::NDB];
+  for (int r = 0; r < QB; ++r)
 #pragma unroll
-  for (int d = 0; d < C::NDB; ++d) o[d] = acc_t{};
-  float m = -INFINITY, l = 0.0f, sink2 = 0.0f;
+    for (int d = 0; d < C::NDB; ++d) o[r][d] = acc_t{};
+  float m[QB], l[QB], tmax[QB];
+  float sink2 = 0.0f;
   const bool has_sink = a.sinks != nullptr;
-  if (has_sink) {
-    sink2 = half_to_f32<E>(((const uint16_t*)a.sinks)[h]) * kLog2e;
-    m = sink2;
+  if (has_sink) sink2 = half_to_f32<E>(((const uint16_t*)a.sinks)[h]) * kLog2e;
+#pragma unroll
+  for (int r = 0; r < QB; ++r) {
+    m[r] = has_sink ? sink2 : -INFINITY;
+    l[r] = 0.0f;
+    tmax[r] = -INFINITY;
   }
 
   const uint8_t* kbase = (const uint8_t*)a.k + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * C::RB;
   const uint8_t* vbase = (const uint8_t*)a.v + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * C::RB;
-  const uint8_t* mrow = a.mask + (size_t)iq * a.Lk;
 
   // direct loads: per lane, byte offsets of its 16-byte chunk within the tile
   // (row blk*ROWS_PER_KB + lane/CPR, global chunk permuted by the row's XOR)
@@ -160,71 +182,103 @@ prefill_fast_kernel(FwdArgs a) {
   const int tr_chunk = ((lane >> 4) & 1) * 2 + (tr_c >> 1);  // chunk within a 32-column block
   const int tr_half = (tr_c & 1) * 8;
 
-  auto compute = [&](int t, const uint8_t* Ks) {
-    const int k0 = t * BN;
-    const bool full = k0 + BN <= w_kfull;
-    const uint8_t* Vs = Ks + C::TILE_BYTES;
-
-    acc_t s[C::NSB];
+  // S^T = K Q^T for one tile into s (zeroed here)
+  auto qk = [&](const uint8_t* Ks, acc_t (&s)[QB][C::NSB]) {
 #pragma unroll
-    for (int nb = 0; nb < C::NSB; ++nb) s[nb] = acc_t{};
+    for (int r = 0; r < QB; ++r)
 #pragma unroll
-    for (int c = 0; c < C::NQC; ++c) {
+      for (int nb = 0; nb < C::NSB; ++nb) s[r][nb] = acc_t{};
+#pragma unroll
+    for (int c = 0; c < C::NQC; ++c)
 #pragma unroll
       for (int nb = 0; nb < C::NSB; ++nb) {
         const int row = nb * MF + col;
         const u32x4 kop =
             *reinterpret_cast<const u32x4*>(Ks + row * C::RB + (((2 * c + kg) ^ swz_k<D>(row)) * 16));
-        s[nb] = mma16<E, MF>(kop, qop[c], s[nb]);
+#pragma unroll
+        for (int r = 0; r < QB; ++r) s[r][nb] = mma16<E, MF>(kop, qop[r][c], s[r][nb]);
       }
-    }
+  };
 
-    float mx = -INFINITY;
-    if (full) {
+  // scaled row maxima of a tile every row sees in full
+  auto tile_max_full = [&](acc_t (&s)[QB][C::NSB]) {
+#pragma unroll
+    for (int r = 0; r < QB; ++r) {
+      float mx = -INFINITY;
 #pragma unroll
       for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
-        for (int i = 0; i < ACC; ++i) mx = fmaxf(mx, s[nb][i]);
-    } else {
+        for (int i = 0; i < ACC; ++i) mx = fmaxf(mx, s[r][nb][i]);
+      mx = row_max<MF>(mx);
+      tmax[r] = mx * a.c;
+    }
+  };
+  // the same for a tile some row does not fully see: hidden scores become -inf
+  auto tile_max_masked = [&](int t, acc_t (&s)[QB][C::NSB]) {
+    const int k0 = t * BN;
+#pragma unroll
+    for (int r = 0; r < QB; ++r) {
+      const bool row_ok = iq[r] < a.Lq;
+      if (a.mask_kind == kMaskBool) {
+        const uint8_t* mrow = a.mask + (size_t)min(iq[r], a.Lq - 1) * a.Lk;
+#pragma unroll
+        for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+          for (int i = 0; i < ACC; ++i) {
+            const int key = k0 + nb * MF + acc_row<MF>(i, kg);
+            const bool vis = row_ok & (key < a.Lk) & (mrow[min(key, a.Lk - 1)] != 0);
+            s[r][nb][i] = vis ? s[r][nb][i] : -INFINITY;
+          }
+      } else {
+        // causal (or no mask past the last key)
+        const int lim = a.mask_kind == kMaskCausal ? min(iq[r] + shift, a.Lk - 1) : a.Lk - 1;
+#pragma unroll
+        for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+          for (int i = 0; i < ACC; ++i) {
+            const int key = k0 + nb * MF + acc_row<MF>(i, kg);
+            const bool vis = row_ok & (key <= lim);
+            s[r][nb][i] = vis ? s[r][nb][i] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
-        for (int i = 0; i < ACC; ++i) {
-          const int key = k0 + nb * MF + acc_row<MF>(i, kg);
-          bool vis = key < a.Lk && iq < a.Lq;
-          if (a.mask_kind == kMaskCausal) vis = vis && key <= iq + shift;
-          else if (a.mask_kind == kMaskBool) vis = vis && mrow[key] != 0;
-          if (!vis) s[nb][i] = -INFINITY;
-          mx = fmaxf(mx, s[nb][i]);
+        for (int i = 0; i < ACC; ++i) mx = fmaxf(mx, s[r][nb][i]);
+      mx = row_max<MF>(mx);
+      tmax[r] = (mx == -INFINITY) ? -INFINITY : mx * a.c;
+    }
+  };
+
+  // weights of one tile, rounded to 16 bits for the MFMA; the running sum adds
+  // the same rounded weights (two per v_dot2), so numerator and denominator agree
+  auto weights = [&](acc_t (&s)[QB][C::NSB], uint32_t (&pk)[QB][C::NPK]) {
+#pragma unroll
+    for (int r = 0; r < QB; ++r) {
+      const float mu = (m[r] == -INFINITY) ? 0.0f : m[r];
+#pragma unroll
+      for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+        for (int i = 0; i < ACC; i += 2) {
+          const float p0 = fast_exp2(fmaf(s[r][nb][i], a.c, -mu));
+          const float p1 = fast_exp2(fmaf(s[r][nb][i + 1], a.c, -mu));
+          pk[r][(nb * ACC + i) / 2] = pack2<E>(p0, p1);
         }
-    }
-    mx = row_max<MF>(mx);
-    const float tmax = (mx == -INFINITY) ? -INFINITY : mx * a.c;
-    softmax_rebase<C::NDB>(tmax, m, l, o);
-    const float mu = (m == -INFINITY) ? 0.0f : m;
-
-    // weights, rounded to 16 bits for the MFMA; the running sum adds the same
-    // rounded weights (two per v_dot2), so numerator and denominator agree
-    uint32_t pk[C::NSB * ACC / 2];
+      float lsum0 = 0.0f, lsum1 = 0.0f;
 #pragma unroll
-    for (int nb = 0; nb < C::NSB; ++nb)
-#pragma unroll
-      for (int i = 0; i < ACC; i += 2) {
-        const float p0 = fast_exp2(fmaf(s[nb][i], a.c, -mu));
-        const float p1 = fast_exp2(fmaf(s[nb][i + 1], a.c, -mu));
-        pk[(nb * ACC + i) / 2] = pack2<E>(p0, p1);
+      for (int j = 0; j < C::NPK; j += 2) {
+        lsum0 = pair_sum<E>(pk[r][j], lsum0);
+        lsum1 = pair_sum<E>(pk[r][j + 1], lsum1);
       }
-    float lsum0 = 0.0f, lsum1 = 0.0f;
-#pragma unroll
-    for (int j = 0; j < C::NSB * ACC / 2; j += 2) {
-      lsum0 = pair_sum<E>(pk[j], lsum0);
-      lsum1 = pair_sum<E>(pk[j + 1], lsum1);
+      l[r] += lsum0 + lsum1;
     }
-    l += lsum0 + lsum1;
+  };
 
+  // O^T += V^T P^T for one tile
+  auto pv = [&](const uint8_t* Vs, const uint32_t (&pk)[QB][C::NPK]) {
 #pragma unroll
     for (int t8 = 0; t8 < C::NPV; ++t8) {
-      const u32x4 pb = {pk[4 * t8], pk[4 * t8 + 1], pk[4 * t8 + 2], pk[4 * t8 + 3]};
       const int keyA = ((8 * t8) / ACC) * MF + acc_row<MF>((8 * t8) % ACC, kg) + tr_e;
       const int keyB = ((8 * t8 + 4) / ACC) * MF + acc_row<MF>((8 * t8 + 4) % ACC, kg) + tr_e;
       const uint8_t* vA = Vs + keyA * C::RB + tr_half;
@@ -236,41 +290,91 @@ prefill_fast_kernel(FwdArgs a) {
         const u32x2 ra = lds_read_tr16((const uint16_t*)(vA + ((ch ^ swA) * 16)));
         const u32x2 rb = lds_read_tr16((const uint16_t*)(vB + ((ch ^ swB) * 16)));
         const u32x4 va = {ra[0], ra[1], rb[0], rb[1]};
-        o[db] = mma16<E, MF>(va, pb, o[db]);
+#pragma unroll
+        for (int r = 0; r < QB; ++r) {
+          const u32x4 pb = {pk[r][4 * t8], pk[r][4 * t8 + 1], pk[r][4 * t8 + 2], pk[r][4 * t8 + 3]};
+          o[r][db] = mma16<E, MF>(va, pb, o[r][db]);
+        }
       }
     }
   };
 
-  // one barrier per tile: tile t's loads have landed (own wait + barrier) and
-  // every wavefront has finished tile t-1, whose stage the next loads reuse
+  // Pipelined step t: tile t's weights and PV, tile t+1's scores and maxima.
+  // Scur holds tile t, Snext tile t+1 and Sload (last read for tile t-1)
+  // receives tile t+3.
+  acc_t sa[QB][C::NSB], sb[QB][C::NSB];
+  uint32_t pk[QB][C::NPK];
+  auto step = [&](int t, acc_t (&scur)[QB][C::NSB], acc_t (&snext)[QB][C::NSB], const uint8_t* Scur,
+                  const uint8_t* Snext, uint8_t* Sload) {
+    // Tile t+1 has landed: the loads complete in issue order, so waiting
+    // until only tile t+2's are outstanding suffices. The barrier then also
+    // guarantees every wavefront has finished tile t-1 (its LDS reads are
+    // drained before it arrives). A plain s_barrier: the release fence of
+    // __syncthreads would also wait for tile t+2's loads.
+    if (t + 2 < ntiles) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(C::LOADS_PER_TILE));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 3 < ntiles) issue_tile((t + 3) * BN, Sload);
+    if ((t + 1) * BN > w_kfull) tile_max_masked(t, scur);
+#pragma unroll
+    for (int r = 0; r < QB; ++r) softmax_rebase<C::NDB>(tmax[r], m[r], l[r], o[r]);
+    qk(Snext, snext);
+    weights(scur, pk);
+    pv(Scur + C::TILE_BYTES, pk);
+    tile_max_full(snext);
+  };
+
+  // prologue: tiles 0..2 in flight, tile 0's scores and maxima
   if (ntiles > 0) issue_tile(0, lds0);
-  for (int t = 0; t < ntiles; t += 2) {
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 1 < ntiles) issue_tile((t + 1) * BN, lds1);
-    if (wave_live && t * BN < w_kend) compute(t, lds0);
+  if (ntiles > 1) issue_tile(BN, lds1);
+  if (ntiles > 2) issue_tile(2 * BN, lds2);
+  if (ntiles > 2) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * C::LOADS_PER_TILE));
+  } else if (ntiles > 1) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(C::LOADS_PER_TILE));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  }
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (ntiles > 0) {
+    qk(lds0, sa);
+    tile_max_full(sa);
+  }
+  // Stage of step t is t % 4 and scores alternate between sa (even t) and sb,
+  // so every call has fixed arguments. The last step also scores a next
+  // tile, from a stage holding stale data, and discards the result: one extra
+  // QK^T per workgroup keeps a separate final step out of the loop.
+  for (int t = 0; t < ntiles; t += 4) {
+    step(t, sa, sb, lds0, lds1, lds3);
     if (t + 1 >= ntiles) break;
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 2 < ntiles) issue_tile((t + 2) * BN, lds0);
-    if (wave_live && (t + 1) * BN < w_kend) compute(t + 1, lds1);
+    step(t + 1, sb, sa, lds1, lds2, lds0);
+    if (t + 2 >= ntiles) break;
+    step(t + 2, sa, sb, lds2, lds3, lds1);
+    if (t + 3 >= ntiles) break;
+    step(t + 3, sb, sa, lds3, lds0, lds2);
   }
 
   if (!wave_live) return;
-  float lt = row_sum<MF>(l);
-  if (has_sink) lt += fast_exp2(sink2 - m);
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  if (iq >= a.Lq) return;
-  uint16_t* op = (uint16_t*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq) * D;
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
+  for (int r = 0; r < QB; ++r) {
+    float lt = row_sum<MF>(l[r]);
+    if (has_sink) lt += fast_exp2(sink2 - m[r]);
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    if (iq[r] >= a.Lq) continue;
+    uint16_t* op = (uint16_t*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq[r]) * D;
 #pragma unroll
-    for (int g4 = 0; g4 < ACC / 4; ++g4) {
-      const int dv = db * MF + g4 * 4 * C::KG + kg * 4;
-      const u32x2 st = {pack2<E>(o[db][g4 * 4 + 0] * inv, o[db][g4 * 4 + 1] * inv),
-                        pack2<E>(o[db][g4 * 4 + 2] * inv, o[db][g4 * 4 + 3] * inv)};
-      st_global8(op + dv, st);
-    }
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < ACC / 4; ++g4) {
+        const int dv = db * MF + g4 * 4 * C::KG + kg * 4;
+        const u32x2 st = {pack2<E>(o[r][db][g4 * 4 + 0] * inv, o[r][db][g4 * 4 + 1] * inv),
+                          pack2<E>(o[r][db][g4 * 4 + 2] * inv, o[r][db][g4 * 4 + 3] * inv)};
+        st_global8(op + dv, st);
+      }
+  }
 }
 
 }  // namespace sdpa

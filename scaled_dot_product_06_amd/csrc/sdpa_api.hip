@@ -188,17 +188,17 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
     *plan = p;
     return SDPA_OK;
   }
-  const int mf = prefill_mf(dtype, (int)D, (int)Dv);
+  const int rows = prefill_rows(dtype, (int)D, (int)Dv);
   const int nw = prefill_waves(dtype, (int)D, (int)Dv);
   const int64_t heads = gcd64(group, nw);
-  const int64_t bm = (nw / heads) * mf;
+  const int64_t bm = (nw / heads) * rows;
   const int64_t nqb = (Lq + bm - 1) / bm;
   if ((B * Hq / heads) * nqb > INT_MAX)
     return fail(SDPA_ERR_UNSUPPORTED, "Lq (%lld) needs %lld query blocks per head block; more than INT_MAX "
                 "workgroups in all", (long long)Lq, (long long)nqb);
   p.route = SDPA_ROUTE_PREFILL;
   p.kernels = 1;
-  p.rows_per_wave = mf;
+  p.rows_per_wave = rows;
   p.waves = nw;
   p.block_n = prefill_bn(dtype, (int)D, (int)Dv);
   p.heads_per_group = (int32_t)heads;

@@ -107,6 +107,69 @@ def cpu_baseline(p, seconds: float):
                       f"each; numpy float64, {dt:.1f} s"}
 
 
+PEAK_FP32_MFMA_TFLOPS = 157.3
+OTHER_WORKLOADS = (1, 2, 4)   # timed and reported; not the headline metric
+
+
+def measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, rounds=5):
+    """Per-call kernel time (HIP events on the library's stream, median of
+    `rounds` batches of `calls`) of the f32 causal prefill, the 8193-key bf16
+    decode and the f16 prefill with a boolean mask and sinks, each against its
+    own roofline. Decode K/V rotates over copies spanning > 2x the 256 MB MALL
+    so every call streams from HBM."""
+    import numpy as np
+    res = {}
+    for num in OTHER_WORKLOADS:
+        p = gen.workload(num)
+        q = to_dev(p.q, p.dtype)
+        mask = None if p.mask is None else torch.from_numpy(np.ascontiguousarray(p.mask)).to(dev)
+        sinks = None if p.sinks is None else to_dev(p.sinks, p.dtype)
+        decode = p.Lq == 1
+        copies = 1
+        if decode:
+            copies = max(1, -(-2 * 256 * 2 ** 20 // decode_bytes(p)))
+        ks = [to_dev(p.k, p.dtype)]
+        vs = [to_dev(p.v, p.dtype)]
+        for _ in range(copies - 1):
+            ks.append(ks[0].clone())
+            vs.append(vs[0].clone())
+        out = torch.empty((p.B, p.Hq, p.Lq, p.Dv), dtype=q.dtype, device=dev)
+
+        def call(i):
+            sd.attention(q, ks[i % copies], vs[i % copies], p.scale, p.mask_kind, mask, sinks, out=out,
+                         stream=stream.cuda_stream)
+
+        for i in range(20):
+            call(i)
+        torch.cuda.synchronize()
+        times = []
+        for r in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(calls):
+                call(r * calls + i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / calls * 1e3)
+        us = sorted(times)[len(times) // 2]
+        rec = {"workload": p.name, "us_per_call": round(us, 2)}
+        if decode:
+            gbps = decode_bytes(p) / us / 1e3
+            rec.update({"kv_bytes_per_call": decode_bytes(p), "GB/s": round(gbps, 1),
+                        "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "kv_copies": copies})
+        else:
+            flop = prefill_flop(p)
+            tf = flop / us / 1e6
+            peak = PEAK_FP32_MFMA_TFLOPS if p.dtype == gen.F32 else PEAK_BF16_TFLOPS
+            rec.update({"flop_per_call": flop, "TFLOP/s": round(tf, 2), "peak_TFLOP/s": peak,
+                        "frac_mfma_peak": round(tf / peak, 4)})
+        res[str(num)] = rec
+        log(f"{p.name}: {us:.1f} us/call " + (f"{rec['GB/s']} GB/s" if decode else f"{rec['TFLOP/s']} TFLOP/s"))
+        del ks, vs, q, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +179,8 @@ def main() -> int:
                     help="extra untimed stepping (seconds) after the warmup steps, so GPU clocks settle")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true", help="skip the reported-only workloads (f32 prefill, "
+                    "8193-key decode, f16 masked prefill with sinks)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
@@ -197,6 +262,8 @@ def main() -> int:
         f"bf16 MFMA peak); decode {dec_ms * 1e3:.1f} us/call = {gbps:.0f} GB/s "
         f"({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM peak); step {step_ms:.3f} ms; wall {wall:.2f} s")
 
+    others = measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log) if not args.no_others else None
+
     pre_plan = sd.sdpa_plan(pre.B, pre.Hq, pre.Hkv, pre.Lq, pre.Lk, pre.D, pre.Dv, pre.mask_kind, False, False,
                             pre.dtype)
     dec_plan = sd.sdpa_plan(dec.B, dec.Hq, dec.Hkv, dec.Lq, dec.Lk, dec.D, dec.Dv, dec.mask_kind, False, False,
@@ -242,6 +309,7 @@ def main() -> int:
             "traffic": traffic_dec,
         },
         "cpu_baseline": None,
+        "other_workloads": others,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the prefill workload ...")

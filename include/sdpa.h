@@ -69,9 +69,11 @@ typedef struct sdpa_plan_t {
   int64_t keys_per_split; /* decode: keys per first-pass workgroup (a power of two, 64..1024,
                              from Lk alone so that batch items never change it) */
   int64_t splits;         /* decode: key blocks per (batch, kv head) */
-  int64_t grid[3];        /* workgroups of the first kernel (x, y, z) */
-  int64_t scratch_bytes;  /* device scratch the call uses, 0 for prefill; decode: per (batch, kv head,
-                             split, packed row) a 16-byte {max, sum} slot and Dv f32 partial outputs */
+  int64_t grid[3];        /* workgroups of the attention kernel (decode: its first pass) (x, y, z) */
+  int64_t scratch_bytes;  /* device scratch the call uses. Decode: per (batch, kv head, split, packed
+                             row) a 16-byte {max, sum} slot and Dv f32 partial outputs. Prefill: 0,
+                             except f16/bf16 with a boolean mask, whose mask a first small kernel
+                             packs into Lq x ceil(Lk/32) 32-bit words (bit j of word w: key 32w+j) */
 } sdpa_plan_t;
 
 /*
@@ -99,8 +101,9 @@ typedef struct sdpa_plan_t {
  * The call is asynchronous: validation errors return before anything is
  * enqueued; a launch failure returns SDPA_ERR_HIP. A given plan gives the
  * same bits run to run, and each batch item's bits do not depend on B.
- * The decode route takes its scratch from a per-(device, stream) buffer that
- * the library allocates on first use and keeps (sdpa_release_workspace frees).
+ * Scratch (decode partials, packed mask bits) comes from a per-(device,
+ * stream) buffer that the library allocates on first use, grows when a call
+ * needs more, and keeps (sdpa_release_workspace frees).
  */
 int sdpa_forward(const void* q, const void* k, const void* v, void* out,
                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
@@ -124,7 +127,7 @@ int sdpa_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
  * stays valid until the thread's next sdpa_* call. */
 const char* sdpa_last_error(void);
 
-/* Wait for the streams that used cached decode scratch, then free it.
+/* Wait for the streams that used cached scratch, then free it.
  * Returns SDPA_OK or SDPA_ERR_HIP. */
 int sdpa_release_workspace(void);
 

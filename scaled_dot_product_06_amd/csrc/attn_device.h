@@ -164,6 +164,13 @@ template <int MF> __device__ __forceinline__ float row_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x if bit `pos` of `word` is set, else -inf: a signed one-bit field extract
+// gives an all-ones or all-zeros keep mask, and one bitfield insert selects.
+__device__ __forceinline__ float keep_if_bit(float x, uint32_t word, int pos) {
+  const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)word, (unsigned)pos, 1u);
+  return __uint_as_float((keep & __float_as_uint(x)) | (~keep & 0xFF800000u));
+}
+
 // Work item (head block hb, query block qb) of prefill workgroup n, for a 1-D
 // grid of head_blocks * nqb workgroups. The dispatcher deals workgroups to the
 // 8 XCDs round-robin; this order makes each XCD walk the head blocks of one

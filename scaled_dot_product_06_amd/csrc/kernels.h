@@ -15,6 +15,9 @@ struct FwdArgs {
   const void* v;
   void* out;
   const uint8_t* mask;   // [Lq, Lk] bytes when mask_kind == kMaskBool
+  const uint32_t* mbits; // 16-bit prefill with a boolean mask: the mask packed as
+                         // [Lq, mwords] words, bit j of word w = key 32w + j visible
+  int mwords;            // ceil(Lk / 32)
   const void* sinks;     // [Hq] in the element type, or null
   int B, Hq, Hkv, Lq, Lk;
   int group;             // Hq / Hkv
@@ -53,6 +56,10 @@ hipError_t launch_prefill(int elem, int D, int Dv, const PrefillShape& s, const 
 hipError_t launch_decode(int elem, int D, int Dv, const DecodeShape& s, const FwdArgs& a,
                          hipStream_t stream, bool* ok);
 hipError_t launch_zero_fill(void* out, int64_t bytes, hipStream_t stream);
+hipError_t launch_mask_bits(const uint8_t* mask, uint32_t* bits, int64_t Lq, int64_t Lk, hipStream_t stream);
+constexpr int64_t mask_words(int64_t Lk) { return (Lk + 31) / 32; }
+// The 16-bit prefill kernels read a boolean mask as packed bits.
+constexpr bool prefill_packs_mask(int elem, int mask_kind) { return elem != kF32 && mask_kind == kMaskBool; }
 
 // Geometry rules shared by the launchers (template arguments) and the planner.
 constexpr int kPrefillWaves = 4;

@@ -122,6 +122,18 @@ prefill_fast_kernel(FwdArgs a) {
     }
   }
 
+  // boolean mask: each lane's row of packed mask words; the word of tile t
+  // is fetched one step ahead (before that step's tile loads are issued)
+  const bool bool_mask = a.mask_kind == kMaskBool;
+  const uint32_t* mbrow[QB];
+  uint32_t mw_cur[QB], mw_nxt[QB];
+#pragma unroll
+  for (int r = 0; r < QB; ++r) {
+    mbrow[r] = bool_mask ? a.mbits + (size_t)min(iq[r], a.Lq - 1) * a.mwords : nullptr;
+    mw_cur[r] = 0u;
+    mw_nxt[r] = (bool_mask && ntiles > 0) ? mbrow[r][0] : 0u;
+  }
+
   acc_t o[QB][C::NDB];
 #pragma unroll
   for (int r = 0; r < QB; ++r)
@@ -214,21 +226,18 @@ prefill_fast_kernel(FwdArgs a) {
     }
   };
   // the same for a tile some row does not fully see: hidden scores become -inf
-  auto tile_max_masked = [&](int t, acc_t (&s)[QB][C::NSB]) {
+  auto tile_max_masked = [&](int t, acc_t (&s)[QB][C::NSB], const uint32_t (&mw)[QB]) {
     const int k0 = t * BN;
 #pragma unroll
     for (int r = 0; r < QB; ++r) {
       const bool row_ok = iq[r] < a.Lq;
       if (a.mask_kind == kMaskBool) {
-        const uint8_t* mrow = a.mask + (size_t)min(iq[r], a.Lq - 1) * a.Lk;
+        // the tile's 32 keys are one word of the row's packed mask (zero past
+        // Lk); the lane's keys sit at acc_row(i, kg) = acc_row(i, 0) + 4 kg
+        static_assert(BN == 32 && C::NSB == 1, "one mask word per tile");
+        const uint32_t wsh = row_ok ? (mw[r] >> (4 * kg)) : 0u;
 #pragma unroll
-        for (int nb = 0; nb < C::NSB; ++nb)
-#pragma unroll
-          for (int i = 0; i < ACC; ++i) {
-            const int key = k0 + nb * MF + acc_row<MF>(i, kg);
-            const bool vis = row_ok & (key < a.Lk) & (mrow[min(key, a.Lk - 1)] != 0);
-            s[r][nb][i] = vis ? s[r][nb][i] : -INFINITY;
-          }
+        for (int i = 0; i < ACC; ++i) s[r][0][i] = keep_if_bit(s[r][0][i], wsh, acc_row<MF>(i, 0));
       } else {
         // causal (or no mask past the last key)
         const int lim = a.mask_kind == kMaskCausal ? min(iq[r] + shift, a.Lk - 1) : a.Lk - 1;
@@ -306,6 +315,13 @@ prefill_fast_kernel(FwdArgs a) {
   uint32_t pk[QB][C::NPK];
   auto step = [&](int t, acc_t (&scur)[QB][C::NSB], acc_t (&snext)[QB][C::NSB], const uint8_t* Scur,
                   const uint8_t* Snext, uint8_t* Sload) {
+    if (bool_mask) {
+#pragma unroll
+      for (int r = 0; r < QB; ++r) {
+        mw_cur[r] = mw_nxt[r];
+        mw_nxt[r] = t + 1 < ntiles ? mbrow[r][t + 1] : 0u;
+      }
+    }
     // Tile t+1 has landed: the loads complete in issue order, so waiting
     // until only tile t+2's are outstanding suffices. The barrier then also
     // guarantees every wavefront has finished tile t-1 (its LDS reads are
@@ -318,7 +334,7 @@ prefill_fast_kernel(FwdArgs a) {
     }
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (t + 3 < ntiles) issue_tile((t + 3) * BN, Sload);
-    if ((t + 1) * BN > w_kfull) tile_max_masked(t, scur);
+    if ((t + 1) * BN > w_kfull) tile_max_masked(t, scur, mw_cur);
 #pragma unroll
     for (int r = 0; r < QB; ++r) softmax_rebase<C::NDB>(tmax[r], m[r], l[r], o[r]);
     qk(Snext, snext);

@@ -114,10 +114,25 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
 
   const uint16_t* kp = (const uint16_t*)a.k + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * D;
   const uint16_t* vp = (const uint16_t*)a.v + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * DV;
-  const uint8_t* mrow = a.mask + (size_t)iq * a.Lk;
+  // boolean mask: the lane's row of packed mask words (tile t covers words
+  // t*BN/32 ..), fetched with the K/V tile one step ahead
+  constexpr int MWT = BN / 32;
+  static_assert(BN % 32 == 0, "tiles hold whole mask words");
+  const bool bool_mask = a.mask_kind == kMaskBool;
+  const uint32_t* mbrow = bool_mask ? a.mbits + (size_t)min(iq, a.Lq - 1) * a.mwords : nullptr;
+  uint32_t mwn[MWT], mwc[MWT];
+#pragma unroll
+  for (int w = 0; w < MWT; ++w) mwn[w] = mwc[w] = 0u;
 
   u32x4 kr[C::KPT], vr[C::VPT];
   auto load_tile = [&](int k0) {
+    if (bool_mask) {
+#pragma unroll
+      for (int w = 0; w < MWT; ++w) {
+        const int idx = k0 / 32 + w;
+        mwn[w] = idx < a.mwords ? mbrow[idx] : 0u;
+      }
+    }
 #pragma unroll
     for (int it = 0; it < C::KPT; ++it) {
       const int c = tid + it * C::NT;
@@ -167,6 +182,8 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
     __syncthreads();
     store_tile();
     __syncthreads();
+#pragma unroll
+    for (int w = 0; w < MWT; ++w) mwc[w] = mwn[w];
     if (t + 1 < ntiles) load_tile(k0 + BN);
     if (!wave_live || k0 >= w_kend) continue;
     const bool full = k0 + BN <= w_kfull;
@@ -190,16 +207,27 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
       for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
         for (int i = 0; i < ACC; ++i) mx = fmaxf(mx, s[nb][i]);
+    } else if (bool_mask) {
+      // lane's keys: nb*MF + acc_row(i, 0) + 4 kg; packed bits are zero past Lk
+#pragma unroll
+      for (int nb = 0; nb < C::NSB; ++nb) {
+        const uint32_t wsh = iq < a.Lq ? (mwc[(nb * MF) / 32] >> (4 * kg)) : 0u;
+#pragma unroll
+        for (int i = 0; i < ACC; ++i) {
+          s[nb][i] = keep_if_bit(s[nb][i], wsh, (nb * MF) % 32 + acc_row<MF>(i, 0));
+          mx = fmaxf(mx, s[nb][i]);
+        }
+      }
     } else {
+      // causal diagonal, or keys past Lk
+      const int lim = a.mask_kind == kMaskCausal ? min(iq + shift, a.Lk - 1) : a.Lk - 1;
 #pragma unroll
       for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
         for (int i = 0; i < ACC; ++i) {
           const int key = k0 + nb * MF + acc_row<MF>(i, kg);
-          bool vis = key < a.Lk && iq < a.Lq;
-          if (a.mask_kind == kMaskCausal) vis = vis && key <= iq + shift;
-          else if (a.mask_kind == kMaskBool) vis = vis && mrow[key] != 0;
-          if (!vis) s[nb][i] = -INFINITY;
+          const bool vis = (iq < a.Lq) & (key <= lim);
+          s[nb][i] = vis ? s[nb][i] : -INFINITY;
           mx = fmaxf(mx, s[nb][i]);
         }
     }

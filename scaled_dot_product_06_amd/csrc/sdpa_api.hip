@@ -1,5 +1,6 @@
 // The C ABI (include/sdpa.h): argument validation, the router between the
-// prefill and decode kernels, decode scratch, and the launches.
+// prefill and decode kernels, scratch (decode partials, packed mask bits),
+// and the launches.
 //
 // The router keeps the shape of the rules in nuvec-core
 // "tests/attention_plan.rs" (a fused tiled kernel for many queries; for few
@@ -51,6 +52,36 @@ hipError_t launch_zero_fill(void* out, int64_t bytes, hipStream_t stream) {
   if (blocks > (1 << 20)) blocks = 1 << 20;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (u32x4_t*)out, n16);
+  return hipGetLastError();
+}
+
+// Packs the [Lq, Lk] byte mask into bits for the 16-bit prefill kernels: word
+// w of row i holds keys 32w..32w+31, bit j set iff mask[i][32w + j] != 0 (keys
+// past Lk read as 0). One wavefront reads 64 consecutive mask bytes of a row
+// and a ballot turns them into two words; a grid-stride loop covers any size.
+__global__ void __launch_bounds__(256) mask_bits_kernel(const uint8_t* mask, uint32_t* bits, int64_t Lq,
+                                                        int64_t Lk, int64_t nwords) {
+  const int lane = threadIdx.x & 63;
+  const int64_t segs = (Lk + 63) / 64;
+  const int64_t total = Lq * segs;
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / 64);
+  for (int64_t wv = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); wv < total; wv += nwaves) {
+    const int64_t row = wv / segs, seg = wv % segs;
+    const int64_t key = seg * 64 + lane;
+    const bool on = key < Lk && mask[row * Lk + key] != 0;
+    const uint64_t word2 = __ballot(on);
+    const int64_t w = seg * 2 + (lane >> 5);
+    if ((lane & 31) == 0 && w < nwords) bits[row * nwords + w] = (uint32_t)(word2 >> (lane & 32));
+  }
+}
+
+hipError_t launch_mask_bits(const uint8_t* mask, uint32_t* bits, int64_t Lq, int64_t Lk, hipStream_t stream) {
+  const int64_t waves = Lq * ((Lk + 63) / 64);
+  int64_t blocks = (waves + 3) / 4;
+  if (blocks > (1 << 16)) blocks = 1 << 16;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(mask_bits_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, mask, bits, Lq, Lk,
+                     mask_words(Lk));
   return hipGetLastError();
 }
 
@@ -205,6 +236,13 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
   p.grid[0] = (B * Hq / heads) * nqb;   // one workgroup per (head block, query block)
   p.grid[1] = 1;
   p.grid[2] = 1;
+  if (prefill_packs_mask(dtype, mask_kind)) {
+    // the boolean mask is packed into bits by a first small kernel
+    int64_t sb;
+    if (!mul3(Lq, mask_words(Lk), 4, &sb)) return fail(SDPA_ERR_INVALID, "mask-bit scratch size overflows");
+    p.kernels = 2;
+    p.scratch_bytes = sb;
+  }
   *plan = p;
   return SDPA_OK;
 }
@@ -316,6 +354,15 @@ int sdpa_forward(const void* q, const void* k, const void* v, void* out, int64_t
   } else {
     a.head_blocks = (int)(B * Hq / p.heads_per_group);
     a.nqb = (int)(p.grid[0] / a.head_blocks);
+    if (prefill_packs_mask(dtype, mask_kind)) {
+      void* bits = nullptr;
+      e = get_scratch(stream, (size_t)p.scratch_bytes, &bits);
+      if (e != hipSuccess) return fail(SDPA_ERR_HIP, "mask-bit scratch allocation failed: %s", hipGetErrorString(e));
+      e = launch_mask_bits(mask, (uint32_t*)bits, Lq, Lk, stream);
+      if (e != hipSuccess) return fail(SDPA_ERR_HIP, "mask packing launch failed: %s", hipGetErrorString(e));
+      a.mbits = (const uint32_t*)bits;
+      a.mwords = (int)mask_words(Lk);
+    }
     PrefillShape s{p.rows_per_wave, p.waves, p.heads_per_group, p.block_n,
                    (int)((p.waves / p.heads_per_group) * p.rows_per_wave)};
     e = launch_prefill(dtype, (int)D, (int)Dv, s, a, stream, &ok);

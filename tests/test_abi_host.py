@@ -56,8 +56,12 @@ def test_workload_routes(number, route):
         assert p["splits"] * p["keys_per_split"] >= w["Lk"] > (p["splits"] - 1) * p["keys_per_split"]
         assert p["scratch_bytes"] == w["B"] * w["Hkv"] * p["splits"] * rows * (w["Dv"] + 4) * 4
         assert p["grid"] == (p["splits"], w["Hkv"], w["B"])
+    elif w["mask_kind"] == 2 and w["dtype"] != 0:
+        # 16-bit prefill with a boolean mask: the mask is first packed into bits
+        assert p["kernels"] == 2 and p["scratch_bytes"] == w["Lq"] * -(-w["Lk"] // 32) * 4
     else:
         assert p["kernels"] == 1 and p["scratch_bytes"] == 0
+    if route == "prefill":
         rows_per_block = p["waves"] // p["heads_per_group"] * p["rows_per_wave"]
         head_blocks = w["B"] * w["Hq"] // p["heads_per_group"]
         assert p["grid"] == (head_blocks * -(-w["Lq"] // rows_per_block), 1, 1)

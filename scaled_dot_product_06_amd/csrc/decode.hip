@@ -12,16 +12,16 @@ static hipError_t launch_one(const DecodeShape& s, const FwdArgs& a, hipStream_t
                          stream, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      dim3 grid2(a.rows, a.Hkv, a.B * (DV / kReduceCols));
+      dim3 grid2(a.rows, a.Hkv, a.B * (DV / reduce_cols(DV)));
       hipLaunchKernelGGL((decode_reduce_kernel<E, DV>), grid2, dim3(256), 0, stream, a);
       return hipGetLastError();
     }
   }
-    hipLaunchKernelGGL((decode_split_kernel<E, 32, D, DV, kDecodeWaves>), grid1, dim3(kDecodeWaves * 64), 0,
-                       stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<E, 32, D, DV, kDecodeWaves>), grid1, dim3(kDecodeWaves * 64), 0,
+                     stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid2(a.rows, a.Hkv, a.B * (DV / kReduceCols));
+  dim3 grid2(a.rows, a.Hkv, a.B * (DV / reduce_cols(DV)));
   hipLaunchKernelGGL((decode_reduce_kernel<E, DV>), grid2, dim3(256), 0, stream, a);
   return hipGetLastError();
 }

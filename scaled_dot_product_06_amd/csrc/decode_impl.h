@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   }
 }
 
-// One 256-thread workgroup per (16-column slice, query row, kv head, batch
+// One 256-thread workgroup per (CS-column slice, query row, kv head, batch
 // item). Pass 1 finds
 // the largest split maximum (with the sink). Pass 2 walks the splits in chunks
 // of 256: each thread turns one split's maximum into its weight in LDS and adds
@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
 // (independent loads, many in flight). The groups' sums meet in LDS.
 template <class E, int DV>
 __global__ void __launch_bounds__(256) decode_reduce_kernel(FwdArgs a) {
-  constexpr int CS = kReduceCols;    // value columns per workgroup
+  constexpr int CS = reduce_cols(DV);  // value columns per workgroup
   constexpr int NCG = CS / 4;        // four-column groups
   constexpr int SG = 256 / NCG;      // split lanes
   static_assert(DV % CS == 0, "value columns split into whole slices");

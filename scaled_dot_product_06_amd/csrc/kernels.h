@@ -65,7 +65,8 @@ constexpr bool prefill_packs_mask(int elem, int mask_kind) { return elem != kF32
 constexpr int kPrefillWaves = 4;
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeBN = 32;       // keys per decode tile
-constexpr int kReduceCols = 16;     // value columns per decode-reduce workgroup
+// value columns per decode-reduce workgroup: 32 when they divide Dv, else 16
+constexpr int reduce_cols(int DV) { return DV % 32 == 0 ? 32 : 16; }
 constexpr int head_max(int D, int Dv) { return D > Dv ? D : Dv; }
 // 32x32 MFMA tiles (32 query rows per wavefront) up to 128-wide heads; 16x16
 // tiles above, where a 32-row output accumulator would not fit in registers.

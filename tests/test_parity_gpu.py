@@ -105,6 +105,29 @@ def test_prefill_lengths(Lq, Lk):
         _full_check(p, f"prefill Lq={Lq} Lk={Lk}")
 
 
+def _mask_patterns(Lq, Lk):
+    """Boolean masks that probe the 16-bit prefill's packed 32-key mask words: keys on
+    word edges only (bits 0 and 31, and the ragged last key), a diagonal stripe that
+    shifts by row, and rows hidden entirely (whose output is zero, sinks or not)."""
+    i = np.arange(Lq)[:, None]
+    j = np.arange(Lk)[None, :]
+    return {
+        "word_edges": (j % 32 == 0) | (j % 32 == 31) | (j == Lk - 1),
+        "stripes": (i + j) % 3 == 0,
+        "rows_off": (i % 5 != 2) & (j % 7 != 3),
+    }
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("Lk", [1, 31, 32, 33, 63, 64, 65, 100, 1025])
+def test_prefill_bool_mask_word_edges(D, Lk):
+    for dtype in (BF16, F16):
+        p = gen.make_problem(1300 + Lk + D, 1, 4, 2, 70, Lk, D, D, dtype, 2, sinks=True)
+        for name, pattern in _mask_patterns(p.Lq, Lk).items():
+            p.mask = np.ascontiguousarray(np.broadcast_to(pattern, (p.Lq, Lk)).astype(np.uint8))
+            _full_check(p, f"bool mask {name} D={D} Lk={Lk}")
+
+
 # --- edge cases -------------------------------------------------------------------------------
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")

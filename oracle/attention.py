@@ -23,6 +23,12 @@ softmax row per query, in float64 on the exact values of the stored inputs:
 * a boolean mask is one ``[Lq, Lk]`` matrix shared by every batch item and
   head, nonzero meaning "attend" (nuvec-core "tests/attention_plan.rs",
   ``attention()``; fast.rs, ``window_mask``);
+* a sliding window (causal only) of w keys: query ``i`` at position
+  ``pos = i + Lk - Lq`` sees key ``j`` iff ``pos - w < j <= pos``, the band of
+  nuvec-core "tests/fast.rs" (``window_mask``, and the windowed-kernel tests
+  ``windows_run_fused_and_equal_the_boolean_mask`` and
+  ``window_errors_empty_inputs_and_full_windows``); a window of at least Lk
+  keys is plain causal attention;
 * an optional per-query-head sink is one extra logit in the softmax
   denominator with no value row. Reading taken: the sink is added as given,
   after scaling (it is not multiplied by ``scale``), and takes part in the row
@@ -39,9 +45,14 @@ import numpy as np
 MASK_NONE, MASK_CAUSAL, MASK_BOOL = 0, 1, 2
 
 
-def visible_keys(i: int, Lq: int, Lk: int, mask_kind: int, mask=None) -> np.ndarray:
+def visible_keys(i: int, Lq: int, Lk: int, mask_kind: int, mask=None, window=None) -> np.ndarray:
     """Boolean [Lk] vector: which keys query row ``i`` may attend to."""
     j = np.arange(Lk)
+    if window is not None:
+        if mask_kind != MASK_CAUSAL or window < 1:
+            raise ValueError("a window needs the causal mask and at least one key")
+        pos = i + Lk - Lq
+        return (j <= pos) & (j > pos - window)
     if mask_kind == MASK_NONE:
         return np.ones(Lk, dtype=bool)
     if mask_kind == MASK_CAUSAL:
@@ -51,12 +62,12 @@ def visible_keys(i: int, Lq: int, Lk: int, mask_kind: int, mask=None) -> np.ndar
     raise ValueError(f"unknown mask kind {mask_kind}")
 
 
-def _visible_matrix(rows_i, Lq, Lk, mask_kind, mask):
-    return np.stack([visible_keys(int(i), Lq, Lk, mask_kind, mask) for i in rows_i]) \
+def _visible_matrix(rows_i, Lq, Lk, mask_kind, mask, window=None):
+    return np.stack([visible_keys(int(i), Lq, Lk, mask_kind, mask, window) for i in rows_i]) \
         if len(rows_i) else np.zeros((0, Lk), dtype=bool)
 
 
-def head_probabilities(q_rows, k_head, rows_i, Lq, scale, mask_kind, mask=None, sink=None):
+def head_probabilities(q_rows, k_head, rows_i, Lq, scale, mask_kind, mask=None, sink=None, window=None):
     """Softmax weights for some query rows of one head.
 
     q_rows [n, D], k_head [Lk, D] float64. Returns (p [n, Lk], p_sink [n]):
@@ -66,7 +77,7 @@ def head_probabilities(q_rows, k_head, rows_i, Lq, scale, mask_kind, mask=None, 
     """
     Lk = k_head.shape[0]
     s = scale * (q_rows @ k_head.T)                      # scores, [n, Lk]
-    vis = _visible_matrix(rows_i, Lq, Lk, mask_kind, mask)
+    vis = _visible_matrix(rows_i, Lq, Lk, mask_kind, mask, window)
     s_vis = np.where(vis, s, -np.inf)
     m = s_vis.max(axis=1) if Lk else np.full(len(rows_i), -np.inf)
     if sink is not None:
@@ -84,11 +95,12 @@ def head_probabilities(q_rows, k_head, rows_i, Lq, scale, mask_kind, mask=None, 
     return p, p_sink
 
 
-def sdpa(q, k, v, scale, mask_kind, mask=None, sinks=None, rows=None):
+def sdpa(q, k, v, scale, mask_kind, mask=None, sinks=None, rows=None, window=None):
     """Attention forward in float64.
 
     q [B,Hq,Lq,D], k [B,Hkv,Lk,D], v [B,Hkv,Lk,Dv] (float64), mask [Lq,Lk]
-    (bool, MASK_BOOL only), sinks [Hq] or None.
+    (bool, MASK_BOOL only), sinks [Hq] or None, window (causal only) None or
+    the number of keys each query row reads back from its position.
 
     rows=None returns out [B,Hq,Lq,Dv]. rows = iterable of (b, h, i) returns
     [len(rows), Dv] for just those query rows.
@@ -106,7 +118,7 @@ def sdpa(q, k, v, scale, mask_kind, mask=None, sinks=None, rows=None):
                 hk = h // group
                 sink = None if sinks is None else float(sinks[h])
                 p, _ = head_probabilities(q[b, h], k[b, hk], np.arange(Lq), Lq, scale,
-                                          mask_kind, mask, sink)
+                                          mask_kind, mask, sink, window)
                 out[b, h] = p @ v[b, hk]
         return out
     rows = [tuple(int(x) for x in r) for r in rows]
@@ -120,12 +132,12 @@ def sdpa(q, k, v, scale, mask_kind, mask=None, sinks=None, rows=None):
         idx = [n for n, _ in items]
         ii = np.array([i for _, i in items])
         sink = None if sinks is None else float(sinks[h])
-        p, _ = head_probabilities(q[b, h, ii], k[b, hk], ii, Lq, scale, mask_kind, mask, sink)
+        p, _ = head_probabilities(q[b, h, ii], k[b, hk], ii, Lq, scale, mask_kind, mask, sink, window)
         out[idx] = p @ v[b, hk]
     return out
 
 
-def probabilities(q, k, scale, mask_kind, mask=None, sinks=None):
+def probabilities(q, k, scale, mask_kind, mask=None, sinks=None, window=None):
     """All softmax weights: (p [B,Hq,Lq,Lk], p_sink [B,Hq,Lq])."""
     q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
     B, Hq, Lq, _ = q.shape
@@ -137,5 +149,5 @@ def probabilities(q, k, scale, mask_kind, mask=None, sinks=None):
         for h in range(Hq):
             sink = None if sinks is None else float(sinks[h])
             p[b, h], ps[b, h] = head_probabilities(q[b, h], k[b, h // group], np.arange(Lq),
-                                                   Lq, scale, mask_kind, mask, sink)
+                                                   Lq, scale, mask_kind, mask, sink, window)
     return p, ps

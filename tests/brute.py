@@ -3,8 +3,10 @@ independently of the oracle, for tiny shapes only. Test infrastructure."""
 import math
 
 
-def attention_loops(q, k, v, B, Hq, Hkv, Lq, Lk, D, Dv, scale, mask_kind, mask=None, sinks=None):
-    """q, k, v: nested lists [B][H][L][E]; mask: [Lq][Lk] of 0/1; sinks: [Hq].
+def attention_loops(q, k, v, B, Hq, Hkv, Lq, Lk, D, Dv, scale, mask_kind, mask=None, sinks=None,
+                    window=None):
+    """q, k, v: nested lists [B][H][L][E]; mask: [Lq][Lk] of 0/1; sinks: [Hq];
+    window: with the causal mask, the keys a row reads back from its position.
     Returns nested list [B][Hq][Lq][Dv]."""
     g = Hq // Hkv
     out = []
@@ -17,6 +19,8 @@ def attention_loops(q, k, v, B, Hq, Hkv, Lq, Lk, D, Dv, scale, mask_kind, mask=N
                 keys = []
                 for j in range(Lk):
                     if mask_kind == 1 and j > i + (Lk - Lq):
+                        continue
+                    if window is not None and j + window <= i + (Lk - Lq):
                         continue
                     if mask_kind == 2 and not mask[i][j]:
                         continue

@@ -347,3 +347,82 @@ def test_brute_force_tiny(seed):
                                     scale, kind, bmask.astype(int).tolist(),
                                     None if sinks is None else sinks.tolist()))
     assert np.allclose(got, want.reshape(got.shape), rtol=0, atol=1e-12)
+
+
+# --- sliding windows (nuvec-core tests/fast.rs: window_mask, windowed-kernel tests) --------
+
+def _band(lq, lk, w):
+    """The window written as its boolean band: key j visible from row i iff
+    pos - w < j <= pos with pos = i + lk - lq (fast.rs, window_mask)."""
+    pos = np.arange(lq)[:, None] + (lk - lq)
+    j = np.arange(lk)[None, :]
+    return (j <= pos) & (j > pos - w)
+
+
+@pytest.mark.parametrize("lq,lk", [(1, 9), (5, 9), (9, 9), (12, 7)])
+def test_full_window_is_plain_causal(lq, lk):
+    rng = np.random.default_rng(700 + lq)
+    q, k, v = _rand(rng, 1, 2, lq, 4), _rand(rng, 1, 2, lk, 4), _rand(rng, 1, 2, lk, 3)
+    causal = orc.sdpa(q, k, v, 0.3, 1)
+    for w in (lk, lk + 1, 10 * lk):
+        assert np.array_equal(orc.sdpa(q, k, v, 0.3, 1, window=w), causal)
+
+
+@pytest.mark.parametrize("lq,lk,w", [(4, 9, 3), (9, 9, 1), (7, 20, 5), (12, 7, 2), (1, 30, 8)])
+def test_window_equals_its_band_mask(lq, lk, w):
+    rng = np.random.default_rng(800 + lq * lk + w)
+    q, k, v = _rand(rng, 2, 4, lq, 5), _rand(rng, 2, 2, lk, 5), _rand(rng, 2, 2, lk, 3)
+    sinks = _rand(rng, 4)
+    got = orc.sdpa(q, k, v, 0.4, 1, sinks=sinks, window=w)
+    want = orc.sdpa(q, k, v, 0.4, 2, _band(lq, lk, w), sinks)
+    assert np.array_equal(got, want)
+
+
+def test_window_of_one_returns_the_diagonal_value():
+    # closed form: each row sees only the key at its position
+    rng = np.random.default_rng(901)
+    lq, lk = 6, 10
+    q, k, v = _rand(rng, 1, 1, lq, 4), _rand(rng, 1, 1, lk, 4), _rand(rng, 1, 1, lk, 3)
+    got = orc.sdpa(q, k, v, 0.7, 1, window=1)[0, 0]
+    for i in range(lq):
+        assert np.allclose(got[i], v[0, 0, i + lk - lq], rtol=0, atol=1e-15)
+    sink = 0.25
+    got = orc.sdpa(q, k, v, 0.7, 1, sinks=np.array([sink]), window=1)[0, 0]
+    for i in range(lq):
+        j = i + lk - lq
+        s = 0.7 * float(q[0, 0, i] @ k[0, 0, j])
+        assert np.allclose(got[i], v[0, 0, j] / (1.0 + np.exp(sink - s)), rtol=0, atol=1e-14)
+
+
+def test_one_query_window_equals_its_keys_alone():
+    # a decode row over a window reads exactly the last w keys: the same as no mask over them
+    rng = np.random.default_rng(902)
+    lk, w = 40, 13
+    q, k, v = _rand(rng, 1, 3, 1, 6), _rand(rng, 1, 3, lk, 6), _rand(rng, 1, 3, lk, 5)
+    got = orc.sdpa(q, k, v, 0.5, 1, window=w)
+    want = orc.sdpa(q, k[:, :, lk - w:], v[:, :, lk - w:], 0.5, 0)
+    assert np.allclose(got, want, rtol=0, atol=1e-14)
+
+
+def test_invalid_windows_are_rejected():
+    q = np.zeros((1, 1, 2, 2))
+    with pytest.raises(ValueError):
+        orc.sdpa(q, q, q, 1.0, 1, window=0)
+    with pytest.raises(ValueError):
+        orc.sdpa(q, q, q, 1.0, 0, window=3)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_windows_brute_force_tiny(seed):
+    rng = np.random.default_rng(1000 + seed)
+    hkv = int(rng.integers(1, 3))
+    hq = hkv * int(rng.integers(1, 4))
+    lq, lk = int(rng.integers(1, 10)), int(rng.integers(1, 12))
+    d, dv = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+    w = int(rng.integers(1, 12))
+    q, k, v = _rand(rng, 1, hq, lq, d), _rand(rng, 1, hkv, lk, d), _rand(rng, 1, hkv, lk, dv)
+    sinks = _rand(rng, hq) if seed % 2 else None
+    got = orc.sdpa(q, k, v, 0.6, 1, sinks=sinks, window=w)
+    want = np.array(attention_loops(q.tolist(), k.tolist(), v.tolist(), 1, hq, hkv, lq, lk, d, dv, 0.6, 1,
+                                    None, None if sinks is None else sinks.tolist(), window=w))
+    assert np.allclose(got, want.reshape(got.shape), rtol=0, atol=1e-12)

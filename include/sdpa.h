@@ -123,6 +123,29 @@ int sdpa_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
               int64_t D, int64_t Dv, int mask_kind, int has_mask, int has_sinks,
               int dtype, sdpa_plan_t* plan);
 
+/*
+ * sdpa_forward_windowed - causal attention over a sliding window of keys, as
+ * sdpa_forward with mask_kind SDPA_MASK_CAUSAL and no boolean mask, except
+ * that query row i (position pos = i + Lk - Lq) reads only the keys j with
+ * pos - window < j <= pos: the band of nuvec-core tests/fast.rs (window_mask;
+ * windows_run_fused_and_equal_the_boolean_mask). A row whose band holds no key
+ * is zero. window must be >= 1 (else SDPA_ERR_INVALID); a window of at least
+ * Lk keys is plain causal attention, with the same plan and the same bits as
+ * sdpa_forward (window_errors_empty_inputs_and_full_windows). Decode key
+ * splits cover only the keys the rows read (attention_plan.rs,
+ * windowed_decode_plans_from_the_window_keys). Other arguments, layouts,
+ * ownership, errors and asynchrony as for sdpa_forward.
+ */
+int sdpa_forward_windowed(const void* q, const void* k, const void* v, void* out,
+                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                          int64_t D, int64_t Dv, float scale, int64_t window,
+                          const void* sinks, int dtype, void* stream);
+
+/* The plan sdpa_forward_windowed would use; pure, like sdpa_plan. */
+int sdpa_plan_windowed(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                       int64_t D, int64_t Dv, int64_t window, int has_sinks,
+                       int dtype, sdpa_plan_t* plan);
+
 /* Message of the last error on the calling thread ("" if none). The pointer
  * stays valid until the thread's next sdpa_* call. */
 const char* sdpa_last_error(void);
@@ -131,7 +154,7 @@ const char* sdpa_last_error(void);
  * Returns SDPA_OK or SDPA_ERR_HIP. */
 int sdpa_release_workspace(void);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (2 added the windowed calls). */
 int sdpa_abi_version(void);
 
 #ifdef __cplusplus

@@ -15,7 +15,8 @@ SDPA_OK, SDPA_ERR_INVALID, SDPA_ERR_UNSUPPORTED, SDPA_ERR_HIP = 0, -1, -2, -3
 SDPA_ROUTE_EMPTY, SDPA_ROUTE_ZERO_FILL, SDPA_ROUTE_PREFILL, SDPA_ROUTE_DECODE = 0, 1, 2, 3
 ROUTE_NAMES = {0: "empty", 1: "zero_fill", 2: "prefill", 3: "decode"}
 
-EXPORTED = ("sdpa_forward", "sdpa_plan", "sdpa_last_error", "sdpa_release_workspace", "sdpa_abi_version")
+EXPORTED = ("sdpa_forward", "sdpa_plan", "sdpa_forward_windowed", "sdpa_plan_windowed", "sdpa_last_error",
+            "sdpa_release_workspace", "sdpa_abi_version")
 
 
 class SdpaPlan(ctypes.Structure):
@@ -76,6 +77,12 @@ def load() -> ctypes.CDLL:
     lib.sdpa_plan.argtypes = [i64, i64, i64, i64, i64, i64, i64, c_int, c_int, c_int, c_int,
                               ctypes.POINTER(SdpaPlan)]
     lib.sdpa_plan.restype = c_int
+    lib.sdpa_forward_windowed.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                          i64, vp, c_int, vp]
+    lib.sdpa_forward_windowed.restype = c_int
+    lib.sdpa_plan_windowed.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, c_int, c_int,
+                                       ctypes.POINTER(SdpaPlan)]
+    lib.sdpa_plan_windowed.restype = c_int
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_release_workspace.argtypes = []
@@ -116,6 +123,26 @@ def sdpa_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, has_mask, has_sinks, dtype, 
     return p.as_dict()
 
 
+def sdpa_forward_windowed(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, Dv, scale, window, sinks, dtype, stream,
+                          check: bool = True) -> int:
+    """Raw windowed call (causal attention over a sliding window of keys)."""
+    rc = load().sdpa_forward_windowed(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, Dv, ctypes.c_float(scale), window,
+                                      sinks, dtype, stream)
+    return _check(rc) if check else rc
+
+
+def sdpa_plan_windowed(B, Hq, Hkv, Lq, Lk, D, Dv, window, has_sinks, dtype, check: bool = True):
+    """The windowed call's plan as a dict (or the return code when check=False and it fails)."""
+    p = SdpaPlan()
+    rc = load().sdpa_plan_windowed(B, Hq, Hkv, Lq, Lk, D, Dv, window, int(bool(has_sinks)), dtype,
+                                   ctypes.byref(p))
+    if rc != SDPA_OK:
+        if check:
+            _check(rc)
+        return rc
+    return p.as_dict()
+
+
 def sdpa_release_workspace() -> int:
     return _check(load().sdpa_release_workspace())
 
@@ -135,12 +162,13 @@ def _dtype_code(t):
 
 
 def attention(q, k, v, scale: float, mask_kind: int = SDPA_MASK_NONE, mask=None, sinks=None, out=None,
-              stream=None):
+              stream=None, window=None):
     """softmax(scale * q k^T + mask) v on the GPU through sdpa_forward.
 
     q [B,Hq,Lq,D], k [B,Hkv,Lk,D], v [B,Hkv,Lk,Dv] contiguous CUDA tensors of one
     dtype; mask a contiguous uint8/bool CUDA tensor [Lq,Lk] (mask_kind 2);
-    sinks a CUDA tensor [Hq] of q's dtype. Returns out [B,Hq,Lq,Dv].
+    sinks a CUDA tensor [Hq] of q's dtype. With `window` (causal only), the
+    call goes through sdpa_forward_windowed. Returns out [B,Hq,Lq,Dv].
     """
     import torch
     B, Hq, Lq, D = q.shape
@@ -172,6 +200,12 @@ def attention(q, k, v, scale: float, mask_kind: int = SDPA_MASK_NONE, mask=None,
         out = torch.empty((B, Hq, Lq, Dv), dtype=q.dtype, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
+    if window is not None:
+        if mask_kind != SDPA_MASK_CAUSAL:
+            raise SdpaError(SDPA_ERR_INVALID, "a window needs the causal mask (mask_kind 1)")
+        sdpa_forward_windowed(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, Lq, Lk, D,
+                              Dv, float(scale), int(window), sptr, _dtype_code(q), stream)
+        return out
     sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, Lq, Lk, D, Dv,
                  float(scale), mask_kind, mptr, sptr, _dtype_code(q), stream)
     return out

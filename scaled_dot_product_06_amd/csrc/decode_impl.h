@@ -64,7 +64,8 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   const int split = blockIdx.x;
   const int hkv = blockIdx.y;
   const int b = blockIdx.z;
-  const int ks = split * a.kps;
+  // splits cover the keys the rows read: with a sliding window, from a.koff
+  const int ks = a.koff + split * a.kps;
   const int ke = min(ks + a.kps, a.Lk);
   const int ntiles = (ke - ks + BN - 1) / BN;
 
@@ -169,7 +170,7 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
         if (!full) {
           const int key = k0 + nb * MF + acc_row<MF>(i, kg);
           bool vis = key < ke && row_ok;
-          if (causal_cut) vis = vis && key <= iq + shift;
+          if (causal_cut) vis = vis && key <= iq + shift && (a.window <= 0 || key > iq + shift - a.window);
           else if (a.mask_kind == kMaskBool) vis = vis && mrow[key] != 0;
           if (!vis) s[nb][i] = -INFINITY;
         }

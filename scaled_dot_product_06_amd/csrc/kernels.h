@@ -22,6 +22,9 @@ struct FwdArgs {
   int B, Hq, Hkv, Lq, Lk;
   int group;             // Hq / Hkv
   int mask_kind;
+  int window;            // causal sliding window: row i (position pos = i + Lk - Lq) reads keys
+                         // pos - window < j <= pos; 0 for none
+  int koff;              // decode: first key the windowed rows read (0 without a window)
   float c;               // |scale| * log2(e): scores are taken as c * q.k in base 2
   uint32_t qsign;        // XOR applied to q bits (flips q's sign when scale < 0)
   // prefill

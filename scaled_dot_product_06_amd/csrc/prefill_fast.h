@@ -98,14 +98,21 @@ prefill_fast_kernel(FwdArgs a) {
   const int wi0 = qb * bm + (w % wph) * C::ROWS;
   const int shift = a.Lk - a.Lq;
 
-  // keys the workgroup needs (its last row's causal limit)
+  // keys the workgroup needs: up to its last row's causal limit and, with a
+  // sliding window, from its first row's window start; it visits tiles
+  // tb .. tb + ntiles - 1
   int kend = a.Lk;
   if (a.mask_kind == kMaskCausal) kend = min(a.Lk, min(qb * bm + bm, a.Lq) - 1 + shift + 1);
   if (kend < 0) kend = 0;
-  const int ntiles = (kend + BN - 1) / BN;
-  // keys every row of this wavefront sees
+  int kbeg = 0;
+  if (a.window > 0) kbeg = min(max(0, qb * bm + shift - a.window + 1), kend);
+  const int tb = kbeg / BN;
+  const int ntiles = max((kend + BN - 1) / BN - tb, 0);
+  // keys every row of this wavefront sees: [w_klo, w_kfull)
   int w_kfull = a.mask_kind == kMaskBool ? 0 : a.Lk;
   if (a.mask_kind == kMaskCausal) w_kfull = min(a.Lk, wi0 + shift + 1);
+  int w_klo = 0;
+  if (a.window > 0) w_klo = min(wi0 + C::ROWS, a.Lq) - 1 + shift - a.window + 1;
   const bool wave_live = wi0 < a.Lq;
 
   int iq[QB];
@@ -131,7 +138,7 @@ prefill_fast_kernel(FwdArgs a) {
   for (int r = 0; r < QB; ++r) {
     mbrow[r] = bool_mask ? a.mbits + (size_t)min(iq[r], a.Lq - 1) * a.mwords : nullptr;
     mw_cur[r] = 0u;
-    mw_nxt[r] = (bool_mask && ntiles > 0) ? mbrow[r][0] : 0u;
+    mw_nxt[r] = (bool_mask && ntiles > 0) ? mbrow[r][tb] : 0u;
   }
 
   acc_t o[QB][C::NDB];
@@ -240,13 +247,15 @@ prefill_fast_kernel(FwdArgs a) {
         for (int i = 0; i < ACC; ++i) s[r][0][i] = keep_if_bit(s[r][0][i], wsh, acc_row<MF>(i, 0));
       } else {
         // causal (or no mask past the last key)
+        // causal (and window) limits, or no mask past the last key
         const int lim = a.mask_kind == kMaskCausal ? min(iq[r] + shift, a.Lk - 1) : a.Lk - 1;
+        const int lo = a.window > 0 ? iq[r] + shift - a.window : -1;
 #pragma unroll
         for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
           for (int i = 0; i < ACC; ++i) {
             const int key = k0 + nb * MF + acc_row<MF>(i, kg);
-            const bool vis = row_ok & (key <= lim);
+            const bool vis = row_ok & (key <= lim) & (key > lo);
             s[r][nb][i] = vis ? s[r][nb][i] : -INFINITY;
           }
       }
@@ -319,7 +328,7 @@ prefill_fast_kernel(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < QB; ++r) {
         mw_cur[r] = mw_nxt[r];
-        mw_nxt[r] = t + 1 < ntiles ? mbrow[r][t + 1] : 0u;
+        mw_nxt[r] = t + 1 < ntiles ? mbrow[r][tb + t + 1] : 0u;
       }
     }
     // Tile t+1 has landed: the loads complete in issue order, so waiting
@@ -333,8 +342,9 @@ prefill_fast_kernel(FwdArgs a) {
       __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     }
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (t + 3 < ntiles) issue_tile((t + 3) * BN, Sload);
-    if ((t + 1) * BN > w_kfull) tile_max_masked(t, scur, mw_cur);
+    if (t + 3 < ntiles) issue_tile((tb + t + 3) * BN, Sload);
+    const int kt = tb + t;  // key tile
+    if ((kt + 1) * BN > w_kfull || kt * BN < w_klo) tile_max_masked(kt, scur, mw_cur);
 #pragma unroll
     for (int r = 0; r < QB; ++r) softmax_rebase<C::NDB>(tmax[r], m[r], l[r], o[r]);
     qk(Snext, snext);
@@ -344,9 +354,9 @@ prefill_fast_kernel(FwdArgs a) {
   };
 
   // prologue: tiles 0..2 in flight, tile 0's scores and maxima
-  if (ntiles > 0) issue_tile(0, lds0);
-  if (ntiles > 1) issue_tile(BN, lds1);
-  if (ntiles > 2) issue_tile(2 * BN, lds2);
+  if (ntiles > 0) issue_tile(tb * BN, lds0);
+  if (ntiles > 1) issue_tile((tb + 1) * BN, lds1);
+  if (ntiles > 2) issue_tile((tb + 2) * BN, lds2);
   if (ntiles > 2) {
     __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * C::LOADS_PER_TILE));
   } else if (ntiles > 1) {

@@ -70,10 +70,15 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
   const int iq = wi0 + col;
   const int shift = a.Lk - a.Lq;
 
+  // keys the workgroup needs: up to its last row's causal limit and, with a
+  // sliding window, from its first row's window start (tiles tb .. tb+ntiles-1)
   int kend = a.Lk;
   if (a.mask_kind == kMaskCausal) kend = min(a.Lk, min(qb * bm + bm, a.Lq) - 1 + shift + 1);
   if (kend < 0) kend = 0;
-  const int ntiles = (kend + BN - 1) / BN;
+  int kbeg = 0;
+  if (a.window > 0) kbeg = min(max(0, qb * bm + shift - a.window + 1), kend);
+  const int tb = kbeg / BN;
+  const int ntiles = max((kend + BN - 1) / BN - tb, 0);
 
   const bool wave_live = wi0 < a.Lq;
   const int w_last = min(wi0 + MF, a.Lq) - 1;
@@ -83,6 +88,13 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
     w_kfull = min(a.Lk, wi0 + shift + 1);
   } else if (a.mask_kind == kMaskBool) {
     w_kfull = 0;
+  }
+  // with a window: keys below w_kskip are outside every row's window, keys
+  // from w_klo on inside every row's (lower bound)
+  int w_kskip = 0, w_klo = 0;
+  if (a.window > 0) {
+    w_kskip = wi0 + shift - a.window + 1;
+    w_klo = w_last + shift - a.window + 1;
   }
 
   // Q fragment (B operand of S^T = K Q^T): row iq, k-elements kg*8.. of each KW chunk.
@@ -176,17 +188,17 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
   const int tr_c = lane & 3;
   const int tr_dv = ((lane >> 4) * 16) % MF + 4 * tr_c;
 
-  if (ntiles > 0) load_tile(0);
+  if (ntiles > 0) load_tile(tb * BN);
   for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * BN;
+    const int k0 = (tb + t) * BN;
     __syncthreads();
     store_tile();
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < MWT; ++w) mwc[w] = mwn[w];
     if (t + 1 < ntiles) load_tile(k0 + BN);
-    if (!wave_live || k0 >= w_kend) continue;
-    const bool full = k0 + BN <= w_kfull;
+    if (!wave_live || k0 >= w_kend || k0 + BN <= w_kskip) continue;
+    const bool full = k0 + BN <= w_kfull && k0 >= w_klo;
 
     // S^T = K Q^T
     acc_t s[C::NSB];
@@ -219,14 +231,15 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
         }
       }
     } else {
-      // causal diagonal, or keys past Lk
+      // causal diagonal and window edge, or keys past Lk
       const int lim = a.mask_kind == kMaskCausal ? min(iq + shift, a.Lk - 1) : a.Lk - 1;
+      const int lo = a.window > 0 ? iq + shift - a.window : -1;
 #pragma unroll
       for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
         for (int i = 0; i < ACC; ++i) {
           const int key = k0 + nb * MF + acc_row<MF>(i, kg);
-          const bool vis = (iq < a.Lq) & (key <= lim);
+          const bool vis = (iq < a.Lq) & (key <= lim) & (key > lo);
           s[nb][i] = vis ? s[nb][i] : -INFINITY;
           mx = fmaxf(mx, s[nb][i]);
         }
@@ -330,10 +343,15 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
   const int iq = wi0 + col;
   const int shift = a.Lk - a.Lq;
 
+  // keys the workgroup needs: up to its last row's causal limit and, with a
+  // sliding window, from its first row's window start (tiles tb .. tb+ntiles-1)
   int kend = a.Lk;
   if (a.mask_kind == kMaskCausal) kend = min(a.Lk, min(qb * bm + bm, a.Lq) - 1 + shift + 1);
   if (kend < 0) kend = 0;
-  const int ntiles = (kend + BN - 1) / BN;
+  int kbeg = 0;
+  if (a.window > 0) kbeg = min(max(0, qb * bm + shift - a.window + 1), kend);
+  const int tb = kbeg / BN;
+  const int ntiles = max((kend + BN - 1) / BN - tb, 0);
 
   const bool wave_live = wi0 < a.Lq;
   const int w_last = min(wi0 + MF, a.Lq) - 1;
@@ -343,6 +361,13 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
     w_kfull = min(a.Lk, wi0 + shift + 1);
   } else if (a.mask_kind == kMaskBool) {
     w_kfull = 0;
+  }
+  // with a window: keys below w_kskip are outside every row's window, keys
+  // from w_klo on inside every row's (lower bound)
+  int w_kskip = 0, w_klo = 0;
+  if (a.window > 0) {
+    w_kskip = wi0 + shift - a.window + 1;
+    w_klo = w_last + shift - a.window + 1;
   }
 
   const float* qp = (const float*)a.q + ((size_t)(b * a.Hq + h) * a.Lq + iq) * D;
@@ -419,15 +444,15 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
     }
   };
 
-  if (ntiles > 0) load_tile(0);
+  if (ntiles > 0) load_tile(tb * BN);
   for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * BN;
+    const int k0 = (tb + t) * BN;
     __syncthreads();
     store_tile();
     __syncthreads();
     if (t + 1 < ntiles) load_tile(k0 + BN);
-    if (!wave_live || k0 >= w_kend) continue;
-    const bool full = k0 + BN <= w_kfull;
+    if (!wave_live || k0 >= w_kend || k0 + BN <= w_kskip) continue;
+    const bool full = k0 + BN <= w_kfull && k0 >= w_klo;
 
     acc_t s[C::NSB];
 #pragma unroll
@@ -447,7 +472,8 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
         if (!full) {
           const int key = k0 + nb * MF + acc_row<MF>(i, kg);
           bool vis = key < a.Lk && iq < a.Lq;
-          if (a.mask_kind == kMaskCausal) vis = vis && key <= iq + shift;
+          if (a.mask_kind == kMaskCausal)
+            vis = vis && key <= iq + shift && (a.window <= 0 || key > iq + shift - a.window);
           else if (a.mask_kind == kMaskBool) vis = vis && mrow[key] != 0;
           if (!vis) s[nb][i] = -INFINITY;
         }

@@ -134,9 +134,22 @@ const int64_t kMaxGridYZ = 65535;
 
 int elem_size(int dtype) { return dtype == SDPA_F32 ? 4 : 2; }
 
-// Validation shared by sdpa_plan and sdpa_forward; fills `plan` on success.
+// First key any query row of a windowed call reads: row i (position
+// i + Lk - Lq) reads keys pos - window < j <= pos, so the rows together read
+// [Lk - Lq - window + 1, Lk). 0 without a window.
+int64_t window_first_key(int64_t Lq, int64_t Lk, int64_t window) {
+  if (window <= 0) return 0;
+  const int64_t k0 = Lk - Lq - window + 1;
+  return k0 > 0 ? k0 : 0;
+}
+
+// Validation shared by the plan and forward entry points; fills `plan` on
+// success. `window` is 0 (none) or the windowed calls' window, already
+// checked to be >= 1 with a causal mask; a window of at least Lk keys is
+// plain causal attention and plans (and runs) as such.
 int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D, int64_t Dv,
-                      int mask_kind, bool has_mask, bool has_sinks, int dtype, sdpa_plan_t* plan) {
+                      int mask_kind, bool has_mask, bool has_sinks, int dtype, int64_t window,
+                      sdpa_plan_t* plan) {
   (void)has_sinks;
   if (B < 0) return fail(SDPA_ERR_INVALID, "B must be >= 0 (got %lld)", (long long)B);
   if (Hq < 0) return fail(SDPA_ERR_INVALID, "Hq must be >= 0 (got %lld)", (long long)Hq);
@@ -194,10 +207,12 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
   const int64_t group = Hq / Hkv;
   if (dtype != SDPA_F32 && Lq <= 8 && group * Lq <= 32) {
     const int64_t rows = group * Lq;
-    int64_t kps = pow2_floor(Lk / 64 > 0 ? Lk / 64 : 1);
+    // the key partitions follow the keys the rows read (the window's, if any)
+    const int64_t nkeys = Lk - window_first_key(Lq, Lk, window);
+    int64_t kps = pow2_floor(nkeys / 64 > 0 ? nkeys / 64 : 1);
     if (kps < 64) kps = 64;
     if (kps > 1024) kps = 1024;
-    const int64_t nsplit = (Lk + kps - 1) / kps;
+    const int64_t nsplit = (nkeys + kps - 1) / kps;
     p.route = SDPA_ROUTE_DECODE;
     p.kernels = 2;
     p.rows_per_wave = decode_mf((int)D, (int)rows);
@@ -283,7 +298,7 @@ hipError_t get_scratch(hipStream_t stream, size_t bytes, void** out) {
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 1; }
+int sdpa_abi_version(void) { return 2; }
 
 const char* sdpa_last_error(void) { return g_err.c_str(); }
 
@@ -292,17 +307,31 @@ int sdpa_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_
   g_err.clear();
   if (!plan) return fail(SDPA_ERR_INVALID, "plan must not be NULL");
   sdpa_plan_t p;
-  const int rc = validate_and_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, has_mask != 0, has_sinks != 0, dtype, &p);
+  const int rc = validate_and_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, has_mask != 0, has_sinks != 0, dtype, 0, &p);
   if (rc == SDPA_OK) *plan = p;
   return rc;
 }
 
-int sdpa_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t Hq, int64_t Hkv,
+}  // extern "C"
+
+namespace {
+
+// A windowed call's window as planned: >= 1 (else an error), and 0 (plain
+// causal) once it covers every key.
+int effective_window(int64_t window, int64_t Lk, int64_t* eff) {
+  if (window < 1) return fail(SDPA_ERR_INVALID, "window must be >= 1 (got %lld)", (long long)window);
+  if (window > kMaxLen)
+    return fail(SDPA_ERR_UNSUPPORTED, "window (%lld) exceeds %lld", (long long)window, (long long)kMaxLen);
+  *eff = window >= Lk ? 0 : window;
+  return SDPA_OK;
+}
+
+int forward_impl(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t Hq, int64_t Hkv,
                  int64_t Lq, int64_t Lk, int64_t D, int64_t Dv, float scale, int mask_kind, const uint8_t* mask,
-                 const void* sinks, int dtype, void* stream_v) {
-  g_err.clear();
+                 const void* sinks, int dtype, int64_t window, void* stream_v) {
   sdpa_plan_t p;
-  int rc = validate_and_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, mask != nullptr, sinks != nullptr, dtype, &p);
+  int rc = validate_and_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, mask != nullptr, sinks != nullptr, dtype,
+                             window, &p);
   if (rc != SDPA_OK) return rc;
   if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID, "scale must be finite (got %g)", (double)scale);
   if (p.route == SDPA_ROUTE_EMPTY) return SDPA_OK;
@@ -335,6 +364,7 @@ int sdpa_forward(const void* q, const void* k, const void* v, void* out, int64_t
   a.Lk = (int)Lk;
   a.group = (int)(Hq / Hkv);
   a.mask_kind = mask_kind;
+  a.window = (int)window;
   // scores are used in base 2; a zero scale becomes the smallest normal float,
   // which leaves every finite score's weight at exactly exp2(0) = 1
   a.c = fmaxf(fabsf(scale) * 1.4426950408889634f, FLT_MIN);
@@ -343,6 +373,7 @@ int sdpa_forward(const void* q, const void* k, const void* v, void* out, int64_t
   bool ok = false;
   if (p.route == SDPA_ROUTE_DECODE) {
     a.rows = (int)(a.group * Lq);
+    a.koff = (int)window_first_key(Lq, Lk, window);
     a.kps = (int)p.keys_per_split;
     a.nsplit = (int)p.splits;
     void* part = nullptr;
@@ -371,6 +402,41 @@ int sdpa_forward(const void* q, const void* k, const void* v, void* out, int64_t
                        (long long)Dv);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t Hq, int64_t Hkv,
+                 int64_t Lq, int64_t Lk, int64_t D, int64_t Dv, float scale, int mask_kind, const uint8_t* mask,
+                 const void* sinks, int dtype, void* stream) {
+  g_err.clear();
+  return forward_impl(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, Dv, scale, mask_kind, mask, sinks, dtype, 0, stream);
+}
+
+int sdpa_forward_windowed(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t Hq,
+                          int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D, int64_t Dv, float scale, int64_t window,
+                          const void* sinks, int dtype, void* stream) {
+  g_err.clear();
+  int64_t w = 0;
+  const int rc = effective_window(window, Lk, &w);
+  if (rc != SDPA_OK) return rc;
+  return forward_impl(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, Dv, scale, SDPA_MASK_CAUSAL, nullptr, sinks, dtype, w,
+                      stream);
+}
+
+int sdpa_plan_windowed(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D, int64_t Dv,
+                       int64_t window, int has_sinks, int dtype, sdpa_plan_t* plan) {
+  g_err.clear();
+  if (!plan) return fail(SDPA_ERR_INVALID, "plan must not be NULL");
+  int64_t w = 0;
+  int rc = effective_window(window, Lk, &w);
+  if (rc != SDPA_OK) return rc;
+  sdpa_plan_t p;
+  rc = validate_and_plan(B, Hq, Hkv, Lq, Lk, D, Dv, SDPA_MASK_CAUSAL, false, has_sinks != 0, dtype, w, &p);
+  if (rc == SDPA_OK) *plan = p;
+  return rc;
 }
 
 int sdpa_release_workspace(void) {

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(sd.library_path())
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert sd.sdpa_abi_version() == 1
+    assert sd.sdpa_abi_version() == 2
     out = subprocess.run(["nm", "-D", "--defined-only", sd.library_path()], capture_output=True, text=True).stdout
     for name in _declared_functions():
         assert re.search(rf"\bT {name}$", out, flags=re.M), f"{name} not exported with C linkage"
@@ -155,3 +155,36 @@ def test_errors_are_per_thread():
     t.join()
     assert msgs == [""]
     assert "multiple" in sd.sdpa_last_error()
+
+
+# --- windowed calls ---------------------------------------------------------------------------
+
+def test_full_window_plans_as_causal():
+    for lq, lk in [(1, 4096), (5, 300), (300, 700)]:
+        causal = sd.sdpa_plan(1, 8, 2, lq, lk, 128, 128, 1, False, True, 2)
+        for w in (lk, lk + 1, 1 << 30):
+            assert sd.sdpa_plan_windowed(1, 8, 2, lq, lk, 128, 128, w, True, 2) == causal
+
+
+def test_windowed_decode_splits_follow_the_window():
+    # attention_plan.rs, windowed_decode_plans_from_the_window_keys: the partitions follow
+    # the keys the rows read, not the cache length
+    causal = sd.sdpa_plan(1, 64, 8, 1, 4096, 64, 64, 1, False, False, 1)
+    win = sd.sdpa_plan_windowed(1, 64, 8, 1, 4096, 64, 64, 128, False, 1)
+    alone = sd.sdpa_plan(1, 64, 8, 1, 128, 64, 64, 0, False, False, 1)
+    assert win["route"] == causal["route"] == "decode"
+    assert win["splits"] * win["keys_per_split"] >= 128 > (win["splits"] - 1) * win["keys_per_split"]
+    assert win["splits"] < causal["splits"]
+    assert (win["keys_per_split"], win["splits"]) == (alone["keys_per_split"], alone["splits"])
+    # several query rows read the union of their windows
+    w4 = sd.sdpa_plan_windowed(1, 8, 2, 4, 9000, 128, 128, 300, False, 2)
+    assert w4["splits"] * w4["keys_per_split"] >= 303
+
+
+@pytest.mark.parametrize("window", [0, -1, -(1 << 40)])
+def test_invalid_windows_are_rejected(window):
+    assert sd.sdpa_plan_windowed(1, 4, 2, 5, 9, 64, 64, window, False, 2, check=False) == -1
+    assert "window" in sd.sdpa_last_error()
+    f = sd.sdpa_forward_windowed
+    assert f(None, None, None, None, 1, 4, 2, 5, 9, 64, 64, 0.1, window, None, 2, None, check=False) == -1
+    assert "window" in sd.sdpa_last_error()

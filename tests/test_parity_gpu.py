@@ -8,6 +8,7 @@ import zlib
 import numpy as np
 import pytest
 
+from oracle import attention as orc
 from scaled_dot_product_06_amd import inputs as gen
 from tests.gpu_util import (TOL, assert_parity, compare, device_inputs, from_device, oracle_rows, run_gpu,
                             sample_rows, say, to_device)
@@ -126,6 +127,66 @@ def test_prefill_bool_mask_word_edges(D, Lk):
         for name, pattern in _mask_patterns(p.Lq, Lk).items():
             p.mask = np.ascontiguousarray(np.broadcast_to(pattern, (p.Lq, Lk)).astype(np.uint8))
             _full_check(p, f"bool mask {name} D={D} Lk={Lk}")
+
+
+# --- sliding windows (nuvec-core tests/fast.rs, windowed-kernel tests) -------------------------
+
+# (Lq, Lk, D, Hq, Hkv, window): one-query decode over windows below the keys (short and long
+# caches), few-query decode, prefill chunks with windows of 1 to above the keys
+WINDOW_CASES = [(1, 300, 64, 8, 1, 128), (1, 4096, 64, 8, 8, 128), (1, 9000, 128, 8, 1, 3),
+                (1, 2000, 256, 4, 1, 1024), (4, 600, 128, 4, 2, 7), (8, 1500, 64, 4, 4, 128),
+                (40, 300, 64, 4, 2, 7), (97, 400, 128, 2, 1, 33), (64, 640, 64, 2, 2, 1),
+                (300, 700, 256, 2, 1, 128), (33, 45, 64, 4, 2, 100), (2, 5000, 256, 4, 2, 1024),
+                (130, 130, 128, 4, 4, 64), (200, 900, 96, 4, 2, 50)]
+
+
+def _window_check(p, w, what):
+    from scaled_dot_product_06_amd import attention
+    import torch
+    q, k, v, _, sinks = device_inputs(p)
+    got = from_device(attention(q, k, v, p.scale, 1, None, sinks, window=w), p.dtype)
+    torch.cuda.synchronize()
+    qq, kk, vv, _, ss = p.widened()
+    want = orc.sdpa(qq, kk, vv, p.scale, 1, None, ss, window=w)
+    assert_parity(p, got, want, what)
+    assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_windows(case, dtype):
+    Lq, Lk, D, Hq, Hkv, w = case
+    dt = {"f32": F32, "f16": F16, "bf16": BF16}[dtype]
+    for sinks in (False, True):
+        p = gen.make_problem(2000 + Lq + Lk + w, 1, Hq, Hkv, Lq, Lk, D, D, dt, 1, sinks=sinks)
+        _window_check(p, w, f"window {w} sinks={sinks}")
+
+
+def test_full_window_is_causal_bit_for_bit():
+    import torch
+    from scaled_dot_product_06_amd import attention
+    for (Lq, Lk, dt) in [(1, 3000, BF16), (70, 70, F16), (5, 9, F32), (130, 400, BF16)]:
+        p = gen.make_problem(3100 + Lq, 1, 4, 2, Lq, Lk, 128, 128, dt, 1, sinks=True)
+        q, k, v, _, s = device_inputs(p)
+        causal = attention(q, k, v, p.scale, 1, None, s)
+        for w in (Lk, Lk + 5):
+            win = attention(q, k, v, p.scale, 1, None, s, window=w)
+            torch.cuda.synchronize()
+            assert torch.equal(win.view(torch.int16) if dt != F32 else win,
+                               causal.view(torch.int16) if dt != F32 else causal), (Lq, Lk, w)
+
+
+@pytest.mark.parametrize("Lk,w", [(300, 128), (4096, 128), (9000, 300), (2000, 1024)])
+def test_one_query_window_equals_its_keys_alone(Lk, w):
+    # a decode row over a window gives the same bits as an unmasked call over exactly its keys
+    import torch
+    from scaled_dot_product_06_amd import attention
+    p = gen.make_problem(3200 + Lk, 1, 8, 2, 1, Lk, 128, 128, BF16, 1, sinks=True)
+    q, k, v, _, s = device_inputs(p)
+    win = attention(q, k, v, p.scale, 1, None, s, window=w)
+    alone = attention(q, k[:, :, Lk - w:].contiguous(), v[:, :, Lk - w:].contiguous(), p.scale, 0, None, s)
+    torch.cuda.synchronize()
+    assert torch.equal(win.view(torch.int16), alone.view(torch.int16))
 
 
 # --- edge cases -------------------------------------------------------------------------------

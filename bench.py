@@ -34,22 +34,28 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PREFILL_WORKLOAD, DECODE_WORKLOAD = 3, 5
 
 
-def causal_pairs(Lq: int, Lk: int) -> int:
-    """Visible (query, key) pairs of a bottom-right aligned causal mask."""
+def causal_pairs(Lq: int, Lk: int, window: int = 0) -> int:
+    """Visible (query, key) pairs of a bottom-right aligned causal mask, and of
+    its sliding-window band (row at position pos reads pos - window < j <= pos)."""
     total = 0
     for i in range(Lq):
-        total += max(0, min(Lk, i + Lk - Lq + 1))
+        pos = i + Lk - Lq
+        hi = min(Lk, pos + 1)
+        lo = max(0, pos - window + 1) if window else 0
+        total += max(0, hi - lo)
     return total
 
 
-def prefill_flop(p) -> int:
-    pairs = causal_pairs(p.Lq, p.Lk) if p.mask_kind == 1 else p.Lq * p.Lk
+def prefill_flop(p, window: int = 0) -> int:
+    pairs = causal_pairs(p.Lq, p.Lk, window) if p.mask_kind == 1 else p.Lq * p.Lk
     return p.B * p.Hq * pairs * 2 * (p.D + p.Dv)
 
 
-def decode_bytes(p) -> int:
+def decode_bytes(p, window: int = 0) -> int:
+    """K/V bytes a decode call reads: every key, or the rows' windows."""
     esize = 4 if p.dtype == 0 else 2
-    return p.B * p.Hkv * p.Lk * (p.D + p.Dv) * esize
+    keys = min(p.Lk, window + p.Lq - 1) if window else p.Lk
+    return p.B * p.Hkv * keys * (p.D + p.Dv) * esize
 
 
 def _traffic_for(kernel_tag: str):
@@ -109,25 +115,31 @@ def cpu_baseline(p, seconds: float):
 
 PEAK_FP32_MFMA_TFLOPS = 157.3
 OTHER_WORKLOADS = (1, 2, 4)   # timed and reported; not the headline metric
+# sliding-window calls on the headline shapes (reported): (workload, window)
+WINDOWED_WORKLOADS = ((5, 4096), (3, 1024))
 
 
 def measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, rounds=5):
     """Per-call kernel time (HIP events on the library's stream, median of
     `rounds` batches of `calls`) of the f32 causal prefill, the 8193-key bf16
-    decode and the f16 prefill with a boolean mask and sinks, each against its
-    own roofline. Decode K/V rotates over copies spanning > 2x the 256 MB MALL
-    so every call streams from HBM."""
+    decode, the f16 prefill with a boolean mask and sinks, and sliding-window
+    calls on the headline shapes, each against its own roofline (windowed work
+    counts only the keys in the band). Decode K/V rotates over copies whose
+    windows together span > 2x the 256 MB MALL, so every call streams from HBM."""
     import numpy as np
     res = {}
-    for num in OTHER_WORKLOADS:
+    for num, window in [(n, 0) for n in OTHER_WORKLOADS] + list(WINDOWED_WORKLOADS):
         p = gen.workload(num)
+        if window:
+            p.name += f" window {window}"
+            p.mask_kind = 1   # windows are causal (the same as no mask for a single query)
         q = to_dev(p.q, p.dtype)
         mask = None if p.mask is None else torch.from_numpy(np.ascontiguousarray(p.mask)).to(dev)
         sinks = None if p.sinks is None else to_dev(p.sinks, p.dtype)
         decode = p.Lq == 1
         copies = 1
         if decode:
-            copies = max(1, -(-2 * 256 * 2 ** 20 // decode_bytes(p)))
+            copies = max(1, -(-2 * 256 * 2 ** 20 // decode_bytes(p, window)))
         ks = [to_dev(p.k, p.dtype)]
         vs = [to_dev(p.v, p.dtype)]
         for _ in range(copies - 1):
@@ -137,7 +149,7 @@ def measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, 
 
         def call(i):
             sd.attention(q, ks[i % copies], vs[i % copies], p.scale, p.mask_kind, mask, sinks, out=out,
-                         stream=stream.cuda_stream)
+                         stream=stream.cuda_stream, window=window or None)
 
         for i in range(20):
             call(i)
@@ -153,17 +165,19 @@ def measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, 
             times.append(e0.elapsed_time(e1) / calls * 1e3)
         us = sorted(times)[len(times) // 2]
         rec = {"workload": p.name, "us_per_call": round(us, 2)}
+        if window:
+            rec["window"] = window
         if decode:
-            gbps = decode_bytes(p) / us / 1e3
-            rec.update({"kv_bytes_per_call": decode_bytes(p), "GB/s": round(gbps, 1),
+            gbps = decode_bytes(p, window) / us / 1e3
+            rec.update({"kv_bytes_per_call": decode_bytes(p, window), "GB/s": round(gbps, 1),
                         "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "kv_copies": copies})
         else:
-            flop = prefill_flop(p)
+            flop = prefill_flop(p, window)
             tf = flop / us / 1e6
             peak = PEAK_FP32_MFMA_TFLOPS if p.dtype == gen.F32 else PEAK_BF16_TFLOPS
             rec.update({"flop_per_call": flop, "TFLOP/s": round(tf, 2), "peak_TFLOP/s": peak,
                         "frac_mfma_peak": round(tf / peak, 4)})
-        res[str(num)] = rec
+        res[f"{num}w{window}" if window else str(num)] = rec
         log(f"{p.name}: {us:.1f} us/call " + (f"{rec['GB/s']} GB/s" if decode else f"{rec['TFLOP/s']} TFLOP/s"))
         del ks, vs, q, out
         torch.cuda.empty_cache()

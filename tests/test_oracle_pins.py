@@ -426,3 +426,89 @@ def test_windows_brute_force_tiny(seed):
     want = np.array(attention_loops(q.tolist(), k.tolist(), v.tolist(), 1, hq, hkv, lq, lk, d, dv, 0.6, 1,
                                     None, None if sinks is None else sinks.tolist(), window=w))
     assert np.allclose(got, want.reshape(got.shape), rtol=0, atol=1e-12)
+
+
+# --- paged caches (nuvec-core tests/fast.rs: paged helper, paged attention and write tests) ----
+
+from oracle import paged as pgd  # noqa: E402
+
+
+def _paged(keys, values, bs, rng, spare=3):
+    """Caches holding keys/values [B, Hkv, N, D] in blocks of bs positions at shuffled
+    block indices (plus `spare` unused blocks), and the block table [B, ceil(N/bs)]."""
+    B, hkv, n, d = keys.shape
+    per = -(-n // bs)
+    blocks = B * per + spare
+    order = rng.permutation(blocks)
+    kc = np.zeros((blocks, hkv, bs, d))
+    vc = np.zeros((blocks, hkv, bs, values.shape[3]))
+    for s in range(B):
+        for j in range(per):
+            blk, m = order[s * per + j], min(bs, n - j * bs)
+            kc[blk, :, :m] = keys[s, :, j * bs:j * bs + m]
+            vc[blk, :, :m] = values[s, :, j * bs:j * bs + m]
+    return kc, vc, order[:B * per].reshape(B, per).astype(np.int32)
+
+
+@pytest.mark.parametrize("lq,kind,window", [(1, 0, None), (3, 1, None), (1, 1, 5), (4, 1, 7)])
+def test_paged_equals_contiguous(lq, kind, window):
+    rng = np.random.default_rng(1100 + lq)
+    B, hq, hkv, n, bs = 3, 4, 2, 37, 8
+    keys, values = _rand(rng, B, hkv, n, 6), _rand(rng, B, hkv, n, 5)
+    q = _rand(rng, B, hq, lq, 6)
+    kc, vc, table = _paged(keys, values, bs, rng)
+    lengths = np.array([37, 9, 20], dtype=np.int32)
+    sinks = _rand(rng, hq)
+    got = pgd.paged_sdpa(q, kc, vc, table, lengths, 0.4, kind, sinks, window)
+    for s, n_s in enumerate(lengths):
+        want = orc.sdpa(q[s:s + 1], keys[s:s + 1, :, :n_s], values[s:s + 1, :, :n_s], 0.4, kind, None, sinks,
+                        window=window)
+        assert np.array_equal(got[s:s + 1], want)
+
+
+def test_paged_blocks_outside_the_keys_are_never_read():
+    # unused blocks and rows past a sequence's length may hold anything (NaN here)
+    rng = np.random.default_rng(1201)
+    keys, values = _rand(rng, 2, 1, 20, 4), _rand(rng, 2, 1, 20, 4)
+    q = _rand(rng, 2, 2, 1, 4)
+    kc, vc, table = _paged(keys, values, 8, rng)
+    lengths = np.array([13, 20], dtype=np.int32)
+    kc2, vc2 = kc.copy(), vc.copy()
+    used = {(int(table[s, j // 8]), j % 8) for s in range(2) for j in range(int(lengths[s]))}
+    for blk in range(kc.shape[0]):
+        for r in range(8):
+            if (blk, r) not in used:
+                kc2[blk, :, r] = np.nan
+                vc2[blk, :, r] = np.nan
+    a = pgd.paged_sdpa(q, kc, vc, table, lengths, 0.5, 0)
+    b = pgd.paged_sdpa(q, kc2, vc2, table, lengths, 0.5, 0)
+    assert np.array_equal(a, b) and np.isfinite(b).all()
+
+
+def test_paged_hostile_tables_and_lengths_are_clamped():
+    # reading taken: lengths to [0, capacity], entries to [0, blocks - 1]; the result
+    # equals the same call on the clamped table and lengths
+    rng = np.random.default_rng(1202)
+    blocks, hkv, bs, d = 5, 2, 8, 4
+    kc, vc = _rand(rng, blocks, hkv, bs, d), _rand(rng, blocks, hkv, bs, d)
+    q = _rand(rng, 2, 4, 1, d)
+    table = np.array([[0, 1005, -5, 2**31 - 1], [4, -1, 3, 7]], dtype=np.int64)
+    lengths = np.array([4 * bs + 1, 2**31 - 1], dtype=np.int64)
+    got = pgd.paged_sdpa(q, kc, vc, table, lengths, 0.125, 1)
+    want = pgd.paged_sdpa(q, kc, vc, np.clip(table, 0, blocks - 1), np.array([4 * bs, 4 * bs]), 0.125, 1)
+    assert np.array_equal(got, want) and np.isfinite(got).all()
+    # a length of zero or below gives zeros
+    assert not pgd.paged_sdpa(q, kc, vc, table, np.array([0, -3]), 0.125, 1).any()
+
+
+def test_paged_write_places_rows_and_skips_bad_slots():
+    rng = np.random.default_rng(1203)
+    blocks, hkv, bs, d = 6, 2, 4, 3
+    cache = _rand(rng, blocks, hkv, bs, d)
+    new = _rand(rng, 6, hkv, d)
+    slots = np.array([-1, 3, blocks * bs, 2**31 - 1, 7, -(2**31)])
+    got = pgd.paged_write(cache, new, slots)
+    want = cache.copy()
+    want[0, :, 3] = new[1]          # slot 3: block 0, row 3
+    want[1, :, 3] = new[4]          # slot 7: block 1, row 3
+    assert np.array_equal(got, want)

@@ -146,6 +146,73 @@ int sdpa_plan_windowed(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t L
                        int64_t D, int64_t Dv, int64_t window, int has_sinks,
                        int dtype, sdpa_plan_t* plan);
 
+/*
+ * sdpa_paged_forward - attention of a few new query rows per sequence over a
+ * paged key/value cache (nuvec-core tests/fast.rs: the paged() cache builder,
+ * paged_attention_equals_contiguous_attention,
+ * paged_windows_and_sinks_equal_contiguous_attention,
+ * paged_attention_clamps_hostile_tables_and_lengths).
+ *
+ *   q       [B, Hq, Lq, D]                 device, dtype
+ *   kcache  [blocks, Hkv, bs, D]           device, dtype
+ *   vcache  [blocks, Hkv, bs, Dv]          device, dtype
+ *   table   [B, max_blocks] int32          device: sequence b's key j is row
+ *           j % bs of block table[b][j / bs]
+ *   lengths [B] int32                      device: sequence b's key count
+ *   out     [B, Hq, Lq, Dv]                device, dtype, written in full
+ *
+ * Sequence b is attention over its lengths[b] keys gathered back into order,
+ * exactly as sdpa_forward (or sdpa_forward_windowed) over those keys: the
+ * causal mask and the window are aligned to lengths[b]. Entries and lengths
+ * read from device memory are clamped, never trusted: a length to
+ * [0, max_blocks * bs], a table entry to [0, blocks - 1]; only the entries
+ * that cover a sequence's (windowed) keys are read, and no block outside the
+ * cache. A sequence with no key gives zero rows.
+ *   mask_kind  SDPA_MASK_NONE or SDPA_MASK_CAUSAL (a boolean mask is
+ *          SDPA_ERR_INVALID).
+ *   window 0 for none, else >= 1 with SDPA_MASK_CAUSAL (as in
+ *          sdpa_forward_windowed); negative, or positive without the causal
+ *          mask, is SDPA_ERR_INVALID.
+ *   scale, sinks, head sizes as for sdpa_forward.
+ *   dtype  SDPA_F16 or SDPA_BF16 (SDPA_F32 is SDPA_ERR_UNSUPPORTED).
+ *   Lq <= 8 and (Hq / Hkv) * Lq <= 32: the decode kernels (split-key first
+ *          pass, log-sum-exp reduce); larger query counts are
+ *          SDPA_ERR_UNSUPPORTED.
+ * The key splits follow the cache capacity max_blocks * bs (or, with a
+ * window, the window's keys), not the lengths, which stay on the device.
+ * Ownership, alignment, scratch, errors and asynchrony as for sdpa_forward.
+ */
+int sdpa_paged_forward(const void* q, const void* kcache, const void* vcache, void* out,
+                       const int32_t* table, const int32_t* lengths,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
+                       int64_t D, int64_t Dv, int64_t blocks, int64_t bs, int64_t max_blocks,
+                       float scale, int mask_kind, int64_t window, const void* sinks,
+                       int dtype, void* stream);
+
+/* The plan sdpa_paged_forward would use; pure, like sdpa_plan. */
+int sdpa_plan_paged(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t D, int64_t Dv,
+                    int64_t blocks, int64_t bs, int64_t max_blocks, int mask_kind,
+                    int64_t window, int has_sinks, int dtype, sdpa_plan_t* plan);
+
+/*
+ * sdpa_paged_write - write n new rows into a paged cache in place
+ * (nuvec-core tests/fast.rs, paged_write_matches_the_fallback_and_writes_in_place,
+ * paged_write_skips_out_of_range_slots).
+ *
+ *   cache  [blocks, Hkv, bs, E]  device, dtype; rows written in place
+ *   rows   [n, Hkv, E]           device, dtype
+ *   slots  [n] int32             device: row r goes to block slots[r] / bs,
+ *          position slots[r] % bs, for every head
+ * A slot outside [0, blocks * bs) is skipped: nothing is written for it.
+ * Two rows with the same slot race (either may win). E * sizeof(dtype) must
+ * be a multiple of 16 bytes (else SDPA_ERR_UNSUPPORTED); cache and rows must
+ * be 16-byte aligned and must not overlap. n == 0 enqueues nothing. One
+ * kernel, no scratch; asynchronous on `stream`.
+ */
+int sdpa_paged_write(void* cache, const void* rows, const int32_t* slots, int64_t n,
+                     int64_t blocks, int64_t Hkv, int64_t bs, int64_t E, int dtype,
+                     void* stream);
+
 /* Message of the last error on the calling thread ("" if none). The pointer
  * stays valid until the thread's next sdpa_* call. */
 const char* sdpa_last_error(void);
@@ -154,7 +221,7 @@ const char* sdpa_last_error(void);
  * Returns SDPA_OK or SDPA_ERR_HIP. */
 int sdpa_release_workspace(void);
 
-/* ABI version of this header: 2 (2 added the windowed calls). */
+/* ABI version of this header: 3 (2 added the windowed calls, 3 the paged ones). */
 int sdpa_abi_version(void);
 
 #ifdef __cplusplus

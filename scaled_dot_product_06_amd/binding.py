@@ -15,8 +15,8 @@ SDPA_OK, SDPA_ERR_INVALID, SDPA_ERR_UNSUPPORTED, SDPA_ERR_HIP = 0, -1, -2, -3
 SDPA_ROUTE_EMPTY, SDPA_ROUTE_ZERO_FILL, SDPA_ROUTE_PREFILL, SDPA_ROUTE_DECODE = 0, 1, 2, 3
 ROUTE_NAMES = {0: "empty", 1: "zero_fill", 2: "prefill", 3: "decode"}
 
-EXPORTED = ("sdpa_forward", "sdpa_plan", "sdpa_forward_windowed", "sdpa_plan_windowed", "sdpa_last_error",
-            "sdpa_release_workspace", "sdpa_abi_version")
+EXPORTED = ("sdpa_forward", "sdpa_plan", "sdpa_forward_windowed", "sdpa_plan_windowed", "sdpa_paged_forward",
+            "sdpa_plan_paged", "sdpa_paged_write", "sdpa_last_error", "sdpa_release_workspace", "sdpa_abi_version")
 
 
 class SdpaPlan(ctypes.Structure):
@@ -83,6 +83,14 @@ def load() -> ctypes.CDLL:
     lib.sdpa_plan_windowed.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, c_int, c_int,
                                        ctypes.POINTER(SdpaPlan)]
     lib.sdpa_plan_windowed.restype = c_int
+    lib.sdpa_paged_forward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64,
+                                       ctypes.c_float, c_int, i64, vp, c_int, vp]
+    lib.sdpa_paged_forward.restype = c_int
+    lib.sdpa_plan_paged.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, i64, c_int, i64, c_int, c_int,
+                                    ctypes.POINTER(SdpaPlan)]
+    lib.sdpa_plan_paged.restype = c_int
+    lib.sdpa_paged_write.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, c_int, vp]
+    lib.sdpa_paged_write.restype = c_int
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_release_workspace.argtypes = []
@@ -141,6 +149,33 @@ def sdpa_plan_windowed(B, Hq, Hkv, Lq, Lk, D, Dv, window, has_sinks, dtype, chec
             _check(rc)
         return rc
     return p.as_dict()
+
+
+def sdpa_paged_forward(q, kcache, vcache, out, table, lengths, B, Hq, Hkv, Lq, D, Dv, blocks, bs, max_blocks,
+                       scale, mask_kind, window, sinks, dtype, stream, check: bool = True) -> int:
+    """Raw paged call (attention over a paged key/value cache)."""
+    rc = load().sdpa_paged_forward(q, kcache, vcache, out, table, lengths, B, Hq, Hkv, Lq, D, Dv, blocks, bs,
+                                   max_blocks, ctypes.c_float(scale), mask_kind, window, sinks, dtype, stream)
+    return _check(rc) if check else rc
+
+
+def sdpa_plan_paged(B, Hq, Hkv, Lq, D, Dv, blocks, bs, max_blocks, mask_kind, window, has_sinks, dtype,
+                    check: bool = True):
+    """The paged call's plan as a dict (or the return code when check=False and it fails)."""
+    p = SdpaPlan()
+    rc = load().sdpa_plan_paged(B, Hq, Hkv, Lq, D, Dv, blocks, bs, max_blocks, mask_kind, window,
+                                int(bool(has_sinks)), dtype, ctypes.byref(p))
+    if rc != SDPA_OK:
+        if check:
+            _check(rc)
+        return rc
+    return p.as_dict()
+
+
+def sdpa_paged_write(cache, rows, slots, n, blocks, Hkv, bs, E, dtype, stream, check: bool = True) -> int:
+    """Raw paged cache write (rows into slots, in place)."""
+    rc = load().sdpa_paged_write(cache, rows, slots, n, blocks, Hkv, bs, E, dtype, stream)
+    return _check(rc) if check else rc
 
 
 def sdpa_release_workspace() -> int:
@@ -209,3 +244,67 @@ def attention(q, k, v, scale: float, mask_kind: int = SDPA_MASK_NONE, mask=None,
     sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, Lq, Lk, D, Dv,
                  float(scale), mask_kind, mptr, sptr, _dtype_code(q), stream)
     return out
+
+
+def _gpu_tensor(name, t, dtype=None):
+    if not t.is_cuda or not t.is_contiguous():
+        raise SdpaError(SDPA_ERR_INVALID, f"{name} must be a contiguous GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise SdpaError(SDPA_ERR_INVALID, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def paged_attention(q, kcache, vcache, table, lengths, scale: float, mask_kind: int = SDPA_MASK_CAUSAL,
+                    window: int = 0, sinks=None, out=None, stream=None):
+    """Attention over a paged cache through sdpa_paged_forward.
+
+    q [B,Hq,Lq,D]; kcache [blocks,Hkv,bs,D], vcache [blocks,Hkv,bs,Dv] of q's
+    dtype; table [B,max_blocks] and lengths [B] int32; all contiguous GPU
+    tensors. window 0 = none. Returns out [B,Hq,Lq,Dv].
+    """
+    import torch
+    B, Hq, Lq, D = q.shape
+    blocks, Hkv, bs, _ = kcache.shape
+    Dv = vcache.shape[3]
+    for name, t in (("q", q), ("kcache", kcache), ("vcache", vcache)):
+        _gpu_tensor(name, t, q.dtype)
+    for name, t in (("table", table), ("lengths", lengths)):
+        _gpu_tensor(name, t, torch.int32)
+    if tuple(kcache.shape) != (blocks, Hkv, bs, D) or tuple(vcache.shape[:3]) != (blocks, Hkv, bs):
+        raise SdpaError(SDPA_ERR_INVALID, f"kcache {tuple(kcache.shape)} / vcache {tuple(vcache.shape)} do not "
+                        f"match q {tuple(q.shape)}")
+    if table.dim() != 2 or table.shape[0] != B or tuple(lengths.shape) != (B,):
+        raise SdpaError(SDPA_ERR_INVALID, f"table must be [{B}, max_blocks] and lengths [{B}]")
+    sptr = None
+    if sinks is not None:
+        if tuple(sinks.shape) != (Hq,) or sinks.dtype != q.dtype or not sinks.is_cuda:
+            raise SdpaError(SDPA_ERR_INVALID, f"sinks must be a GPU tensor of shape ({Hq},) and dtype {q.dtype}")
+        sinks = sinks.contiguous()
+        sptr = sinks.data_ptr()
+    if out is None:
+        out = torch.empty((B, Hq, Lq, Dv), dtype=q.dtype, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    sdpa_paged_forward(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), out.data_ptr(), table.data_ptr(),
+                       lengths.data_ptr(), B, Hq, Hkv, Lq, D, Dv, blocks, bs, table.shape[1], float(scale),
+                       mask_kind, int(window), sptr, _dtype_code(q), stream)
+    return out
+
+
+def paged_write(cache, rows, slots, stream=None):
+    """Writes rows [n,Hkv,E] into cache [blocks,Hkv,bs,E] at slots [n] (int32), in
+    place, through sdpa_paged_write; slots outside the cache are skipped.
+    Returns cache."""
+    import torch
+    blocks, Hkv, bs, E = cache.shape
+    n = rows.shape[0]
+    _gpu_tensor("cache", cache)
+    _gpu_tensor("rows", rows, cache.dtype)
+    _gpu_tensor("slots", slots, torch.int32)
+    if tuple(rows.shape) != (n, Hkv, E) or tuple(slots.shape) != (n,):
+        raise SdpaError(SDPA_ERR_INVALID, f"rows {tuple(rows.shape)} / slots {tuple(slots.shape)} do not match "
+                        f"cache {tuple(cache.shape)}")
+    if stream is None:
+        stream = torch.cuda.current_stream(cache.device).cuda_stream
+    sdpa_paged_write(cache.data_ptr(), rows.data_ptr(), slots.data_ptr(), n, blocks, Hkv, bs, E,
+                     _dtype_code(cache), stream)
+    return cache

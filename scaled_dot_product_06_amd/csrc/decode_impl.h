@@ -45,7 +45,13 @@ struct DecodeCfg {
   static_assert(D % KW == 0, "head size must be a whole number of MFMA k-steps");
 };
 
-template <class E, int MF, int D, int DV, int NW>
+// PAGED: K and V are paged caches ([blocks, Hkv, bs, D]); sequence b has
+// lengths[b] keys (clamped to [0, max_blocks * bs]), key j in row j % bs of
+// block table[b][j / bs] (clamped to [0, blocks - 1]). The split's table
+// entries are staged in LDS once, so each key row's address needs no further
+// global read (nuvec-core "tests/fast.rs", paged_attention_equals_contiguous_
+// attention and paged_attention_clamps_hostile_tables_and_lengths).
+template <class E, int MF, int D, int DV, int NW, bool PAGED = false>
 __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   using C = DecodeCfg<MF, D, DV, NW>;
   using acc_t = typename Mfma<MF>::acc_t;
@@ -64,17 +70,32 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   const int split = blockIdx.x;
   const int hkv = blockIdx.y;
   const int b = blockIdx.z;
-  // splits cover the keys the rows read: with a sliding window, from a.koff
-  const int ks = a.koff + split * a.kps;
-  const int ke = min(ks + a.kps, a.Lk);
-  const int ntiles = (ke - ks + BN - 1) / BN;
+  // the keys this batch item holds: all Lk, or the sequence's clamped length
+  int Lk = a.Lk, koff = a.koff;
+  if constexpr (PAGED) {
+    Lk = min(max(a.lengths[b], 0), a.max_blocks * a.bs);
+    koff = a.window > 0 ? max(0, Lk - a.Lq - a.window + 1) : 0;
+  }
+  // splits cover the keys the rows read: with a sliding window, from koff
+  const int ks = koff + split * a.kps;
+  const int ke = min(ks + a.kps, Lk);
+  const int ntiles = ks < ke ? (ke - ks + BN - 1) / BN : 0;
+  // paged: clamped block ids of this split's keys (at most kps + 1 <= 1025)
+  __shared__ int32_t ptab[PAGED ? 1025 : 1];
+  const int e0 = PAGED ? ks / max(a.bs, 1) : 0;
+  if constexpr (PAGED) {
+    const int ne = ntiles > 0 ? (ke - 1) / a.bs - e0 + 1 : 0;
+    for (int i = threadIdx.x; i < ne; i += NW * 64)
+      ptab[i] = min(max(a.table[(size_t)b * a.max_blocks + e0 + i], 0), a.blocks - 1);
+    __syncthreads();
+  }
 
   // packed query rows: row r -> head hkv*group + r / Lq, position r % Lq
   const int r = col;
   const bool row_ok = r < a.rows;
   const int h = hkv * a.group + (row_ok ? r / a.Lq : 0);
   const int iq = row_ok ? r % a.Lq : 0;
-  const int shift = a.Lk - a.Lq;
+  const int shift = Lk - a.Lq;
 
   const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(b * a.Hq + h) * a.Lq + iq) * D;
   u32x4 qop[C::NQC];
@@ -97,14 +118,22 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   for (int d = 0; d < C::NDBW; ++d) o[d] = acc_t{};
   float m = -INFINITY, l = 0.0f;
 
-  const uint16_t* kp = (const uint16_t*)a.k + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * D;
-  const uint16_t* vp = (const uint16_t*)a.v + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * DV;
+  // contiguous: this (batch, kv head)'s rows; paged: the cache base (rows from key_row)
+  const uint16_t* kp = (const uint16_t*)a.k + (PAGED ? 0 : (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * D);
+  const uint16_t* vp = (const uint16_t*)a.v + (PAGED ? 0 : (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * DV);
   const uint8_t* mrow = a.mask + (size_t)iq * a.Lk;
   const bool causal_cut = a.mask_kind == kMaskCausal && a.Lq > 1;
 
   // Two register tiles (A and B) cycle so that two tiles of K/V loads are in
   // flight while the LDS copy of a third is being computed.
   u32x4 kra[C::KPT], vra[C::VPT], krb[C::KPT], vrb[C::VPT];
+  // row of key `key` in the K/V arrays: contiguous, or through the block table
+  auto key_row = [&](int key) -> size_t {
+    if constexpr (PAGED)
+      return ((size_t)ptab[key / a.bs - e0] * a.Hkv + hkv) * a.bs + key % a.bs;
+    else
+      return (size_t)key;
+  };
   auto load_tile = [&](int k0, u32x4* kr, u32x4* vr) {
 #pragma unroll
     for (int it = 0; it < C::KPT; ++it) {
@@ -112,7 +141,7 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
       if (C::KCH % C::NT == 0 || c < C::KCH) {
         const int rr = c / (D / 8), cc = c % (D / 8);
         const int key = k0 + rr;
-        kr[it] = key < ke ? ld_global16_nt(kp + (size_t)key * D + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+        kr[it] = key < ke ? ld_global16_nt(kp + key_row(key) * D + cc * 8) : u32x4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
@@ -121,7 +150,7 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
       if (C::VCH % C::NT == 0 || c < C::VCH) {
         const int rr = c / (DV / 8), cc = c % (DV / 8);
         const int key = k0 + rr;
-        vr[it] = key < ke ? ld_global16_nt(vp + (size_t)key * DV + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+        vr[it] = key < ke ? ld_global16_nt(vp + key_row(key) * DV + cc * 8) : u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -252,7 +281,7 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   }
 }
 
-// One 256-thread workgroup per (CS-column slice, query row, kv head, batch
+// One 256-thread workgroup per (query row and CS-column slice, kv head, batch
 // item). Pass 1 finds
 // the largest split maximum (with the sink). Pass 2 walks the splits in chunks
 // of 256: each thread turns one split's maximum into its weight in LDS and adds
@@ -268,8 +297,8 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(FwdArgs a) {
   __shared__ float fw[256];
   __shared__ float red[4];
   __shared__ f32x4 accs[SG][NCG];
-  const int r = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z / (DV / CS);
-  const int c0 = (blockIdx.z % (DV / CS)) * CS;
+  const int r = blockIdx.x / (DV / CS), hkv = blockIdx.y, b = blockIdx.z;
+  const int c0 = (blockIdx.x % (DV / CS)) * CS;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int h = hkv * a.group + r / a.Lq;
   const int iq = r % a.Lq;

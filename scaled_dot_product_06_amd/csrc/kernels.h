@@ -25,6 +25,11 @@ struct FwdArgs {
   int window;            // causal sliding window: row i (position pos = i + Lk - Lq) reads keys
                          // pos - window < j <= pos; 0 for none
   int koff;              // decode: first key the windowed rows read (0 without a window)
+  // paged caches: k and v are [blocks, Hkv, bs, D/Dv]; sequence b's key j is row j % bs
+  // of block table[b][j / bs]; its length is lengths[b] (both clamped in the kernel)
+  const int32_t* table;  // [B, max_blocks]
+  const int32_t* lengths;  // [B]
+  int blocks, bs, max_blocks;
   float c;               // |scale| * log2(e): scores are taken as c * q.k in base 2
   uint32_t qsign;        // XOR applied to q bits (flips q's sign when scale < 0)
   // prefill
@@ -58,6 +63,10 @@ hipError_t launch_prefill(int elem, int D, int Dv, const PrefillShape& s, const 
                           hipStream_t stream, bool* ok);
 hipError_t launch_decode(int elem, int D, int Dv, const DecodeShape& s, const FwdArgs& a,
                          hipStream_t stream, bool* ok);
+hipError_t launch_decode_paged(int elem, int D, int Dv, const DecodeShape& s, const FwdArgs& a,
+                               hipStream_t stream, bool* ok);
+hipError_t launch_paged_write(void* cache, const void* rows, const int32_t* slots, int64_t n, int64_t blocks,
+                              int64_t Hkv, int64_t bs, int64_t row_bytes, hipStream_t stream);
 hipError_t launch_zero_fill(void* out, int64_t bytes, hipStream_t stream);
 hipError_t launch_mask_bits(const uint8_t* mask, uint32_t* bits, int64_t Lq, int64_t Lk, hipStream_t stream);
 constexpr int64_t mask_words(int64_t Lk) { return (Lk + 31) / 32; }

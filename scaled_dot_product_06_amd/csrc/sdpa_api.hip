@@ -143,6 +143,15 @@ int64_t window_first_key(int64_t Lq, int64_t Lk, int64_t window) {
   return k0 > 0 ? k0 : 0;
 }
 
+// Keys per decode split for a call whose rows read `nkeys` keys: about a
+// 64th of them, a power of two in [64, 1024].
+int64_t keys_per_split(int64_t nkeys) {
+  int64_t kps = pow2_floor(nkeys / 64 > 0 ? nkeys / 64 : 1);
+  if (kps < 64) kps = 64;
+  if (kps > 1024) kps = 1024;
+  return kps;
+}
+
 // Validation shared by the plan and forward entry points; fills `plan` on
 // success. `window` is 0 (none) or the windowed calls' window, already
 // checked to be >= 1 with a causal mask; a window of at least Lk keys is
@@ -209,9 +218,7 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
     const int64_t rows = group * Lq;
     // the key partitions follow the keys the rows read (the window's, if any)
     const int64_t nkeys = Lk - window_first_key(Lq, Lk, window);
-    int64_t kps = pow2_floor(nkeys / 64 > 0 ? nkeys / 64 : 1);
-    if (kps < 64) kps = 64;
-    if (kps > 1024) kps = 1024;
+    const int64_t kps = keys_per_split(nkeys);
     const int64_t nsplit = (nkeys + kps - 1) / kps;
     p.route = SDPA_ROUTE_DECODE;
     p.kernels = 2;
@@ -298,7 +305,7 @@ hipError_t get_scratch(hipStream_t stream, size_t bytes, void** out) {
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 2; }
+int sdpa_abi_version(void) { return 3; }
 
 const char* sdpa_last_error(void) { return g_err.c_str(); }
 
@@ -437,6 +444,173 @@ int sdpa_plan_windowed(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t L
   rc = validate_and_plan(B, Hq, Hkv, Lq, Lk, D, Dv, SDPA_MASK_CAUSAL, false, has_sinks != 0, dtype, w, &p);
   if (rc == SDPA_OK) *plan = p;
   return rc;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validation and plan of a paged call (decode route only); fills `plan`.
+int validate_and_plan_paged(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t D, int64_t Dv,
+                            int64_t blocks, int64_t bs, int64_t max_blocks, int mask_kind, int64_t window,
+                            int dtype, sdpa_plan_t* plan) {
+  if (mask_kind != SDPA_MASK_NONE && mask_kind != SDPA_MASK_CAUSAL)
+    return fail(SDPA_ERR_INVALID, "paged attention takes mask_kind 0 (none) or 1 (causal) (got %d)", mask_kind);
+  if (window < 0) return fail(SDPA_ERR_INVALID, "window must be 0 (none) or >= 1 (got %lld)", (long long)window);
+  if (window > 0 && mask_kind != SDPA_MASK_CAUSAL)
+    return fail(SDPA_ERR_INVALID, "a window needs mask_kind SDPA_MASK_CAUSAL");
+  if (blocks < 1) return fail(SDPA_ERR_INVALID, "blocks must be >= 1 (got %lld)", (long long)blocks);
+  if (bs < 1) return fail(SDPA_ERR_INVALID, "bs must be >= 1 (got %lld)", (long long)bs);
+  if (max_blocks < 1) return fail(SDPA_ERR_INVALID, "max_blocks must be >= 1 (got %lld)", (long long)max_blocks);
+  int64_t cap;
+  if (__builtin_mul_overflow(max_blocks, bs, &cap) || cap > kMaxLen)
+    return fail(SDPA_ERR_UNSUPPORTED, "capacity max_blocks * bs exceeds %lld", (long long)kMaxLen);
+  if (blocks > INT_MAX) return fail(SDPA_ERR_UNSUPPORTED, "blocks (%lld) exceeds INT_MAX", (long long)blocks);
+  if (window > kMaxLen)
+    return fail(SDPA_ERR_UNSUPPORTED, "window (%lld) exceeds %lld", (long long)window, (long long)kMaxLen);
+  // the q / out / dtype / head checks of the contiguous call, with Lk = the capacity
+  sdpa_plan_t p;
+  int rc = validate_and_plan(B, Hq, Hkv, Lq, cap, D, Dv, mask_kind, false, false, dtype, 0, &p);
+  if (rc != SDPA_OK) return rc;
+  int64_t n;
+  const int64_t es = elem_size(dtype);
+  if (!mul4(blocks, Hkv, bs, D > Dv ? D : Dv, &n) || __builtin_mul_overflow(n, es, &n))
+    return fail(SDPA_ERR_INVALID, "shape overflow: cache bytes do not fit in 64 bits");
+  if (!mul3(B, max_blocks, 4, &n)) return fail(SDPA_ERR_INVALID, "shape overflow: table bytes do not fit in 64 bits");
+  if (dtype == SDPA_F32)
+    return fail(SDPA_ERR_UNSUPPORTED, "paged attention is built for SDPA_F16 and SDPA_BF16 only");
+  if (p.route == SDPA_ROUTE_EMPTY) {
+    *plan = p;
+    return SDPA_OK;
+  }
+  const int64_t group = Hq / Hkv;
+  if (Lq > 8 || group * Lq > 32)
+    return fail(SDPA_ERR_UNSUPPORTED, "paged attention runs the decode kernels: Lq (%lld) <= 8 and "
+                "(Hq/Hkv)*Lq (%lld) <= 32 needed", (long long)Lq, (long long)(group * Lq));
+  // key splits from the capacity (lengths stay on the device), or from the
+  // keys a window lets the rows read
+  int64_t nkeys = cap;
+  if (window > 0 && window + Lq - 1 < nkeys) nkeys = window + Lq - 1;
+  const int64_t kps = keys_per_split(nkeys);
+  const int64_t nsplit = (nkeys + kps - 1) / kps;
+  const int64_t rows = group * Lq;
+  p.route = SDPA_ROUTE_DECODE;
+  p.kernels = 2;
+  p.rows_per_wave = decode_mf((int)D, (int)rows);
+  p.waves = kDecodeWaves;
+  p.block_n = kDecodeBN;
+  p.heads_per_group = (int32_t)group;
+  p.keys_per_split = kps;
+  p.splits = nsplit;
+  p.grid[0] = nsplit;
+  p.grid[1] = Hkv;
+  p.grid[2] = B;
+  if (Hkv > kMaxGridYZ || B > kMaxGridYZ)
+    return fail(SDPA_ERR_UNSUPPORTED, "decode grid: Hkv (%lld) and B (%lld) must be <= 65535", (long long)Hkv,
+                (long long)B);
+  int64_t sb;
+  if (!mul4(B * Hkv, nsplit, rows, (Dv + 4) * 4, &sb)) return fail(SDPA_ERR_INVALID, "decode scratch size overflows");
+  p.scratch_bytes = sb;
+  *plan = p;
+  return SDPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_plan_paged(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t D, int64_t Dv, int64_t blocks,
+                    int64_t bs, int64_t max_blocks, int mask_kind, int64_t window, int has_sinks, int dtype,
+                    sdpa_plan_t* plan) {
+  g_err.clear();
+  (void)has_sinks;
+  if (!plan) return fail(SDPA_ERR_INVALID, "plan must not be NULL");
+  sdpa_plan_t p;
+  const int rc = validate_and_plan_paged(B, Hq, Hkv, Lq, D, Dv, blocks, bs, max_blocks, mask_kind, window, dtype, &p);
+  if (rc == SDPA_OK) *plan = p;
+  return rc;
+}
+
+int sdpa_paged_forward(const void* q, const void* kcache, const void* vcache, void* out, const int32_t* table,
+                       const int32_t* lengths, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t D,
+                       int64_t Dv, int64_t blocks, int64_t bs, int64_t max_blocks, float scale, int mask_kind,
+                       int64_t window, const void* sinks, int dtype, void* stream_v) {
+  g_err.clear();
+  sdpa_plan_t p;
+  int rc = validate_and_plan_paged(B, Hq, Hkv, Lq, D, Dv, blocks, bs, max_blocks, mask_kind, window, dtype, &p);
+  if (rc != SDPA_OK) return rc;
+  if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID, "scale must be finite (got %g)", (double)scale);
+  if (p.route == SDPA_ROUTE_EMPTY) return SDPA_OK;
+  if (!out || !q) return fail(SDPA_ERR_INVALID, "q and out must not be NULL");
+  if (!kcache || !vcache) return fail(SDPA_ERR_INVALID, "kcache and vcache must not be NULL");
+  if (!table || !lengths) return fail(SDPA_ERR_INVALID, "table and lengths must not be NULL");
+  if (((uintptr_t)out | (uintptr_t)q | (uintptr_t)kcache | (uintptr_t)vcache) & 15)
+    return fail(SDPA_ERR_INVALID, "q, kcache, vcache and out must be 16-byte aligned");
+  if (((uintptr_t)table | (uintptr_t)lengths) & 3)
+    return fail(SDPA_ERR_INVALID, "table and lengths must be 4-byte aligned");
+  hipStream_t stream = (hipStream_t)stream_v;
+  FwdArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q;
+  a.k = kcache;
+  a.v = vcache;
+  a.out = out;
+  a.sinks = sinks;
+  a.B = (int)B;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.Lq = (int)Lq;
+  a.Lk = (int)(max_blocks * bs);
+  a.group = (int)(Hq / Hkv);
+  a.mask_kind = mask_kind;
+  a.window = (int)window;
+  a.table = table;
+  a.lengths = lengths;
+  a.blocks = (int)blocks;
+  a.bs = (int)bs;
+  a.max_blocks = (int)max_blocks;
+  a.c = fmaxf(fabsf(scale) * 1.4426950408889634f, FLT_MIN);
+  a.qsign = scale < 0.0f ? 0x80008000u : 0u;
+  a.rows = (int)(a.group * Lq);
+  a.kps = (int)p.keys_per_split;
+  a.nsplit = (int)p.splits;
+  void* part = nullptr;
+  hipError_t e = get_scratch(stream, (size_t)p.scratch_bytes, &part);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "decode scratch allocation failed: %s", hipGetErrorString(e));
+  a.part = (float*)part;
+  DecodeShape s{p.rows_per_wave, p.waves, p.block_n};
+  bool ok = false;
+  e = launch_decode_paged(dtype, (int)D, (int)Dv, s, a, stream, &ok);
+  if (!ok) return fail(SDPA_ERR_UNSUPPORTED, "no kernel built for dtype %d, D=%lld, Dv=%lld", dtype, (long long)D,
+                       (long long)Dv);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SDPA_OK;
+}
+
+int sdpa_paged_write(void* cache, const void* rows, const int32_t* slots, int64_t n, int64_t blocks, int64_t Hkv,
+                     int64_t bs, int64_t E, int dtype, void* stream) {
+  g_err.clear();
+  if (dtype != SDPA_F32 && dtype != SDPA_F16 && dtype != SDPA_BF16)
+    return fail(SDPA_ERR_INVALID, "dtype must be SDPA_F32, SDPA_F16 or SDPA_BF16 (got %d)", dtype);
+  if (n < 0) return fail(SDPA_ERR_INVALID, "n must be >= 0 (got %lld)", (long long)n);
+  if (blocks < 0) return fail(SDPA_ERR_INVALID, "blocks must be >= 0 (got %lld)", (long long)blocks);
+  if (Hkv < 0) return fail(SDPA_ERR_INVALID, "Hkv must be >= 0 (got %lld)", (long long)Hkv);
+  if (bs < 1) return fail(SDPA_ERR_INVALID, "bs must be >= 1 (got %lld)", (long long)bs);
+  if (E < 0) return fail(SDPA_ERR_INVALID, "E must be >= 0 (got %lld)", (long long)E);
+  int64_t row_bytes, nb;
+  if (__builtin_mul_overflow(E, (int64_t)elem_size(dtype), &row_bytes) || !mul4(blocks, Hkv, bs, row_bytes, &nb) ||
+      !mul3(n, Hkv, row_bytes, &nb))
+    return fail(SDPA_ERR_INVALID, "shape overflow: cache or row bytes do not fit in 64 bits");
+  if (row_bytes % 16 != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "a cache row (E * element size = %lld bytes) must be a multiple of 16 bytes",
+                (long long)row_bytes);
+  if (n == 0 || Hkv == 0 || E == 0) return SDPA_OK;
+  if (!cache || !rows || !slots) return fail(SDPA_ERR_INVALID, "cache, rows and slots must not be NULL");
+  if ((((uintptr_t)cache | (uintptr_t)rows) & 15) || ((uintptr_t)slots & 3))
+    return fail(SDPA_ERR_INVALID, "cache and rows must be 16-byte aligned, slots 4-byte aligned");
+  const hipError_t e = launch_paged_write(cache, rows, slots, n, blocks, Hkv, bs, row_bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "paged write launch failed: %s", hipGetErrorString(e));
+  return SDPA_OK;
 }
 
 int sdpa_release_workspace(void) {

@@ -17,7 +17,11 @@ generators", OOPSLA 2014). From that word:
 Values are rounded to nearest-even into the storage type; normals are rounded
 to float32 first and then to float16/bfloat16. Storage arrays are numpy
 ``float32`` / ``float16`` and, for bfloat16, ``uint16`` holding the bit
-pattern. Tensor ids: q=1, k=2, v=3, mask=4, sinks=5.
+pattern. Tensor ids: q=1, k=2, v=3, mask=4, sinks=5, block order=6.
+
+Paged caches (``block_order``, ``paged_cache``) only move these arrays into
+blocks at shuffled places; the block order is a Fisher-Yates shuffle whose
+step i swaps with index ``x(i) mod (i + 1)`` of stream 6.
 """
 from __future__ import annotations
 
@@ -31,7 +35,7 @@ DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
 DTYPE_BY_NAME = {"f32": F32, "f16": F16, "bf16": BF16}
 STORAGE = {F32: np.float32, F16: np.float16, BF16: np.uint16}
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_MASK, TENSOR_SINKS = 1, 2, 3, 4, 5
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_MASK, TENSOR_SINKS, TENSOR_PAGES = 1, 2, 3, 4, 5, 6
 
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
@@ -223,3 +227,43 @@ def workload(number: int) -> Problem:
     w = dict(WORKLOADS[number])
     name = w.pop("name")
     return make_problem(number, name=name, **w)
+
+
+# ---- paged caches -------------------------------------------------------------------------
+
+NAN_BITS = {F32: np.float32(np.nan), F16: np.float16(np.nan), BF16: np.uint16(0x7FC0)}
+
+
+def block_order(seed: int, blocks: int) -> np.ndarray:
+    """A seeded permutation of range(blocks) (Fisher-Yates on stream 6)."""
+    w = words(seed, TENSOR_PAGES, 0, max(blocks, 1))
+    order = np.arange(blocks, dtype=np.int64)
+    for i in range(blocks - 1, 0, -1):
+        j = int(w[i] % np.uint64(i + 1))
+        order[i], order[j] = order[j], order[i]
+    return order
+
+
+def paged_cache(x: np.ndarray, bs: int, order: np.ndarray, blocks: int, fill=0):
+    """Copies a storage array x [B, Hkv, N, E] into a cache [blocks, Hkv, bs, E]:
+    positions j*bs .. j*bs+bs-1 of sequence s go to block order[s * per + j],
+    per = ceil(N / bs). Rows no sequence owns hold `fill` (a value, or "nan").
+    Returns (cache, table [B, per] int32)."""
+    B, hkv, n, e = x.shape
+    per = -(-n // bs)
+    assert blocks >= B * per and len(order) >= B * per
+    cache = np.empty((blocks, hkv, bs, e), dtype=x.dtype)
+    cache[...] = NAN_BITS[_storage_code(x.dtype)] if isinstance(fill, str) else fill
+    for s in range(B):
+        for j in range(per):
+            m = min(bs, n - j * bs)
+            cache[order[s * per + j], :, :m] = x[s, :, j * bs:j * bs + m]
+    table = np.asarray(order[:B * per], dtype=np.int32).reshape(B, per)
+    return cache, table
+
+
+def _storage_code(dt) -> int:
+    for code, st in STORAGE.items():
+        if np.dtype(st) == np.dtype(dt):
+            return code
+    raise ValueError(f"not a storage dtype: {dt}")

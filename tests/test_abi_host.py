@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(sd.library_path())
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert sd.sdpa_abi_version() == 2
+    assert sd.sdpa_abi_version() == 3
     out = subprocess.run(["nm", "-D", "--defined-only", sd.library_path()], capture_output=True, text=True).stdout
     for name in _declared_functions():
         assert re.search(rf"\bT {name}$", out, flags=re.M), f"{name} not exported with C linkage"
@@ -188,3 +188,90 @@ def test_invalid_windows_are_rejected(window):
     f = sd.sdpa_forward_windowed
     assert f(None, None, None, None, 1, 4, 2, 5, 9, 64, 64, 0.1, window, None, 2, None, check=False) == -1
     assert "window" in sd.sdpa_last_error()
+
+
+# --- paged calls ------------------------------------------------------------------------------
+
+def _plan_paged(B=2, Hq=8, Hkv=2, Lq=1, D=128, Dv=128, blocks=40, bs=16, max_blocks=20, mask=1, window=0,
+                sinks=0, dtype=2):
+    return sd.sdpa_plan_paged(B, Hq, Hkv, Lq, D, Dv, blocks, bs, max_blocks, mask, window, sinks, dtype,
+                              check=False)
+
+
+def test_paged_plans_are_decode_plans_over_the_capacity():
+    # fast.rs, paged_attention_equals_contiguous_attention: with two passes the key
+    # partitions follow the table's capacity (max_blocks * bs), not the lengths
+    for (B, Hq, Hkv, Lq, D, bs, mb) in [(2, 8, 2, 1, 128, 32, 94), (1, 8, 2, 4, 128, 64, 33),
+                                        (3, 8, 2, 1, 128, 32, 10), (2, 4, 1, 4, 64, 16, 5)]:
+        p = _plan_paged(B=B, Hq=Hq, Hkv=Hkv, Lq=Lq, D=D, Dv=D, bs=bs, max_blocks=mb)
+        c = sd.sdpa_plan(B, Hq, Hkv, Lq, mb * bs, D, D, 1, False, False, 2)
+        assert p == c, (p, c)
+
+
+def test_paged_window_plans_follow_the_window():
+    full = _plan_paged(Lq=1, bs=32, max_blocks=128)
+    win = _plan_paged(Lq=1, bs=32, max_blocks=128, window=128)
+    assert win["splits"] * win["keys_per_split"] >= 128 and win["splits"] < full["splits"]
+    four = _plan_paged(Lq=4, bs=32, max_blocks=128, window=300)
+    assert four["splits"] * four["keys_per_split"] >= 303
+    assert _plan_paged(window=1 << 30) == _plan_paged()
+
+
+@pytest.mark.parametrize("kwargs,code,needle", [
+    (dict(mask=2), -1, "mask_kind"),
+    (dict(mask=0, window=5), -1, "window"),
+    (dict(window=-1), -1, "window"),
+    (dict(blocks=0), -1, "blocks"),
+    (dict(bs=0), -1, "bs"),
+    (dict(max_blocks=0), -1, "max_blocks"),
+    (dict(Hq=4, Hkv=3), -1, "multiple"),
+    (dict(dtype=0), -2, "F16"),
+    (dict(dtype=7), -1, "dtype"),
+    (dict(Lq=9), -2, "decode"),
+    (dict(Hq=66, Hkv=2, Lq=1), -2, "decode"),
+    (dict(D=72, Dv=72), -2, "head sizes"),
+    (dict(bs=1 << 20, max_blocks=1 << 20), -2, "capacity"),
+])
+def test_invalid_paged_arguments_are_rejected(kwargs, code, needle):
+    assert _plan_paged(**kwargs) == code
+    assert needle in sd.sdpa_last_error()
+
+
+def test_paged_forward_validates_before_touching_memory():
+    f = sd.sdpa_paged_forward
+    args = dict(B=1, Hq=4, Hkv=2, Lq=1, D=64, Dv=64, blocks=4, bs=8, max_blocks=2, scale=0.1, mask_kind=1,
+                window=0, sinks=None, dtype=2, stream=None)
+
+    def call(ptrs, **over):
+        a = dict(args, **over)
+        return f(*ptrs, a["B"], a["Hq"], a["Hkv"], a["Lq"], a["D"], a["Dv"], a["blocks"], a["bs"],
+                 a["max_blocks"], a["scale"], a["mask_kind"], a["window"], a["sinks"], a["dtype"], a["stream"],
+                 check=False)
+
+    none = (None,) * 6
+    assert call(none) == -1 and "NULL" in sd.sdpa_last_error()
+    assert call((16, 16, 16, 16, None, 16)) == -1 and "table" in sd.sdpa_last_error()
+    assert call((16, 16, 16, 8, 16, 16)) == -1 and "aligned" in sd.sdpa_last_error()
+    assert call((16, 16, 16, 16, 16, 18)) == -1 and "aligned" in sd.sdpa_last_error()
+    assert call(none, scale=float("inf")) == -1 and "scale" in sd.sdpa_last_error()
+    assert call(none, Hkv=3) == -1 and "multiple" in sd.sdpa_last_error()
+    # empty calls are successful no-ops, even with null pointers
+    assert call(none, Lq=0) == 0
+    assert call(none, B=0) == 0
+
+
+def test_paged_write_validates_before_touching_memory():
+    w = sd.sdpa_paged_write
+    assert w(None, None, None, 3, 6, 2, 4, 64, 2, None, check=False) == -1
+    assert "NULL" in sd.sdpa_last_error()
+    assert w(None, None, None, -1, 6, 2, 4, 64, 2, None, check=False) == -1
+    assert w(None, None, None, 3, 6, 2, 0, 64, 2, None, check=False) == -1
+    assert "bs" in sd.sdpa_last_error()
+    assert w(None, None, None, 3, 6, 2, 4, 63, 2, None, check=False) == -2
+    assert "16 bytes" in sd.sdpa_last_error()
+    assert w(None, None, None, 3, 6, 2, 4, 64, 9, None, check=False) == -1
+    assert w(16, 16, 18, 3, 6, 2, 4, 64, 2, None, check=False) == -1
+    assert "aligned" in sd.sdpa_last_error()
+    assert w(None, None, None, 0, 6, 2, 4, 64, 2, None, check=False) == 0
+    # f32 rows of 4 elements are 16 bytes
+    assert w(None, None, None, 0, 6, 2, 4, 4, 0, None, check=False) == 0

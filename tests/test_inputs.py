@@ -53,3 +53,27 @@ def test_workload_shapes():
     assert p.q.dtype == np.float16 and p.sinks.shape == (16,) and p.mask.shape == (1024, 1801)
     q, k, v, m, s = p.widened()
     assert q.dtype == np.float64 and m.dtype == bool
+
+
+def test_block_order_is_a_seeded_permutation():
+    for n in (1, 2, 7, 100):
+        o = gen.block_order(3, n)
+        assert sorted(o.tolist()) == list(range(n))
+        assert np.array_equal(o, gen.block_order(3, n))
+    assert not np.array_equal(gen.block_order(3, 100), gen.block_order(4, 100))
+
+
+def test_paged_cache_places_every_position_once():
+    x = gen.tensor(9, gen.TENSOR_K, (3, 2, 37, 8), gen.F16, "uniform")
+    bs, blocks = 8, 3 * 5 + 3
+    cache, table = gen.paged_cache(x, bs, gen.block_order(9, blocks), blocks, fill="nan")
+    assert table.shape == (3, 5) and table.dtype == np.int32
+    assert len(set(table.ravel().tolist())) == 15
+    for s in range(3):
+        for j in range(37):
+            assert np.array_equal(cache[table[s, j // bs], :, j % bs], x[s, :, j])
+    # rows that no position owns (the tail of each last block, the spare blocks) hold the fill
+    owned = {(int(table[s, j // bs]), j % bs) for s in range(3) for j in range(37)}
+    for blk in range(blocks):
+        for r in range(bs):
+            assert np.isnan(cache[blk, :, r]).all() == ((blk, r) not in owned)

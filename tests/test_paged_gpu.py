@@ -1,0 +1,220 @@
+"""GPU parity of the paged calls (sdpa_paged_forward, sdpa_paged_write) against
+the CPU float64 oracle (oracle/paged.py) and against the contiguous call, on
+seeded inputs. The cases follow nuvec-core "tests/fast.rs":
+paged_attention_equals_contiguous_attention,
+paged_windows_and_sinks_equal_contiguous_attention,
+paged_attention_clamps_hostile_tables_and_lengths,
+paged_write_matches_the_fallback_and_writes_in_place and
+paged_write_skips_out_of_range_slots."""
+import zlib
+
+import numpy as np
+import pytest
+
+from oracle import paged as pgd
+from scaled_dot_product_06_amd import inputs as gen
+from tests.gpu_util import TOL, compare, from_device, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+F32, F16, BF16 = gen.F32, gen.F16, gen.BF16
+DT = {"f32": F32, "f16": F16, "bf16": BF16}
+
+# (B, Hq, Hkv, Lq, D, bs, lengths, window): the pages' paged cases (window 0 = none),
+# then block sizes of one and of five positions, empty and short sequences
+CASES = [
+    (1, 4, 4, 1, 128, 16, (37,), 0), (3, 8, 2, 1, 128, 32, (1, 64, 300), 0), (2, 4, 1, 4, 64, 16, (4, 77), 0),
+    (2, 2, 2, 1, 256, 8, (9, 513), 0), (2, 8, 2, 1, 128, 32, (1500, 3000), 0), (1, 8, 2, 4, 128, 64, (2100,), 0),
+    (1, 4, 2, 1, 256, 16, (1100,), 0),
+    (2, 8, 1, 1, 64, 16, (40, 300), 128), (2, 4, 2, 4, 64, 16, (9, 77), 5), (1, 4, 1, 1, 512, 16, (600,), 64),
+    (2, 8, 2, 1, 128, 32, (1500, 3000), 128), (1, 4, 4, 1, 256, 8, (513,), 512),
+    (1, 8, 2, 1, 128, 1, (2500,), 0), (3, 8, 2, 3, 96, 5, (0, 2, 61), 0), (3, 16, 2, 2, 128, 16, (1, 700, 64), 40),
+]
+
+
+def _ids(c):
+    B, Hq, Hkv, Lq, D, bs, lens, w = c
+    return f"B{B}_H{Hq}-{Hkv}_Lq{Lq}_D{D}_bs{bs}_L{'-'.join(map(str, lens))}_w{w}"
+
+
+class Paged:
+    """One paged call's inputs: storage arrays, a clean cache (unowned rows zero) for
+    the oracle and a poisoned one (unowned rows, and blocks wholly before each
+    sequence's window, NaN) for the GPU."""
+
+    def __init__(self, seed, B, Hq, Hkv, Lq, D, Dv, bs, lengths, window, dtype, sinks, mask_kind=1, spare=3):
+        n = max(max(lengths), 1)
+        p = gen.make_problem(seed, B, Hq, Hkv, Lq, n, D, Dv, dtype, 0, sinks=sinks)
+        per = -(-n // bs)
+        blocks = B * per + spare
+        order = gen.block_order(seed, blocks)
+        self.p, self.bs, self.blocks, self.window, self.mask_kind = p, bs, blocks, window, mask_kind
+        self.lengths = np.asarray(lengths, dtype=np.int32)
+        self.kc, self.table = gen.paged_cache(p.k, bs, order, blocks)
+        self.vc, _ = gen.paged_cache(p.v, bs, order, blocks)
+        self.kc_nan, _ = gen.paged_cache(p.k, bs, order, blocks, fill="nan")
+        self.vc_nan, _ = gen.paged_cache(p.v, bs, order, blocks, fill="nan")
+        if window:
+            nan = gen.NAN_BITS[dtype]
+            for s, ln in enumerate(lengths):
+                first = max(ln - Lq - window + 1, 0)
+                for j in range(first // bs):
+                    self.kc_nan[self.table[s, j]] = nan
+                    self.vc_nan[self.table[s, j]] = nan
+
+    def oracle(self):
+        p = self.p
+        w = lambda a: gen.widen(a, p.dtype)
+        sinks = None if p.sinks is None else w(p.sinks)
+        return pgd.paged_sdpa(w(p.q), w(self.kc), w(self.vc), self.table, self.lengths, p.scale, self.mask_kind,
+                              sinks, self.window or None)
+
+    def run(self, poisoned=True, table=None, lengths=None):
+        import torch
+        from scaled_dot_product_06_amd import paged_attention
+        p = self.p
+        kc, vc = (self.kc_nan, self.vc_nan) if poisoned else (self.kc, self.vc)
+        table = self.table if table is None else table
+        lengths = self.lengths if lengths is None else lengths
+        dq, dk, dv = (to_device(a, p.dtype) for a in (p.q, kc, vc))
+        dt = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).cuda()
+        dl = torch.from_numpy(np.ascontiguousarray(lengths, dtype=np.int32)).cuda()
+        ds = None if p.sinks is None else to_device(p.sinks, p.dtype)
+        o = paged_attention(dq, dk, dv, dt, dl, p.scale, self.mask_kind, self.window, ds)
+        torch.cuda.synchronize()
+        return from_device(o, p.dtype)
+
+
+def _assert_close(got, want, dtype, what):
+    bad, max_abs, max_rel = compare(got, want, dtype)
+    say(f"  {what}: max_abs={max_abs:.3e} max_rel={max_rel:.3e} failing={bad}/{want.size}")
+    assert bad == 0, f"{what}: {bad} elements outside tolerance {TOL[dtype]}"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_paged_equals_the_oracle(case, dtype):
+    B, Hq, Hkv, Lq, D, bs, lengths, w = case
+    for sinks in (False, True):
+        seed = 3000 + zlib.crc32(repr((case, dtype, sinks)).encode()) % 100000
+        say(f"paged {_ids(case)} {dtype} sinks={sinks} seed={seed}")
+        pc = Paged(seed, B, Hq, Hkv, Lq, D, D, bs, lengths, w, DT[dtype], sinks)
+        got = pc.run()
+        assert np.isfinite(got).all(), "a NaN block or row was read"
+        _assert_close(got, pc.oracle(), DT[dtype], f"{_ids(case)} sinks={sinks}")
+
+
+@pytest.mark.parametrize("D,Dv", [(96, 64), (192, 128)])
+def test_paged_value_head_differs(D, Dv):
+    pc = Paged(77 + D, 2, 8, 2, 2, D, Dv, 16, (33, 250), 0, BF16, True)
+    _assert_close(pc.run(), pc.oracle(), BF16, f"D={D} Dv={Dv}")
+
+
+@pytest.mark.parametrize("case", [c for c in CASES if max(c[6]) < 8192], ids=_ids)
+def test_paged_equals_contiguous_bit_for_bit(case):
+    # below 8,192 keys of capacity both calls split the keys into the same 64-key
+    # partitions, so the paged result is the contiguous one, bit for bit, per sequence
+    import torch
+    from scaled_dot_product_06_amd import attention
+    B, Hq, Hkv, Lq, D, bs, lengths, w = case
+    pc = Paged(41 + sum(lengths), B, Hq, Hkv, Lq, D, D, bs, lengths, w, BF16, True)
+    got = pc.run()
+    p = pc.p
+    for s, ln in enumerate(lengths):
+        q = to_device(p.q[s:s + 1], BF16)
+        k = to_device(np.ascontiguousarray(p.k[s:s + 1, :, :ln]), BF16)
+        v = to_device(np.ascontiguousarray(p.v[s:s + 1, :, :ln]), BF16)
+        o = attention(q, k, v, p.scale, 1, None, to_device(p.sinks, BF16), window=w or None)
+        torch.cuda.synchronize()
+        want = from_device(o, BF16)
+        assert np.array_equal(got[s:s + 1], want), f"sequence {s} (length {ln})"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("B,Hq,Hkv,Lq,D,bs,max_blocks", [(2, 4, 2, 1, 64, 8, 4), (2, 4, 2, 3, 128, 16, 3),
+                                                        (2, 8, 2, 1, 128, 32, 64)])
+def test_hostile_tables_and_lengths_are_clamped(B, Hq, Hkv, Lq, D, bs, max_blocks, dtype):
+    blocks = 5
+    seed = 5000 + max_blocks
+    pc = Paged(seed, 1, Hq, Hkv, Lq, D, D, bs, (blocks * bs,), 0, DT[dtype], False, spare=0)
+    p = pc.p
+    q = gen.tensor(seed, gen.TENSOR_Q, (B, Hq, Lq, D), DT[dtype], "normal")
+    pc.p = gen.Problem(B, Hq, Hkv, Lq, max_blocks * bs, D, D, DT[dtype], 1, 0.125, q, p.k, p.v)
+    i = np.arange(B * max_blocks)
+    table = np.select([i % 4 == 0, i % 4 == 1, i % 4 == 2], [i % blocks, blocks + 1000, -5],
+                      2**31 - 1).astype(np.int32).reshape(B, max_blocks)
+    lengths = np.array([max_blocks * bs + 1, 2**31 - 1][:B], dtype=np.int32)
+    pc.table, pc.lengths = table, lengths
+    got = pc.run(poisoned=False)
+    assert np.isfinite(got).all()
+    _assert_close(got, pc.oracle(), DT[dtype], f"hostile B={B} max_blocks={max_blocks}")
+    # negative and zero lengths give zero rows
+    pc.lengths = np.array([0, -7][:B], dtype=np.int32)
+    assert not pc.run(poisoned=False).any()
+
+
+def test_paged_batch_items_equal_each_item_alone():
+    pc = Paged(61, 3, 8, 2, 1, 128, 128, 16, (900, 17, 400), 0, BF16, True)
+    got = pc.run()
+    for s in range(3):
+        one = Paged(61, 3, 8, 2, 1, 128, 128, 16, (900, 17, 400), 0, BF16, True)
+        one.p.q = one.p.q[s:s + 1]
+        one.table, one.lengths = one.table[s:s + 1], one.lengths[s:s + 1]
+        assert np.array_equal(one.run(), got[s:s + 1])
+
+
+# --- the cache write ---------------------------------------------------------------------------
+
+def _write_on_gpu(cache, rows, slots, dtype, guard=64):
+    """Runs the write on a cache placed between two guard regions of one allocation;
+    returns (cache after, guards unchanged)."""
+    import torch
+    from scaled_dot_product_06_amd import paged_write
+    flat = np.concatenate([np.full(guard, gen.NAN_BITS[dtype], dtype=cache.dtype), cache.ravel(),
+                           np.full(guard, gen.NAN_BITS[dtype], dtype=cache.dtype)])
+    dev = to_device(flat, dtype)
+    dcache = dev[guard:guard + cache.size].view(cache.shape)
+    paged_write(dcache, to_device(rows, dtype), torch.from_numpy(np.asarray(slots, dtype=np.int32)).cuda())
+    torch.cuda.synchronize()
+    host = dev.cpu()
+    raw = (host.view(torch.int16).numpy().view(np.uint16) if dtype == BF16 else host.numpy())
+    guards_ok = np.array_equal(raw[:guard].view(np.uint8), flat[:guard].view(np.uint8)) and \
+        np.array_equal(raw[-guard:].view(np.uint8), flat[-guard:].view(np.uint8))
+    return raw[guard:guard + cache.size].reshape(cache.shape), guards_ok
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_paged_write_matches_the_oracle(dtype):
+    dt = DT[dtype]
+    cache = gen.tensor(71, gen.TENSOR_K, (6, 2, 4, 64), dt, "normal")
+    rows = gen.tensor(71, gen.TENSOR_V, (5, 2, 64), dt, "normal")
+    slots = [23, 0, 5, 17, 6]
+    got, guards = _write_on_gpu(cache, rows, slots, dt)
+    want = pgd.paged_write(cache, rows, slots)
+    assert guards and np.array_equal(got.view(np.uint8), want.view(np.uint8))
+    # slot 5 is block 1, position 1
+    assert np.array_equal(got[1, :, 1].view(np.uint8), rows[2].view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_paged_write_skips_out_of_range_slots(dtype):
+    dt = DT[dtype]
+    blocks, hkv, bs, d = 6, 2, 4, 64
+    cache = gen.tensor(72, gen.TENSOR_K, (blocks, hkv, bs, d), dt, "normal")
+    rows = gen.tensor(72, gen.TENSOR_V, (6, hkv, d), dt, "normal")
+    slots = [-1, 3, blocks * bs, 2**31 - 1, 7, -(2**31)]
+    got, guards = _write_on_gpu(cache, rows, slots, dt)
+    want = pgd.paged_write(cache, rows[[1, 4]], [3, 7])
+    assert guards, "a write landed outside the cache"
+    assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+
+
+def test_paged_write_many_rows_and_wide_heads():
+    # more rows than one grid's worth of threads per pass, 512-wide rows
+    blocks, hkv, bs, d = 300, 4, 16, 512
+    n = 4000
+    cache = gen.tensor(73, gen.TENSOR_K, (blocks, hkv, bs, d), BF16, "uniform")
+    rows = gen.tensor(73, gen.TENSOR_V, (n, hkv, d), BF16, "uniform")
+    slots = gen.block_order(73, blocks * bs)[:n]
+    got, guards = _write_on_gpu(cache, rows, slots, BF16)
+    assert guards and np.array_equal(got, pgd.paged_write(cache, rows, slots))

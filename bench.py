@@ -184,6 +184,61 @@ def measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, 
     return res
 
 
+# paged-cache decode on the long-context decode shape (reported): (workload, block size, window)
+PAGED_WORKLOADS = ((5, 16, 0), (5, 16, 4096))
+
+
+def measure_paged_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, rounds=5):
+    """Per-call kernel time of decode over a paged cache: the long-context decode
+    workload's K/V copied into blocks of 16 positions at shuffled places (three
+    spare blocks), every sequence at its full length, with and without a sliding
+    window. Counted bytes are the K/V rows the call reads (block ids excluded)."""
+    import numpy as np
+    res = {}
+    for num, bs, window in PAGED_WORKLOADS:
+        p = gen.workload(num)
+        per = -(-p.Lk // bs)
+        blocks = p.B * per + 3
+        order = gen.block_order(num, blocks)
+        kc, table = gen.paged_cache(p.k, bs, order, blocks)
+        vc, _ = gen.paged_cache(p.v, bs, order, blocks)
+        q = to_dev(p.q, p.dtype)
+        kd, vd = to_dev(kc, p.dtype), to_dev(vc, p.dtype)
+        del kc, vc
+        td = torch.from_numpy(table).to(dev)
+        ld = torch.full((p.B,), p.Lk, dtype=torch.int32, device=dev)
+        out = torch.empty((p.B, p.Hq, p.Lq, p.Dv), dtype=q.dtype, device=dev)
+        nbytes = decode_bytes(p, window)
+        mask_kind = 1 if window else p.mask_kind
+
+        def call():
+            sd.paged_attention(q, kd, vd, td, ld, p.scale, mask_kind, window, out=out, stream=stream.cuda_stream)
+
+        for _ in range(20):
+            call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(calls):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / calls * 1e3)
+        us = sorted(times)[len(times) // 2]
+        gbps = nbytes / us / 1e3
+        name = f"{p.name} paged bs={bs}" + (f" window {window}" if window else "")
+        res[f"{num}p{bs}" + (f"w{window}" if window else "")] = {
+            "workload": name, "us_per_call": round(us, 2), "block_size": bs, "blocks": blocks,
+            "window": window or None, "kv_bytes_per_call": nbytes, "GB/s": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+        log(f"{name}: {us:.1f} us/call {gbps:.0f} GB/s")
+        del q, kd, vd, td, ld, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,7 +249,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip the reported-only workloads (f32 prefill, "
-                    "8193-key decode, f16 masked prefill with sinks)")
+                    "8193-key decode, f16 masked prefill with sinks, sliding windows, paged decode)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
@@ -276,7 +331,10 @@ def main() -> int:
         f"bf16 MFMA peak); decode {dec_ms * 1e3:.1f} us/call = {gbps:.0f} GB/s "
         f"({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM peak); step {step_ms:.3f} ms; wall {wall:.2f} s")
 
-    others = measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log) if not args.no_others else None
+    others = None
+    if not args.no_others:
+        others = measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log)
+        others.update(measure_paged_workloads(torch, sd, gen, dev, to_dev, stream, log))
 
     pre_plan = sd.sdpa_plan(pre.B, pre.Hq, pre.Hkv, pre.Lq, pre.Lk, pre.D, pre.Dv, pre.mask_kind, False, False,
                             pre.dtype)

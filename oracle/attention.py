@@ -29,6 +29,13 @@ softmax row per query, in float64 on the exact values of the stored inputs:
   ``windows_run_fused_and_equal_the_boolean_mask`` and
   ``window_errors_empty_inputs_and_full_windows``); a window of at least Lk
   keys is plain causal attention;
+* an additive mask (nuvec-core "tests/fast.rs",
+  ``attention_kernels_match_the_fallback``: a float mask of shape
+  ``[1, Hq, Lq, Lk]`` in the input type, passed where a boolean mask could
+  be) is added to the scaled scores, ``scale * q . k + mask[b, h, i, j]``;
+  it broadcasts over batch items and heads. Reading taken: a key whose mask
+  entry is ``-inf`` is excluded like a masked key, so a row whose every entry
+  is ``-inf`` outputs zero, as an all-masked row does;
 * an optional per-query-head sink is one extra logit in the softmax
   denominator with no value row. Reading taken: the sink is added as given,
   after scaling (it is not multiplied by ``scale``), and takes part in the row
@@ -42,7 +49,7 @@ from __future__ import annotations
 
 import numpy as np
 
-MASK_NONE, MASK_CAUSAL, MASK_BOOL = 0, 1, 2
+MASK_NONE, MASK_CAUSAL, MASK_BOOL, MASK_ADDITIVE = 0, 1, 2, 3
 
 
 def visible_keys(i: int, Lq: int, Lk: int, mask_kind: int, mask=None, window=None) -> np.ndarray:
@@ -59,6 +66,8 @@ def visible_keys(i: int, Lq: int, Lk: int, mask_kind: int, mask=None, window=Non
         return j <= i + Lk - Lq
     if mask_kind == MASK_BOOL:
         return np.asarray(mask[i], dtype=bool).copy()
+    if mask_kind == MASK_ADDITIVE:
+        return np.ones(Lk, dtype=bool)   # -inf entries are dropped with the scores
     raise ValueError(f"unknown mask kind {mask_kind}")
 
 
@@ -67,17 +76,22 @@ def _visible_matrix(rows_i, Lq, Lk, mask_kind, mask, window=None):
         if len(rows_i) else np.zeros((0, Lk), dtype=bool)
 
 
-def head_probabilities(q_rows, k_head, rows_i, Lq, scale, mask_kind, mask=None, sink=None, window=None):
+def head_probabilities(q_rows, k_head, rows_i, Lq, scale, mask_kind, mask=None, sink=None, window=None,
+                       bias=None):
     """Softmax weights for some query rows of one head.
 
-    q_rows [n, D], k_head [Lk, D] float64. Returns (p [n, Lk], p_sink [n]):
-    the weight of every key (0 where masked) and the sink's share of the
-    denominator (0 without a sink). A row with no visible key and no sink has
-    all weights 0.
+    q_rows [n, D], k_head [Lk, D] float64; bias [n, Lk] the additive mask rows
+    (MASK_ADDITIVE only). Returns (p [n, Lk], p_sink [n]): the weight of every
+    key (0 where masked) and the sink's share of the denominator (0 without a
+    sink). A row with no visible key and no sink has all weights 0.
     """
     Lk = k_head.shape[0]
     s = scale * (q_rows @ k_head.T)                      # scores, [n, Lk]
     vis = _visible_matrix(rows_i, Lq, Lk, mask_kind, mask, window)
+    if mask_kind == MASK_ADDITIVE:
+        bias = np.asarray(bias, dtype=np.float64)
+        vis = vis & ~np.isneginf(bias)
+        s = s + np.where(vis, bias, 0.0)
     s_vis = np.where(vis, s, -np.inf)
     m = s_vis.max(axis=1) if Lk else np.full(len(rows_i), -np.inf)
     if sink is not None:
@@ -95,12 +109,19 @@ def head_probabilities(q_rows, k_head, rows_i, Lq, scale, mask_kind, mask=None, 
     return p, p_sink
 
 
+def _bias(mask, B, Hq, Lq, Lk):
+    """The additive mask broadcast to [B, Hq, Lq, Lk] (a read-only view)."""
+    m = np.asarray(mask, dtype=np.float64)
+    return np.broadcast_to(m.reshape((1,) * (4 - m.ndim) + m.shape), (B, Hq, Lq, Lk))
+
+
 def sdpa(q, k, v, scale, mask_kind, mask=None, sinks=None, rows=None, window=None):
     """Attention forward in float64.
 
     q [B,Hq,Lq,D], k [B,Hkv,Lk,D], v [B,Hkv,Lk,Dv] (float64), mask [Lq,Lk]
-    (bool, MASK_BOOL only), sinks [Hq] or None, window (causal only) None or
-    the number of keys each query row reads back from its position.
+    (bool, MASK_BOOL) or an additive float mask broadcastable to
+    [B,Hq,Lq,Lk] (MASK_ADDITIVE), sinks [Hq] or None, window (causal only)
+    None or the number of keys each query row reads back from its position.
 
     rows=None returns out [B,Hq,Lq,Dv]. rows = iterable of (b, h, i) returns
     [len(rows), Dv] for just those query rows.
@@ -111,6 +132,7 @@ def sdpa(q, k, v, scale, mask_kind, mask=None, sinks=None, rows=None, window=Non
     if Hq % Hkv:
         raise ValueError("query heads must be a multiple of key/value heads")
     group = Hq // Hkv
+    bias = _bias(mask, B, Hq, Lq, Lk) if mask_kind == MASK_ADDITIVE else None
     if rows is None:
         out = np.zeros((B, Hq, Lq, Dv))
         for b in range(B):
@@ -118,7 +140,8 @@ def sdpa(q, k, v, scale, mask_kind, mask=None, sinks=None, rows=None, window=Non
                 hk = h // group
                 sink = None if sinks is None else float(sinks[h])
                 p, _ = head_probabilities(q[b, h], k[b, hk], np.arange(Lq), Lq, scale,
-                                          mask_kind, mask, sink, window)
+                                          mask_kind, mask, sink, window,
+                                          None if bias is None else bias[b, h])
                 out[b, h] = p @ v[b, hk]
         return out
     rows = [tuple(int(x) for x in r) for r in rows]
@@ -132,7 +155,8 @@ def sdpa(q, k, v, scale, mask_kind, mask=None, sinks=None, rows=None, window=Non
         idx = [n for n, _ in items]
         ii = np.array([i for _, i in items])
         sink = None if sinks is None else float(sinks[h])
-        p, _ = head_probabilities(q[b, h, ii], k[b, hk], ii, Lq, scale, mask_kind, mask, sink, window)
+        p, _ = head_probabilities(q[b, h, ii], k[b, hk], ii, Lq, scale, mask_kind, mask, sink, window,
+                                  None if bias is None else bias[b, h, ii])
         out[idx] = p @ v[b, hk]
     return out
 
@@ -143,11 +167,13 @@ def probabilities(q, k, scale, mask_kind, mask=None, sinks=None, window=None):
     B, Hq, Lq, _ = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
     group = Hq // Hkv
+    bias = _bias(mask, B, Hq, Lq, Lk) if mask_kind == MASK_ADDITIVE else None
     p = np.zeros((B, Hq, Lq, Lk))
     ps = np.zeros((B, Hq, Lq))
     for b in range(B):
         for h in range(Hq):
             sink = None if sinks is None else float(sinks[h])
             p[b, h], ps[b, h] = head_probabilities(q[b, h], k[b, h // group], np.arange(Lq),
-                                                   Lq, scale, mask_kind, mask, sink, window)
+                                                   Lq, scale, mask_kind, mask, sink, window,
+                                                   None if bias is None else bias[b, h])
     return p, ps

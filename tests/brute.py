@@ -5,9 +5,10 @@ import math
 
 def attention_loops(q, k, v, B, Hq, Hkv, Lq, Lk, D, Dv, scale, mask_kind, mask=None, sinks=None,
                     window=None):
-    """q, k, v: nested lists [B][H][L][E]; mask: [Lq][Lk] of 0/1; sinks: [Hq];
-    window: with the causal mask, the keys a row reads back from its position.
-    Returns nested list [B][Hq][Lq][Dv]."""
+    """q, k, v: nested lists [B][H][L][E]; mask: [Lq][Lk] of 0/1 (kind 2), or
+    the additive mask [B][Hq][Lq][Lk] of floats (kind 3, -inf drops the key);
+    sinks: [Hq]; window: with the causal mask, the keys a row reads back from
+    its position. Returns nested list [B][Hq][Lq][Dv]."""
     g = Hq // Hkv
     out = []
     for b in range(B):
@@ -24,10 +25,12 @@ def attention_loops(q, k, v, B, Hq, Hkv, Lq, Lk, D, Dv, scale, mask_kind, mask=N
                         continue
                     if mask_kind == 2 and not mask[i][j]:
                         continue
+                    if mask_kind == 3 and mask[b][h][i][j] == -math.inf:
+                        continue
                     dot = 0.0
                     for c in range(D):
                         dot += q[b][h][i][c] * k[b][kh][j][c]
-                    keys.append((j, scale * dot))
+                    keys.append((j, scale * dot + (mask[b][h][i][j] if mask_kind == 3 else 0.0)))
                 logits = [s for _, s in keys]
                 if sinks is not None:
                     logits.append(sinks[h])

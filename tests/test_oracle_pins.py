@@ -512,3 +512,104 @@ def test_paged_write_places_rows_and_skips_bad_slots():
     want[0, :, 3] = new[1]          # slot 3: block 0, row 3
     want[1, :, 3] = new[4]          # slot 7: block 1, row 3
     assert np.array_equal(got, want)
+
+
+# --- additive masks (nuvec-core tests/fast.rs, attention_kernels_match_the_fallback) -------
+
+def _additive_case(rng, B=2, hq=4, hkv=2, lq=5, lk=9, d=6, dv=5):
+    return (_rand(rng, B, hq, lq, d), _rand(rng, B, hkv, lk, d), _rand(rng, B, hkv, lk, dv),
+            _rand(rng, 1, hq, lq, lk))
+
+
+def test_zero_additive_mask_is_no_mask():
+    q, k, v, _ = _additive_case(np.random.default_rng(1300))
+    got = orc.sdpa(q, k, v, 0.4, orc.MASK_ADDITIVE, np.zeros((1, 4, 5, 9)))
+    assert np.array_equal(got, orc.sdpa(q, k, v, 0.4, orc.MASK_NONE))
+
+
+def test_additive_zero_or_minus_inf_is_the_boolean_mask():
+    rng = np.random.default_rng(1301)
+    q, k, v, _ = _additive_case(rng)
+    bmask = rng.random((5, 9)) < 0.5
+    bmask[2] = False                              # one row sees nothing: zeros either way
+    add = np.where(bmask, 0.0, -np.inf)
+    sinks = _rand(rng, 4)
+    for s in (None, sinks):
+        got = orc.sdpa(q, k, v, 0.4, orc.MASK_ADDITIVE, add, s)
+        assert np.array_equal(got, orc.sdpa(q, k, v, 0.4, orc.MASK_BOOL, bmask, s))
+    assert not got[:, :, 2].any()
+
+
+def test_constant_additive_mask_cancels_without_a_sink():
+    q, k, v, _ = _additive_case(np.random.default_rng(1302))
+    got = orc.sdpa(q, k, v, 0.4, orc.MASK_ADDITIVE, np.full((5, 9), 3.7))
+    assert np.allclose(got, orc.sdpa(q, k, v, 0.4, orc.MASK_NONE), rtol=0, atol=1e-13)
+
+
+def test_additive_mask_as_log_weights_closed_form():
+    # zero queries make every score 0, so the weights are exp(mask) / (sum exp(mask) + exp(sink))
+    rng = np.random.default_rng(1303)
+    lk, dv = 7, 3
+    v = _rand(rng, 1, 1, lk, dv)
+    w = rng.uniform(0.1, 2.0, lk)
+    sink = 0.3
+    got = orc.sdpa(np.zeros((1, 1, 1, 4)), _rand(rng, 1, 1, lk, 4), v, 0.9, orc.MASK_ADDITIVE,
+                   np.log(w)[None], np.array([sink]))
+    want = (w @ v[0, 0]) / (w.sum() + math.exp(sink))
+    assert np.allclose(got[0, 0, 0], want, rtol=1e-14, atol=0)
+
+
+def test_additive_mask_broadcasts_over_batch_and_heads():
+    rng = np.random.default_rng(1304)
+    q, k, v, add = _additive_case(rng)
+    full = np.broadcast_to(add, (2, 4, 5, 9)).copy()
+    a = orc.sdpa(q, k, v, 0.4, orc.MASK_ADDITIVE, add)
+    assert np.array_equal(a, orc.sdpa(q, k, v, 0.4, orc.MASK_ADDITIVE, full))
+    two_d = add[0, 1]
+    b = orc.sdpa(q, k, v, 0.4, orc.MASK_ADDITIVE, two_d)
+    assert np.array_equal(b, orc.sdpa(q, k, v, 0.4, orc.MASK_ADDITIVE, np.broadcast_to(two_d, (2, 4, 5, 9))))
+    # a per-(batch, head) mask really is read per batch item and head
+    per = _rand(rng, 2, 4, 5, 9)
+    c = orc.sdpa(q, k, v, 0.4, orc.MASK_ADDITIVE, per)
+    for bb in range(2):
+        for h in range(4):
+            one = orc.sdpa(q[bb:bb + 1, h:h + 1], k[bb:bb + 1, h // 2:h // 2 + 1], v[bb:bb + 1, h // 2:h // 2 + 1],
+                           0.4, orc.MASK_ADDITIVE, per[bb, h])
+            assert np.array_equal(c[bb, h], one[0, 0])
+
+
+def test_additive_mask_against_torch_cpu_float64():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(1305)
+    q, k, v, add = _additive_case(rng, lq=7, lk=11)
+    out = orc.sdpa(q, k, v, 0.31, orc.MASK_ADDITIVE, add)
+    tk = torch.from_numpy(k).repeat_interleave(2, dim=1)
+    tv = torch.from_numpy(v).repeat_interleave(2, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), tk, tv, attn_mask=torch.from_numpy(add), scale=0.31).numpy()
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_additive_brute_force_tiny(seed):
+    rng = np.random.default_rng(1400 + seed)
+    hkv = int(rng.integers(1, 3))
+    hq = hkv * int(rng.integers(1, 4))
+    B = int(rng.integers(1, 3))
+    lq, lk = int(rng.integers(1, 10)), int(rng.integers(1, 10))
+    d, dv = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+    q, k, v = _rand(rng, B, hq, lq, d), _rand(rng, B, hkv, lk, d), _rand(rng, B, hkv, lk, dv)
+    add = 2.0 * _rand(rng, B, hq, lq, lk)
+    add[rng.random(add.shape) < 0.3] = -np.inf
+    sinks = _rand(rng, hq) if seed % 2 else None
+    scale = float(rng.uniform(0.1, 1.0))
+    got = orc.sdpa(q, k, v, scale, orc.MASK_ADDITIVE, add, sinks)
+    want = np.array(attention_loops(q.tolist(), k.tolist(), v.tolist(), B, hq, hkv, lq, lk, d, dv, scale, 3,
+                                    add.tolist(), None if sinks is None else sinks.tolist()))
+    assert np.allclose(got, want.reshape(got.shape), rtol=0, atol=1e-12)
+
+
+def test_additive_mask_rejects_a_window():
+    q, k, v, add = _additive_case(np.random.default_rng(1306))
+    with pytest.raises(ValueError):
+        orc.sdpa(q, k, v, 0.4, orc.MASK_ADDITIVE, add, window=3)

@@ -38,8 +38,14 @@ enum { SDPA_F32 = 0, SDPA_F16 = 1, SDPA_BF16 = 2 };
  *                  the first Lq - Lk rows see nothing and output zeros.
  * SDPA_MASK_BOOL   a device uint8 matrix [Lq, Lk], nonzero = visible, shared by
  *                  every batch item and head (nuvec-core tests/attention_plan.rs,
- *                  attention(); tests/fast.rs, window_mask). */
-enum { SDPA_MASK_NONE = 0, SDPA_MASK_CAUSAL = 1, SDPA_MASK_BOOL = 2 };
+ *                  attention(); tests/fast.rs, window_mask).
+ * SDPA_MASK_ADDITIVE  values in the element type added to the scaled scores,
+ *                  scale * q.k + mask[b, h, i, j], through a strided view that may
+ *                  broadcast over batch items and heads (tests/fast.rs,
+ *                  attention_kernels_match_the_fallback: an additive [1, Hq, Lq, Lk]
+ *                  mask). A -inf entry drops its key; a row of -inf outputs zeros.
+ *                  Only sdpa_forward_strided takes one (sdpa_plan plans it). */
+enum { SDPA_MASK_NONE = 0, SDPA_MASK_CAUSAL = 1, SDPA_MASK_BOOL = 2, SDPA_MASK_ADDITIVE = 3 };
 
 /* Return codes. */
 enum {
@@ -213,6 +219,45 @@ int sdpa_paged_write(void* cache, const void* rows, const int32_t* slots, int64_
                      int64_t blocks, int64_t Hkv, int64_t bs, int64_t E, int dtype,
                      void* stream);
 
+/* A strided view of a [B, H, L, E] operand: element [b, h, l, e] is at
+ * data + (b * stride_b + h * stride_h + l * stride_l + e) elements. The last
+ * (feature) axis is contiguous. */
+typedef struct sdpa_view_t {
+  const void* data;
+  int64_t stride_b, stride_h, stride_l;
+} sdpa_view_t;
+
+/*
+ * sdpa_forward_strided - sdpa_forward (and sdpa_forward_windowed) over strided
+ * views, and the only call that takes an additive mask: q, k and v may be
+ * views such as a transposed [B, L, H, D] array or a slice of a longer cache
+ * (nuvec-core tests/fast.rs: attention_kernels_match_the_fallback reads K/V
+ * as transposed views of [B, L, H, D]; the capped-attention inputs take q as
+ * a transposed view and K/V as a slice of a cache; the windowed tests read
+ * K/V as slices of a larger cache).
+ *
+ *   q, k, v  non-NULL views of [B,Hq,Lq,D], [B,Hkv,Lk,D], [B,Hkv,Lk,Dv] in
+ *            dtype. Strides >= 0 (0 repeats an axis). Each data pointer must
+ *            be 16-byte aligned and each stride * sizeof(dtype) a multiple of
+ *            16 bytes; k and v row strides below 2^26 bytes.
+ *   out      contiguous [B, Hq, Lq, Dv], as for sdpa_forward.
+ *   mask_kind / mask  NONE and CAUSAL take no mask (NULL). BOOL: mask->data is
+ *            the uint8 [Lq, Lk] matrix with strides (0, 0, Lk). ADDITIVE:
+ *            mask->data holds dtype values, element [b, h, i, j] at strides
+ *            (stride_b, stride_h, stride_l) and contiguous along j; stride 0
+ *            broadcasts (0, h, l for one mask shared by every batch item).
+ *   window   0 for none; otherwise >= 1 with SDPA_MASK_CAUSAL, as in
+ *            sdpa_forward_windowed.
+ * Plans come from sdpa_plan (sdpa_plan_windowed with a window); strides do
+ * not change the plan. Other arguments, ownership, errors, scratch and
+ * asynchrony as for sdpa_forward.
+ */
+int sdpa_forward_strided(const sdpa_view_t* q, const sdpa_view_t* k, const sdpa_view_t* v, void* out,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                         int64_t D, int64_t Dv, float scale, int mask_kind,
+                         const sdpa_view_t* mask, const void* sinks, int64_t window,
+                         int dtype, void* stream);
+
 /* Message of the last error on the calling thread ("" if none). The pointer
  * stays valid until the thread's next sdpa_* call. */
 const char* sdpa_last_error(void);
@@ -221,7 +266,8 @@ const char* sdpa_last_error(void);
  * Returns SDPA_OK or SDPA_ERR_HIP. */
 int sdpa_release_workspace(void);
 
-/* ABI version of this header: 3 (2 added the windowed calls, 3 the paged ones). */
+/* ABI version of this header: 4 (2 added the windowed calls, 3 the paged ones,
+ * 4 strided views and additive masks). */
 int sdpa_abi_version(void);
 
 #ifdef __cplusplus

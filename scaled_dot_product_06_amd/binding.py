@@ -10,13 +10,14 @@ import os
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
 
 SDPA_F32, SDPA_F16, SDPA_BF16 = 0, 1, 2
-SDPA_MASK_NONE, SDPA_MASK_CAUSAL, SDPA_MASK_BOOL = 0, 1, 2
+SDPA_MASK_NONE, SDPA_MASK_CAUSAL, SDPA_MASK_BOOL, SDPA_MASK_ADDITIVE = 0, 1, 2, 3
 SDPA_OK, SDPA_ERR_INVALID, SDPA_ERR_UNSUPPORTED, SDPA_ERR_HIP = 0, -1, -2, -3
 SDPA_ROUTE_EMPTY, SDPA_ROUTE_ZERO_FILL, SDPA_ROUTE_PREFILL, SDPA_ROUTE_DECODE = 0, 1, 2, 3
 ROUTE_NAMES = {0: "empty", 1: "zero_fill", 2: "prefill", 3: "decode"}
 
 EXPORTED = ("sdpa_forward", "sdpa_plan", "sdpa_forward_windowed", "sdpa_plan_windowed", "sdpa_paged_forward",
-            "sdpa_plan_paged", "sdpa_paged_write", "sdpa_last_error", "sdpa_release_workspace", "sdpa_abi_version")
+            "sdpa_plan_paged", "sdpa_paged_write", "sdpa_forward_strided", "sdpa_last_error", "sdpa_release_workspace",
+            "sdpa_abi_version")
 
 
 class SdpaPlan(ctypes.Structure):
@@ -46,6 +47,12 @@ class SdpaPlan(ctypes.Structure):
             "grid": tuple(self.grid),
             "scratch_bytes": self.scratch_bytes,
         }
+
+
+class SdpaView(ctypes.Structure):
+    """sdpa_view_t: a data pointer and element strides (batch, head, row)."""
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("stride_l", ctypes.c_int64)]
 
 
 class SdpaError(RuntimeError):
@@ -91,6 +98,10 @@ def load() -> ctypes.CDLL:
     lib.sdpa_plan_paged.restype = c_int
     lib.sdpa_paged_write.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, c_int, vp]
     lib.sdpa_paged_write.restype = c_int
+    pv = ctypes.POINTER(SdpaView)
+    lib.sdpa_forward_strided.argtypes = [pv, pv, pv, vp, i64, i64, i64, i64, i64, i64, i64, ctypes.c_float, c_int,
+                                         pv, vp, i64, c_int, vp]
+    lib.sdpa_forward_strided.restype = c_int
     lib.sdpa_last_error.argtypes = []
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_release_workspace.argtypes = []
@@ -178,6 +189,19 @@ def sdpa_paged_write(cache, rows, slots, n, blocks, Hkv, bs, E, dtype, stream, c
     return _check(rc) if check else rc
 
 
+def sdpa_forward_strided(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, Dv, scale, mask_kind, mask, sinks, window, dtype,
+                         stream, check: bool = True) -> int:
+    """Raw strided call: q, k, v (and mask, or None) are (data, stride_b, stride_h, stride_l) tuples
+    or SdpaView objects (None for a NULL view)."""
+    def view(x):
+        if x is None:
+            return None
+        return ctypes.byref(x if isinstance(x, SdpaView) else SdpaView(*x))
+    rc = load().sdpa_forward_strided(view(q), view(k), view(v), out, B, Hq, Hkv, Lq, Lk, D, Dv,
+                                     ctypes.c_float(scale), mask_kind, view(mask), sinks, window, dtype, stream)
+    return _check(rc) if check else rc
+
+
 def sdpa_release_workspace() -> int:
     return _check(load().sdpa_release_workspace())
 
@@ -196,27 +220,43 @@ def _dtype_code(t):
     return codes[t.dtype]
 
 
+def _view(name, t, shape):
+    """(data, stride_b, stride_h, stride_l) of a 4-D GPU tensor whose last axis is contiguous."""
+    if not t.is_cuda:
+        raise SdpaError(SDPA_ERR_INVALID, f"{name} must be a GPU tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise SdpaError(SDPA_ERR_INVALID, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise SdpaError(SDPA_ERR_INVALID, f"{name} must be contiguous along its last axis")
+    return (t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
 def attention(q, k, v, scale: float, mask_kind: int = SDPA_MASK_NONE, mask=None, sinks=None, out=None,
               stream=None, window=None):
-    """softmax(scale * q k^T + mask) v on the GPU through sdpa_forward.
+    """softmax(scale * q k^T + mask) v on the GPU.
 
-    q [B,Hq,Lq,D], k [B,Hkv,Lk,D], v [B,Hkv,Lk,Dv] contiguous CUDA tensors of one
-    dtype; mask a contiguous uint8/bool CUDA tensor [Lq,Lk] (mask_kind 2);
-    sinks a CUDA tensor [Hq] of q's dtype. With `window` (causal only), the
-    call goes through sdpa_forward_windowed. Returns out [B,Hq,Lq,Dv].
+    q [B,Hq,Lq,D], k [B,Hkv,Lk,D], v [B,Hkv,Lk,Dv] GPU tensors of one dtype;
+    contiguous ones go through sdpa_forward (sdpa_forward_windowed with a
+    `window`, causal only), views whose last axis is contiguous (a transposed
+    [B,L,H,D] array, a slice of a longer cache) through sdpa_forward_strided.
+    mask: a contiguous uint8/bool [Lq,Lk] tensor (mask_kind 2), or an
+    additive mask of q's dtype broadcastable to [B,Hq,Lq,Lk] (mask_kind 3,
+    any strides with a contiguous last axis). sinks: [Hq] of q's dtype.
+    Returns out [B,Hq,Lq,Dv] (contiguous).
     """
     import torch
     B, Hq, Lq, D = q.shape
     _, Hkv, Lk, _ = k.shape
     Dv = v.shape[3]
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise SdpaError(SDPA_ERR_INVALID, f"{name} must be a contiguous GPU tensor")
+        if not t.is_cuda:
+            raise SdpaError(SDPA_ERR_INVALID, f"{name} must be a GPU tensor")
         if t.dtype != q.dtype:
             raise SdpaError(SDPA_ERR_INVALID, f"{name} has dtype {t.dtype}, q has {q.dtype}")
     if tuple(k.shape) != (B, Hkv, Lk, D) or tuple(v.shape[:3]) != (B, Hkv, Lk):
         raise SdpaError(SDPA_ERR_INVALID, f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
     mptr = None
+    mview = None
     if mask_kind == SDPA_MASK_BOOL:
         if mask is None or tuple(mask.shape) != (Lq, Lk) or not mask.is_contiguous() or not mask.is_cuda:
             raise SdpaError(SDPA_ERR_INVALID, f"mask must be a contiguous GPU tensor of shape ({Lq}, {Lk})")
@@ -225,6 +265,17 @@ def attention(q, k, v, scale: float, mask_kind: int = SDPA_MASK_NONE, mask=None,
         if mask.dtype != torch.uint8:
             raise SdpaError(SDPA_ERR_INVALID, "mask must be uint8 or bool")
         mptr = mask.data_ptr()
+        mview = (mptr, 0, 0, Lk)
+    elif mask_kind == SDPA_MASK_ADDITIVE:
+        if mask is None or mask.dtype != q.dtype or not mask.is_cuda or mask.dim() < 2 or mask.dim() > 4:
+            raise SdpaError(SDPA_ERR_INVALID, f"an additive mask must be a 2-4 dimensional GPU tensor of {q.dtype}")
+        m4 = mask.reshape((1,) * (4 - mask.dim()) + tuple(mask.shape)) if mask.dim() < 4 else mask
+        try:
+            m4 = m4.expand(B, Hq, Lq, Lk)
+        except RuntimeError:
+            raise SdpaError(SDPA_ERR_INVALID, f"additive mask {tuple(mask.shape)} does not broadcast to "
+                            f"({B}, {Hq}, {Lq}, {Lk})")
+        mview = _view("mask", m4, (B, Hq, Lq, Lk))
     sptr = None
     if sinks is not None:
         if tuple(sinks.shape) != (Hq,) or sinks.dtype != q.dtype or not sinks.is_cuda:
@@ -235,9 +286,15 @@ def attention(q, k, v, scale: float, mask_kind: int = SDPA_MASK_NONE, mask=None,
         out = torch.empty((B, Hq, Lq, Dv), dtype=q.dtype, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
+    if window is not None and mask_kind != SDPA_MASK_CAUSAL:
+        raise SdpaError(SDPA_ERR_INVALID, "a window needs the causal mask (mask_kind 1)")
+    contiguous = q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
+    if not contiguous or mask_kind == SDPA_MASK_ADDITIVE:
+        sdpa_forward_strided(_view("q", q, (B, Hq, Lq, D)), _view("k", k, (B, Hkv, Lk, D)),
+                             _view("v", v, (B, Hkv, Lk, Dv)), out.data_ptr(), B, Hq, Hkv, Lq, Lk, D, Dv,
+                             float(scale), mask_kind, mview, sptr, int(window or 0), _dtype_code(q), stream)
+        return out
     if window is not None:
-        if mask_kind != SDPA_MASK_CAUSAL:
-            raise SdpaError(SDPA_ERR_INVALID, "a window needs the causal mask (mask_kind 1)")
         sdpa_forward_windowed(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, Lq, Lk, D,
                               Dv, float(scale), int(window), sptr, _dtype_code(q), stream)
         return out

@@ -171,6 +171,43 @@ __device__ __forceinline__ float keep_if_bit(float x, uint32_t word, int pos) {
   return __uint_as_float((keep & __float_as_uint(x)) | (~keep & 0xFF800000u));
 }
 
+// Additive-mask values of keys key .. key+3 of one mask row, widened to f32
+// and converted to base 2 (times log2 e); keys at or past Lk read as -inf.
+// `vec`: the row start is aligned for one 8-byte (16-bit types) or 16-byte
+// (f32) load of the group, and key is a multiple of 4.
+template <class E> __device__ __forceinline__ f32x4 mask4(const void* row, int key, int Lk, bool vec);
+template <class E> __device__ __forceinline__ f32x4 mask4_16(const void* row, int key, int Lk, bool vec) {
+  const uint16_t* p = (const uint16_t*)row + key;
+  f32x4 r;
+  if (vec && key + 4 <= Lk) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+    r = {half_to_f32<E>((uint16_t)(x[0] & 0xFFFFu)), half_to_f32<E>((uint16_t)(x[0] >> 16)),
+         half_to_f32<E>((uint16_t)(x[1] & 0xFFFFu)), half_to_f32<E>((uint16_t)(x[1] >> 16))};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = key + e < Lk ? half_to_f32<E>(p[e]) : -INFINITY;
+  }
+  return r * kLog2e;
+}
+template <> __device__ __forceinline__ f32x4 mask4<ElemBF16>(const void* row, int key, int Lk, bool vec) {
+  return mask4_16<ElemBF16>(row, key, Lk, vec);
+}
+template <> __device__ __forceinline__ f32x4 mask4<ElemF16>(const void* row, int key, int Lk, bool vec) {
+  return mask4_16<ElemF16>(row, key, Lk, vec);
+}
+struct ElemF32 {};
+template <> __device__ __forceinline__ f32x4 mask4<ElemF32>(const void* row, int key, int Lk, bool vec) {
+  const float* p = (const float*)row + key;
+  f32x4 r;
+  if (vec && key + 4 <= Lk) {
+    r = *reinterpret_cast<const f32x4*>(p);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = key + e < Lk ? p[e] : -INFINITY;
+  }
+  return r * kLog2e;
+}
+
 // Work item (head block hb, query block qb) of prefill workgroup n, for a 1-D
 // grid of head_blocks * nqb workgroups. The dispatcher deals workgroups to the
 // 8 XCDs round-robin; this order makes each XCD walk the head blocks of one

@@ -97,7 +97,7 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   const int iq = row_ok ? r % a.Lq : 0;
   const int shift = Lk - a.Lq;
 
-  const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(b * a.Hq + h) * a.Lq + iq) * D;
+  const uint16_t* qp = (const uint16_t*)a.q + b * a.qs[0] + h * a.qs[1] + (int64_t)iq * a.qs[2];
   u32x4 qop[C::NQC];
 #pragma unroll
   for (int c = 0; c < C::NQC; ++c) {
@@ -118,21 +118,32 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   for (int d = 0; d < C::NDBW; ++d) o[d] = acc_t{};
   float m = -INFINITY, l = 0.0f;
 
-  // contiguous: this (batch, kv head)'s rows; paged: the cache base (rows from key_row)
-  const uint16_t* kp = (const uint16_t*)a.k + (PAGED ? 0 : (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * D);
-  const uint16_t* vp = (const uint16_t*)a.v + (PAGED ? 0 : (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * DV);
+  // strided: this (batch, kv head)'s rows; paged: the cache base (rows through the table)
+  const uint16_t* kp = (const uint16_t*)a.k + (PAGED ? 0 : b * a.ks[0] + hkv * a.ks[1]);
+  const uint16_t* vp = (const uint16_t*)a.v + (PAGED ? 0 : b * a.vs[0] + hkv * a.vs[1]);
   const uint8_t* mrow = a.mask + (size_t)iq * a.Lk;
   const bool causal_cut = a.mask_kind == kMaskCausal && a.Lq > 1;
+  // additive mask: the lane's row (values in the element type, added in base 2)
+  const bool additive = a.mask_kind == kMaskAdditive;
+  const uint16_t* arow = additive ? (const uint16_t*)a.amask + b * a.ms[0] + h * a.ms[1] + (int64_t)iq * a.ms[2]
+                                  : nullptr;
+  const float sc = additive ? 1.0f : a.c;
 
   // Two register tiles (A and B) cycle so that two tiles of K/V loads are in
   // flight while the LDS copy of a third is being computed.
   u32x4 kra[C::KPT], vra[C::VPT], krb[C::KPT], vrb[C::VPT];
-  // row of key `key` in the K/V arrays: contiguous, or through the block table
-  auto key_row = [&](int key) -> size_t {
+  // element offsets of key `key`'s K and V rows: strided, or through the block table
+  auto k_off = [&](int key) -> int64_t {
     if constexpr (PAGED)
-      return ((size_t)ptab[key / a.bs - e0] * a.Hkv + hkv) * a.bs + key % a.bs;
+      return (((int64_t)ptab[key / a.bs - e0] * a.Hkv + hkv) * a.bs + key % a.bs) * D;
     else
-      return (size_t)key;
+      return key * a.ks[2];
+  };
+  auto v_off = [&](int key) -> int64_t {
+    if constexpr (PAGED)
+      return (((int64_t)ptab[key / a.bs - e0] * a.Hkv + hkv) * a.bs + key % a.bs) * DV;
+    else
+      return key * a.vs[2];
   };
   auto load_tile = [&](int k0, u32x4* kr, u32x4* vr) {
 #pragma unroll
@@ -141,7 +152,7 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
       if (C::KCH % C::NT == 0 || c < C::KCH) {
         const int rr = c / (D / 8), cc = c % (D / 8);
         const int key = k0 + rr;
-        kr[it] = key < ke ? ld_global16_nt(kp + key_row(key) * D + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+        kr[it] = key < ke ? ld_global16_nt(kp + k_off(key) + cc * 8) : u32x4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
@@ -150,7 +161,7 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
       if (C::VCH % C::NT == 0 || c < C::VCH) {
         const int rr = c / (DV / 8), cc = c % (DV / 8);
         const int key = k0 + rr;
-        vr[it] = key < ke ? ld_global16_nt(vp + key_row(key) * DV + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+        vr[it] = key < ke ? ld_global16_nt(vp + v_off(key) + cc * 8) : u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -190,7 +201,7 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
       s[nb] = acc;
     }
 
-    const bool full = k0 + BN <= ke && a.mask_kind != kMaskBool && !causal_cut;
+    const bool full = k0 + BN <= ke && a.mask_kind != kMaskBool && !additive && !causal_cut;
     float mx = -INFINITY;
 #pragma unroll
     for (int nb = 0; nb < C::NSB; ++nb)
@@ -199,14 +210,21 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
         if (!full) {
           const int key = k0 + nb * MF + acc_row<MF>(i, kg);
           bool vis = key < ke && row_ok;
-          if (causal_cut) vis = vis && key <= iq + shift && (a.window <= 0 || key > iq + shift - a.window);
-          else if (a.mask_kind == kMaskBool) vis = vis && mrow[key] != 0;
-          if (!vis) s[nb][i] = -INFINITY;
+          if (additive) {
+            // base-2 score with the mask added
+            float add = -INFINITY;
+            if (vis) add = half_to_f32<E>(arow[key]) * kLog2e;
+            s[nb][i] = vis ? fmaf(s[nb][i], a.c, add) : -INFINITY;
+          } else {
+            if (causal_cut) vis = vis && key <= iq + shift && (a.window <= 0 || key > iq + shift - a.window);
+            else if (a.mask_kind == kMaskBool) vis = vis && mrow[key] != 0;
+            if (!vis) s[nb][i] = -INFINITY;
+          }
         }
         mx = fmaxf(mx, s[nb][i]);
       }
     mx = row_max<MF>(mx);
-    const float tmax = (mx == -INFINITY) ? -INFINITY : mx * a.c;
+    const float tmax = (mx == -INFINITY) ? -INFINITY : mx * sc;
     softmax_rebase<C::NDBW>(tmax, m, l, o);
     const float mu = (m == -INFINITY) ? 0.0f : m;
 
@@ -216,8 +234,8 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
     for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
       for (int i = 0; i < ACC; i += 2) {
-        const float p0 = fast_exp2(fmaf(s[nb][i], a.c, -mu));
-        const float p1 = fast_exp2(fmaf(s[nb][i + 1], a.c, -mu));
+        const float p0 = fast_exp2(fmaf(s[nb][i], sc, -mu));
+        const float p1 = fast_exp2(fmaf(s[nb][i + 1], sc, -mu));
         lsum += p0 + p1;
         pk[(nb * ACC + i) / 2] = pack2<E>(p0, p1);
       }

@@ -7,7 +7,7 @@
 namespace sdpa {
 
 enum Elem { kF32 = 0, kF16 = 1, kBF16 = 2 };
-enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskBool = 2 };
+enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskBool = 2, kMaskAdditive = 3 };
 
 struct FwdArgs {
   const void* q;
@@ -19,6 +19,13 @@ struct FwdArgs {
                          // [Lq, mwords] words, bit j of word w = key 32w + j visible
   int mwords;            // ceil(Lk / 32)
   const void* sinks;     // [Hq] in the element type, or null
+  // element strides (batch, head, row) of q, k and v; the feature axis is contiguous
+  int64_t qs[3], ks[3], vs[3];
+  // additive mask (mask_kind == kMaskAdditive): values in the element type at
+  // amask + b*ms[0] + h*ms[1] + i*ms[2] + j, added to the scaled scores
+  const void* amask;
+  int64_t ms[3];
+  int mvec;              // 1: every additive-mask row start is aligned for 4-element vector loads
   int B, Hq, Hkv, Lq, Lk;
   int group;             // Hq / Hkv
   int mask_kind;
@@ -83,11 +90,14 @@ constexpr int head_max(int D, int Dv) { return D > Dv ? D : Dv; }
 // 32x32 MFMA tiles (32 query rows per wavefront) up to 128-wide heads; 16x16
 // tiles above, where a 32-row output accumulator would not fit in registers.
 constexpr int prefill_mf(int elem, int D, int Dv) { return head_max(D, Dv) <= 128 ? 32 : 16; }
-// The 64/128-wide 16-bit prefill shapes run the pipelined direct-load kernel.
-constexpr bool prefill_is_fast(int elem, int D, int Dv) { return elem != kF32 && D == Dv && (D == 64 || D == 128); }
-constexpr int prefill_bn(int elem, int D, int Dv) {
+// The 64/128-wide 16-bit prefill shapes run the pipelined direct-load kernel,
+// except with an additive mask (the generic kernel reads it).
+constexpr bool prefill_is_fast(int elem, int D, int Dv, int mask_kind) {
+  return elem != kF32 && D == Dv && (D == 64 || D == 128) && mask_kind != kMaskAdditive;
+}
+constexpr int prefill_bn(int elem, int D, int Dv, int mask_kind) {
   return elem == kF32 ? (head_max(D, Dv) <= 128 ? 32 : 16)
-                      : (prefill_is_fast(elem, D, Dv) || head_max(D, Dv) > 256 ? 32 : 64);
+                      : (prefill_is_fast(elem, D, Dv, mask_kind) || head_max(D, Dv) > 256 ? 32 : 64);
 }
 constexpr int prefill_rows(int elem, int D, int Dv) { return prefill_mf(elem, D, Dv); }
 constexpr int prefill_waves(int elem, int D, int Dv) { return kPrefillWaves; }

@@ -8,16 +8,20 @@ template <class E, int D, int DV>
 static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_t stream) {
   constexpr int elem = std::is_same<E, ElemBF16>::value ? kBF16 : kF16;
   constexpr int MF = prefill_mf(elem, D, DV);
-  constexpr int BN = prefill_bn(elem, D, DV);
   dim3 grid(a.head_blocks * a.nqb, 1, 1);
-  if constexpr (prefill_is_fast(elem, D, DV)) {
+  if (a.mask_kind == kMaskAdditive) {
+    constexpr int BN = prefill_bn(elem, D, DV, kMaskAdditive);
+    hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves, true>), grid, dim3(kPrefillWaves * 64), 0,
+                       stream, a);
+  } else if constexpr (prefill_is_fast(elem, D, DV, kMaskNone)) {
     using C = FastCfg<D>;
-    static_assert(MF == C::MF && BN == C::BN && prefill_waves(elem, D, DV) == C::NW &&
-                      prefill_rows(elem, D, DV) == C::ROWS,
+    static_assert(MF == C::MF && prefill_bn(elem, D, DV, kMaskNone) == C::BN &&
+                      prefill_waves(elem, D, DV) == C::NW && prefill_rows(elem, D, DV) == C::ROWS,
                   "planner geometry must match the kernel");
     hipLaunchKernelGGL((prefill_fast_kernel<E, D>), grid, dim3(C::NW * 64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves>), grid, dim3(kPrefillWaves * 64), 0,
+    constexpr int BN = prefill_bn(elem, D, DV, kMaskNone);
+    hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves, false>), grid, dim3(kPrefillWaves * 64), 0,
                        stream, a);
   }
   return hipGetLastError();

@@ -6,10 +6,14 @@ namespace sdpa {
 template <int D, int DV>
 static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_t stream) {
   constexpr int MF = prefill_mf(kF32, D, DV);
-  constexpr int BN = prefill_bn(kF32, D, DV);
+  constexpr int BN = prefill_bn(kF32, D, DV, kMaskNone);
   dim3 grid(a.head_blocks * a.nqb, 1, 1);
-  hipLaunchKernelGGL((prefill_f32_kernel<MF, D, DV, BN, kPrefillWaves>), grid, dim3(kPrefillWaves * 64), 0,
-                     stream, a);
+  if (a.mask_kind == kMaskAdditive)
+    hipLaunchKernelGGL((prefill_f32_kernel<MF, D, DV, BN, kPrefillWaves, true>), grid, dim3(kPrefillWaves * 64), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((prefill_f32_kernel<MF, D, DV, BN, kPrefillWaves, false>), grid, dim3(kPrefillWaves * 64),
+                       0, stream, a);
   return hipGetLastError();
 }
 

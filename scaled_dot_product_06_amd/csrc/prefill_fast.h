@@ -120,7 +120,7 @@ prefill_fast_kernel(FwdArgs a) {
 #pragma unroll
   for (int r = 0; r < QB; ++r) {
     iq[r] = wi0 + r * MF + col;
-    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(b * a.Hq + h) * a.Lq + iq[r]) * D;
+    const uint16_t* qp = (const uint16_t*)a.q + b * a.qs[0] + h * a.qs[1] + (int64_t)iq[r] * a.qs[2];
 #pragma unroll
     for (int c = 0; c < C::NQC; ++c) {
       u32x4 x = {0u, 0u, 0u, 0u};
@@ -157,8 +157,11 @@ prefill_fast_kernel(FwdArgs a) {
     tmax[r] = -INFINITY;
   }
 
-  const uint8_t* kbase = (const uint8_t*)a.k + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * C::RB;
-  const uint8_t* vbase = (const uint8_t*)a.v + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * C::RB;
+  // K/V rows through their element strides (row strides below 2^26 bytes, so
+  // the per-lane offsets within a tile fit in 32 bits)
+  const uint8_t* kbase = (const uint8_t*)a.k + (b * a.ks[0] + hkv * a.ks[1]) * 2;
+  const uint8_t* vbase = (const uint8_t*)a.v + (b * a.vs[0] + hkv * a.vs[1]) * 2;
+  const uint32_t krs = (uint32_t)(a.ks[2] * 2), vrs = (uint32_t)(a.vs[2] * 2);
 
   // direct loads: per lane, byte offsets of its 16-byte chunk within the tile
   // (row blk*ROWS_PER_KB + lane/CPR, global chunk permuted by the row's XOR)
@@ -170,21 +173,21 @@ prefill_fast_kernel(FwdArgs a) {
   for (int it = 0; it < C::LOADS_PER_WAVE; ++it) {
     const int row = (w + C::NW * it) * C::ROWS_PER_KB + ld_row;
     ldrow[it] = row;
-    offk[it] = row * C::RB + (ld_slot ^ swz_k<D>(row)) * 16;
-    offv[it] = row * C::RB + (ld_slot ^ swz_v<D>(row)) * 16;
+    offk[it] = row * krs + (ld_slot ^ swz_k<D>(row)) * 16;
+    offv[it] = row * vrs + (ld_slot ^ swz_v<D>(row)) * 16;
   }
   auto issue_tile = [&](int k0, uint8_t* sbase) {
-    const uint8_t* kt = kbase + (size_t)k0 * C::RB;
-    const uint8_t* vt = vbase + (size_t)k0 * C::RB;
+    const uint8_t* kt = kbase + (size_t)k0 * krs;
+    const uint8_t* vt = vbase + (size_t)k0 * vrs;
     const bool tail = k0 + BN > a.Lk;
 #pragma unroll
     for (int it = 0; it < C::LOADS_PER_WAVE; ++it) {
       uint32_t ok = offk[it], ov = offv[it];
       if (tail) {
         // rows past the end read the last real row instead; those keys get weight 0
-        const int over = max(k0 + ldrow[it] - (a.Lk - 1), 0) * C::RB;
-        ok -= over;
-        ov -= over;
+        const uint32_t over = (uint32_t)max(k0 + ldrow[it] - (a.Lk - 1), 0);
+        ok -= over * krs;
+        ov -= over * vrs;
       }
       const int blk = w + C::NW * it;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + ok),

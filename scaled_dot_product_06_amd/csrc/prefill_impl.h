@@ -16,6 +16,13 @@
 // formula test): row i sees keys j <= i + Lk - Lq. Workgroups stop at their
 // last visible key; only tiles that cross a row's last key are masked per
 // element. Late (long) query blocks are dispatched first.
+//
+// ADD instantiations read an additive mask (nuvec-core "tests/fast.rs",
+// attention_kernels_match_the_fallback): each lane fetches its row's mask
+// values for a tile before the next tile's K/V loads are issued, and adds them
+// (in base 2) to the scaled scores. Q, K and V are read through element
+// strides (batch, head, row), so views such as a transposed [B, L, H, D]
+// array or a slice of a longer cache need no copy.
 #pragma once
 
 #include "attn_device.h"
@@ -41,7 +48,7 @@ struct PrefillCfg {
   static_assert(BN % MF == 0 && BN % KW == 0, "tile must hold whole MFMA blocks");
 };
 
-template <class E, int MF, int D, int DV, int BN, int NW>
+template <class E, int MF, int D, int DV, int BN, int NW, bool ADD>
 __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
   using C = PrefillCfg<MF, D, DV, BN, NW>;
   using acc_t = typename Mfma<MF>::acc_t;
@@ -86,7 +93,7 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
   if (a.mask_kind == kMaskCausal) {
     w_kend = min(a.Lk, w_last + shift + 1);
     w_kfull = min(a.Lk, wi0 + shift + 1);
-  } else if (a.mask_kind == kMaskBool) {
+  } else if (ADD || a.mask_kind == kMaskBool) {
     w_kfull = 0;
   }
   // with a window: keys below w_kskip are outside every row's window, keys
@@ -98,7 +105,7 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
   }
 
   // Q fragment (B operand of S^T = K Q^T): row iq, k-elements kg*8.. of each KW chunk.
-  const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(b * a.Hq + h) * a.Lq + iq) * D;
+  const uint16_t* qp = (const uint16_t*)a.q + b * a.qs[0] + h * a.qs[1] + (int64_t)iq * a.qs[2];
   u32x4 qop[C::NQC];
 #pragma unroll
   for (int c = 0; c < C::NQC; ++c) {
@@ -124,8 +131,13 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
     m = sink2;
   }
 
-  const uint16_t* kp = (const uint16_t*)a.k + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * D;
-  const uint16_t* vp = (const uint16_t*)a.v + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * DV;
+  const uint16_t* kp = (const uint16_t*)a.k + b * a.ks[0] + hkv * a.ks[1];
+  const uint16_t* vp = (const uint16_t*)a.v + b * a.vs[0] + hkv * a.vs[1];
+  const int64_t ksl = a.ks[2], vsl = a.vs[2];
+  // additive mask: the lane's row (clamped for lanes past the last query row)
+  const void* arow = nullptr;
+  if constexpr (ADD)
+    arow = (const uint16_t*)a.amask + b * a.ms[0] + h * a.ms[1] + (int64_t)min(iq, a.Lq - 1) * a.ms[2];
   // boolean mask: the lane's row of packed mask words (tile t covers words
   // t*BN/32 ..), fetched with the K/V tile one step ahead
   constexpr int MWT = BN / 32;
@@ -151,7 +163,7 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
       if (C::KCH % C::NT == 0 || c < C::KCH) {
         const int r = c / (D / 8), cc = c % (D / 8);
         const int key = k0 + r;
-        kr[it] = key < a.Lk ? ld_global16(kp + (size_t)key * D + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+        kr[it] = key < a.Lk ? ld_global16(kp + key * ksl + cc * 8) : u32x4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
@@ -160,7 +172,7 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
       if (C::VCH % C::NT == 0 || c < C::VCH) {
         const int r = c / (DV / 8), cc = c % (DV / 8);
         const int key = k0 + r;
-        vr[it] = key < a.Lk ? ld_global16(vp + (size_t)key * DV + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+        vr[it] = key < a.Lk ? ld_global16(vp + key * vsl + cc * 8) : u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -196,6 +208,17 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < MWT; ++w) mwc[w] = mwn[w];
+    // additive mask values of this tile, issued ahead of the next tile's loads
+    f32x4 madd[ADD ? C::NSB * ACC / 4 : 1];
+    if constexpr (ADD) {
+      if (wave_live) {
+#pragma unroll
+        for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+          for (int g = 0; g < ACC / 4; ++g)
+            madd[nb * (ACC / 4) + g] = mask4<E>(arow, k0 + nb * MF + acc_row<MF>(4 * g, kg), a.Lk, a.mvec != 0);
+      }
+    }
     if (t + 1 < ntiles) load_tile(k0 + BN);
     if (!wave_live || k0 >= w_kend || k0 + BN <= w_kskip) continue;
     const bool full = k0 + BN <= w_kfull && k0 >= w_klo;
@@ -219,6 +242,15 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
       for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
         for (int i = 0; i < ACC; ++i) mx = fmaxf(mx, s[nb][i]);
+    } else if (ADD) {
+      // base-2 scores with the mask added; keys past Lk carry -inf from the mask read
+#pragma unroll
+      for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+        for (int i = 0; i < ACC; ++i) {
+          s[nb][i] = iq < a.Lq ? fmaf(s[nb][i], a.c, madd[nb * (ACC / 4) + i / 4][i % 4]) : -INFINITY;
+          mx = fmaxf(mx, s[nb][i]);
+        }
     } else if (bool_mask) {
       // lane's keys: nb*MF + acc_row(i, 0) + 4 kg; packed bits are zero past Lk
 #pragma unroll
@@ -244,8 +276,10 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
           mx = fmaxf(mx, s[nb][i]);
         }
     }
+    // scores are in base 2 already with an additive mask, else scaled here
+    const float sc = ADD ? 1.0f : a.c;
     mx = row_max<MF>(mx);
-    const float tmax = (mx == -INFINITY) ? -INFINITY : mx * a.c;
+    const float tmax = (mx == -INFINITY) ? -INFINITY : mx * sc;
     softmax_rebase<C::NDB>(tmax, m, l, o);
     const float mu = (m == -INFINITY) ? 0.0f : m;
 
@@ -255,8 +289,8 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
     for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
       for (int i = 0; i < ACC; i += 2) {
-        const float p0 = fast_exp2(fmaf(s[nb][i], a.c, -mu));
-        const float p1 = fast_exp2(fmaf(s[nb][i + 1], a.c, -mu));
+        const float p0 = fast_exp2(fmaf(s[nb][i], sc, -mu));
+        const float p1 = fast_exp2(fmaf(s[nb][i + 1], sc, -mu));
         lsum += p0 + p1;
         pk[(nb * ACC + i) / 2] = pack2<E>(p0, p1);
       }
@@ -314,7 +348,7 @@ struct PrefillCfgF32 {
   static_assert(D % KWF == 0 && BN % MF == 0, "shape");
 };
 
-template <int MF, int D, int DV, int BN, int NW>
+template <int MF, int D, int DV, int BN, int NW, bool ADD>
 __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
   using C = PrefillCfgF32<MF, D, DV, BN, NW>;
   using acc_t = typename Mfma<MF>::acc_t;
@@ -359,7 +393,7 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
   if (a.mask_kind == kMaskCausal) {
     w_kend = min(a.Lk, w_last + shift + 1);
     w_kfull = min(a.Lk, wi0 + shift + 1);
-  } else if (a.mask_kind == kMaskBool) {
+  } else if (ADD || a.mask_kind == kMaskBool) {
     w_kfull = 0;
   }
   // with a window: keys below w_kskip are outside every row's window, keys
@@ -370,7 +404,7 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
     w_klo = w_last + shift - a.window + 1;
   }
 
-  const float* qp = (const float*)a.q + ((size_t)(b * a.Hq + h) * a.Lq + iq) * D;
+  const float* qp = (const float*)a.q + b * a.qs[0] + h * a.qs[1] + (int64_t)iq * a.qs[2];
   float qop[C::NQS];
 #pragma unroll
   for (int s = 0; s < C::NQS; ++s) {
@@ -396,8 +430,12 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
     m = sink2;
   }
 
-  const float* kp = (const float*)a.k + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * D;
-  const float* vp = (const float*)a.v + (size_t)(b * a.Hkv + hkv) * (size_t)a.Lk * DV;
+  const float* kp = (const float*)a.k + b * a.ks[0] + hkv * a.ks[1];
+  const float* vp = (const float*)a.v + b * a.vs[0] + hkv * a.vs[1];
+  const int64_t ksl = a.ks[2], vsl = a.vs[2];
+  const void* arow = nullptr;
+  if constexpr (ADD)
+    arow = (const float*)a.amask + b * a.ms[0] + h * a.ms[1] + (int64_t)min(iq, a.Lq - 1) * a.ms[2];
   const uint8_t* mrow = a.mask + (size_t)iq * a.Lk;
 
   u32x4 kr[C::KPT], vr[C::VPT];
@@ -408,7 +446,7 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
       if (C::KCH % C::NT == 0 || c < C::KCH) {
         const int r = c / (D / 4), cc = c % (D / 4);
         const int key = k0 + r;
-        kr[it] = key < a.Lk ? ld_global16(kp + (size_t)key * D + cc * 4) : u32x4{0u, 0u, 0u, 0u};
+        kr[it] = key < a.Lk ? ld_global16(kp + key * ksl + cc * 4) : u32x4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
@@ -417,7 +455,7 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
       if (C::VCH % C::NT == 0 || c < C::VCH) {
         const int r = c / (DV / 4), cc = c % (DV / 4);
         const int key = k0 + r;
-        vr[it] = key < a.Lk ? ld_global16(vp + (size_t)key * DV + cc * 4) : u32x4{0u, 0u, 0u, 0u};
+        vr[it] = key < a.Lk ? ld_global16(vp + key * vsl + cc * 4) : u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -450,6 +488,17 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
     __syncthreads();
     store_tile();
     __syncthreads();
+    f32x4 madd[ADD ? C::NSB * ACC / 4 : 1];
+    if constexpr (ADD) {
+      if (wave_live) {
+#pragma unroll
+        for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+          for (int g = 0; g < ACC / 4; ++g)
+            madd[nb * (ACC / 4) + g] =
+                mask4<ElemF32>(arow, k0 + nb * MF + acc_row<MF>(4 * g, kg), a.Lk, a.mvec != 0);
+      }
+    }
     if (t + 1 < ntiles) load_tile(k0 + BN);
     if (!wave_live || k0 >= w_kend || k0 + BN <= w_kskip) continue;
     const bool full = k0 + BN <= w_kfull && k0 >= w_klo;
@@ -469,7 +518,10 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
     for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
       for (int i = 0; i < ACC; ++i) {
-        if (!full) {
+        if (ADD) {
+          // base-2 scores with the mask added; keys past Lk carry -inf from the mask read
+          s[nb][i] = iq < a.Lq ? fmaf(s[nb][i], a.c, madd[nb * (ACC / 4) + i / 4][i % 4]) : -INFINITY;
+        } else if (!full) {
           const int key = k0 + nb * MF + acc_row<MF>(i, kg);
           bool vis = key < a.Lk && iq < a.Lq;
           if (a.mask_kind == kMaskCausal)
@@ -479,8 +531,9 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
         }
         mx = fmaxf(mx, s[nb][i]);
       }
+    const float sc = ADD ? 1.0f : a.c;
     mx = row_max<MF>(mx);
-    const float tmax = (mx == -INFINITY) ? -INFINITY : mx * a.c;
+    const float tmax = (mx == -INFINITY) ? -INFINITY : mx * sc;
     softmax_rebase<C::NDB>(tmax, m, l, o);
     const float mu = (m == -INFINITY) ? 0.0f : m;
 
@@ -489,7 +542,7 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
     for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
       for (int i = 0; i < ACC; ++i) {
-        const float p = fast_exp2(fmaf(s[nb][i], a.c, -mu));
+        const float p = fast_exp2(fmaf(s[nb][i], sc, -mu));
         s[nb][i] = p;
         lsum += p;
       }

@@ -169,10 +169,16 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
   if (Dv < 0) return fail(SDPA_ERR_INVALID, "Dv must be >= 0 (got %lld)", (long long)Dv);
   if (dtype != SDPA_F32 && dtype != SDPA_F16 && dtype != SDPA_BF16)
     return fail(SDPA_ERR_INVALID, "dtype must be SDPA_F32, SDPA_F16 or SDPA_BF16 (got %d)", dtype);
-  if (mask_kind != SDPA_MASK_NONE && mask_kind != SDPA_MASK_CAUSAL && mask_kind != SDPA_MASK_BOOL)
-    return fail(SDPA_ERR_INVALID, "mask_kind must be 0 (none), 1 (causal) or 2 (bool) (got %d)", mask_kind);
+  if (mask_kind != SDPA_MASK_NONE && mask_kind != SDPA_MASK_CAUSAL && mask_kind != SDPA_MASK_BOOL &&
+      mask_kind != SDPA_MASK_ADDITIVE)
+    return fail(SDPA_ERR_INVALID, "mask_kind must be 0 (none), 1 (causal), 2 (bool) or 3 (additive) (got %d)",
+                mask_kind);
   if (mask_kind == SDPA_MASK_BOOL && !has_mask)
     return fail(SDPA_ERR_INVALID, "mask_kind is SDPA_MASK_BOOL but mask is NULL");
+  if (mask_kind == SDPA_MASK_ADDITIVE && !has_mask)
+    return fail(SDPA_ERR_INVALID, "mask_kind is SDPA_MASK_ADDITIVE but mask is NULL");
+  if (window > 0 && mask_kind != SDPA_MASK_CAUSAL)
+    return fail(SDPA_ERR_INVALID, "a window needs mask_kind SDPA_MASK_CAUSAL (got %d)", mask_kind);
   if (Hkv == 0 && Hq != 0) return fail(SDPA_ERR_INVALID, "Hkv must be positive when Hq (%lld) is", (long long)Hq);
   if (Hkv != 0 && Hq % Hkv != 0)
     return fail(SDPA_ERR_INVALID, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
@@ -253,7 +259,7 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
   p.kernels = 1;
   p.rows_per_wave = rows;
   p.waves = nw;
-  p.block_n = prefill_bn(dtype, (int)D, (int)Dv);
+  p.block_n = prefill_bn(dtype, (int)D, (int)Dv, mask_kind);
   p.heads_per_group = (int32_t)heads;
   p.grid[0] = (B * Hq / heads) * nqb;   // one workgroup per (head block, query block)
   p.grid[1] = 1;
@@ -305,7 +311,7 @@ hipError_t get_scratch(hipStream_t stream, size_t bytes, void** out) {
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 3; }
+int sdpa_abi_version(void) { return 4; }
 
 const char* sdpa_last_error(void) { return g_err.c_str(); }
 
@@ -333,36 +339,81 @@ int effective_window(int64_t window, int64_t Lk, int64_t* eff) {
   return SDPA_OK;
 }
 
-int forward_impl(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t Hq, int64_t Hkv,
-                 int64_t Lq, int64_t Lk, int64_t D, int64_t Dv, float scale, int mask_kind, const uint8_t* mask,
-                 const void* sinks, int dtype, int64_t window, void* stream_v) {
+// Element strides (batch, head, row) of one [B, H, L, E] operand.
+struct Strides {
+  int64_t b, h, l;
+};
+Strides contiguous(int64_t H, int64_t L, int64_t E) { return Strides{H * L * E, L * E, E}; }
+
+// The operands of one forward call as views: data pointers and element strides.
+struct Views {
+  const void *q, *k, *v;
+  Strides qs, ks, vs;
+  const void* mask;   // bool: uint8 [Lq, Lk] rows of Lk bytes; additive: dtype elements at ms
+  Strides ms;
+};
+
+// A view's strides are non-negative and its largest element offset fits in 63 bits.
+int check_view(const char* name, const Strides& st, int64_t n0, int64_t n1, int64_t n2, int64_t E) {
+  if (st.b < 0 || st.h < 0 || st.l < 0)
+    return fail(SDPA_ERR_INVALID, "%s strides must be >= 0 (got %lld, %lld, %lld)", name, (long long)st.b,
+                (long long)st.h, (long long)st.l);
+  int64_t x, y, z, t;
+  if (__builtin_mul_overflow(n0 > 0 ? n0 - 1 : 0, st.b, &x) || __builtin_mul_overflow(n1 > 0 ? n1 - 1 : 0, st.h, &y) ||
+      __builtin_mul_overflow(n2 > 0 ? n2 - 1 : 0, st.l, &z) || __builtin_add_overflow(x, y, &t) ||
+      __builtin_add_overflow(t, z, &t) || __builtin_add_overflow(t, E, &t) || t > (INT64_MAX >> 2))
+    return fail(SDPA_ERR_INVALID, "%s: element offsets overflow", name);
+  return SDPA_OK;
+}
+
+// 16-byte loads read q, k and v rows: every row start must be 16-byte aligned.
+int check_rows_aligned(const char* name, const void* p, const Strides& st, int64_t es) {
+  if (((uintptr_t)p & 15) || ((st.b * es) & 15) || ((st.h * es) & 15) || ((st.l * es) & 15))
+    return fail(SDPA_ERR_INVALID, "%s must be 16-byte aligned, with every stride * element size a multiple of 16 "
+                "bytes", name);
+  return SDPA_OK;
+}
+
+int forward_impl(const Views& x, void* out, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                 int64_t Dv, float scale, int mask_kind, const void* sinks, int dtype, int64_t window,
+                 void* stream_v) {
   sdpa_plan_t p;
-  int rc = validate_and_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, mask != nullptr, sinks != nullptr, dtype,
+  int rc = validate_and_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, x.mask != nullptr, sinks != nullptr, dtype,
                              window, &p);
   if (rc != SDPA_OK) return rc;
   if (!std::isfinite(scale)) return fail(SDPA_ERR_INVALID, "scale must be finite (got %g)", (double)scale);
+  const int64_t es = elem_size(dtype);
+  if ((rc = check_view("q", x.qs, B, Hq, Lq, D)) != SDPA_OK) return rc;
+  if ((rc = check_view("k", x.ks, B, Hkv, Lk, D)) != SDPA_OK) return rc;
+  if ((rc = check_view("v", x.vs, B, Hkv, Lk, Dv)) != SDPA_OK) return rc;
+  if (mask_kind == SDPA_MASK_ADDITIVE && (rc = check_view("mask", x.ms, B, Hq, Lq, Lk)) != SDPA_OK) return rc;
+  if (x.ks.l * es >= (int64_t(1) << 26) || x.vs.l * es >= (int64_t(1) << 26))
+    return fail(SDPA_ERR_UNSUPPORTED, "k and v row strides must be below 2^26 bytes");
   if (p.route == SDPA_ROUTE_EMPTY) return SDPA_OK;
   if (!out) return fail(SDPA_ERR_INVALID, "out must not be NULL");
-  if (!q) return fail(SDPA_ERR_INVALID, "q must not be NULL");
-  if (((uintptr_t)out | (uintptr_t)q) & 15)
-    return fail(SDPA_ERR_INVALID, "q and out must be 16-byte aligned");
+  if (!x.q) return fail(SDPA_ERR_INVALID, "q must not be NULL");
+  if ((uintptr_t)out & 15) return fail(SDPA_ERR_INVALID, "q and out must be 16-byte aligned");
+  if ((rc = check_rows_aligned("q", x.q, x.qs, es)) != SDPA_OK) return rc;
+  if (mask_kind == SDPA_MASK_ADDITIVE && ((uintptr_t)x.mask % es))
+    return fail(SDPA_ERR_INVALID, "an additive mask must be aligned to its element size");
   hipStream_t stream = (hipStream_t)stream_v;
   hipError_t e;
   if (p.route == SDPA_ROUTE_ZERO_FILL) {
-    e = launch_zero_fill(out, B * Hq * Lq * Dv * elem_size(dtype), stream);
+    e = launch_zero_fill(out, B * Hq * Lq * Dv * es, stream);
     if (e != hipSuccess) return fail(SDPA_ERR_HIP, "zero-fill launch failed: %s", hipGetErrorString(e));
     return SDPA_OK;
   }
-  if (!k || !v) return fail(SDPA_ERR_INVALID, "k and v must not be NULL");
-  if (((uintptr_t)k | (uintptr_t)v) & 15) return fail(SDPA_ERR_INVALID, "k and v must be 16-byte aligned");
+  if (!x.k || !x.v) return fail(SDPA_ERR_INVALID, "k and v must not be NULL");
+  if ((rc = check_rows_aligned("k", x.k, x.ks, es)) != SDPA_OK) return rc;
+  if ((rc = check_rows_aligned("v", x.v, x.vs, es)) != SDPA_OK) return rc;
 
   FwdArgs a;
   memset(&a, 0, sizeof a);
-  a.q = q;
-  a.k = k;
-  a.v = v;
+  a.q = x.q;
+  a.k = x.k;
+  a.v = x.v;
   a.out = out;
-  a.mask = mask_kind == SDPA_MASK_BOOL ? mask : nullptr;
+  a.mask = mask_kind == SDPA_MASK_BOOL ? (const uint8_t*)x.mask : nullptr;
   a.sinks = sinks;
   a.B = (int)B;
   a.Hq = (int)Hq;
@@ -372,6 +423,22 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int64_t
   a.group = (int)(Hq / Hkv);
   a.mask_kind = mask_kind;
   a.window = (int)window;
+  const Strides* st[3] = {&x.qs, &x.ks, &x.vs};
+  int64_t* dst[3] = {a.qs, a.ks, a.vs};
+  for (int i = 0; i < 3; ++i) {
+    dst[i][0] = st[i]->b;
+    dst[i][1] = st[i]->h;
+    dst[i][2] = st[i]->l;
+  }
+  if (mask_kind == SDPA_MASK_ADDITIVE) {
+    a.amask = x.mask;
+    a.ms[0] = x.ms.b;
+    a.ms[1] = x.ms.h;
+    a.ms[2] = x.ms.l;
+    // four-element groups load as one vector when every row start is aligned for it
+    const int64_t va = 4 * es;
+    a.mvec = ((uintptr_t)x.mask % va == 0) && (x.ms.b % 4 == 0) && (x.ms.h % 4 == 0) && (x.ms.l % 4 == 0);
+  }
   // scores are used in base 2; a zero scale becomes the smallest normal float,
   // which leaves every finite score's weight at exactly exp2(0) = 1
   a.c = fmaxf(fabsf(scale) * 1.4426950408889634f, FLT_MIN);
@@ -396,7 +463,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int64_t
       void* bits = nullptr;
       e = get_scratch(stream, (size_t)p.scratch_bytes, &bits);
       if (e != hipSuccess) return fail(SDPA_ERR_HIP, "mask-bit scratch allocation failed: %s", hipGetErrorString(e));
-      e = launch_mask_bits(mask, (uint32_t*)bits, Lq, Lk, stream);
+      e = launch_mask_bits((const uint8_t*)x.mask, (uint32_t*)bits, Lq, Lk, stream);
       if (e != hipSuccess) return fail(SDPA_ERR_HIP, "mask packing launch failed: %s", hipGetErrorString(e));
       a.mbits = (const uint32_t*)bits;
       a.mwords = (int)mask_words(Lk);
@@ -411,6 +478,21 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int64_t
   return SDPA_OK;
 }
 
+// The views of a contiguous call.
+Views contiguous_views(const void* q, const void* k, const void* v, const void* mask, int64_t Hq, int64_t Hkv,
+                       int64_t Lq, int64_t Lk, int64_t D, int64_t Dv) {
+  Views x;
+  x.q = q;
+  x.k = k;
+  x.v = v;
+  x.qs = contiguous(Hq, Lq, D);
+  x.ks = contiguous(Hkv, Lk, D);
+  x.vs = contiguous(Hkv, Lk, Dv);
+  x.mask = mask;
+  x.ms = Strides{0, 0, Lk};
+  return x;
+}
+
 }  // namespace
 
 extern "C" {
@@ -419,7 +501,10 @@ int sdpa_forward(const void* q, const void* k, const void* v, void* out, int64_t
                  int64_t Lq, int64_t Lk, int64_t D, int64_t Dv, float scale, int mask_kind, const uint8_t* mask,
                  const void* sinks, int dtype, void* stream) {
   g_err.clear();
-  return forward_impl(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, Dv, scale, mask_kind, mask, sinks, dtype, 0, stream);
+  if (mask_kind == SDPA_MASK_ADDITIVE)
+    return fail(SDPA_ERR_INVALID, "an additive mask needs its strides: call sdpa_forward_strided");
+  return forward_impl(contiguous_views(q, k, v, mask, Hq, Hkv, Lq, Lk, D, Dv), out, B, Hq, Hkv, Lq, Lk, D, Dv, scale,
+                      mask_kind, sinks, dtype, 0, stream);
 }
 
 int sdpa_forward_windowed(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t Hq,
@@ -429,8 +514,8 @@ int sdpa_forward_windowed(const void* q, const void* k, const void* v, void* out
   int64_t w = 0;
   const int rc = effective_window(window, Lk, &w);
   if (rc != SDPA_OK) return rc;
-  return forward_impl(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, Dv, scale, SDPA_MASK_CAUSAL, nullptr, sinks, dtype, w,
-                      stream);
+  return forward_impl(contiguous_views(q, k, v, nullptr, Hq, Hkv, Lq, Lk, D, Dv), out, B, Hq, Hkv, Lq, Lk, D, Dv,
+                      scale, SDPA_MASK_CAUSAL, sinks, dtype, w, stream);
 }
 
 int sdpa_plan_windowed(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D, int64_t Dv,
@@ -574,6 +659,9 @@ int sdpa_paged_forward(const void* q, const void* kcache, const void* vcache, vo
   a.rows = (int)(a.group * Lq);
   a.kps = (int)p.keys_per_split;
   a.nsplit = (int)p.splits;
+  a.qs[0] = Hq * Lq * D;
+  a.qs[1] = Lq * D;
+  a.qs[2] = D;
   void* part = nullptr;
   hipError_t e = get_scratch(stream, (size_t)p.scratch_bytes, &part);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "decode scratch allocation failed: %s", hipGetErrorString(e));
@@ -611,6 +699,38 @@ int sdpa_paged_write(void* cache, const void* rows, const int32_t* slots, int64_
   const hipError_t e = launch_paged_write(cache, rows, slots, n, blocks, Hkv, bs, row_bytes, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "paged write launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
+}
+
+int sdpa_forward_strided(const sdpa_view_t* q, const sdpa_view_t* k, const sdpa_view_t* v, void* out, int64_t B,
+                         int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D, int64_t Dv, float scale,
+                         int mask_kind, const sdpa_view_t* mask, const void* sinks, int64_t window, int dtype,
+                         void* stream) {
+  g_err.clear();
+  if (!q || !k || !v) return fail(SDPA_ERR_INVALID, "the q, k and v views must not be NULL");
+  int64_t w = 0;
+  if (window != 0) {
+    if (mask_kind != SDPA_MASK_CAUSAL)
+      return fail(SDPA_ERR_INVALID, "a window needs mask_kind SDPA_MASK_CAUSAL (got %d)", mask_kind);
+    const int rc = effective_window(window, Lk, &w);
+    if (rc != SDPA_OK) return rc;
+  }
+  Views x;
+  x.q = q->data;
+  x.k = k->data;
+  x.v = v->data;
+  x.qs = Strides{q->stride_b, q->stride_h, q->stride_l};
+  x.ks = Strides{k->stride_b, k->stride_h, k->stride_l};
+  x.vs = Strides{v->stride_b, v->stride_h, v->stride_l};
+  x.mask = nullptr;
+  x.ms = Strides{0, 0, 0};
+  if (mask_kind == SDPA_MASK_BOOL || mask_kind == SDPA_MASK_ADDITIVE) {
+    if (!mask || !mask->data) return fail(SDPA_ERR_INVALID, "mask_kind %d needs a mask view", mask_kind);
+    x.mask = mask->data;
+    x.ms = Strides{mask->stride_b, mask->stride_h, mask->stride_l};
+    if (mask_kind == SDPA_MASK_BOOL && (x.ms.b != 0 || x.ms.h != 0 || x.ms.l != Lk))
+      return fail(SDPA_ERR_UNSUPPORTED, "a boolean mask is one contiguous [Lq, Lk] matrix (strides 0, 0, Lk)");
+  }
+  return forward_impl(x, out, B, Hq, Hkv, Lq, Lk, D, Dv, scale, mask_kind, sinks, dtype, w, stream);
 }
 
 int sdpa_release_workspace(void) {

@@ -17,7 +17,8 @@ generators", OOPSLA 2014). From that word:
 Values are rounded to nearest-even into the storage type; normals are rounded
 to float32 first and then to float16/bfloat16. Storage arrays are numpy
 ``float32`` / ``float16`` and, for bfloat16, ``uint16`` holding the bit
-pattern. Tensor ids: q=1, k=2, v=3, mask=4, sinks=5, block order=6.
+pattern. Tensor ids: q=1, k=2, v=3, mask=4, sinks=5, block order=6, additive
+mask values=7, additive mask -inf positions=8.
 
 Paged caches (``block_order``, ``paged_cache``) only move these arrays into
 blocks at shuffled places; the block order is a Fisher-Yates shuffle whose
@@ -36,6 +37,7 @@ DTYPE_BY_NAME = {"f32": F32, "f16": F16, "bf16": BF16}
 STORAGE = {F32: np.float32, F16: np.float16, BF16: np.uint16}
 
 TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_MASK, TENSOR_SINKS, TENSOR_PAGES = 1, 2, 3, 4, 5, 6
+TENSOR_ADD, TENSOR_ADD_HOLES = 7, 8
 
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
@@ -267,3 +269,20 @@ def _storage_code(dt) -> int:
         if np.dtype(st) == np.dtype(dt):
             return code
     raise ValueError(f"not a storage dtype: {dt}")
+
+
+# ---- additive masks -------------------------------------------------------------------------
+
+NEG_INF_BITS = {F32: np.float32(-np.inf), F16: np.float16(-np.inf), BF16: np.uint16(0xFF80)}
+
+
+def additive_mask(seed: int, shape, dtype: int, holes: float = 0.0) -> np.ndarray:
+    """An additive mask in storage type: N(0,1) values (stream 7), with entries set to
+    -inf where the uniform draw of stream 8 falls below 2*holes - 1 (probability
+    `holes`)."""
+    m = tensor(seed, TENSOR_ADD, shape, dtype, "normal")
+    if holes > 0:
+        count = m.size
+        u = uniform_pm1(seed, TENSOR_ADD_HOLES, count).reshape(m.shape)
+        m[u < 2.0 * holes - 1.0] = NEG_INF_BITS[dtype]
+    return m

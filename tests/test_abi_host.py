@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(sd.library_path())
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert sd.sdpa_abi_version() == 3
+    assert sd.sdpa_abi_version() == 4
     out = subprocess.run(["nm", "-D", "--defined-only", sd.library_path()], capture_output=True, text=True).stdout
     for name in _declared_functions():
         assert re.search(rf"\bT {name}$", out, flags=re.M), f"{name} not exported with C linkage"
@@ -275,3 +275,47 @@ def test_paged_write_validates_before_touching_memory():
     assert w(None, None, None, 0, 6, 2, 4, 64, 2, None, check=False) == 0
     # f32 rows of 4 elements are 16 bytes
     assert w(None, None, None, 0, 6, 2, 4, 4, 0, None, check=False) == 0
+
+
+# --- strided views and additive masks ----------------------------------------------------------
+
+def _strided(q=(16, 4 * 5 * 64, 5 * 64, 64), k=(16, 2 * 9 * 64, 9 * 64, 64), v=(16, 2 * 9 * 64, 9 * 64, 64),
+             mask_kind=0, mask=None, window=0, B=1, Hq=4, Hkv=2, Lq=5, Lk=9, D=64, Dv=64, dtype=2, out=16,
+             scale=0.1):
+    return sd.sdpa_forward_strided(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, Dv, scale, mask_kind, mask, None, window,
+                                   dtype, None, check=False)
+
+
+def test_additive_masks_plan_on_the_generic_prefill_kernel():
+    fast = sd.sdpa_plan(1, 8, 2, 300, 300, 128, 128, 0, False, False, 2)
+    add = sd.sdpa_plan(1, 8, 2, 300, 300, 128, 128, 3, True, False, 2)
+    assert fast["route"] == add["route"] == "prefill"
+    assert (fast["block_n"], add["block_n"]) == (32, 64)
+    dec = sd.sdpa_plan(1, 8, 2, 1, 3000, 128, 128, 3, True, False, 2)
+    assert dec["route"] == "decode"
+    assert sd.sdpa_plan(1, 8, 2, 1, 3000, 128, 128, 3, False, False, 2, check=False) == -1
+    assert "ADDITIVE" in sd.sdpa_last_error()
+
+
+def test_strided_call_validates_before_touching_memory():
+    assert _strided(q=None) == -1 and "views" in sd.sdpa_last_error()
+    assert _strided(k=(16, -64, 64, 64)) == -1 and ">= 0" in sd.sdpa_last_error()
+    assert _strided(v=(16, 0, 0, 36)) == -1 and "16-byte" in sd.sdpa_last_error()   # 72-byte rows
+    assert _strided(q=(8, 0, 0, 64)) == -1 and "aligned" in sd.sdpa_last_error()
+    assert _strided(k=(16, 0, 0, 1 << 25)) == -2 and "2^26" in sd.sdpa_last_error()
+    assert _strided(q=(16, 1 << 62, 0, 64), B=3) == -1 and "overflow" in sd.sdpa_last_error()
+    assert _strided(mask_kind=2) == -1 and "mask view" in sd.sdpa_last_error()
+    assert _strided(mask_kind=2, mask=(16, 0, 0, 10)) == -2 and "boolean" in sd.sdpa_last_error()
+    assert _strided(mask_kind=3) == -1 and "mask view" in sd.sdpa_last_error()
+    assert _strided(mask_kind=3, mask=(17, 0, 0, 9)) == -1 and "element size" in sd.sdpa_last_error()
+    assert _strided(mask_kind=3, mask=(16, 0, 0, 9), window=4) == -1 and "window" in sd.sdpa_last_error()
+    assert _strided(mask_kind=1, window=-2) == -1 and "window" in sd.sdpa_last_error()
+    assert _strided(scale=float("nan")) == -1 and "scale" in sd.sdpa_last_error()
+    # empty calls are successful no-ops
+    assert _strided(Lq=0) == 0 and _strided(B=0) == 0
+
+
+def test_contiguous_call_refuses_an_additive_mask():
+    f = sd.sdpa_forward
+    assert f(16, 16, 16, 16, 1, 2, 2, 4, 4, 64, 64, 0.1, 3, 16, None, 2, None, check=False) == -1
+    assert "sdpa_forward_strided" in sd.sdpa_last_error()

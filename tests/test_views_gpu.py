@@ -1,0 +1,181 @@
+"""GPU parity of strided views and additive masks (sdpa_forward_strided) against
+the CPU float64 oracle, on seeded inputs. The cases follow nuvec-core
+"tests/fast.rs": attention_kernels_match_the_fallback (K/V as transposed views
+of [B, L, H, D], an additive [1, Hq, Lq, Lk] mask next to none, causal and
+boolean masks, with and without sinks, scale 0.3), the capped-attention
+inputs (q as a transposed view, K/V as a slice of a longer cache) and the
+windowed tests (K and V as slices of one larger cache)."""
+import zlib
+
+import numpy as np
+import pytest
+
+from oracle import attention as orc
+from scaled_dot_product_06_amd import inputs as gen
+from tests.gpu_util import TOL, compare, from_device, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+F32, F16, BF16 = gen.F32, gen.F16, gen.BF16
+DT = {"f32": F32, "f16": F16, "bf16": BF16}
+
+# (B, Hq, Hkv, Lq, Lk, D, Dv): the kernel-vs-fallback shapes (as in the contiguous grid)
+SHAPES = [
+    (2, 4, 4, 1, 37, 64, 64), (1, 8, 2, 4, 50, 128, 128), (1, 4, 4, 2, 33, 96, 64), (1, 2, 1, 1, 20, 192, 128),
+    (1, 8, 1, 1, 1100, 128, 128), (1, 16, 2, 1, 9000, 128, 128), (2, 4, 2, 33, 45, 64, 64),
+    (1, 2, 2, 100, 100, 80, 80), (1, 4, 4, 64, 96, 128, 128), (1, 2, 2, 40, 40, 96, 64),
+]
+
+
+def _ids(s):
+    return "x".join(map(str, s))
+
+
+def _kv_transposed(a, dtype):
+    """[B, H, L, E] values as a transposed view of a [B, L, H, E] device array."""
+    return to_device(np.ascontiguousarray(a.transpose(0, 2, 1, 3)), dtype).transpose(1, 2)
+
+
+def _slice_of_cache(a, dtype, before, after):
+    """[B, H, L, E] values as rows before .. before+L of a longer [B, H, before+L+after, E] cache."""
+    B, H, L, E = a.shape
+    big = np.zeros((B, H, before + L + after, E), dtype=a.dtype)
+    big[:, :, before:before + L] = a
+    return to_device(big, dtype)[:, :, before:before + L]
+
+
+def _check(got, want, dtype, what):
+    bad, max_abs, max_rel = compare(got, want, dtype)
+    say(f"  {what}: max_abs={max_abs:.3e} max_rel={max_rel:.3e} failing={bad}/{want.size}")
+    assert bad == 0, f"{what}: {bad} elements outside tolerance {TOL[dtype]}"
+
+
+def _masks(p, seed, holes=0.1):
+    """(mask_kind, device mask, oracle mask) for none, causal, boolean and additive
+    [1, Hq, Lq, Lk] masks."""
+    import torch
+    bmask = gen.diagonal_bool_mask(seed, p.Lq, p.Lk)
+    add = gen.additive_mask(seed, (1, p.Hq, p.Lq, p.Lk), p.dtype, holes)
+    return [
+        (0, None, None),
+        (1, None, None),
+        (2, torch.from_numpy(bmask).cuda(), bmask != 0),
+        (3, to_device(add, p.dtype), gen.widen(add, p.dtype)),
+    ]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=_ids)
+def test_transposed_kv_views_every_mask(shape, dtype):
+    import torch
+    from scaled_dot_product_06_amd import attention
+    B, Hq, Hkv, Lq, Lk, D, Dv = shape
+    seed = 7000 + zlib.crc32(repr((shape, dtype)).encode()) % 100000
+    p = gen.make_problem(seed, B, Hq, Hkv, Lq, Lk, D, Dv, DT[dtype], 0, dist="uniform", sinks=True, scale=0.3)
+    q, k, v, _, s = p.widened()
+    dq = to_device(p.q, p.dtype)
+    dk, dv = _kv_transposed(p.k, p.dtype), _kv_transposed(p.v, p.dtype)
+    assert Hkv == 1 or not dk.is_contiguous()   # one kv head: the transposed view is contiguous
+    ds = to_device(p.sinks, p.dtype)
+    for kind, dmask, omask in _masks(p, seed):
+        for with_sinks in (False, True):
+            got = attention(dq, dk, dv, p.scale, kind, dmask, ds if with_sinks else None)
+            torch.cuda.synchronize()
+            want = orc.sdpa(q, k, v, p.scale, kind, omask, s if with_sinks else None)
+            _check(from_device(got, p.dtype), want, p.dtype, f"{_ids(shape)} {dtype} mask={kind} sinks={with_sinks}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("Lq,Lk,D,Hq,Hkv,w", [(1, 300, 64, 8, 1, 0), (4, 700, 128, 8, 2, 0), (77, 150, 128, 8, 2, 0),
+                                             (300, 500, 256, 4, 2, 0), (5, 9000, 128, 16, 2, 300),
+                                             (129, 1000, 64, 4, 2, 100)])
+def test_query_view_and_kv_cache_slices(Lq, Lk, D, Hq, Hkv, w, dtype):
+    # q as a transposed view of [B, Lq, Hq, D]; K and V as overlapping slices of one cache
+    import torch
+    from scaled_dot_product_06_amd import attention
+    dt = DT[dtype]
+    seed = 7100 + Lq + Lk + D
+    p = gen.make_problem(seed, 1, Hq, Hkv, Lq, Lk, D, D, dt, 1, sinks=True)
+    big = gen.tensor(seed, gen.TENSOR_K, (1, Hkv, Lk + 17, D), dt, "normal")
+    dbig = to_device(big, dt)
+    dk, dv = dbig[:, :, 5:5 + Lk], dbig[:, :, 9:9 + Lk]
+    dq = to_device(np.ascontiguousarray(p.q.transpose(0, 2, 1, 3)), dt).transpose(1, 2)
+    ds = to_device(p.sinks, dt)
+    got = attention(dq, dk, dv, p.scale, 1, None, ds, window=w or None)
+    torch.cuda.synchronize()
+    wq, wb, ws = gen.widen(p.q, dt), gen.widen(big, dt), gen.widen(p.sinks, dt)
+    want = orc.sdpa(wq, wb[:, :, 5:5 + Lk], wb[:, :, 9:9 + Lk], p.scale, 1, None, ws, window=w or None)
+    _check(from_device(got, dt), want, dt, f"Lq={Lq} Lk={Lk} D={D} w={w}")
+
+
+@pytest.mark.parametrize("dtype,shape,kind", [
+    ("bf16", (2, 8, 2, 300, 300, 128, 128), 1),   # pipelined 16-bit prefill
+    ("f16", (1, 8, 2, 200, 333, 64, 64), 2),
+    ("bf16", (1, 4, 2, 100, 250, 256, 256), 1),   # generic 16-bit prefill
+    ("f32", (1, 4, 2, 70, 90, 128, 128), 1),      # f32 prefill
+    ("bf16", (2, 16, 2, 1, 5000, 256, 256), 0),   # decode
+    ("f16", (1, 8, 2, 3, 999, 96, 64), 1),
+])
+def test_views_equal_the_contiguous_call_bit_for_bit(dtype, shape, kind):
+    import torch
+    from scaled_dot_product_06_amd import attention
+    B, Hq, Hkv, Lq, Lk, D, Dv = shape
+    dt = DT[dtype]
+    p = gen.make_problem(7200 + Lk, B, Hq, Hkv, Lq, Lk, D, Dv, dt, kind, sinks=True)
+    dq, dk, dv = (to_device(a, dt) for a in (p.q, p.k, p.v))
+    mask = None if p.mask is None else torch.from_numpy(p.mask).cuda()
+    ds = to_device(p.sinks, dt)
+    want = attention(dq, dk, dv, p.scale, kind, mask, ds)
+    vq = to_device(np.ascontiguousarray(p.q.transpose(0, 2, 1, 3)), dt).transpose(1, 2)
+    got = attention(vq, _kv_transposed(p.k, dt), _slice_of_cache(p.v, dt, 3, 2), p.scale, kind, mask, ds)
+    torch.cuda.synchronize()
+    bits = torch.int32 if dt == F32 else torch.int16
+    assert torch.equal(got.view(bits), want.view(bits))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("Lq,Lk", [(1, 4096), (3, 1001), (70, 257), (130, 131)])
+def test_additive_mask_layouts(Lq, Lk, dtype):
+    """Full [B, Hq, Lq, Lk], per-head [1, Hq, ...], per-batch [B, 1, ...] and 2-D [Lq, Lk]
+    masks; rows of Lk % 4 != 0 elements and a mask starting one element in (scalar
+    reads), -inf holes, and one row masked out entirely (zeros, sinks or not)."""
+    import torch
+    from scaled_dot_product_06_amd import attention
+    dt = DT[dtype]
+    B, Hq, Hkv, D = 2, 8, 2, 128
+    seed = 7300 + Lq + Lk
+    p = gen.make_problem(seed, B, Hq, Hkv, Lq, Lk, D, D, dt, 0, sinks=True)
+    q, k, v, _, s = p.widened()
+    dq, dk, dv = (to_device(a, dt) for a in (p.q, p.k, p.v))
+    ds = to_device(p.sinks, dt)
+    for shape in [(B, Hq, Lq, Lk), (1, Hq, Lq, Lk), (B, 1, Lq, Lk), (Lq, Lk)]:
+        add = gen.additive_mask(seed + len(shape), shape, dt, holes=0.2)
+        add[..., Lq // 2, :] = gen.NEG_INF_BITS[dt]
+        for offset in (0, 1):
+            flat = np.concatenate([np.zeros(offset, dtype=add.dtype), add.ravel()])
+            dmask = to_device(flat, dt)[offset:].view(shape)
+            for sinks in (None, ds):
+                got = attention(dq, dk, dv, p.scale, 3, dmask, sinks)
+                torch.cuda.synchronize()
+                want = orc.sdpa(q, k, v, p.scale, 3, gen.widen(add, dt), None if sinks is None else s)
+                g = from_device(got, dt)
+                assert not g[:, :, Lq // 2].any()
+                _check(g, want, dt, f"mask {shape} offset {offset} sinks={sinks is not None}")
+
+
+def test_additive_mask_on_the_masked_prefill_workload_sampled_rows():
+    # the f16 D=256 GQA prefill shape (1024 x 1801) with an additive [1, Hq, Lq, Lk] mask and sinks
+    import torch
+    from scaled_dot_product_06_amd import attention
+    from tests.gpu_util import sample_rows
+    p = gen.workload(4)
+    add = gen.additive_mask(4, (1, p.Hq, p.Lq, p.Lk), p.dtype, holes=0.1)
+    dq, dk, dv = (to_device(a, p.dtype) for a in (p.q, p.k, p.v))
+    got = attention(dq, dk, dv, p.scale, 3, to_device(add, p.dtype), to_device(p.sinks, p.dtype))
+    torch.cuda.synchronize()
+    g = from_device(got, p.dtype)
+    assert np.isfinite(g).all()
+    rows = sample_rows(p, 256, seed=44)
+    q, k, v, _, s = p.widened()
+    want = orc.sdpa(q, k, v, p.scale, 3, gen.widen(add, p.dtype), s, rows=rows)
+    _check(np.stack([g[b, h, i] for b, h, i in rows]), want, p.dtype, "workload 4 shape, additive mask")

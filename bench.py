@@ -239,6 +239,65 @@ def measure_paged_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, 
     return res
 
 
+def _time_calls(torch, stream, call, calls=50, rounds=5):
+    """Median per-call time (us) over `rounds` batches of `calls`, HIP events on `stream`."""
+    for _ in range(20):
+        call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(calls):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / calls * 1e3)
+    return sorted(times)[len(times) // 2]
+
+
+def measure_strided_workloads(torch, sd, gen, dev, to_dev, stream, log):
+    """Calls through sdpa_forward_strided: the causal prefill with q, K and V as
+    transposed views of [B, L, H, D] arrays (the layout a model's projections
+    produce), and the f16 masked-prefill shape with an additive [1, Hq, Lq, Lk]
+    mask (N(0,1) values, 10 % -inf) and sinks. Prefill FLOP as for the
+    contiguous calls (the additive mask counts every pair); the additive line
+    also reports the mask bytes it reads."""
+    import numpy as np
+    res = {}
+    p = gen.workload(3)
+    tv = lambda a: to_dev(np.ascontiguousarray(a.transpose(0, 2, 1, 3)), p.dtype).transpose(1, 2)
+    q, k, v = tv(p.q), tv(p.k), tv(p.v)
+    out = torch.empty((p.B, p.Hq, p.Lq, p.Dv), dtype=q.dtype, device=dev)
+    us = _time_calls(torch, stream, lambda: sd.attention(q, k, v, p.scale, p.mask_kind, out=out,
+                                                         stream=stream.cuda_stream))
+    flop = prefill_flop(p)
+    tf = flop / us / 1e6
+    res["3v"] = {"workload": p.name + ", q/k/v as transposed [B,L,H,D] views", "us_per_call": round(us, 2),
+                 "flop_per_call": flop, "TFLOP/s": round(tf, 2), "peak_TFLOP/s": PEAK_BF16_TFLOPS,
+                 "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    log(f"{res['3v']['workload']}: {us:.1f} us/call {tf:.1f} TFLOP/s")
+    del q, k, v, out
+    p = gen.workload(4)
+    add = gen.additive_mask(4, (1, p.Hq, p.Lq, p.Lk), p.dtype, holes=0.1)
+    q, k, v = (to_dev(a, p.dtype) for a in (p.q, p.k, p.v))
+    m, s = to_dev(add, p.dtype), to_dev(p.sinks, p.dtype)
+    out = torch.empty((p.B, p.Hq, p.Lq, p.Dv), dtype=q.dtype, device=dev)
+    us = _time_calls(torch, stream, lambda: sd.attention(q, k, v, p.scale, 3, m, s, out=out,
+                                                         stream=stream.cuda_stream))
+    flop = p.B * p.Hq * p.Lq * p.Lk * 2 * (p.D + p.Dv)
+    tf = flop / us / 1e6
+    mbytes = add.size * add.itemsize
+    res["4a"] = {"workload": "f16 GQA prefill additive-mask+sinks B1 H16/2 L1024x1801 D256",
+                 "us_per_call": round(us, 2), "flop_per_call": flop, "TFLOP/s": round(tf, 2),
+                 "peak_TFLOP/s": PEAK_BF16_TFLOPS, "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                 "mask_bytes_per_call": mbytes, "mask_GB/s": round(mbytes / us / 1e3, 1)}
+    log(f"{res['4a']['workload']}: {us:.1f} us/call {tf:.1f} TFLOP/s, mask {mbytes / us / 1e3:.0f} GB/s")
+    del q, k, v, m, s, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,7 +308,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip the reported-only workloads (f32 prefill, "
-                    "8193-key decode, f16 masked prefill with sinks, sliding windows, paged decode)")
+                    "8193-key decode, f16 masked prefill with sinks, sliding windows, paged decode, "
+                    "strided views, additive mask)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
@@ -335,6 +395,7 @@ def main() -> int:
     if not args.no_others:
         others = measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log)
         others.update(measure_paged_workloads(torch, sd, gen, dev, to_dev, stream, log))
+        others.update(measure_strided_workloads(torch, sd, gen, dev, to_dev, stream, log))
 
     pre_plan = sd.sdpa_plan(pre.B, pre.Hq, pre.Hkv, pre.Lq, pre.Lk, pre.D, pre.Dv, pre.mask_kind, False, False,
                             pre.dtype)

@@ -171,36 +171,41 @@ __device__ __forceinline__ float keep_if_bit(float x, uint32_t word, int pos) {
   return __uint_as_float((keep & __float_as_uint(x)) | (~keep & 0xFF800000u));
 }
 
-// Additive-mask values of keys key .. key+3 of one mask row, widened to f32
-// and converted to base 2 (times log2 e); keys at or past Lk read as -inf.
-// `vec`: the row start is aligned for one 8-byte (16-bit types) or 16-byte
-// (f32) load of the group, and key is a multiple of 4.
-template <class E> __device__ __forceinline__ f32x4 mask4(const void* row, int key, int Lk, bool vec);
-template <class E> __device__ __forceinline__ f32x4 mask4_16(const void* row, int key, int Lk, bool vec) {
+// Additive masks: four consecutive values (keys key .. key+3) of one mask row,
+// fetched with one 8-byte (16-bit types) or 16-byte (f32) load. The row needs
+// only element alignment: global memory is accessed in unaligned mode, where
+// multi-dword loads take any byte address. The last group of a row, which may
+// run past Lk, is read element by element.
+//
+// 16-bit types: the raw patterns (two per word), so a prefetched tile of the
+// mask takes half the registers; keys at or past Lk hold the pattern of -inf.
+template <class E> __device__ __forceinline__ uint16_t neg_inf_bits();
+template <> __device__ __forceinline__ uint16_t neg_inf_bits<ElemBF16>() { return 0xFF80u; }
+template <> __device__ __forceinline__ uint16_t neg_inf_bits<ElemF16>() { return 0xFC00u; }
+template <class E> __device__ __forceinline__ u32x2 mask4_bits(const void* row, int key, int Lk) {
   const uint16_t* p = (const uint16_t*)row + key;
-  f32x4 r;
-  if (vec && key + 4 <= Lk) {
-    const u32x2 x = *reinterpret_cast<const u32x2*>(p);
-    r = {half_to_f32<E>((uint16_t)(x[0] & 0xFFFFu)), half_to_f32<E>((uint16_t)(x[0] >> 16)),
-         half_to_f32<E>((uint16_t)(x[1] & 0xFFFFu)), half_to_f32<E>((uint16_t)(x[1] >> 16))};
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = key + e < Lk ? half_to_f32<E>(p[e]) : -INFINITY;
+  if (key + 4 <= Lk) {
+    u32x2 x;
+    __builtin_memcpy(&x, p, 8);
+    return x;
   }
-  return r * kLog2e;
+  uint32_t h[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[e] = key + e < Lk ? p[e] : neg_inf_bits<E>();
+  return u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
 }
-template <> __device__ __forceinline__ f32x4 mask4<ElemBF16>(const void* row, int key, int Lk, bool vec) {
-  return mask4_16<ElemBF16>(row, key, Lk, vec);
+// Element e (0..3) of a mask4_bits group, widened and converted to base 2.
+template <class E> __device__ __forceinline__ float mask_bits_value(u32x2 g, int e) {
+  const uint32_t w = g[e / 2];
+  return half_to_f32<E>((uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu))) * kLog2e;
 }
-template <> __device__ __forceinline__ f32x4 mask4<ElemF16>(const void* row, int key, int Lk, bool vec) {
-  return mask4_16<ElemF16>(row, key, Lk, vec);
-}
-struct ElemF32 {};
-template <> __device__ __forceinline__ f32x4 mask4<ElemF32>(const void* row, int key, int Lk, bool vec) {
+
+// f32: the values converted to base 2 (times log2 e); keys at or past Lk read as -inf.
+__device__ __forceinline__ f32x4 mask4_f32(const void* row, int key, int Lk) {
   const float* p = (const float*)row + key;
   f32x4 r;
-  if (vec && key + 4 <= Lk) {
-    r = *reinterpret_cast<const f32x4*>(p);
+  if (key + 4 <= Lk) {
+    __builtin_memcpy(&r, p, 16);
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) r[e] = key + e < Lk ? p[e] : -INFINITY;

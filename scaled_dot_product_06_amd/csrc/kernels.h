@@ -25,7 +25,6 @@ struct FwdArgs {
   // amask + b*ms[0] + h*ms[1] + i*ms[2] + j, added to the scaled scores
   const void* amask;
   int64_t ms[3];
-  int mvec;              // 1: every additive-mask row start is aligned for 4-element vector loads
   int B, Hq, Hkv, Lq, Lk;
   int group;             // Hq / Hkv
   int mask_kind;

@@ -19,8 +19,9 @@
 //
 // ADD instantiations read an additive mask (nuvec-core "tests/fast.rs",
 // attention_kernels_match_the_fallback): each lane fetches its row's mask
-// values for a tile before the next tile's K/V loads are issued, and adds them
-// (in base 2) to the scaled scores. Q, K and V are read through element
+// values for the next tile together with that tile's K/V (a whole step ahead,
+// kept as packed 16-bit values), and adds them (in base 2) to the scaled
+// scores. Q, K and V are read through element
 // strides (batch, head, row), so views such as a transposed [B, L, H, D]
 // array or a slice of a longer cache need no copy.
 #pragma once
@@ -149,7 +150,19 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
   for (int w = 0; w < MWT; ++w) mwn[w] = mwc[w] = 0u;
 
   u32x4 kr[C::KPT], vr[C::VPT];
+  // additive mask: the lane's values for the next tile (mnx) and this one (mcu)
+  constexpr int MG = ADD ? C::NSB * ACC / 4 : 1;
+  u32x2 mnx[MG], mcu[MG];
   auto load_tile = [&](int k0) {
+    if constexpr (ADD) {
+      if (wave_live) {
+#pragma unroll
+        for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+          for (int g = 0; g < ACC / 4; ++g)
+            mnx[nb * (ACC / 4) + g] = mask4_bits<E>(arow, k0 + nb * MF + acc_row<MF>(4 * g, kg), a.Lk);
+      }
+    }
     if (bool_mask) {
 #pragma unroll
       for (int w = 0; w < MWT; ++w) {
@@ -208,16 +221,9 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < MWT; ++w) mwc[w] = mwn[w];
-    // additive mask values of this tile, issued ahead of the next tile's loads
-    f32x4 madd[ADD ? C::NSB * ACC / 4 : 1];
     if constexpr (ADD) {
-      if (wave_live) {
 #pragma unroll
-        for (int nb = 0; nb < C::NSB; ++nb)
-#pragma unroll
-          for (int g = 0; g < ACC / 4; ++g)
-            madd[nb * (ACC / 4) + g] = mask4<E>(arow, k0 + nb * MF + acc_row<MF>(4 * g, kg), a.Lk, a.mvec != 0);
-      }
+      for (int g = 0; g < MG; ++g) mcu[g] = mnx[g];
     }
     if (t + 1 < ntiles) load_tile(k0 + BN);
     if (!wave_live || k0 >= w_kend || k0 + BN <= w_kskip) continue;
@@ -248,7 +254,8 @@ __global__ void __launch_bounds__(NW * 64) prefill_kernel(FwdArgs a) {
       for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
         for (int i = 0; i < ACC; ++i) {
-          s[nb][i] = iq < a.Lq ? fmaf(s[nb][i], a.c, madd[nb * (ACC / 4) + i / 4][i % 4]) : -INFINITY;
+          s[nb][i] = iq < a.Lq ? fmaf(s[nb][i], a.c, mask_bits_value<E>(mcu[nb * (ACC / 4) + i / 4], i % 4))
+                               : -INFINITY;
           mx = fmaxf(mx, s[nb][i]);
         }
     } else if (bool_mask) {
@@ -439,7 +446,20 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
   const uint8_t* mrow = a.mask + (size_t)iq * a.Lk;
 
   u32x4 kr[C::KPT], vr[C::VPT];
+  // additive mask: the lane's values for the next tile (mnx) and this one (mcu)
+  constexpr int MG = ADD ? C::NSB * ACC / 4 : 1;
+  f32x4 mnx[MG], mcu[MG];
   auto load_tile = [&](int k0) {
+    if constexpr (ADD) {
+      if (wave_live) {
+#pragma unroll
+        for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+          for (int g = 0; g < ACC / 4; ++g)
+            mnx[nb * (ACC / 4) + g] =
+                mask4_f32(arow, k0 + nb * MF + acc_row<MF>(4 * g, kg), a.Lk);
+      }
+    }
 #pragma unroll
     for (int it = 0; it < C::KPT; ++it) {
       const int c = tid + it * C::NT;
@@ -488,16 +508,9 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
     __syncthreads();
     store_tile();
     __syncthreads();
-    f32x4 madd[ADD ? C::NSB * ACC / 4 : 1];
     if constexpr (ADD) {
-      if (wave_live) {
 #pragma unroll
-        for (int nb = 0; nb < C::NSB; ++nb)
-#pragma unroll
-          for (int g = 0; g < ACC / 4; ++g)
-            madd[nb * (ACC / 4) + g] =
-                mask4<ElemF32>(arow, k0 + nb * MF + acc_row<MF>(4 * g, kg), a.Lk, a.mvec != 0);
-      }
+      for (int g = 0; g < MG; ++g) mcu[g] = mnx[g];
     }
     if (t + 1 < ntiles) load_tile(k0 + BN);
     if (!wave_live || k0 >= w_kend || k0 + BN <= w_kskip) continue;
@@ -520,7 +533,7 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
       for (int i = 0; i < ACC; ++i) {
         if (ADD) {
           // base-2 scores with the mask added; keys past Lk carry -inf from the mask read
-          s[nb][i] = iq < a.Lq ? fmaf(s[nb][i], a.c, madd[nb * (ACC / 4) + i / 4][i % 4]) : -INFINITY;
+          s[nb][i] = iq < a.Lq ? fmaf(s[nb][i], a.c, mcu[nb * (ACC / 4) + i / 4][i % 4]) : -INFINITY;
         } else if (!full) {
           const int key = k0 + nb * MF + acc_row<MF>(i, kg);
           bool vis = key < a.Lk && iq < a.Lq;

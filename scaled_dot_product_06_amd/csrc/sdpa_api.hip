@@ -435,9 +435,6 @@ int forward_impl(const Views& x, void* out, int64_t B, int64_t Hq, int64_t Hkv, 
     a.ms[0] = x.ms.b;
     a.ms[1] = x.ms.h;
     a.ms[2] = x.ms.l;
-    // four-element groups load as one vector when every row start is aligned for it
-    const int64_t va = 4 * es;
-    a.mvec = ((uintptr_t)x.mask % va == 0) && (x.ms.b % 4 == 0) && (x.ms.h % 4 == 0) && (x.ms.l % 4 == 0);
   }
   // scores are used in base 2; a zero scale becomes the smallest normal float,
   // which leaves every finite score's weight at exactly exp2(0) = 1

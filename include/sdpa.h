@@ -91,9 +91,11 @@ typedef struct sdpa_plan_t {
  *   out   [B, Hq,  Lq, Dv]   device, dtype, written in full
  *   Hq must be a multiple of Hkv; query head h reads kv head h / (Hq / Hkv).
  *   scale  any finite float, applied to q.k as given (1/sqrt(D) is usual).
- *   mask_kind  SDPA_MASK_*; `mask` is required (device [Lq, Lk] uint8) iff
- *          mask_kind == SDPA_MASK_BOOL and ignored otherwise. A raw pointer
- *          carries no shape: the caller guarantees Lq*Lk readable bytes.
+ *   mask_kind  SDPA_MASK_NONE, _CAUSAL or _BOOL; `mask` is required (device
+ *          [Lq, Lk] uint8) iff mask_kind == SDPA_MASK_BOOL and ignored
+ *          otherwise. A raw pointer carries no shape: the caller guarantees
+ *          Lq*Lk readable bytes. SDPA_MASK_ADDITIVE is SDPA_ERR_INVALID here
+ *          (an additive mask needs its strides: sdpa_forward_strided).
  *   sinks  NULL, or device [Hq] in dtype: one logit per query head that joins
  *          the softmax denominator only (no value row) and is not multiplied
  *          by `scale`.

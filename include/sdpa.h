@@ -182,12 +182,13 @@ int sdpa_plan_windowed(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t L
  *          sdpa_forward_windowed); negative, or positive without the causal
  *          mask, is SDPA_ERR_INVALID.
  *   scale, sinks, head sizes as for sdpa_forward.
- *   dtype  SDPA_F16 or SDPA_BF16 (SDPA_F32 is SDPA_ERR_UNSUPPORTED).
- *   Lq <= 8 and (Hq / Hkv) * Lq <= 32: the decode kernels (split-key first
- *          pass, log-sum-exp reduce); larger query counts are
- *          SDPA_ERR_UNSUPPORTED.
- * The key splits follow the cache capacity max_blocks * bs (or, with a
- * window, the window's keys), not the lengths, which stay on the device.
+ *   dtype  SDPA_F16 or SDPA_BF16: the decode kernels (split-key first pass,
+ *          log-sum-exp reduce), for Lq <= 8 and (Hq / Hkv) * Lq <= 32 (larger
+ *          query counts are SDPA_ERR_UNSUPPORTED); their key splits follow
+ *          the cache capacity max_blocks * bs (or, with a window, the
+ *          window's keys), not the lengths, which stay on the device.
+ *          SDPA_F32: the f32 tiled kernel over the capacity's key range, any
+ *          Lq, reading each K/V row through the table.
  * Ownership, alignment, scratch, errors and asynchrony as for sdpa_forward.
  */
 int sdpa_paged_forward(const void* q, const void* kcache, const void* vcache, void* out,

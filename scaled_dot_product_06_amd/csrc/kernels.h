@@ -69,6 +69,7 @@ hipError_t launch_prefill(int elem, int D, int Dv, const PrefillShape& s, const 
                           hipStream_t stream, bool* ok);
 hipError_t launch_decode(int elem, int D, int Dv, const DecodeShape& s, const FwdArgs& a,
                          hipStream_t stream, bool* ok);
+hipError_t launch_prefill_f32_paged(int D, int Dv, const FwdArgs& a, hipStream_t stream, bool* ok);
 hipError_t launch_decode_paged(int elem, int D, int Dv, const DecodeShape& s, const FwdArgs& a,
                                hipStream_t stream, bool* ok);
 hipError_t launch_paged_write(void* cache, const void* rows, const int32_t* slots, int64_t n, int64_t blocks,

@@ -28,4 +28,24 @@ hipError_t launch_prefill_f32(int D, int Dv, const PrefillShape& s, const FwdArg
   return hipSuccess;
 }
 
+template <int D, int DV>
+static hipError_t launch_paged_one(const FwdArgs& a, hipStream_t stream) {
+  constexpr int MF = prefill_mf(kF32, D, DV);
+  constexpr int BN = prefill_bn(kF32, D, DV, kMaskNone);
+  dim3 grid(a.head_blocks * a.nqb, 1, 1);
+  hipLaunchKernelGGL((prefill_f32_kernel<MF, D, DV, BN, kPrefillWaves, false, true>), grid,
+                     dim3(kPrefillWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_f32_paged(int D, int Dv, const FwdArgs& a, hipStream_t stream, bool* ok) {
+  *ok = true;
+#define SDPA_PAIR(d, dv) \
+  if (D == d && Dv == dv) return launch_paged_one<d, dv>(a, stream);
+  SDPA_HEAD_PAIRS(SDPA_PAIR)
+#undef SDPA_PAIR
+  *ok = false;
+  return hipSuccess;
+}
+
 }  // namespace sdpa

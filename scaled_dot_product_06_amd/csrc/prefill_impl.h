@@ -355,7 +355,12 @@ struct PrefillCfgF32 {
   static_assert(D % KWF == 0 && BN % MF == 0, "shape");
 };
 
-template <int MF, int D, int DV, int BN, int NW, bool ADD>
+// PAGED: K and V are paged caches ([blocks, Hkv, bs, D/Dv]); batch item b has
+// lengths[b] keys (clamped to [0, max_blocks * bs]), key j in row j % bs of
+// block table[b][j / bs] (clamped to [0, blocks - 1]); the causal mask and the
+// window are aligned to that length (nuvec-core "tests/fast.rs",
+// paged_attention_equals_contiguous_attention and its f32 cases).
+template <int MF, int D, int DV, int BN, int NW, bool ADD, bool PAGED = false>
 __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
   using C = PrefillCfgF32<MF, D, DV, BN, NW>;
   using acc_t = typename Mfma<MF>::acc_t;
@@ -382,12 +387,15 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
   const int h = h0 + w / wph;
   const int wi0 = qb * bm + (w % wph) * MF;
   const int iq = wi0 + col;
-  const int shift = a.Lk - a.Lq;
+  // the keys this batch item holds: all Lk, or the sequence's clamped length
+  int Lk = a.Lk;
+  if constexpr (PAGED) Lk = min(max(a.lengths[b], 0), a.max_blocks * a.bs);
+  const int shift = Lk - a.Lq;
 
   // keys the workgroup needs: up to its last row's causal limit and, with a
   // sliding window, from its first row's window start (tiles tb .. tb+ntiles-1)
-  int kend = a.Lk;
-  if (a.mask_kind == kMaskCausal) kend = min(a.Lk, min(qb * bm + bm, a.Lq) - 1 + shift + 1);
+  int kend = Lk;
+  if (a.mask_kind == kMaskCausal) kend = min(Lk, min(qb * bm + bm, a.Lq) - 1 + shift + 1);
   if (kend < 0) kend = 0;
   int kbeg = 0;
   if (a.window > 0) kbeg = min(max(0, qb * bm + shift - a.window + 1), kend);
@@ -396,10 +404,10 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
 
   const bool wave_live = wi0 < a.Lq;
   const int w_last = min(wi0 + MF, a.Lq) - 1;
-  int w_kend = a.Lk, w_kfull = a.Lk;
+  int w_kend = Lk, w_kfull = Lk;
   if (a.mask_kind == kMaskCausal) {
-    w_kend = min(a.Lk, w_last + shift + 1);
-    w_kfull = min(a.Lk, wi0 + shift + 1);
+    w_kend = min(Lk, w_last + shift + 1);
+    w_kfull = min(Lk, wi0 + shift + 1);
   } else if (ADD || a.mask_kind == kMaskBool) {
     w_kfull = 0;
   }
@@ -437,9 +445,15 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
     m = sink2;
   }
 
-  const float* kp = (const float*)a.k + b * a.ks[0] + hkv * a.ks[1];
-  const float* vp = (const float*)a.v + b * a.vs[0] + hkv * a.vs[1];
+  const float* kp = (const float*)a.k + (PAGED ? 0 : b * a.ks[0] + hkv * a.ks[1]);
+  const float* vp = (const float*)a.v + (PAGED ? 0 : b * a.vs[0] + hkv * a.vs[1]);
   const int64_t ksl = a.ks[2], vsl = a.vs[2];
+  // paged: cache row of key `key` through the (clamped) block table
+  const int32_t* trow = PAGED ? a.table + (size_t)b * a.max_blocks : nullptr;
+  auto cache_row = [&](int key) -> int64_t {
+    const int blk = min(max(trow[key / a.bs], 0), a.blocks - 1);
+    return ((int64_t)blk * a.Hkv + hkv) * a.bs + key % a.bs;
+  };
   const void* arow = nullptr;
   if constexpr (ADD)
     arow = (const float*)a.amask + b * a.ms[0] + h * a.ms[1] + (int64_t)min(iq, a.Lq - 1) * a.ms[2];
@@ -466,7 +480,11 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
       if (C::KCH % C::NT == 0 || c < C::KCH) {
         const int r = c / (D / 4), cc = c % (D / 4);
         const int key = k0 + r;
-        kr[it] = key < a.Lk ? ld_global16(kp + key * ksl + cc * 4) : u32x4{0u, 0u, 0u, 0u};
+        // paged: keys before the workgroup's first visible key are not read (a
+        // cache may hold anything there, e.g. blocks wholly before a window)
+        const bool live = key < Lk && (!PAGED || key >= kbeg);
+        const int64_t off = PAGED ? (live ? cache_row(key) * D : 0) : key * ksl;
+        kr[it] = live ? ld_global16(kp + off + cc * 4) : u32x4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
@@ -475,7 +493,9 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
       if (C::VCH % C::NT == 0 || c < C::VCH) {
         const int r = c / (DV / 4), cc = c % (DV / 4);
         const int key = k0 + r;
-        vr[it] = key < a.Lk ? ld_global16(vp + key * vsl + cc * 4) : u32x4{0u, 0u, 0u, 0u};
+        const bool live = key < Lk && (!PAGED || key >= kbeg);
+        const int64_t off = PAGED ? (live ? cache_row(key) * DV : 0) : key * vsl;
+        vr[it] = live ? ld_global16(vp + off + cc * 4) : u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -536,7 +556,7 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
           s[nb][i] = iq < a.Lq ? fmaf(s[nb][i], a.c, mcu[nb * (ACC / 4) + i / 4][i % 4]) : -INFINITY;
         } else if (!full) {
           const int key = k0 + nb * MF + acc_row<MF>(i, kg);
-          bool vis = key < a.Lk && iq < a.Lq;
+          bool vis = key < Lk && iq < a.Lq;
           if (a.mask_kind == kMaskCausal)
             vis = vis && key <= iq + shift && (a.window <= 0 || key > iq + shift - a.window);
           else if (a.mask_kind == kMaskBool) vis = vis && mrow[key] != 0;

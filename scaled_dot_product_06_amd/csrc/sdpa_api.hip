@@ -559,9 +559,8 @@ int validate_and_plan_paged(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int6
   if (!mul4(blocks, Hkv, bs, D > Dv ? D : Dv, &n) || __builtin_mul_overflow(n, es, &n))
     return fail(SDPA_ERR_INVALID, "shape overflow: cache bytes do not fit in 64 bits");
   if (!mul3(B, max_blocks, 4, &n)) return fail(SDPA_ERR_INVALID, "shape overflow: table bytes do not fit in 64 bits");
-  if (dtype == SDPA_F32)
-    return fail(SDPA_ERR_UNSUPPORTED, "paged attention is built for SDPA_F16 and SDPA_BF16 only");
-  if (p.route == SDPA_ROUTE_EMPTY) {
+  if (p.route == SDPA_ROUTE_EMPTY || dtype == SDPA_F32) {
+    // f32: the f32 prefill kernel over the capacity's key range, any Lq
     *plan = p;
     return SDPA_OK;
   }
@@ -652,19 +651,29 @@ int sdpa_paged_forward(const void* q, const void* kcache, const void* vcache, vo
   a.bs = (int)bs;
   a.max_blocks = (int)max_blocks;
   a.c = fmaxf(fabsf(scale) * 1.4426950408889634f, FLT_MIN);
-  a.qsign = scale < 0.0f ? 0x80008000u : 0u;
-  a.rows = (int)(a.group * Lq);
-  a.kps = (int)p.keys_per_split;
-  a.nsplit = (int)p.splits;
+  a.qsign = scale < 0.0f ? (dtype == SDPA_F32 ? 0x80000000u : 0x80008000u) : 0u;
   a.qs[0] = Hq * Lq * D;
   a.qs[1] = Lq * D;
   a.qs[2] = D;
+  bool ok = false;
+  hipError_t e;
+  if (p.route == SDPA_ROUTE_PREFILL) {
+    a.head_blocks = (int)(B * Hq / p.heads_per_group);
+    a.nqb = (int)(p.grid[0] / a.head_blocks);
+    e = launch_prefill_f32_paged((int)D, (int)Dv, a, stream, &ok);
+    if (!ok) return fail(SDPA_ERR_UNSUPPORTED, "no kernel built for dtype %d, D=%lld, Dv=%lld", dtype, (long long)D,
+                         (long long)Dv);
+    if (e != hipSuccess) return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return SDPA_OK;
+  }
+  a.rows = (int)(a.group * Lq);
+  a.kps = (int)p.keys_per_split;
+  a.nsplit = (int)p.splits;
   void* part = nullptr;
-  hipError_t e = get_scratch(stream, (size_t)p.scratch_bytes, &part);
+  e = get_scratch(stream, (size_t)p.scratch_bytes, &part);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "decode scratch allocation failed: %s", hipGetErrorString(e));
   a.part = (float*)part;
   DecodeShape s{p.rows_per_wave, p.waves, p.block_n};
-  bool ok = false;
   e = launch_decode_paged(dtype, (int)D, (int)Dv, s, a, stream, &ok);
   if (!ok) return fail(SDPA_ERR_UNSUPPORTED, "no kernel built for dtype %d, D=%lld, Dv=%lld", dtype, (long long)D,
                        (long long)Dv);

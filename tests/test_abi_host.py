@@ -225,7 +225,6 @@ def test_paged_window_plans_follow_the_window():
     (dict(bs=0), -1, "bs"),
     (dict(max_blocks=0), -1, "max_blocks"),
     (dict(Hq=4, Hkv=3), -1, "multiple"),
-    (dict(dtype=0), -2, "F16"),
     (dict(dtype=7), -1, "dtype"),
     (dict(Lq=9), -2, "decode"),
     (dict(Hq=66, Hkv=2, Lq=1), -2, "decode"),
@@ -319,3 +318,11 @@ def test_contiguous_call_refuses_an_additive_mask():
     f = sd.sdpa_forward
     assert f(16, 16, 16, 16, 1, 2, 2, 4, 4, 64, 64, 0.1, 3, 16, None, 2, None, check=False) == -1
     assert "sdpa_forward_strided" in sd.sdpa_last_error()
+
+
+def test_f32_paged_plans_are_prefill_plans():
+    # f32 paged calls run the f32 tiled kernel over the capacity's keys, for any Lq
+    for Lq in (1, 4, 9, 300):
+        p = _plan_paged(Lq=Lq, dtype=0)
+        assert p["route"] == "prefill" and p["scratch_bytes"] == 0
+        assert p == sd.sdpa_plan(2, 8, 2, Lq, 20 * 16, 128, 128, 1, False, False, 0)

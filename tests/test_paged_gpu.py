@@ -91,7 +91,7 @@ def _assert_close(got, want, dtype, what):
     assert bad == 0, f"{what}: {bad} elements outside tolerance {TOL[dtype]}"
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("case", CASES, ids=_ids)
 def test_paged_equals_the_oracle(case, dtype):
     B, Hq, Hkv, Lq, D, bs, lengths, w = case
@@ -110,27 +110,30 @@ def test_paged_value_head_differs(D, Dv):
     _assert_close(pc.run(), pc.oracle(), BF16, f"D={D} Dv={Dv}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("case", [c for c in CASES if max(c[6]) < 8192], ids=_ids)
-def test_paged_equals_contiguous_bit_for_bit(case):
-    # below 8,192 keys of capacity both calls split the keys into the same 64-key
-    # partitions, so the paged result is the contiguous one, bit for bit, per sequence
+def test_paged_equals_contiguous_bit_for_bit(case, dtype):
+    # 16-bit: below 8,192 keys of capacity both calls split the keys into the same
+    # 64-key partitions; f32: both run the f32 tiled kernel over the same key tiles.
+    # Either way the paged result is the contiguous one, bit for bit, per sequence.
     import torch
     from scaled_dot_product_06_amd import attention
     B, Hq, Hkv, Lq, D, bs, lengths, w = case
-    pc = Paged(41 + sum(lengths), B, Hq, Hkv, Lq, D, D, bs, lengths, w, BF16, True)
+    dt = DT[dtype]
+    pc = Paged(41 + sum(lengths), B, Hq, Hkv, Lq, D, D, bs, lengths, w, dt, True)
     got = pc.run()
     p = pc.p
     for s, ln in enumerate(lengths):
-        q = to_device(p.q[s:s + 1], BF16)
-        k = to_device(np.ascontiguousarray(p.k[s:s + 1, :, :ln]), BF16)
-        v = to_device(np.ascontiguousarray(p.v[s:s + 1, :, :ln]), BF16)
-        o = attention(q, k, v, p.scale, 1, None, to_device(p.sinks, BF16), window=w or None)
+        q = to_device(p.q[s:s + 1], dt)
+        k = to_device(np.ascontiguousarray(p.k[s:s + 1, :, :ln]), dt)
+        v = to_device(np.ascontiguousarray(p.v[s:s + 1, :, :ln]), dt)
+        o = attention(q, k, v, p.scale, 1, None, to_device(p.sinks, dt), window=w or None)
         torch.cuda.synchronize()
-        want = from_device(o, BF16)
+        want = from_device(o, dt)
         assert np.array_equal(got[s:s + 1], want), f"sequence {s} (length {ln})"
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("B,Hq,Hkv,Lq,D,bs,max_blocks", [(2, 4, 2, 1, 64, 8, 4), (2, 4, 2, 3, 128, 16, 3),
                                                         (2, 8, 2, 1, 128, 32, 64)])
 def test_hostile_tables_and_lengths_are_clamped(B, Hq, Hkv, Lq, D, bs, max_blocks, dtype):
@@ -218,3 +221,11 @@ def test_paged_write_many_rows_and_wide_heads():
     slots = gen.block_order(73, blocks * bs)[:n]
     got, guards = _write_on_gpu(cache, rows, slots, BF16)
     assert guards and np.array_equal(got, pgd.paged_write(cache, rows, slots))
+
+
+def test_f32_paged_prefill_many_queries():
+    # f32 paged calls take any number of query rows (the tiled kernel)
+    pc = Paged(91, 2, 4, 2, 70, 64, 64, 16, (100, 333), 0, F32, True)
+    _assert_close(pc.run(), pc.oracle(), F32, "f32 paged, 70 queries")
+    pc = Paged(92, 1, 8, 2, 40, 128, 128, 8, (500,), 64, F32, False)
+    _assert_close(pc.run(), pc.oracle(), F32, "f32 paged, 40 queries, window 64")

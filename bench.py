@@ -58,9 +58,17 @@ def decode_bytes(p, window: int = 0) -> int:
     return p.B * p.Hkv * keys * (p.D + p.Dv) * esize
 
 
+# The sources that define each profiled kernel (its code, its argument block and
+# the device helpers it uses); a change to any of them voids its stored traffic.
+KERNEL_SOURCES = {
+    "prefill": ("attn_device.h", "kernels.h", "prefill_fast.h"),
+    "decode": ("attn_device.h", "kernels.h", "decode_impl.h", "decode.hip"),
+}
+
+
 def _traffic_for(kernel_tag: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources (else None)."""
+    taken on the kernel's current sources (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -68,15 +76,15 @@ def _traffic_for(kernel_tag: str):
         rec = json.load(open(path)).get(kernel_tag)
     except Exception:
         return None
-    if not rec or rec.get("source_sha256") != kernel_source_hash():
+    if not rec or rec.get("source_sha256") != kernel_source_hash(kernel_tag):
         return None
     return rec.get("bytes_per_launch")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel_tag: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "scaled_dot_product_06_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[kernel_tag]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()

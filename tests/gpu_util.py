@@ -88,9 +88,8 @@ def sample_rows(p: gen.Problem, n: int, seed: int = 0):
     rows = set()
     for b in {0, p.B - 1}:
         for h in {0, p.Hq - 1, p.Hq // 2}:
-            for i in {0, 1, p.Lq - 1, p.Lq // 2, min(p.Lq - 1, 31), min(p.Lq - 1, 32),
-                      min(p.Lq - 1, 127), min(p.Lq - 1, 128)}:
-                rows.add((b, h, i))
+            for i in {0, 1, p.Lq - 1, p.Lq // 2, 31, 32, 127, 128}:
+                rows.add((b, h, min(i, p.Lq - 1)))
     while len(rows) < n:
         rows.add((int(rng.integers(p.B)), int(rng.integers(p.Hq)), int(rng.integers(p.Lq))))
     return sorted(rows)

@@ -284,6 +284,35 @@ def test_largest_heads_long_keys():
         _full_check(p, f"D=512 Lq={Lq} Lk={Lk}")
 
 
+@pytest.mark.parametrize("Lk,D,mask_kind", [(262145, 128, 0), (300001, 64, 1), (1 << 20, 64, 0)])
+def test_decode_more_splits_than_one_reduce_chunk(Lk, D, mask_kind):
+    # 1024-key splits: 257, 293 and 1024 of them, so the reduce walks its splits in
+    # several chunks of 256 (and the last split holds one key in the first case)
+    p = gen.make_problem(600 + Lk % 97, 1, 8, 1, 1, Lk, D, D, BF16, mask_kind, sinks=True)
+    plan = __import__("scaled_dot_product_06_amd").sdpa_plan(*p.shape_args(), mask_kind, False, True, BF16)
+    assert plan["route"] == "decode" and plan["splits"] > 256
+    _full_check(p, f"decode Lk={Lk} splits={plan['splits']}")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Lk", [(1000, 4, 2, 70), (65535, 2, 1, 5)])
+def test_decode_large_batch(B, Hq, Hkv, Lk):
+    # the decode grid's z dimension is the batch; 65,535 is its limit
+    p = gen.make_problem(700 + B % 13, B, Hq, Hkv, 1, Lk, 64, 64, F16, 1, dist="uniform")
+    got = from_device(run_gpu(p), p.dtype)
+    rows = sample_rows(p, 300, seed=B)
+    want = oracle_rows(p, rows)
+    assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want, f"decode B={B}, sampled rows")
+
+
+def test_long_prefill_sampled_rows():
+    # 16,384 x 16,384 causal, one head pair: positions well past 2^13 in every index
+    p = gen.make_problem(801, 1, 2, 1, 16384, 16384, 64, 64, BF16, 1)
+    got = from_device(run_gpu(p), p.dtype)
+    rows = sample_rows(p, 200, seed=801)
+    want = oracle_rows(p, rows)
+    assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want, "prefill 16k x 16k, sampled rows")
+
+
 # --- properties -------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("Lq,Lk,dtype", [(1, 3000, BF16), (4, 777, F16), (150, 300, BF16), (60, 60, F32)])

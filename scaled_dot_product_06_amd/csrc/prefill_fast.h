@@ -204,6 +204,30 @@ prefill_fast_kernel(FwdArgs a) {
   const int tr_chunk = ((lane >> 4) & 1) * 2 + (tr_c >> 1);  // chunk within a 32-column block
   const int tr_half = (tr_c & 1) * 8;
 
+  // per-lane byte offsets of the K and V^T operands within a stage, fixed for the
+  // whole walk: each LDS read is then one lane register plus the stage's
+  // constant offset (folded into the instruction), with no address arithmetic
+  uint32_t ko[C::NQC][C::NSB];
+#pragma unroll
+  for (int c = 0; c < C::NQC; ++c)
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb) {
+      const int row = nb * MF + col;
+      ko[c][nb] = row * C::RB + (((2 * c + kg) ^ swz_k<D>(row)) * 16);
+    }
+  uint32_t vo[C::NPV][C::NDB][2];
+#pragma unroll
+  for (int t8 = 0; t8 < C::NPV; ++t8) {
+    const int keyA = ((8 * t8) / ACC) * MF + acc_row<MF>((8 * t8) % ACC, kg) + tr_e;
+    const int keyB = ((8 * t8 + 4) / ACC) * MF + acc_row<MF>((8 * t8 + 4) % ACC, kg) + tr_e;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int ch = db * 4 + tr_chunk;
+      vo[t8][db][0] = C::TILE_BYTES + keyA * C::RB + tr_half + ((ch ^ swz_v<D>(keyA)) * 16);
+      vo[t8][db][1] = C::TILE_BYTES + keyB * C::RB + tr_half + ((ch ^ swz_v<D>(keyB)) * 16);
+    }
+  }
+
   // S^T = K Q^T for one tile into s (zeroed here)
   auto qk = [&](const uint8_t* Ks, acc_t (&s)[QB][C::NSB]) {
 #pragma unroll
@@ -214,9 +238,7 @@ prefill_fast_kernel(FwdArgs a) {
     for (int c = 0; c < C::NQC; ++c)
 #pragma unroll
       for (int nb = 0; nb < C::NSB; ++nb) {
-        const int row = nb * MF + col;
-        const u32x4 kop =
-            *reinterpret_cast<const u32x4*>(Ks + row * C::RB + (((2 * c + kg) ^ swz_k<D>(row)) * 16));
+        const u32x4 kop = *reinterpret_cast<const u32x4*>(Ks + ko[c][nb]);
 #pragma unroll
         for (int r = 0; r < QB; ++r) s[r][nb] = mma16<E, MF>(kop, qop[r][c], s[r][nb]);
       }
@@ -296,20 +318,14 @@ prefill_fast_kernel(FwdArgs a) {
     }
   };
 
-  // O^T += V^T P^T for one tile
-  auto pv = [&](const uint8_t* Vs, const uint32_t (&pk)[QB][C::NPK]) {
+  // O^T += V^T P^T for one tile (St: the tile's stage; V follows K in it)
+  auto pv = [&](const uint8_t* St, const uint32_t (&pk)[QB][C::NPK]) {
 #pragma unroll
     for (int t8 = 0; t8 < C::NPV; ++t8) {
-      const int keyA = ((8 * t8) / ACC) * MF + acc_row<MF>((8 * t8) % ACC, kg) + tr_e;
-      const int keyB = ((8 * t8 + 4) / ACC) * MF + acc_row<MF>((8 * t8 + 4) % ACC, kg) + tr_e;
-      const uint8_t* vA = Vs + keyA * C::RB + tr_half;
-      const uint8_t* vB = Vs + keyB * C::RB + tr_half;
-      const int swA = swz_v<D>(keyA), swB = swz_v<D>(keyB);
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
-        const int ch = db * 4 + tr_chunk;
-        const u32x2 ra = lds_read_tr16((const uint16_t*)(vA + ((ch ^ swA) * 16)));
-        const u32x2 rb = lds_read_tr16((const uint16_t*)(vB + ((ch ^ swB) * 16)));
+        const u32x2 ra = lds_read_tr16((const uint16_t*)(St + vo[t8][db][0]));
+        const u32x2 rb = lds_read_tr16((const uint16_t*)(St + vo[t8][db][1]));
         const u32x4 va = {ra[0], ra[1], rb[0], rb[1]};
 #pragma unroll
         for (int r = 0; r < QB; ++r) {
@@ -352,7 +368,7 @@ prefill_fast_kernel(FwdArgs a) {
     for (int r = 0; r < QB; ++r) softmax_rebase<C::NDB>(tmax[r], m[r], l[r], o[r]);
     qk(Snext, snext);
     weights(scur, pk);
-    pv(Scur + C::TILE_BYTES, pk);
+    pv(Scur, pk);
     tile_max_full(snext);
   };
 

@@ -1,0 +1,86 @@
+"""The library's calls inside a captured HIP graph (torch.cuda.CUDAGraph): each
+route is captured once, after an eager call on the capture stream has sized the
+stream's scratch (so the capture allocates nothing), then replayed several
+times with eager work on the output in between; every replay must give the
+eager call's bits. The library enqueues no memset nodes (zeros come from a
+fill kernel), so replays after the first see the same work."""
+import numpy as np
+import pytest
+
+import scaled_dot_product_06_amd as sd
+from scaled_dot_product_06_amd import inputs as gen
+from tests.gpu_util import to_device
+
+pytestmark = pytest.mark.gpu
+
+F32, F16, BF16 = gen.F32, gen.F16, gen.BF16
+
+
+def _call(kind, B, Hq, Hkv, Lq, Lk, D, dtype):
+    """(name, call(out, stream), out shape): one call of each route."""
+    import torch
+    mask_kind = {"window": 1, "paged": 1, "views": 1, "additive": 0}.get(kind, kind)
+    p = gen.make_problem(9000 + Lq + Lk, B, Hq, Hkv, Lq, Lk, D, D, dtype, mask_kind, sinks=True)
+    q, k, v = (to_device(a, dtype) for a in (p.q, p.k, p.v))
+    s = to_device(p.sinks, dtype)
+    mask = None if p.mask is None else torch.from_numpy(p.mask).cuda()
+    if kind == "window":
+        return lambda out, st: sd.attention(q, k, v, p.scale, 1, None, s, out=out, stream=st, window=33)
+    if kind == "additive":
+        add = to_device(gen.additive_mask(9, (1, Hq, Lq, Lk), dtype, 0.1), dtype)
+        return lambda out, st: sd.attention(q, k, v, p.scale, 3, add, s, out=out, stream=st)
+    if kind == "views":
+        kt = to_device(np.ascontiguousarray(p.k.transpose(0, 2, 1, 3)), dtype).transpose(1, 2)
+        return lambda out, st: sd.attention(q, kt, v, p.scale, 1, None, s, out=out, stream=st)
+    if kind == "paged":
+        bs = 16
+        per = -(-Lk // bs)
+        blocks = B * per + 3
+        order = gen.block_order(3, blocks)
+        kc, table = gen.paged_cache(p.k, bs, order, blocks)
+        vc, _ = gen.paged_cache(p.v, bs, order, blocks)
+        dk, dv = to_device(kc, dtype), to_device(vc, dtype)
+        dt = torch.from_numpy(table).cuda()
+        dl = torch.full((B,), Lk, dtype=torch.int32, device="cuda")
+        return lambda out, st: sd.paged_attention(q, dk, dv, dt, dl, p.scale, 1, 0, s, out=out, stream=st)
+    return lambda out, st: sd.attention(q, k, v, p.scale, mask_kind, mask, s, out=out, stream=st)
+
+
+CASES = [
+    (1, 2, 8, 2, 300, 300, 128, BF16),      # pipelined prefill
+    (2, 1, 8, 2, 100, 257, 256, F16),       # mask packing + generic prefill (two kernels, scratch)
+    (1, 1, 4, 2, 40, 70, 64, F32),          # f32 prefill
+    (0, 2, 16, 2, 1, 9000, 256, BF16),      # decode split + reduce (scratch)
+    (1, 1, 8, 2, 5, 0, 128, BF16),          # no keys: the fill kernel
+    ("window", 1, 8, 2, 3, 2000, 128, BF16),
+    ("additive", 1, 8, 2, 70, 257, 128, BF16),
+    ("views", 1, 8, 2, 64, 200, 128, F16),
+    ("paged", 2, 8, 2, 1, 3000, 128, BF16),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_graph_replays_equal_the_eager_call(case):
+    import torch
+    kind, B, Hq, Hkv, Lq, Lk, D, dtype = case
+    call = _call(kind, B, Hq, Hkv, Lq, Lk, D, dtype)
+    tdt = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}[dtype]
+    stream = torch.cuda.Stream()
+    want = torch.empty((B, Hq, Lq, D), dtype=tdt, device="cuda")
+    with torch.cuda.stream(stream):
+        call(want, stream.cuda_stream)          # sizes this stream's scratch
+    torch.cuda.synchronize()
+    out = torch.full_like(want, float("nan"))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        call(out, stream.cuda_stream)
+    torch.cuda.synchronize()
+    bits = torch.int32 if dtype == F32 else torch.int16
+    for replay in range(4):
+        out.fill_(float("nan"))                 # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(bits), want.view(bits)), f"replay {replay}"
+    del graph
+    torch.cuda.synchronize()

@@ -264,6 +264,44 @@ def test_scale_values(dtype, scale):
         _full_check(p, f"scale={scale} Lq={Lq}")
 
 
+@pytest.mark.parametrize("scale", [-0.7, 0.0])
+@pytest.mark.parametrize("route", ["fast-f16", "fast-bf16", "generic-256", "decode-f16", "window", "additive",
+                                   "paged", "paged-f32"])
+def test_negative_and_zero_scale_on_every_path(route, scale):
+    # q's sign is flipped in the kernels (scores use |scale|); zero scale gives the mean
+    # of the visible rows
+    import torch
+    from scaled_dot_product_06_amd import attention, paged_attention
+    dt = {"fast-f16": F16, "decode-f16": F16, "paged-f32": F32}.get(route, BF16)
+    D = 256 if route == "generic-256" else 128
+    Lq = 1 if route.startswith(("decode", "paged")) else 70
+    p = gen.make_problem(4000 + len(route) + int(10 * scale), 2, 8, 2, Lq, 333, D, D, dt, 1, sinks=True,
+                         scale=scale)
+    qq, kk, vv, _, ss = p.widened()
+    q, k, v, _, sk = device_inputs(p)
+    if route == "window":
+        got = attention(q, k, v, scale, 1, None, sk, window=50)
+        want = orc.sdpa(qq, kk, vv, scale, 1, None, ss, window=50)
+    elif route == "additive":
+        add = gen.additive_mask(5, (1, 8, Lq, 333), dt, 0.1)
+        got = attention(q, k, v, scale, 3, to_device(add, dt), sk)
+        want = orc.sdpa(qq, kk, vv, scale, 3, gen.widen(add, dt), ss)
+    elif route.startswith("paged"):
+        from oracle import paged as pgd
+        bs, blocks = 16, 2 * 21 + 3
+        kc, table = gen.paged_cache(p.k, bs, gen.block_order(4, blocks), blocks)
+        vc, _ = gen.paged_cache(p.v, bs, gen.block_order(4, blocks), blocks)
+        lengths = np.array([333, 200], dtype=np.int32)
+        got = paged_attention(q, to_device(kc, dt), to_device(vc, dt), torch.from_numpy(table).cuda(),
+                              torch.from_numpy(lengths).cuda(), scale, 1, 0, sk)
+        want = pgd.paged_sdpa(qq, gen.widen(kc, dt), gen.widen(vc, dt), table, lengths, scale, 1, ss)
+    else:
+        got = attention(q, k, v, scale, 1, None, sk)
+        want = orc.sdpa(qq, kk, vv, scale, 1, None, ss)
+    torch.cuda.synchronize()
+    assert_parity(p, from_device(got, dt), want, f"{route} scale={scale}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_wide_score_range(dtype):
     """Scores spread over tens of units: the running maximum moves many times.

@@ -1,9 +1,12 @@
-"""The library's calls inside a captured HIP graph (torch.cuda.CUDAGraph): each
+"""Calls in captured graphs and on concurrent streams.
+
+The library's calls inside a captured HIP graph (torch.cuda.CUDAGraph): each
 route is captured once, after an eager call on the capture stream has sized the
 stream's scratch (so the capture allocates nothing), then replayed several
 times with eager work on the output in between; every replay must give the
 eager call's bits. The library enqueues no memset nodes (zeros come from a
-fill kernel), so replays after the first see the same work."""
+fill kernel), so replays after the first see the same work. And calls issued
+from several host threads, each on its own stream, at once."""
 import numpy as np
 import pytest
 
@@ -84,3 +87,47 @@ def test_graph_replays_equal_the_eager_call(case):
         assert torch.equal(out.view(bits), want.view(bits)), f"replay {replay}"
     del graph
     torch.cuda.synchronize()
+
+
+def test_concurrent_streams_and_threads():
+    """Decode and masked-prefill calls (both use scratch) issued from four host threads,
+    each on its own stream, with no synchronisation between them: the library keeps
+    one scratch buffer per (device, stream), so every result is the single-stream one."""
+    import threading
+
+    import torch
+    cases = [_call(0, 2, 16, 2, 1, 9000, 256, BF16), _call(2, 1, 8, 2, 100, 257, 256, F16),
+             _call("window", 1, 8, 2, 3, 2000, 128, BF16), _call("paged", 2, 8, 2, 1, 3000, 128, BF16)]
+    shapes = [(2, 16, 1, 256, torch.bfloat16), (1, 8, 100, 256, torch.float16), (1, 8, 3, 128, torch.bfloat16),
+              (2, 8, 1, 128, torch.bfloat16)]
+    wants = []
+    for call, (B, H, L, D, dt) in zip(cases, shapes):
+        w = torch.empty((B, H, L, D), dtype=dt, device="cuda")
+        call(w, torch.cuda.current_stream().cuda_stream)
+        wants.append(w)
+    torch.cuda.synchronize()
+    outs = [[torch.empty_like(w) for _ in range(8)] for w in wants]
+    errors = []
+
+    def worker(i):
+        try:
+            torch.cuda.set_device(0)
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for o in outs[i]:
+                    cases[i](o, st.cuda_stream)
+            st.synchronize()
+        except Exception as e:          # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for w, os_ in zip(wants, outs):
+        bits = torch.int16
+        for o in os_:
+            assert torch.equal(o.view(bits), w.view(bits))

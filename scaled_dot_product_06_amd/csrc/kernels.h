@@ -87,19 +87,26 @@ constexpr int kDecodeBN = 32;       // keys per decode tile
 // value columns per decode-reduce workgroup: 32 when they divide Dv, else 16
 constexpr int reduce_cols(int DV) { return DV % 32 == 0 ? 32 : 16; }
 constexpr int head_max(int D, int Dv) { return D > Dv ? D : Dv; }
-// 32x32 MFMA tiles (32 query rows per wavefront) up to 128-wide heads; 16x16
-// tiles above, where a 32-row output accumulator would not fit in registers.
-constexpr int prefill_mf(int elem, int D, int Dv) { return head_max(D, Dv) <= 128 ? 32 : 16; }
-// The 64/128-wide 16-bit prefill shapes run the pipelined direct-load kernel,
-// except with an additive mask (the generic kernel reads it).
-constexpr bool prefill_is_fast(int elem, int D, int Dv, int mask_kind) {
-  return elem != kF32 && D == Dv && (D == 64 || D == 128) && mask_kind != kMaskAdditive;
+// The 64/128/256-wide 16-bit prefill shapes can run the pipelined direct-load
+// kernel (32-row tiles, 32-key steps), except with an additive mask (the
+// generic kernel reads it).
+constexpr bool prefill_can_fast(int elem, int D, int Dv, int mask_kind) {
+  return elem != kF32 && D == Dv && (D == 64 || D == 128 || D == 256) && mask_kind != kMaskAdditive;
 }
-constexpr int prefill_bn(int elem, int D, int Dv, int mask_kind) {
-  return elem == kF32 ? (head_max(D, Dv) <= 128 ? 32 : 16)
-                      : (prefill_is_fast(elem, D, Dv, mask_kind) || head_max(D, Dv) > 256 ? 32 : 64);
+constexpr int kFastRows = 32, kFastBN = 32;
+// At 256-wide heads the pipelined kernel holds one wavefront per SIMD and one
+// workgroup per compute unit, so it runs only when its grid has at least this
+// many workgroups (MI355X's compute units); smaller calls keep the generic
+// kernel's 16-row tiles, which put twice as many wavefronts on the chip.
+constexpr int kFastMinGridWide = 256;
+constexpr bool prefill_fast_needs_grid(int D) { return D > 128; }
+// Generic kernel: 32x32 MFMA tiles (32 query rows per wavefront) up to
+// 128-wide heads; 16x16 tiles above, where a 32-row output accumulator would
+// leave too few registers for its staging.
+constexpr int prefill_generic_mf(int elem, int D, int Dv) { return head_max(D, Dv) <= 128 ? 32 : 16; }
+constexpr int prefill_generic_bn(int elem, int D, int Dv) {
+  return elem == kF32 ? (head_max(D, Dv) <= 128 ? 32 : 16) : (head_max(D, Dv) > 256 ? 32 : 64);
 }
-constexpr int prefill_rows(int elem, int D, int Dv) { return prefill_mf(elem, D, Dv); }
 constexpr int prefill_waves(int elem, int D, int Dv) { return kPrefillWaves; }
 // 16x16 tiles when the packed query rows fit (and the head is a whole number
 // of 32-wide k-steps), else 32x32.

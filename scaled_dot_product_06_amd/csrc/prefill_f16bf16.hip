@@ -7,24 +7,31 @@ namespace sdpa {
 template <class E, int D, int DV>
 static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_t stream) {
   constexpr int elem = std::is_same<E, ElemBF16>::value ? kBF16 : kF16;
-  constexpr int MF = prefill_mf(elem, D, DV);
+  constexpr int MF = prefill_generic_mf(elem, D, DV);
+  constexpr int BN = prefill_generic_bn(elem, D, DV);
   dim3 grid(a.head_blocks * a.nqb, 1, 1);
   if (a.mask_kind == kMaskAdditive) {
-    constexpr int BN = prefill_bn(elem, D, DV, kMaskAdditive);
     hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves, true>), grid, dim3(kPrefillWaves * 64), 0,
                        stream, a);
-  } else if constexpr (prefill_is_fast(elem, D, DV, kMaskNone)) {
+    return hipGetLastError();
+  }
+  if constexpr (prefill_can_fast(elem, D, DV, kMaskNone)) {
     using C = FastCfg<D>;
-    static_assert(MF == C::MF && prefill_bn(elem, D, DV, kMaskNone) == C::BN &&
-                      prefill_waves(elem, D, DV) == C::NW && prefill_rows(elem, D, DV) == C::ROWS,
+    static_assert(C::MF == kFastRows && C::ROWS == kFastRows && C::BN == kFastBN && C::NW == kPrefillWaves,
                   "planner geometry must match the kernel");
-    hipLaunchKernelGGL((prefill_fast_kernel<E, D>), grid, dim3(C::NW * 64), 0, stream, a);
-  } else {
-    constexpr int BN = prefill_bn(elem, D, DV, kMaskNone);
+    // the plan chose the pipelined kernel (32-row tiles) or, at 256-wide
+    // heads on a grid too small to fill the chip, the generic one
+    if (s.mf == C::MF && s.block_n == C::BN) {
+      hipLaunchKernelGGL((prefill_fast_kernel<E, D>), grid, dim3(C::NW * 64), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (!prefill_can_fast(elem, D, DV, kMaskNone) || prefill_fast_needs_grid(D)) {
     hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves, false>), grid, dim3(kPrefillWaves * 64), 0,
                        stream, a);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  return hipErrorInvalidConfiguration;
 }
 
 hipError_t launch_prefill_16(int elem, int D, int Dv, const PrefillShape& s, const FwdArgs& a,

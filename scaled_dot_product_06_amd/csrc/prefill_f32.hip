@@ -5,8 +5,8 @@ namespace sdpa {
 
 template <int D, int DV>
 static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_t stream) {
-  constexpr int MF = prefill_mf(kF32, D, DV);
-  constexpr int BN = prefill_bn(kF32, D, DV, kMaskNone);
+  constexpr int MF = prefill_generic_mf(kF32, D, DV);
+  constexpr int BN = prefill_generic_bn(kF32, D, DV);
   dim3 grid(a.head_blocks * a.nqb, 1, 1);
   if (a.mask_kind == kMaskAdditive)
     hipLaunchKernelGGL((prefill_f32_kernel<MF, D, DV, BN, kPrefillWaves, true>), grid, dim3(kPrefillWaves * 64), 0,
@@ -30,8 +30,8 @@ hipError_t launch_prefill_f32(int D, int Dv, const PrefillShape& s, const FwdArg
 
 template <int D, int DV>
 static hipError_t launch_paged_one(const FwdArgs& a, hipStream_t stream) {
-  constexpr int MF = prefill_mf(kF32, D, DV);
-  constexpr int BN = prefill_bn(kF32, D, DV, kMaskNone);
+  constexpr int MF = prefill_generic_mf(kF32, D, DV);
+  constexpr int BN = prefill_generic_bn(kF32, D, DV);
   dim3 grid(a.head_blocks * a.nqb, 1, 1);
   hipLaunchKernelGGL((prefill_f32_kernel<MF, D, DV, BN, kPrefillWaves, false, true>), grid,
                      dim3(kPrefillWaves * 64), 0, stream, a);

@@ -1,4 +1,4 @@
-// Prefill for 16-bit inputs with D = Dv in {64, 128}: the tiled online-softmax
+// Prefill for 16-bit inputs with D = Dv in {64, 128, 256}: the tiled online-softmax
 // walk of lattice-inference "src/attention/flash.rs" (run_tiled_attention_head)
 // with the bottom-right causal alignment of nuvec-core "tests/fast.rs"
 // (attention_fallback_matches_a_direct_formula), laid out for gfx950:
@@ -6,7 +6,9 @@
 //  * each wavefront owns one 32-row MFMA block of query rows and the
 //    workgroup's four wavefronts share every K/V tile (one head each under
 //    grouped queries); the register budget leaves room for two wavefronts
-//    per SIMD, which hide each other's latencies;
+//    per SIMD, which hide each other's latencies (at 256-wide heads the
+//    32-row output and query fragments take one wavefront's whole register
+//    file, and the software pipeline alone keeps the SIMD busy);
 //  * K and V tiles go from global memory straight into LDS
 //    (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16 * lane),
 //    four stages, three tiles ahead of the compute, one barrier per tile;
@@ -52,14 +54,19 @@ struct FastCfg {
   static constexpr int NPV = BN / KW;           // k-steps of PV
   static constexpr int NDB = D / MF;            // 32-column output blocks
   static constexpr int NPK = NSB * ACC / 2;     // packed weight pairs per query block
-  static_assert(D == 64 || D == 128, "fast prefill covers 64- and 128-wide heads");
+  static constexpr int WPE = D <= 128 ? 2 : 1;  // wavefronts per SIMD the registers allow
+  static_assert(D == 64 || D == 128 || D == 256, "fast prefill covers 64-, 128- and 256-wide heads");
   static_assert(LOADS % NW == 0, "loads divide among wavefronts");
 };
 
 // chunk permutations (XOR masks) for the K and V tiles
 template <int D> __device__ __forceinline__ int swz_k(int row) { return row % FastCfg<D>::CPR; }
+// (V: the row's place among the rows sharing one 256-byte line of banks;
+// rows of 256 bytes or more start on the same bank, so consecutive rows differ)
 template <int D> __device__ __forceinline__ int swz_v(int row) {
-  return 4 * ((row / (256 / FastCfg<D>::RB)) % (FastCfg<D>::CPR / 4));
+  constexpr int RPL = FastCfg<D>::RB >= 256 ? 1 : 256 / FastCfg<D>::RB;  // rows per 256-byte line
+  constexpr int NX = FastCfg<D>::CPR / 4 < 4 ? FastCfg<D>::CPR / 4 : 4;
+  return 4 * ((row / RPL) % NX);
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations
@@ -69,7 +76,7 @@ template <int D> __device__ __forceinline__ int swz_v(int row) {
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <class E, int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FastCfg<D>::WPE, FastCfg<D>::WPE)))
 prefill_fast_kernel(FwdArgs a) {
   using C = FastCfg<D>;
   constexpr int MF = C::MF, ACC = C::ACC, BN = C::BN, QB = C::QB;

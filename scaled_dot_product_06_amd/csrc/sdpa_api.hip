@@ -247,9 +247,16 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
     *plan = p;
     return SDPA_OK;
   }
-  const int rows = prefill_rows(dtype, (int)D, (int)Dv);
+  // pipelined kernel (32-row tiles) where it applies and, at 256-wide heads,
+  // where its grid fills the chip; else the generic kernel's geometry
   const int nw = prefill_waves(dtype, (int)D, (int)Dv);
   const int64_t heads = gcd64(group, nw);
+  bool fast = prefill_can_fast(dtype, (int)D, (int)Dv, mask_kind);
+  if (fast && prefill_fast_needs_grid((int)D)) {
+    const int64_t fbm = (nw / heads) * kFastRows;
+    fast = (B * Hq / heads) * ((Lq + fbm - 1) / fbm) >= kFastMinGridWide;
+  }
+  const int rows = fast ? kFastRows : prefill_generic_mf(dtype, (int)D, (int)Dv);
   const int64_t bm = (nw / heads) * rows;
   const int64_t nqb = (Lq + bm - 1) / bm;
   if ((B * Hq / heads) * nqb > INT_MAX)
@@ -259,7 +266,7 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
   p.kernels = 1;
   p.rows_per_wave = rows;
   p.waves = nw;
-  p.block_n = prefill_bn(dtype, (int)D, (int)Dv, mask_kind);
+  p.block_n = fast ? kFastBN : prefill_generic_bn(dtype, (int)D, (int)Dv);
   p.heads_per_group = (int32_t)heads;
   p.grid[0] = (B * Hq / heads) * nqb;   // one workgroup per (head block, query block)
   p.grid[1] = 1;

@@ -129,6 +129,43 @@ def test_prefill_bool_mask_word_edges(D, Lk):
             _full_check(p, f"bool mask {name} D={D} Lk={Lk}")
 
 
+# --- 256-wide heads on the pipelined kernel -------------------------------------------------
+# A grid of at least one workgroup per compute unit routes 256-wide 16-bit heads to the
+# pipelined 32-row kernel (smaller calls keep the generic 16-row one, as workload 4 does).
+# Ragged on both axes: 520 query rows (17 blocks of 32) over 1297 keys (40.5 tiles).
+
+WIDE = dict(B=2, Hq=32, Hkv=4, Lq=520, Lk=1297, D=256)
+
+
+@pytest.mark.parametrize("mask_kind,sinks", [(0, False), (1, False), (1, True), (2, True)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_wide_heads_pipelined_sampled_rows(mask_kind, sinks, dtype):
+    w = WIDE
+    p = gen.make_problem(1700 + 10 * mask_kind + sinks, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], w["D"],
+                         w["D"], DT[dtype], mask_kind, sinks=sinks)
+    say(f"wide pipelined: {p!r}")
+    got = from_device(run_gpu(p), p.dtype)
+    assert np.all(np.isfinite(got))
+    rows = sample_rows(p, 120, seed=17 + mask_kind)
+    want = oracle_rows(p, rows)
+    assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want,
+                  f"256-wide pipelined mask {mask_kind} sinks {sinks}, sampled rows")
+
+
+def test_wide_heads_pipelined_window_sampled_rows():
+    from scaled_dot_product_06_amd import attention
+    import torch
+    w = WIDE
+    p = gen.make_problem(1790, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], w["D"], w["D"], BF16, 1, sinks=True)
+    q, k, v, _, sinks = device_inputs(p)
+    got = from_device(attention(q, k, v, p.scale, 1, None, sinks, window=300), p.dtype)
+    torch.cuda.synchronize()
+    rows = sample_rows(p, 96, seed=23)
+    qq, kk, vv, _, ss = p.widened()
+    want = orc.sdpa(qq, kk, vv, p.scale, 1, None, ss, window=300, rows=rows)
+    assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want, "256-wide pipelined window 300")
+
+
 # --- sliding windows (nuvec-core tests/fast.rs, windowed-kernel tests) -------------------------
 
 # (Lq, Lk, D, Hq, Hkv, window): one-query decode over windows below the keys (short and long

@@ -192,6 +192,34 @@ def measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, 
     return res
 
 
+def measure_wide_workloads(torch, sd, gen, dev, to_dev, stream, log):
+    """The headline prefill shape at 256-wide heads (bf16, causal; seed 31), which
+    plans the pipelined 32-row kernel: per-call kernel time against the bf16
+    MFMA peak (reported)."""
+    p = gen.make_problem(31, 2, 32, 8, 4096, 4096, 256, 256, gen.BF16, 1,
+                         name="bf16 GQA causal prefill B2 H32/8 L4096x4096 D256")
+    q, k, v = (to_dev(a, p.dtype) for a in (p.q, p.k, p.v))
+    out = torch.empty((p.B, p.Hq, p.Lq, p.Dv), dtype=q.dtype, device=dev)
+    plan = sd.sdpa_plan(p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.D, p.Dv, 1, False, False, p.dtype)
+
+    def call():
+        sd.attention(q, k, v, p.scale, 1, out=out, stream=stream.cuda_stream)
+
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    us = _time_calls(torch, stream, call, calls=10, rounds=5)
+    flop = prefill_flop(p)
+    tf = flop / us / 1e6
+    log(f"{p.name}: {us:.1f} us/call {tf:.1f} TFLOP/s")
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return {"3d256": {"workload": p.name, "us_per_call": round(us, 2), "flop_per_call": flop,
+                      "TFLOP/s": round(tf, 2), "peak_TFLOP/s": PEAK_BF16_TFLOPS,
+                      "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4), "rows_per_wave": plan["rows_per_wave"],
+                      "block_n": plan["block_n"]}}
+
+
 # paged-cache decode on the long-context decode shape (reported): (workload, block size, window)
 PAGED_WORKLOADS = ((5, 16, 0), (5, 16, 4096))
 
@@ -317,7 +345,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip the reported-only workloads (f32 prefill, "
                     "8193-key decode, f16 masked prefill with sinks, sliding windows, paged decode, "
-                    "strided views, additive mask)")
+                    "strided views, additive mask, 256-wide prefill)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
@@ -404,6 +432,7 @@ def main() -> int:
         others = measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log)
         others.update(measure_paged_workloads(torch, sd, gen, dev, to_dev, stream, log))
         others.update(measure_strided_workloads(torch, sd, gen, dev, to_dev, stream, log))
+        others.update(measure_wide_workloads(torch, sd, gen, dev, to_dev, stream, log))
 
     pre_plan = sd.sdpa_plan(pre.B, pre.Hq, pre.Hkv, pre.Lq, pre.Lk, pre.D, pre.Dv, pre.mask_kind, False, False,
                             pre.dtype)

@@ -95,9 +95,11 @@ constexpr bool prefill_can_fast(int elem, int D, int Dv, int mask_kind) {
 }
 constexpr int kFastRows = 32, kFastBN = 32;
 // At 256-wide heads the pipelined kernel holds one wavefront per SIMD and one
-// workgroup per compute unit, so it runs only when its grid has at least this
-// many workgroups (MI355X's compute units); smaller calls keep the generic
-// kernel's 16-row tiles, which put twice as many wavefronts on the chip.
+// workgroup per compute unit, so it runs only when one batch item's grid has
+// at least this many workgroups (MI355X's compute units); smaller calls keep
+// the generic kernel's 16-row tiles, which put twice as many wavefronts on the
+// chip. The rule ignores the batch size, so a batch item takes the same kernel
+// (and gives the same bits) alone or within a batch.
 constexpr int kFastMinGridWide = 256;
 constexpr bool prefill_fast_needs_grid(int D) { return D > 128; }
 // Generic kernel: 32x32 MFMA tiles (32 query rows per wavefront) up to

@@ -248,13 +248,14 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
     return SDPA_OK;
   }
   // pipelined kernel (32-row tiles) where it applies and, at 256-wide heads,
-  // where its grid fills the chip; else the generic kernel's geometry
+  // where one batch item's grid fills the chip; else the generic kernel's
+  // geometry
   const int nw = prefill_waves(dtype, (int)D, (int)Dv);
   const int64_t heads = gcd64(group, nw);
   bool fast = prefill_can_fast(dtype, (int)D, (int)Dv, mask_kind);
   if (fast && prefill_fast_needs_grid((int)D)) {
     const int64_t fbm = (nw / heads) * kFastRows;
-    fast = (B * Hq / heads) * ((Lq + fbm - 1) / fbm) >= kFastMinGridWide;
+    fast = (Hq / heads) * ((Lq + fbm - 1) / fbm) >= kFastMinGridWide;
   }
   const int rows = fast ? kFastRows : prefill_generic_mf(dtype, (int)D, (int)Dv);
   const int64_t bm = (nw / heads) * rows;

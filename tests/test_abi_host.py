@@ -329,15 +329,19 @@ def test_f32_paged_plans_are_prefill_plans():
 
 
 def test_wide_heads_plan_the_pipelined_kernel_only_on_full_grids():
-    # 256-wide 16-bit heads take the pipelined 32-row kernel when its grid has a
-    # workgroup per compute unit (256), the generic 16-row kernel below that
-    big = sd.sdpa_plan(2, 32, 4, 520, 1297, 256, 256, 1, False, False, 2)
-    assert (big["rows_per_wave"], big["block_n"], big["grid"][0]) == (32, 32, 16 * 17)
-    edge = sd.sdpa_plan(1, 32, 4, 256, 300, 256, 256, 0, False, False, 1)   # 8 x 8 = 64 workgroups
-    assert (edge["rows_per_wave"], edge["block_n"]) == (16, 64)
+    # 256-wide 16-bit heads take the pipelined 32-row kernel when one batch item's grid
+    # has a workgroup per compute unit (256), the generic 16-row kernel below that; the
+    # batch size never changes the choice
+    big = sd.sdpa_plan(1, 32, 4, 1040, 1297, 256, 256, 1, False, False, 2)   # 8 x 33 = 264
+    assert (big["rows_per_wave"], big["block_n"], big["grid"][0]) == (32, 32, 8 * 33)
+    assert sd.sdpa_plan(3, 32, 4, 1040, 1297, 256, 256, 1, False, False, 2)["rows_per_wave"] == 32
+    edge = sd.sdpa_plan(1, 32, 4, 1000, 1297, 256, 256, 1, False, False, 2)  # 8 x 32 = 256
+    assert (edge["rows_per_wave"], edge["block_n"]) == (32, 32)
+    under = sd.sdpa_plan(1, 32, 4, 992, 1297, 256, 256, 1, False, False, 2)  # 8 x 31 = 248
+    assert (under["rows_per_wave"], under["block_n"]) == (16, 64)
     small = sd.sdpa_plan(1, 16, 2, 1024, 1801, 256, 256, 2, True, True, 1)  # workload 4: 4 x 32 = 128
     assert (small["rows_per_wave"], small["block_n"]) == (16, 64)
-    full = sd.sdpa_plan(2, 16, 2, 1024, 1801, 256, 256, 2, True, True, 1)   # 8 x 32 = 256
-    assert (full["rows_per_wave"], full["block_n"]) == (32, 32)
-    assert sd.sdpa_plan(4, 16, 2, 1024, 1801, 256, 256, 3, True, True, 1)["rows_per_wave"] == 16  # additive
-    assert sd.sdpa_plan(4, 16, 2, 1024, 1801, 192, 192, 1, False, False, 1)["rows_per_wave"] == 16
+    batched = sd.sdpa_plan(8, 16, 2, 1024, 1801, 256, 256, 2, True, True, 1)  # the same per batch item
+    assert (batched["rows_per_wave"], batched["block_n"]) == (16, 64)
+    assert sd.sdpa_plan(1, 64, 8, 1024, 1801, 256, 256, 3, True, True, 1)["rows_per_wave"] == 16  # additive
+    assert sd.sdpa_plan(1, 64, 8, 1024, 1801, 192, 192, 1, False, False, 1)["rows_per_wave"] == 16

@@ -130,11 +130,11 @@ def test_prefill_bool_mask_word_edges(D, Lk):
 
 
 # --- 256-wide heads on the pipelined kernel -------------------------------------------------
-# A grid of at least one workgroup per compute unit routes 256-wide 16-bit heads to the
-# pipelined 32-row kernel (smaller calls keep the generic 16-row one, as workload 4 does).
-# Ragged on both axes: 520 query rows (17 blocks of 32) over 1297 keys (40.5 tiles).
+# A batch item's grid of at least one workgroup per compute unit routes 256-wide 16-bit heads
+# to the pipelined 32-row kernel (smaller calls keep the generic 16-row one, as workload 4
+# does). Ragged on both axes: 1040 query rows (33 blocks of 32) over 1297 keys (40.5 tiles).
 
-WIDE = dict(B=2, Hq=32, Hkv=4, Lq=520, Lk=1297, D=256)
+WIDE = dict(B=2, Hq=32, Hkv=4, Lq=1040, Lk=1297, D=256)
 
 
 @pytest.mark.parametrize("mask_kind,sinks", [(0, False), (1, False), (1, True), (2, True)])
@@ -150,6 +150,19 @@ def test_wide_heads_pipelined_sampled_rows(mask_kind, sinks, dtype):
     want = oracle_rows(p, rows)
     assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want,
                   f"256-wide pipelined mask {mask_kind} sinks {sinks}, sampled rows")
+
+
+def test_wide_heads_pipelined_batch_items_equal_each_item_alone():
+    w = WIDE
+    p = gen.make_problem(1795, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], w["D"], w["D"], BF16, 1, sinks=True)
+    import scaled_dot_product_06_amd as sd
+    assert sd.sdpa_plan(*p.shape_args(), 1, False, True, BF16)["rows_per_wave"] == 32
+    whole = from_device(run_gpu(p), BF16)
+    for b in range(w["B"]):
+        pb = gen.Problem(1, w["Hq"], w["Hkv"], w["Lq"], w["Lk"], w["D"], w["D"], BF16, 1, p.scale, p.q[b:b + 1],
+                         p.k[b:b + 1], p.v[b:b + 1], None, p.sinks)
+        alone = from_device(run_gpu(pb), BF16)
+        assert np.array_equal(whole[b:b + 1], alone), f"batch item {b} differs"
 
 
 def test_wide_heads_pipelined_window_sampled_rows():

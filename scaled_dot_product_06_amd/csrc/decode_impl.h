@@ -151,8 +151,8 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
       const int c = tid + it * C::NT;
       if (C::KCH % C::NT == 0 || c < C::KCH) {
         const int rr = c / (D / 8), cc = c % (D / 8);
-        const int key = k0 + rr;
-        kr[it] = key < ke ? ld_global16_nt(kp + k_off(key) + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+        const int key = min(k0 + rr, ke - 1);  // rows past the split's end re-read its last key (weight 0)
+        kr[it] = ld_global16_nt(kp + k_off(key) + cc * 8);
       }
     }
 #pragma unroll
@@ -160,8 +160,8 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
       const int c = tid + it * C::NT;
       if (C::VCH % C::NT == 0 || c < C::VCH) {
         const int rr = c / (DV / 8), cc = c % (DV / 8);
-        const int key = k0 + rr;
-        vr[it] = key < ke ? ld_global16_nt(vp + v_off(key) + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+        const int key = min(k0 + rr, ke - 1);
+        vr[it] = ld_global16_nt(vp + v_off(key) + cc * 8);
       }
     }
   };
@@ -259,20 +259,43 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
     }
   };
 
-  if (ntiles > 0) load_tile(ks, kra, vra);
-  if (ntiles > 1) load_tile(ks + BN, krb, vrb);
-  for (int t = 0; t < ntiles; t += 2) {
-    __syncthreads();
-    store_tile(kra, vra);
-    __syncthreads();
-    if (t + 2 < ntiles) load_tile(ks + (t + 2) * BN, kra, vra);
-    compute(ks + t * BN);
-    if (t + 1 >= ntiles) break;
-    __syncthreads();
-    store_tile(krb, vrb);
-    __syncthreads();
-    if (t + 3 < ntiles) load_tile(ks + (t + 3) * BN, krb, vrb);
-    compute(ks + (t + 1) * BN);
+  // Every tile load is issued whatever the tile count (rows past the split's
+  // end re-read its last key), so the loads in flight come in the same order
+  // on every path: before a tile's registers go to LDS, exactly the other
+  // tile's loads may still be outstanding, and a counted wait leaves them in
+  // flight. Plain barriers: the fence of __syncthreads would drain them. The
+  // walk is unrolled by four tiles because the compiler's own wait at the
+  // loop's head still drains everything.
+  constexpr int LPT = C::KPT + C::VPT;  // loads per tile and thread
+  auto wait_tile = [&](bool other_in_flight) {
+    if (other_in_flight) {
+      __builtin_amdgcn_s_waitcnt((LPT & 15) | ((LPT >> 4) << 14) | (7 << 4) | (15 << 8));
+    } else {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    }
+  };
+  // one step: tile u's registers to LDS, tile u+2's loads into them, tile u computed
+  auto step = [&](int u, u32x4* kr, u32x4* vr) {
+    wait_tile(true);
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    store_tile(kr, vr);
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    load_tile(ks + (u + 2) * BN, kr, vr);
+    compute(ks + u * BN);
+  };
+  if (ntiles > 0) {
+    load_tile(ks, kra, vra);
+    load_tile(ks + BN, krb, vrb);
+    for (int t = 0; t < ntiles; t += 4) {
+      step(t, kra, vra);
+      if (t + 1 >= ntiles) break;
+      step(t + 1, krb, vrb);
+      if (t + 2 >= ntiles) break;
+      step(t + 2, kra, vra);
+      if (t + 3 >= ntiles) break;
+      step(t + 3, krb, vrb);
+    }
+    wait_tile(false);  // the loads issued past the last tile
   }
 
   const float lt = row_sum<MF>(l);

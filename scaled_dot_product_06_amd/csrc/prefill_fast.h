@@ -191,7 +191,10 @@ prefill_fast_kernel(FwdArgs a) {
     for (int it = 0; it < C::LOADS_PER_WAVE; ++it) {
       uint32_t ok = offk[it], ov = offv[it];
       if (tail) {
-        // rows past the end read the last real row instead; those keys get weight 0
+        // rows past the end read the last real row instead; those keys get
+        // weight 0. Tiles are issued only below the workgroup's kend <= Lk, so
+        // k0 <= Lk - 1 and the offset, (Lk - 1 - k0) rows plus the chunk,
+        // stays non-negative in this unsigned arithmetic.
         const uint32_t over = (uint32_t)max(k0 + ldrow[it] - (a.Lk - 1), 0);
         ok -= over * krs;
         ov -= over * vrs;

@@ -113,9 +113,20 @@ typedef struct sdpa_plan_t {
  * The call is asynchronous: validation errors return before anything is
  * enqueued; a launch failure returns SDPA_ERR_HIP. A given plan gives the
  * same bits run to run, and each batch item's bits do not depend on B.
- * Scratch (decode partials, packed mask bits) comes from a per-(device,
- * stream) buffer that the library allocates on first use, grows when a call
- * needs more, and keeps (sdpa_release_workspace frees).
+ * Scratch (decode partials, packed mask bits; sdpa_plan's scratch_bytes)
+ * comes from a per-(device, stream) buffer that the library allocates with
+ * hipMallocAsync on the stream's first call that needs it. A later call that
+ * needs more replaces it with a buffer at least twice as large; the replaced
+ * buffer is kept, not freed, until sdpa_release_workspace, so graphs captured
+ * earlier on the stream keep valid addresses.
+ * Graph capture: a call may be captured (hipStreamBeginCapture) once the
+ * stream's buffer is large enough; make one call of at least the plan's
+ * scratch_bytes on the same stream, outside the capture, first. A captured
+ * call that would need a larger buffer (or the stream's first buffer) returns
+ * SDPA_ERR_UNSUPPORTED and enqueues nothing. A captured graph keeps using the
+ * buffer of the stream it was captured on: replaying it while other calls on
+ * that stream's buffer run (on the stream, or other replays of graphs captured
+ * there, on any stream) races with them.
  */
 int sdpa_forward(const void* q, const void* k, const void* v, void* out,
                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
@@ -269,8 +280,10 @@ int sdpa_forward_strided(const sdpa_view_t* q, const sdpa_view_t* k, const sdpa_
  * stays valid until the thread's next sdpa_* call. */
 const char* sdpa_last_error(void);
 
-/* Wait for the streams that used cached scratch, then free it.
- * Returns SDPA_OK or SDPA_ERR_HIP. */
+/* Wait for the devices that used cached scratch (hipDeviceSynchronize), then
+ * free every buffer the library holds, replaced ones included. Graphs captured
+ * with that scratch must not be replayed afterwards. Returns SDPA_OK or
+ * SDPA_ERR_HIP. */
 int sdpa_release_workspace(void);
 
 /* ABI version of this header: 4 (2 added the windowed calls, 3 the paged ones,

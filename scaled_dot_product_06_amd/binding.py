@@ -231,6 +231,36 @@ def _view(name, t, shape):
     return (t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
 
 
+def _out_tensor(out, q, shape):
+    """`out` as given (checked: a contiguous GPU tensor of q's dtype and device and the
+    output shape, which the kernels overwrite whole) or a new one."""
+    import torch
+    if out is None:
+        return torch.empty(shape, dtype=q.dtype, device=q.device)
+    if not out.is_cuda or out.device != q.device:
+        raise SdpaError(SDPA_ERR_INVALID, f"out must be a GPU tensor on {q.device}")
+    if out.dtype != q.dtype:
+        raise SdpaError(SDPA_ERR_INVALID, f"out has dtype {out.dtype}, q has {q.dtype}")
+    if tuple(out.shape) != tuple(shape):
+        raise SdpaError(SDPA_ERR_INVALID, f"out has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    if not out.is_contiguous():
+        raise SdpaError(SDPA_ERR_INVALID, "out must be contiguous")
+    return out
+
+
+def _sinks_ptr(sinks, q, Hq):
+    """Device address of the [Hq] sinks, or None. The tensor must be contiguous: a
+    contiguous copy made here could be freed before the asynchronous kernels read it."""
+    if sinks is None:
+        return None
+    if tuple(sinks.shape) != (Hq,) or sinks.dtype != q.dtype or not sinks.is_cuda or sinks.device != q.device:
+        raise SdpaError(SDPA_ERR_INVALID, f"sinks must be a GPU tensor of shape ({Hq},) and dtype {q.dtype} on "
+                        f"{q.device}")
+    if not sinks.is_contiguous():
+        raise SdpaError(SDPA_ERR_INVALID, "sinks must be contiguous")
+    return sinks.data_ptr()
+
+
 def attention(q, k, v, scale: float, mask_kind: int = SDPA_MASK_NONE, mask=None, sinks=None, out=None,
               stream=None, window=None):
     """softmax(scale * q k^T + mask) v on the GPU.
@@ -253,12 +283,15 @@ def attention(q, k, v, scale: float, mask_kind: int = SDPA_MASK_NONE, mask=None,
             raise SdpaError(SDPA_ERR_INVALID, f"{name} must be a GPU tensor")
         if t.dtype != q.dtype:
             raise SdpaError(SDPA_ERR_INVALID, f"{name} has dtype {t.dtype}, q has {q.dtype}")
+        if t.device != q.device:
+            raise SdpaError(SDPA_ERR_INVALID, f"{name} is on {t.device}, q on {q.device}")
     if tuple(k.shape) != (B, Hkv, Lk, D) or tuple(v.shape[:3]) != (B, Hkv, Lk):
         raise SdpaError(SDPA_ERR_INVALID, f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
     mptr = None
     mview = None
     if mask_kind == SDPA_MASK_BOOL:
-        if mask is None or tuple(mask.shape) != (Lq, Lk) or not mask.is_contiguous() or not mask.is_cuda:
+        if mask is None or tuple(mask.shape) != (Lq, Lk) or not mask.is_contiguous() or not mask.is_cuda \
+                or mask.device != q.device:
             raise SdpaError(SDPA_ERR_INVALID, f"mask must be a contiguous GPU tensor of shape ({Lq}, {Lk})")
         if mask.dtype == torch.bool:
             mask = mask.view(torch.uint8)
@@ -267,7 +300,8 @@ def attention(q, k, v, scale: float, mask_kind: int = SDPA_MASK_NONE, mask=None,
         mptr = mask.data_ptr()
         mview = (mptr, 0, 0, Lk)
     elif mask_kind == SDPA_MASK_ADDITIVE:
-        if mask is None or mask.dtype != q.dtype or not mask.is_cuda or mask.dim() < 2 or mask.dim() > 4:
+        if mask is None or mask.dtype != q.dtype or not mask.is_cuda or mask.device != q.device or mask.dim() < 2 \
+                or mask.dim() > 4:
             raise SdpaError(SDPA_ERR_INVALID, f"an additive mask must be a 2-4 dimensional GPU tensor of {q.dtype}")
         m4 = mask.reshape((1,) * (4 - mask.dim()) + tuple(mask.shape)) if mask.dim() < 4 else mask
         try:
@@ -276,14 +310,8 @@ def attention(q, k, v, scale: float, mask_kind: int = SDPA_MASK_NONE, mask=None,
             raise SdpaError(SDPA_ERR_INVALID, f"additive mask {tuple(mask.shape)} does not broadcast to "
                             f"({B}, {Hq}, {Lq}, {Lk})")
         mview = _view("mask", m4, (B, Hq, Lq, Lk))
-    sptr = None
-    if sinks is not None:
-        if tuple(sinks.shape) != (Hq,) or sinks.dtype != q.dtype or not sinks.is_cuda:
-            raise SdpaError(SDPA_ERR_INVALID, f"sinks must be a GPU tensor of shape ({Hq},) and dtype {q.dtype}")
-        sinks = sinks.contiguous()
-        sptr = sinks.data_ptr()
-    if out is None:
-        out = torch.empty((B, Hq, Lq, Dv), dtype=q.dtype, device=q.device)
+    sptr = _sinks_ptr(sinks, q, Hq)
+    out = _out_tensor(out, q, (B, Hq, Lq, Dv))
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     if window is not None and mask_kind != SDPA_MASK_CAUSAL:
@@ -303,9 +331,11 @@ def attention(q, k, v, scale: float, mask_kind: int = SDPA_MASK_NONE, mask=None,
     return out
 
 
-def _gpu_tensor(name, t, dtype=None):
+def _gpu_tensor(name, t, dtype=None, device=None):
     if not t.is_cuda or not t.is_contiguous():
         raise SdpaError(SDPA_ERR_INVALID, f"{name} must be a contiguous GPU tensor")
+    if device is not None and t.device != device:
+        raise SdpaError(SDPA_ERR_INVALID, f"{name} is on {t.device}, expected {device}")
     if dtype is not None and t.dtype != dtype:
         raise SdpaError(SDPA_ERR_INVALID, f"{name} has dtype {t.dtype}, expected {dtype}")
 
@@ -323,22 +353,16 @@ def paged_attention(q, kcache, vcache, table, lengths, scale: float, mask_kind: 
     blocks, Hkv, bs, _ = kcache.shape
     Dv = vcache.shape[3]
     for name, t in (("q", q), ("kcache", kcache), ("vcache", vcache)):
-        _gpu_tensor(name, t, q.dtype)
+        _gpu_tensor(name, t, q.dtype, q.device)
     for name, t in (("table", table), ("lengths", lengths)):
-        _gpu_tensor(name, t, torch.int32)
+        _gpu_tensor(name, t, torch.int32, q.device)
     if tuple(kcache.shape) != (blocks, Hkv, bs, D) or tuple(vcache.shape[:3]) != (blocks, Hkv, bs):
         raise SdpaError(SDPA_ERR_INVALID, f"kcache {tuple(kcache.shape)} / vcache {tuple(vcache.shape)} do not "
                         f"match q {tuple(q.shape)}")
     if table.dim() != 2 or table.shape[0] != B or tuple(lengths.shape) != (B,):
         raise SdpaError(SDPA_ERR_INVALID, f"table must be [{B}, max_blocks] and lengths [{B}]")
-    sptr = None
-    if sinks is not None:
-        if tuple(sinks.shape) != (Hq,) or sinks.dtype != q.dtype or not sinks.is_cuda:
-            raise SdpaError(SDPA_ERR_INVALID, f"sinks must be a GPU tensor of shape ({Hq},) and dtype {q.dtype}")
-        sinks = sinks.contiguous()
-        sptr = sinks.data_ptr()
-    if out is None:
-        out = torch.empty((B, Hq, Lq, Dv), dtype=q.dtype, device=q.device)
+    sptr = _sinks_ptr(sinks, q, Hq)
+    out = _out_tensor(out, q, (B, Hq, Lq, Dv))
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     sdpa_paged_forward(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), out.data_ptr(), table.data_ptr(),

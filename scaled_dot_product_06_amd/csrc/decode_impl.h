@@ -228,6 +228,8 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
     softmax_rebase<C::NDBW>(tmax, m, l, o);
     const float mu = (m == -INFINITY) ? 0.0f : m;
 
+    // weights rounded to 16 bits for the MFMA; the running sum adds the same
+    // rounded weights, so numerator and denominator agree
     uint32_t pk[C::NSB * ACC / 2];
     float lsum = 0.0f;
 #pragma unroll
@@ -236,8 +238,8 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
       for (int i = 0; i < ACC; i += 2) {
         const float p0 = fast_exp2(fmaf(s[nb][i], sc, -mu));
         const float p1 = fast_exp2(fmaf(s[nb][i + 1], sc, -mu));
-        lsum += p0 + p1;
         pk[(nb * ACC + i) / 2] = pack2<E>(p0, p1);
+        lsum = pair_sum<E>(pk[(nb * ACC + i) / 2], lsum);
       }
     l += lsum;
 

@@ -21,6 +21,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "../../include/sdpa.h"
 #include "kernels.h"
@@ -283,36 +284,54 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
   return SDPA_OK;
 }
 
+// Library scratch (decode partials, packed mask bits): one buffer per device
+// and stream, allocated on the stream's first call that needs it and replaced by
+// a larger one when a call needs more. A graph captured on the stream keeps the
+// address of the buffer it was captured with, so a replaced buffer is kept (on
+// the retired list) until sdpa_release_workspace, and a capture never grows the
+// buffer: it cannot allocate memory that outlives the graph, and freeing the
+// old buffer would pull it from under graphs captured earlier.
 struct ScratchEntry {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, ScratchEntry> g_scratch;
+std::vector<std::pair<int, void*>> g_retired;  // (device, buffer) replaced by larger ones
 
-hipError_t get_scratch(hipStream_t stream, size_t bytes, void** out) {
+// Scratch of at least `bytes` for a call on `stream`: SDPA_OK with *out set, or an
+// error code with the message set.
+int get_scratch(hipStream_t stream, size_t bytes, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
   std::lock_guard<std::mutex> lock(g_mu);
   ScratchEntry& s = g_scratch[std::make_pair(dev, stream)];
-  if (s.bytes < bytes) {
-    if (s.ptr) {
-      e = hipFreeAsync(s.ptr, stream);
-      s.ptr = nullptr;
-      s.bytes = 0;
-      if (e != hipSuccess) return e;
-    }
-    const size_t want = (bytes + (size_t(1) << 20) - 1) & ~((size_t(1) << 20) - 1);
-    e = hipMallocAsync(&s.ptr, want, stream);
-    if (e != hipSuccess) {
-      s.ptr = nullptr;
-      return e;
-    }
-    s.bytes = want;
+  if (s.bytes >= bytes) {
+    *out = s.ptr;
+    return SDPA_OK;
   }
-  *out = s.ptr;
-  return hipSuccess;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "hipStreamIsCapturing failed: %s", hipGetErrorString(e));
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(SDPA_ERR_UNSUPPORTED,
+                "the stream is capturing a graph and the call needs %zu bytes of scratch, but the stream holds %zu: "
+                "a capture cannot allocate it. Make one call of at least this size (the plan's scratch_bytes) on "
+                "the same stream before capturing",
+                bytes, s.bytes);
+  // at least double, so that a stream's retired buffers hold less than its current one
+  size_t want = (bytes + (size_t(1) << 20) - 1) & ~((size_t(1) << 20) - 1);
+  if (s.ptr && want < 2 * s.bytes) want = 2 * s.bytes;
+  void* p = nullptr;
+  e = hipMallocAsync(&p, want, stream);
+  if (e != hipSuccess)
+    return fail(SDPA_ERR_HIP, "scratch allocation of %zu bytes failed: %s", want, hipGetErrorString(e));
+  if (s.ptr) g_retired.emplace_back(dev, s.ptr);
+  s.ptr = p;
+  s.bytes = want;
+  *out = p;
+  return SDPA_OK;
 }
 
 }  // namespace
@@ -456,8 +475,7 @@ int forward_impl(const Views& x, void* out, int64_t B, int64_t Hq, int64_t Hkv, 
     a.kps = (int)p.keys_per_split;
     a.nsplit = (int)p.splits;
     void* part = nullptr;
-    e = get_scratch(stream, (size_t)p.scratch_bytes, &part);
-    if (e != hipSuccess) return fail(SDPA_ERR_HIP, "decode scratch allocation failed: %s", hipGetErrorString(e));
+    if ((rc = get_scratch(stream, (size_t)p.scratch_bytes, &part)) != SDPA_OK) return rc;
     a.part = (float*)part;
     DecodeShape s{p.rows_per_wave, p.waves, p.block_n};
     e = launch_decode(dtype, (int)D, (int)Dv, s, a, stream, &ok);
@@ -466,8 +484,7 @@ int forward_impl(const Views& x, void* out, int64_t B, int64_t Hq, int64_t Hkv, 
     a.nqb = (int)(p.grid[0] / a.head_blocks);
     if (prefill_packs_mask(dtype, mask_kind)) {
       void* bits = nullptr;
-      e = get_scratch(stream, (size_t)p.scratch_bytes, &bits);
-      if (e != hipSuccess) return fail(SDPA_ERR_HIP, "mask-bit scratch allocation failed: %s", hipGetErrorString(e));
+      if ((rc = get_scratch(stream, (size_t)p.scratch_bytes, &bits)) != SDPA_OK) return rc;
       e = launch_mask_bits((const uint8_t*)x.mask, (uint32_t*)bits, Lq, Lk, stream);
       if (e != hipSuccess) return fail(SDPA_ERR_HIP, "mask packing launch failed: %s", hipGetErrorString(e));
       a.mbits = (const uint32_t*)bits;
@@ -678,8 +695,7 @@ int sdpa_paged_forward(const void* q, const void* kcache, const void* vcache, vo
   a.kps = (int)p.keys_per_split;
   a.nsplit = (int)p.splits;
   void* part = nullptr;
-  e = get_scratch(stream, (size_t)p.scratch_bytes, &part);
-  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "decode scratch allocation failed: %s", hipGetErrorString(e));
+  if ((rc = get_scratch(stream, (size_t)p.scratch_bytes, &part)) != SDPA_OK) return rc;
   a.part = (float*)part;
   DecodeShape s{p.rows_per_wave, p.waves, p.block_n};
   e = launch_decode_paged(dtype, (int)D, (int)Dv, s, a, stream, &ok);
@@ -753,16 +769,17 @@ int sdpa_release_workspace(void) {
   int cur = 0;
   (void)hipGetDevice(&cur);
   int rc = SDPA_OK;
-  for (auto& kv : g_scratch) {
-    if (!kv.second.ptr) continue;
-    hipError_t e = hipSetDevice(kv.first.first);
+  auto release = [&](int dev, void* ptr) {
+    hipError_t e = hipSetDevice(dev);
     if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e == hipSuccess) e = hipFree(kv.second.ptr);
+    if (e == hipSuccess) e = hipFree(ptr);
     if (e != hipSuccess && rc == SDPA_OK) rc = fail(SDPA_ERR_HIP, "releasing scratch: %s", hipGetErrorString(e));
-    kv.second.ptr = nullptr;
-    kv.second.bytes = 0;
-  }
+  };
+  for (auto& kv : g_scratch)
+    if (kv.second.ptr) release(kv.first.first, kv.second.ptr);
+  for (auto& r : g_retired) release(r.first, r.second);
   g_scratch.clear();
+  g_retired.clear();
   (void)hipSetDevice(cur);
   return rc;
 }

@@ -131,3 +131,71 @@ def test_concurrent_streams_and_threads():
         bits = torch.int16
         for o in os_:
             assert torch.equal(o.view(bits), w.view(bits))
+
+
+def test_graph_replays_after_a_larger_eager_call_on_its_stream():
+    """A graph keeps the scratch it was captured with: a later eager call on the same
+    stream that needs more scratch gets a new, larger buffer, and the captured graph's
+    buffer stays allocated (retired, not freed), so replays still give the eager bits."""
+    import torch
+    small = _call(0, 2, 16, 2, 1, 9000, 256, BF16)
+    large = _call(0, 2, 16, 2, 1, 262145, 256, BF16)
+    plans = [sd.sdpa_plan(2, 16, 2, 1, L, 256, 256, 0, False, True, BF16) for L in (9000, 262145)]
+    assert plans[1]["scratch_bytes"] > 2 * plans[0]["scratch_bytes"]
+    stream = torch.cuda.Stream()
+    want = torch.empty((2, 16, 1, 256), dtype=torch.bfloat16, device="cuda")
+    with torch.cuda.stream(stream):
+        small(want, stream.cuda_stream)         # sizes this stream's scratch for the small call
+    torch.cuda.synchronize()
+    out = torch.full_like(want, float("nan"))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        small(out, stream.cuda_stream)
+    torch.cuda.synchronize()
+    big_out = torch.empty((2, 16, 1, 256), dtype=torch.bfloat16, device="cuda")
+    with torch.cuda.stream(stream):
+        large(big_out, stream.cuda_stream)      # grows the stream's scratch
+    torch.cuda.synchronize()
+    for replay in range(3):
+        out.fill_(float("nan"))
+        with torch.cuda.stream(stream):
+            large(big_out, stream.cuda_stream)  # eager work on the new buffer between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"replay {replay}"
+    del graph
+    torch.cuda.synchronize()
+
+
+def test_first_call_needing_scratch_inside_a_capture_is_refused():
+    """A capture cannot allocate the stream's scratch: the call returns
+    SDPA_ERR_UNSUPPORTED, names the plan's scratch_bytes, and enqueues nothing. A call
+    that needs no scratch (an unmasked prefill) is captured as the stream's first call."""
+    import torch
+    decode = _call(0, 2, 16, 2, 1, 9000, 256, BF16)
+    prefill = _call(1, 2, 8, 2, 300, 300, 128, BF16)
+    stream = torch.cuda.Stream()
+    out = torch.full((2, 16, 1, 256), 3.0, dtype=torch.bfloat16, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(sd.SdpaError) as err:
+        with torch.cuda.graph(graph, stream=stream):
+            decode(out, stream.cuda_stream)
+    assert err.value.code == sd.SDPA_ERR_UNSUPPORTED
+    assert "scratch_bytes" in err.value.message
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+    del graph
+    want = torch.empty((2, 8, 300, 128), dtype=torch.bfloat16, device="cuda")
+    prefill(want, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    fresh = torch.cuda.Stream()
+    got = torch.full_like(want, float("nan"))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=fresh):
+        prefill(got, fresh.cuda_stream)
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    del graph
+    torch.cuda.synchronize()

@@ -10,6 +10,7 @@ import pytest
 
 from oracle import attention as orc
 from scaled_dot_product_06_amd import inputs as gen
+from tests import config_cases as cc
 from tests.gpu_util import (TOL, assert_parity, compare, device_inputs, from_device, oracle_rows, run_gpu,
                             sample_rows, say, to_device)
 
@@ -29,24 +30,22 @@ def _full_check(p, what=""):
 
 
 # --- the five workloads ---------------------------------------------------------------------
+# Each workload at its exact shape, plus the variants of tests/config_cases.py whose outputs
+# are of order one (peaked scores, planted keys in chosen decode splits, heavy sinks), so a
+# lost split, tile or sink fails the check (the CPU negative controls show that it would).
+# Every output element is compared with the oracle, one (batch, head) slice at a time.
 
-@pytest.mark.parametrize("number", [1, 2, 5])
-def test_workload_full(number):
-    p = gen.workload(number)
-    say(f"workload {number}: {p!r}")
-    _full_check(p, f"workload {number}")
-
-
-@pytest.mark.parametrize("number,nrows", [(3, 256), (4, 384)])
-def test_workload_sampled_rows(number, nrows):
-    p = gen.workload(number)
-    say(f"workload {number}: {p!r}")
-    got = from_device(run_gpu(p), p.dtype)
-    assert np.all(np.isfinite(got))
-    rows = sample_rows(p, nrows, seed=number)
-    want = oracle_rows(p, rows)
-    sel = np.stack([got[b, h, i] for b, h, i in rows])
-    assert_parity(p, sel, want, f"workload {number}, {len(rows)} sampled rows")
+@pytest.mark.parametrize("number,kind", cc.all_cases(), ids=lambda x: str(x))
+def test_workload(number, kind):
+    import scaled_dot_product_06_amd as sd
+    p = cc.case(number, kind)
+    say(f"workload {number} {kind}: {p!r}")
+    plan = sd.sdpa_plan(*p.shape_args(), p.mask_kind, p.mask is not None, p.sinks is not None, p.dtype)
+    if number in cc.DECODE:
+        assert plan["route"] == "decode" and plan["keys_per_split"] == cc.KEYS_PER_SPLIT[number]
+    else:
+        assert plan["route"] == "prefill"
+    _full_check(p, f"workload {number} {kind}")
 
 
 # --- coverage grids -------------------------------------------------------------------------
@@ -372,14 +371,17 @@ def test_largest_heads_long_keys():
         _full_check(p, f"D=512 Lq={Lq} Lk={Lk}")
 
 
+@pytest.mark.parametrize("scale", [None, 1.0], ids=["rsqrtD", "peaked"])
 @pytest.mark.parametrize("Lk,D,mask_kind", [(262145, 128, 0), (300001, 64, 1), (1 << 20, 64, 0)])
-def test_decode_more_splits_than_one_reduce_chunk(Lk, D, mask_kind):
+def test_decode_more_splits_than_one_reduce_chunk(Lk, D, mask_kind, scale):
     # 1024-key splits: 257, 293 and 1024 of them, so the reduce walks its splits in
-    # several chunks of 256 (and the last split holds one key in the first case)
-    p = gen.make_problem(600 + Lk % 97, 1, 8, 1, 1, Lk, D, D, BF16, mask_kind, sinks=True)
+    # several chunks of 256 (and the last split holds one key in the first case). At
+    # scale 1/sqrt(D) the outputs are a few thousandths; at scale 1.0 each row's output
+    # is close to its top keys' value rows (order one), wherever they fall
+    p = gen.make_problem(600 + Lk % 97, 1, 8, 1, 1, Lk, D, D, BF16, mask_kind, sinks=True, scale=scale)
     plan = __import__("scaled_dot_product_06_amd").sdpa_plan(*p.shape_args(), mask_kind, False, True, BF16)
     assert plan["route"] == "decode" and plan["splits"] > 256
-    _full_check(p, f"decode Lk={Lk} splits={plan['splits']}")
+    _full_check(p, f"decode Lk={Lk} splits={plan['splits']} scale={p.scale}")
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,Lk", [(1000, 4, 2, 70), (65535, 2, 1, 5)])

@@ -1,0 +1,93 @@
+"""CPU check of the pipelined prefill's tile-load addresses (csrc/prefill_fast.h).
+
+Each lane of each wavefront issues direct-to-LDS loads of one 16-byte chunk of
+a K and a V row per tile. Its offset within the tile is kept as a 32-bit
+unsigned byte offset; for the last, ragged tile, rows past the last key are
+pulled back to the last key by subtracting whole rows from that unsigned
+offset. This replays that arithmetic, modulo 2^32 as the kernel does it, for
+every tile a workgroup issues, over ragged key counts, causal, windowed and
+unmasked calls and strided rows, and checks that every load reads a key row in
+[0, Lk) and a chunk inside the row, i.e. the unsigned offset never wraps.
+"""
+import itertools
+
+import pytest
+
+BN, NW, ROWS = 32, 4, 32
+U32 = 1 << 32
+
+
+def cfg(D):
+    rb = 2 * D
+    return dict(RB=rb, CPR=D // 8, ROWS_PER_KB=1024 // rb, LPW=(BN * rb // 1024) // NW)
+
+
+def swz_k(D, row):
+    return row % (D // 8)
+
+
+def swz_v(D, row):
+    c = cfg(D)
+    rpl = 1 if c["RB"] >= 256 else 256 // c["RB"]
+    nx = min(c["CPR"] // 4, 4)
+    return 4 * ((row // rpl) % nx)
+
+
+def issued_tiles(Lq, Lk, qb, mask_kind, window, heads=4):
+    """Key tiles (start keys) one workgroup of query block qb issues."""
+    wph = NW // heads
+    bm = wph * ROWS
+    shift = Lk - Lq
+    kend = Lk
+    if mask_kind == 1:
+        kend = min(Lk, min(qb * bm + bm, Lq) - 1 + shift + 1)
+    kend = max(kend, 0)
+    kbeg = 0
+    if window > 0:
+        kbeg = min(max(0, qb * bm + shift - window + 1), kend)
+    tb = kbeg // BN
+    ntiles = max((kend + BN - 1) // BN - tb, 0)
+    return [(tb + t) * BN for t in range(ntiles)]
+
+
+def check_tile(D, Lk, k0, rs, swz):
+    """Every lane's load of the tile at key k0 with row stride rs bytes."""
+    c = cfg(D)
+    for w, it, lane in itertools.product(range(NW), range(c["LPW"]), range(64)):
+        row = (w + NW * it) * c["ROWS_PER_KB"] + lane // c["CPR"]
+        slot = lane % c["CPR"]
+        chunk = (slot ^ swz(D, row)) * 16
+        off = (row * rs + chunk) % U32
+        if k0 + BN > Lk:
+            over = max(k0 + row - (Lk - 1), 0)
+            off = (off - over * rs) % U32
+        else:
+            over = 0
+        exact = (row - over) * rs + chunk          # what the offset must be, as a signed value
+        assert off == exact, (D, Lk, k0, rs, row, over)
+        key = k0 + row - over
+        assert 0 <= key <= Lk - 1, (D, Lk, k0, row, key)
+        assert 0 <= chunk < c["RB"]
+
+
+CALLS = [(1, 1), (5, 31), (40, 32), (40, 33), (97, 700), (130, 130), (333, 1297), (64, 96), (1040, 1297),
+         (4096, 4096), (200, 1)]
+
+
+@pytest.mark.parametrize("heads", [1, 4])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("mask_kind,window", [(0, 0), (1, 0), (1, 7), (1, 300), (2, 0)])
+def test_every_issued_tile_reads_inside_the_keys(D, mask_kind, window, heads):
+    # heads: query heads sharing a workgroup (4 under grouped queries; 1 gives 128-row blocks)
+    strides = [2 * D, 2 * D * 3 + 16 * 5, (1 << 26) - 16]   # contiguous, odd, the largest allowed
+    for Lq, Lk in CALLS:
+        nqb = -(-Lq // (ROWS * NW // heads))
+        for qb in range(nqb):
+            tiles = issued_tiles(Lq, Lk, qb, mask_kind, window, heads)
+            for k0 in tiles:
+                assert k0 <= Lk - 1, "a tile starts past the last key"
+            # the ragged last tile is the one that pulls rows back
+            for k0 in [t for t in tiles if t + BN > Lk] + tiles[:1]:
+                for rs in strides:
+                    check_tile(D, Lk, k0, rs, swz_k)
+                    check_tile(D, Lk, k0, rs, swz_v)

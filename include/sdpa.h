@@ -276,6 +276,30 @@ int sdpa_forward_strided(const sdpa_view_t* q, const sdpa_view_t* k, const sdpa_
                          const sdpa_view_t* mask, const void* sinks, int64_t window,
                          int dtype, void* stream);
 
+/*
+ * sdpa_forward_noalloc - sdpa_forward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, validation, kernels and results (the same
+ * bits) as sdpa_forward; it calls no hipMalloc, hipFree or other allocating
+ * routine. Its scratch (decode partials, packed mask bits: the plan's
+ * scratch_bytes) is one fixed array of sdpa_noalloc_scratch_bytes() bytes
+ * (16 MiB) per device, held by the library from load until the process ends.
+ * A call whose plan needs more returns SDPA_ERR_UNSUPPORTED and enqueues
+ * nothing (the decode of B=4, Hq=16, Hkv=2, Lk=65537, D=256 needs 4.3 MB).
+ * Every call on one device shares that device's array: calls on that device
+ * that overlap in time (on different streams, or graph replays) race with
+ * each other; calls ordered on one stream do not. Nothing in the array needs
+ * clearing between calls (each call writes what it later reads).
+ */
+int sdpa_forward_noalloc(const void* q, const void* k, const void* v, void* out,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                         int64_t D, int64_t Dv, float scale,
+                         int mask_kind, const uint8_t* mask, const void* sinks,
+                         int dtype, void* stream);
+
+/* Size in bytes of sdpa_forward_noalloc's per-device scratch array. */
+int64_t sdpa_noalloc_scratch_bytes(void);
+
 /* Message of the last error on the calling thread ("" if none). The pointer
  * stays valid until the thread's next sdpa_* call. */
 const char* sdpa_last_error(void);
@@ -286,8 +310,8 @@ const char* sdpa_last_error(void);
  * SDPA_ERR_HIP. */
 int sdpa_release_workspace(void);
 
-/* ABI version of this header: 4 (2 added the windowed calls, 3 the paged ones,
- * 4 strided views and additive masks). */
+/* ABI version of this header: 5 (2 added the windowed calls, 3 the paged ones,
+ * 4 strided views and additive masks, 5 the allocation-free call). */
 int sdpa_abi_version(void);
 
 #ifdef __cplusplus

@@ -17,7 +17,7 @@ ROUTE_NAMES = {0: "empty", 1: "zero_fill", 2: "prefill", 3: "decode"}
 
 EXPORTED = ("sdpa_forward", "sdpa_plan", "sdpa_forward_windowed", "sdpa_plan_windowed", "sdpa_paged_forward",
             "sdpa_plan_paged", "sdpa_paged_write", "sdpa_forward_strided", "sdpa_last_error", "sdpa_release_workspace",
-            "sdpa_abi_version")
+            "sdpa_abi_version", "sdpa_forward_noalloc", "sdpa_noalloc_scratch_bytes")
 
 
 class SdpaPlan(ctypes.Structure):
@@ -81,6 +81,10 @@ def load() -> ctypes.CDLL:
     lib.sdpa_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ctypes.c_float,
                                  c_int, vp, vp, c_int, vp]
     lib.sdpa_forward.restype = c_int
+    lib.sdpa_forward_noalloc.argtypes = list(lib.sdpa_forward.argtypes)
+    lib.sdpa_forward_noalloc.restype = c_int
+    lib.sdpa_noalloc_scratch_bytes.argtypes = []
+    lib.sdpa_noalloc_scratch_bytes.restype = i64
     lib.sdpa_plan.argtypes = [i64, i64, i64, i64, i64, i64, i64, c_int, c_int, c_int, c_int,
                               ctypes.POINTER(SdpaPlan)]
     lib.sdpa_plan.restype = c_int
@@ -128,6 +132,18 @@ def sdpa_forward(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, Dv, scale, mask_kind, mask
     rc = load().sdpa_forward(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, Dv, ctypes.c_float(scale), mask_kind,
                              mask, sinks, dtype, stream)
     return _check(rc) if check else rc
+
+
+def sdpa_forward_noalloc(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, Dv, scale, mask_kind, mask, sinks, dtype, stream,
+                         check: bool = True) -> int:
+    """Raw allocation-free call (the library's fixed per-device scratch): as sdpa_forward."""
+    rc = load().sdpa_forward_noalloc(q, k, v, out, B, Hq, Hkv, Lq, Lk, D, Dv, ctypes.c_float(scale), mask_kind,
+                                     mask, sinks, dtype, stream)
+    return _check(rc) if check else rc
+
+
+def sdpa_noalloc_scratch_bytes() -> int:
+    return load().sdpa_noalloc_scratch_bytes()
 
 
 def sdpa_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, has_mask, has_sinks, dtype, check: bool = True):

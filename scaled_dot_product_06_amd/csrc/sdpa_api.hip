@@ -318,7 +318,7 @@ int get_scratch(hipStream_t stream, size_t bytes, void** out) {
     return fail(SDPA_ERR_UNSUPPORTED,
                 "the stream is capturing a graph and the call needs %zu bytes of scratch, but the stream holds %zu: "
                 "a capture cannot allocate it. Make one call of at least this size (the plan's scratch_bytes) on "
-                "the same stream before capturing",
+                "the same stream before capturing, or use sdpa_forward_noalloc",
                 bytes, s.bytes);
   // at least double, so that a stream's retired buffers hold less than its current one
   size_t want = (bytes + (size_t(1) << 20) - 1) & ~((size_t(1) << 20) - 1);
@@ -334,11 +334,53 @@ int get_scratch(hipStream_t stream, size_t bytes, void** out) {
   return SDPA_OK;
 }
 
+// Allocation-free scratch: one fixed array per device, resident until the
+// process ends. In host code the array's name is only a stand-in; the device
+// address of each GPU's copy comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is used.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+std::mutex g_fixed_mu;
+std::map<int, void*> g_fixed;   // device -> address of its copy of `scratch`
+
+int fixed_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_fixed_mu);
+  auto it = g_fixed.find(dev);
+  if (it != g_fixed.end()) {
+    *out = it->second;
+    return SDPA_OK;
+  }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || ptr == nullptr)
+    return fail(SDPA_ERR_HIP, "hipGetSymbolAddress of the fixed scratch failed on device %d: %s", dev,
+                hipGetErrorString(e));
+  g_fixed[dev] = ptr;
+  *out = ptr;
+  return SDPA_OK;
+}
+
+// Where a call's scratch comes from: the per-stream cached buffer, or the
+// fixed array (allocation-free calls).
+enum ScratchSource { kScratchCached = 0, kScratchFixed = 1 };
+
+int call_scratch(int source, hipStream_t stream, size_t bytes, void** out) {
+  if (source == kScratchCached) return get_scratch(stream, bytes, out);
+  if (bytes > kNoAllocScratchBytes)
+    return fail(SDPA_ERR_UNSUPPORTED,
+                "the call needs %zu bytes of scratch; sdpa_forward_noalloc holds at most %zu (use sdpa_forward)",
+                bytes, kNoAllocScratchBytes);
+  return fixed_scratch(out);
+}
+
 }  // namespace
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 4; }
+int sdpa_abi_version(void) { return 5; }
 
 const char* sdpa_last_error(void) { return g_err.c_str(); }
 
@@ -403,7 +445,7 @@ int check_rows_aligned(const char* name, const void* p, const Strides& st, int64
 
 int forward_impl(const Views& x, void* out, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                  int64_t Dv, float scale, int mask_kind, const void* sinks, int dtype, int64_t window,
-                 void* stream_v) {
+                 void* stream_v, int scratch_source = kScratchCached) {
   sdpa_plan_t p;
   int rc = validate_and_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, x.mask != nullptr, sinks != nullptr, dtype,
                              window, &p);
@@ -475,7 +517,7 @@ int forward_impl(const Views& x, void* out, int64_t B, int64_t Hq, int64_t Hkv, 
     a.kps = (int)p.keys_per_split;
     a.nsplit = (int)p.splits;
     void* part = nullptr;
-    if ((rc = get_scratch(stream, (size_t)p.scratch_bytes, &part)) != SDPA_OK) return rc;
+    if ((rc = call_scratch(scratch_source, stream, (size_t)p.scratch_bytes, &part)) != SDPA_OK) return rc;
     a.part = (float*)part;
     DecodeShape s{p.rows_per_wave, p.waves, p.block_n};
     e = launch_decode(dtype, (int)D, (int)Dv, s, a, stream, &ok);
@@ -484,7 +526,7 @@ int forward_impl(const Views& x, void* out, int64_t B, int64_t Hq, int64_t Hkv, 
     a.nqb = (int)(p.grid[0] / a.head_blocks);
     if (prefill_packs_mask(dtype, mask_kind)) {
       void* bits = nullptr;
-      if ((rc = get_scratch(stream, (size_t)p.scratch_bytes, &bits)) != SDPA_OK) return rc;
+      if ((rc = call_scratch(scratch_source, stream, (size_t)p.scratch_bytes, &bits)) != SDPA_OK) return rc;
       e = launch_mask_bits((const uint8_t*)x.mask, (uint32_t*)bits, Lq, Lk, stream);
       if (e != hipSuccess) return fail(SDPA_ERR_HIP, "mask packing launch failed: %s", hipGetErrorString(e));
       a.mbits = (const uint32_t*)bits;
@@ -528,6 +570,18 @@ int sdpa_forward(const void* q, const void* k, const void* v, void* out, int64_t
   return forward_impl(contiguous_views(q, k, v, mask, Hq, Hkv, Lq, Lk, D, Dv), out, B, Hq, Hkv, Lq, Lk, D, Dv, scale,
                       mask_kind, sinks, dtype, 0, stream);
 }
+
+int sdpa_forward_noalloc(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t Hq, int64_t Hkv,
+                         int64_t Lq, int64_t Lk, int64_t D, int64_t Dv, float scale, int mask_kind,
+                         const uint8_t* mask, const void* sinks, int dtype, void* stream) {
+  g_err.clear();
+  if (mask_kind == SDPA_MASK_ADDITIVE)
+    return fail(SDPA_ERR_INVALID, "an additive mask needs its strides: call sdpa_forward_strided");
+  return forward_impl(contiguous_views(q, k, v, mask, Hq, Hkv, Lq, Lk, D, Dv), out, B, Hq, Hkv, Lq, Lk, D, Dv, scale,
+                      mask_kind, sinks, dtype, 0, stream, kScratchFixed);
+}
+
+int64_t sdpa_noalloc_scratch_bytes(void) { return (int64_t)kNoAllocScratchBytes; }
 
 int sdpa_forward_windowed(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t Hq,
                           int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D, int64_t Dv, float scale, int64_t window,

@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "sdpa.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(sdpa_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(sdpa_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_expected_entry_points():
@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(sd.library_path())
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert sd.sdpa_abi_version() == 4
+    assert sd.sdpa_abi_version() == 5
     out = subprocess.run(["nm", "-D", "--defined-only", sd.library_path()], capture_output=True, text=True).stdout
     for name in _declared_functions():
         assert re.search(rf"\bT {name}$", out, flags=re.M), f"{name} not exported with C linkage"

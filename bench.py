@@ -90,16 +90,41 @@ def kernel_source_hash(kernel_tag: str) -> str:
     return h.hexdigest()
 
 
-def cpu_baseline(p, seconds: float):
-    """Time the float64 oracle on whole heads of the prefill workload until
-    about `seconds` of CPU work; report algorithmic TFLOP/s."""
-    import numpy as np
-    from oracle import attention as orc
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count() or 1
+        return 1
+
+
+def _time_oracle(p, rows=None):
+    """Seconds for one oracle evaluation of problem p (all rows, or the given ones)."""
+    from oracle import attention as orc
+    q, k, v, m, s = p.widened()
+    t0 = time.perf_counter()
+    orc.sdpa(q, k, v, p.scale, p.mask_kind, m, s, rows=rows)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(p, seconds: float, gen, dec=None):
+    """Time the float64 oracle on the host cores: whole (batch, head) slices of
+    the prefill workload `p` for about `seconds` (the reported value, in
+    TFLOP/s), then each of the five workloads once, in its own unit, with all
+    BLAS threads and, for the three small ones, on one thread. Input
+    generation is outside the timed regions."""
+    from oracle import attention as orc
+    threads = _blas_threads()
     q, k, v, m, s = p.widened()
     group = p.Hq // p.Hkv
     per_head = causal_pairs(p.Lq, p.Lk) * 2 * (p.D + p.Dv)
@@ -116,9 +141,39 @@ def cpu_baseline(p, seconds: float):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": done * per_head / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    per = {}
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        threadpool_limits = None
+    for num in (1, 2, 4, 5, 3):
+        w = p if num == PREFILL_WORKLOAD else (dec if num == DECODE_WORKLOAD and dec is not None else gen.workload(num))
+        if w.Lq == 1:
+            unit, work = "GB/s", decode_bytes(w) / 1e9
+        else:
+            unit, work = "TFLOP/s", prefill_flop(w) / 1e12
+        entry = {"workload": gen.WORKLOADS[num]["name"], "unit": unit}
+        if num == PREFILL_WORKLOAD:
+            # the slices timed above stand for the whole call
+            entry.update({"threads": threads, "seconds": round(dt * p.B * p.Hq / done, 2),
+                          "value": round(done * per_head / dt / 1e12, 5), "sample": f"{done} of {p.B * p.Hq} slices"})
+        else:
+            sec = _time_oracle(w)
+            entry.update({"threads": threads, "seconds": round(sec, 3), "value": round(work / sec, 5)})
+            if num in (1, 2, 5) and threadpool_limits is not None:
+                with threadpool_limits(limits=1):
+                    sec1 = _time_oracle(w)
+                entry["one_thread"] = {"seconds": round(sec1, 3), "value": round(work / sec1, 5)}
+        per[str(num)] = entry
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:
+        affinity = None
+    return {"value": done * per_head / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {p.B * p.Hq} (batch, head) slices of the prefill workload, all {p.Lq} rows "
-                      f"each; numpy float64, {dt:.1f} s"}
+                      f"each; numpy float64 on {threads} BLAS threads, {dt:.1f} s",
+            "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count(), "cpus_allowed": affinity,
+            "blas_threads": threads, "per_workload": per}
 
 
 PEAK_FP32_MFMA_TFLOPS = 157.3
@@ -341,7 +396,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--settle", type=float, default=2.0,
                     help="extra untimed stepping (seconds) after the warmup steps, so GPU clocks settle")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget for cpu_baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for cpu_baseline's "
+                    "prefill sample (the other workloads add about 10 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip the reported-only workloads (f32 prefill, "
                     "8193-key decode, f16 masked prefill with sinks, sliding windows, paged decode, "
@@ -483,7 +539,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the prefill workload ...")
-        result["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds, gen, dec)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -71,14 +71,19 @@ typedef struct sdpa_plan_t {
                              the pipelined kernel (f16/bf16, D == Dv in {64, 128}, and 256 when
                              one batch item's grid has at least 256 workgroups, never with an
                              additive mask), else the generic kernel's 32 (heads up to 128 wide)
-                             or 16 */
+                             or 16 (wider heads; and f32 calls whose 32-row grid for one batch
+                             item would have fewer than 256 workgroups) */
   int32_t waves;          /* wavefronts per workgroup of the first kernel */
   int32_t block_n;        /* keys per tile */
   int32_t heads_per_group;/* prefill: query heads sharing one workgroup's K/V tiles;
                              decode: query heads packed into one wavefront (Hq/Hkv) */
   int64_t keys_per_split; /* decode: keys per first-pass workgroup (a power of two, 64..1024,
                              from Lk alone so that batch items never change it) */
-  int64_t splits;         /* decode: key blocks per (batch, kv head) */
+  int64_t splits;         /* decode: key blocks per (batch, kv head). Prefill: 0, or, for f32 calls
+                             whose 32-row grid for one batch item would have fewer than 256
+                             workgroups (no additive mask), the waves of a workgroup
+                             that split the keys of its one 16-row query block and merge their
+                             partial results (heads_per_group is then 1) */
   int64_t grid[3];        /* workgroups of the attention kernel (decode: its first pass) (x, y, z) */
   int64_t scratch_bytes;  /* device scratch the call uses. Decode: per (batch, kv head, split, packed
                              row) a 16-byte {max, sum} slot and Dv f32 partial outputs. Prefill: 0,

@@ -55,6 +55,7 @@ struct PrefillShape {
   int heads;      // query heads per workgroup (share the K/V tiles)
   int block_n;    // keys per tile
   int block_m;    // query rows per head per workgroup
+  int ksplit;     // > 1: the workgroup's waves split the keys of one query block
 };
 
 struct DecodeShape {
@@ -69,7 +70,8 @@ hipError_t launch_prefill(int elem, int D, int Dv, const PrefillShape& s, const 
                           hipStream_t stream, bool* ok);
 hipError_t launch_decode(int elem, int D, int Dv, const DecodeShape& s, const FwdArgs& a,
                          hipStream_t stream, bool* ok);
-hipError_t launch_prefill_f32_paged(int D, int Dv, const FwdArgs& a, hipStream_t stream, bool* ok);
+hipError_t launch_prefill_f32_paged(int D, int Dv, const PrefillShape& s, const FwdArgs& a, hipStream_t stream,
+                                    bool* ok);
 hipError_t launch_decode_paged(int elem, int D, int Dv, const DecodeShape& s, const FwdArgs& a,
                                hipStream_t stream, bool* ok);
 hipError_t launch_paged_write(void* cache, const void* rows, const int32_t* slots, int64_t n, int64_t blocks,
@@ -106,6 +108,14 @@ constexpr bool prefill_fast_needs_grid(int D) { return D > 128; }
 // 128-wide heads; 16x16 tiles above, where a 32-row output accumulator would
 // leave too few registers for its staging.
 constexpr int prefill_generic_mf(int elem, int D, int Dv) { return head_max(D, Dv) <= 128 ? 32 : 16; }
+// f32 calls whose 32-row grid (for one batch item, so that a batch item gets
+// the same tiles alone or in a batch) has fewer workgroups than this take
+// 16-row tiles instead: twice the wavefronts, each with half the rows.
+constexpr int kF32SmallGrid = 256;
+// Those calls (unless they carry an additive mask) run the key-split f32
+// kernel: one 16-row query block per workgroup, its keys split among the
+// workgroup's waves in tiles of this many keys.
+constexpr int f32_split_bn(int D, int Dv) { return head_max(D, Dv) <= 64 ? 32 : 16; }
 constexpr int prefill_generic_bn(int elem, int D, int Dv) {
   return elem == kF32 ? (head_max(D, Dv) <= 128 ? 32 : 16) : (head_max(D, Dv) > 256 ? 32 : 64);
 }

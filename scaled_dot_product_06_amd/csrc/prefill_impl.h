@@ -613,3 +613,257 @@ __global__ void __launch_bounds__(NW * 64) prefill_f32_kernel(FwdArgs a) {
 }
 
 }  // namespace sdpa
+
+namespace sdpa {
+
+// float32, small calls: the NW wavefronts of a workgroup share one 16-row
+// query block of one head and split its key tiles among themselves (wave w
+// takes tiles w, w + NW, ...), each staging its own tiles in a private LDS
+// region, so the walk needs no workgroup barrier and the longest row block's
+// keys are walked NW ways in parallel. At the end the waves' running maxima,
+// sums and unnormalised outputs meet in LDS and are merged with the same
+// log-sum-exp combine as the decode splits (nuvec-core "tests/attention_plan.rs":
+// a split key axis whose partial results a second step combines), exactly, up
+// to rounding. Masks, windows, sinks, strided q/k/v and paged caches (PAGED) as
+// in prefill_f32_kernel; no additive mask.
+template <int D, int DV, int BN, int NW>
+struct PrefillCfgF32Split {
+  static constexpr int MF = 16;
+  static constexpr int KWF = Mfma<MF>::KWF, ACC = Mfma<MF>::ACC, KG = Mfma<MF>::KG;
+  static constexpr int DVP = (DV + MF - 1) / MF * MF;
+  static constexpr int KST = D + 1;
+  static constexpr int VST = DVP + MF;
+  static constexpr int NQS = D / KWF;
+  static constexpr int NSB = BN / MF;
+  static constexpr int NDB = DVP / MF;
+  static constexpr int KCH = BN * D / 4, VCH = BN * DV / 4;  // 16-byte chunks per tile
+  static constexpr int KPT = (KCH + 63) / 64, VPT = (VCH + 63) / 64;
+  static constexpr int WAVE_ELEMS = BN * KST + BN * VST;      // one wave's tile region
+  static constexpr int MERGE_ELEMS = MF * DVP + 2 * MF;       // one wave's partial rows
+  static constexpr int REGION = WAVE_ELEMS > MERGE_ELEMS ? WAVE_ELEMS : MERGE_ELEMS;
+  static_assert(D % KWF == 0 && BN % MF == 0, "shape");
+};
+
+template <int D, int DV, int BN, int NW, bool PAGED>
+__global__ void __launch_bounds__(NW * 64) prefill_f32_split_kernel(FwdArgs a) {
+  using C = PrefillCfgF32Split<D, DV, BN, NW>;
+  constexpr int MF = C::MF, ACC = C::ACC;
+  using acc_t = typename Mfma<MF>::acc_t;
+  __shared__ __attribute__((aligned(16))) float lds[NW * C::REGION];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane % MF;
+  const int kg = lane / MF;
+  float* Ks = lds + w * C::REGION;
+  float* Vs = Ks + BN * C::KST;
+
+  // workgroup n: (batch, head) n / nqb, query block nqb - 1 - n % nqb (long blocks first)
+  const int n = blockIdx.x;
+  const int bh = n / a.nqb;
+  const int qb = a.nqb - 1 - n % a.nqb;
+  const int b = bh / a.Hq, h = bh % a.Hq;
+  const int hkv = h / a.group;
+  const int i0 = qb * MF;
+  const int iq = i0 + col;
+  // the keys this batch item holds: all Lk, or the sequence's clamped length
+  int Lk = a.Lk;
+  if constexpr (PAGED) Lk = min(max(a.lengths[b], 0), a.max_blocks * a.bs);
+  const int shift = Lk - a.Lq;
+
+  int kend = Lk;
+  if (a.mask_kind == kMaskCausal) kend = min(Lk, min(i0 + MF, a.Lq) - 1 + shift + 1);
+  if (kend < 0) kend = 0;
+  int kbeg = 0;
+  if (a.window > 0) kbeg = min(max(0, i0 + shift - a.window + 1), kend);
+  const int tb = kbeg / BN;
+  const int ntiles = max((kend + BN - 1) / BN - tb, 0);
+  // keys every row sees, [w_klo, w_kfull)
+  int w_kfull = a.mask_kind == kMaskBool ? 0 : Lk;
+  if (a.mask_kind == kMaskCausal) w_kfull = min(Lk, i0 + shift + 1);
+  int w_klo = 0;
+  if (a.window > 0) w_klo = min(i0 + MF, a.Lq) - 1 + shift - a.window + 1;
+
+  const float* qp = (const float*)a.q + b * a.qs[0] + h * a.qs[1] + (int64_t)iq * a.qs[2];
+  float qop[C::NQS];
+#pragma unroll
+  for (int st = 0; st < C::NQS; ++st) {
+    uint32_t x = 0u;
+    if (iq < a.Lq) x = __float_as_uint(qp[st * C::KWF + kg]);
+    qop[st] = __uint_as_float(x ^ a.qsign);
+  }
+  if constexpr (C::DVP > DV) {
+    for (int e = lane; e < BN * (C::DVP - DV); e += 64) {
+      const int r = e / (C::DVP - DV), cc = DV + e % (C::DVP - DV);
+      Vs[r * C::VST + cc] = 0.0f;
+    }
+  }
+
+  acc_t o[C::NDB];
+#pragma unroll
+  for (int d = 0; d < C::NDB; ++d) o[d] = acc_t{};
+  const bool has_sink = a.sinks != nullptr;
+  const float sink2 = has_sink ? ((const float*)a.sinks)[h] * kLog2e : -INFINITY;
+  float m = sink2, l = 0.0f;
+
+  // strided: this (batch, kv head)'s rows; paged: the cache base (rows through the table)
+  const float* kp = (const float*)a.k + (PAGED ? 0 : b * a.ks[0] + hkv * a.ks[1]);
+  const float* vp = (const float*)a.v + (PAGED ? 0 : b * a.vs[0] + hkv * a.vs[1]);
+  const uint8_t* mrow = a.mask + (size_t)min(iq, a.Lq - 1) * a.Lk;
+  const int32_t* trow = PAGED ? a.table + (size_t)b * a.max_blocks : nullptr;
+  auto cache_row = [&](int key) -> int64_t {
+    const int blk = min(max(trow[key / a.bs], 0), a.blocks - 1);
+    return ((int64_t)blk * a.Hkv + hkv) * a.bs + key % a.bs;
+  };
+
+  u32x4 kr[C::KPT], vr[C::VPT];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < C::KPT; ++it) {
+      const int c = lane + it * 64;
+      if (C::KCH % 64 == 0 || c < C::KCH) {
+        const int r = c / (D / 4), cc = c % (D / 4);
+        const int key = k0 + r;
+        // paged: keys before the workgroup's first visible key are not read
+        const bool live = key < Lk && (!PAGED || key >= kbeg);
+        const int64_t off = PAGED ? (live ? cache_row(key) * D : 0) : key * a.ks[2];
+        kr[it] = live ? ld_global16(kp + off + cc * 4) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < C::VPT; ++it) {
+      const int c = lane + it * 64;
+      if (C::VCH % 64 == 0 || c < C::VCH) {
+        const int r = c / (DV / 4), cc = c % (DV / 4);
+        const int key = k0 + r;
+        const bool live = key < Lk && (!PAGED || key >= kbeg);
+        const int64_t off = PAGED ? (live ? cache_row(key) * DV : 0) : key * a.vs[2];
+        vr[it] = live ? ld_global16(vp + off + cc * 4) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  // the wave's own region: its LDS writes and reads stay in order within the wave
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < C::KPT; ++it) {
+      const int c = lane + it * 64;
+      if (C::KCH % 64 == 0 || c < C::KCH) {
+        const int r = c / (D / 4), cc = c % (D / 4);
+        float* dst = &Ks[r * C::KST + cc * 4];   // odd row stride: scalar stores
+        dst[0] = __uint_as_float(kr[it][0]);
+        dst[1] = __uint_as_float(kr[it][1]);
+        dst[2] = __uint_as_float(kr[it][2]);
+        dst[3] = __uint_as_float(kr[it][3]);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < C::VPT; ++it) {
+      const int c = lane + it * 64;
+      if (C::VCH % 64 == 0 || c < C::VCH) {
+        const int r = c / (DV / 4), cc = c % (DV / 4);
+        *reinterpret_cast<u32x4*>(&Vs[r * C::VST + cc * 4]) = vr[it];
+      }
+    }
+  };
+
+  int t = w;
+  if (t < ntiles) load_tile((tb + t) * BN);
+  for (; t < ntiles; t += NW) {
+    const int k0 = (tb + t) * BN;
+    __builtin_amdgcn_wave_barrier();
+    store_tile();
+    __builtin_amdgcn_wave_barrier();
+    if (t + NW < ntiles) load_tile(k0 + NW * BN);
+    const bool full = k0 + BN <= w_kfull && k0 >= w_klo;
+
+    acc_t s[C::NSB];
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb) {
+      acc_t acc = acc_t{};
+#pragma unroll
+      for (int st = 0; st < C::NQS; ++st)
+        acc = mma_f32<MF>(Ks[(nb * MF + col) * C::KST + st * C::KWF + kg], qop[st], acc);
+      s[nb] = acc;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+      for (int i = 0; i < ACC; ++i) {
+        if (!full) {
+          const int key = k0 + nb * MF + acc_row<MF>(i, kg);
+          bool vis = key < Lk && iq < a.Lq;
+          if (a.mask_kind == kMaskCausal)
+            vis = vis && key <= iq + shift && (a.window <= 0 || key > iq + shift - a.window);
+          else if (a.mask_kind == kMaskBool) vis = vis && mrow[key] != 0;
+          if (!vis) s[nb][i] = -INFINITY;
+        }
+        mx = fmaxf(mx, s[nb][i]);
+      }
+    mx = row_max<MF>(mx);
+    const float tmax = (mx == -INFINITY) ? -INFINITY : mx * a.c;
+    softmax_rebase<C::NDB>(tmax, m, l, o);
+    const float mu = (m == -INFINITY) ? 0.0f : m;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+      for (int i = 0; i < ACC; ++i) {
+        const float p = fast_exp2(fmaf(s[nb][i], a.c, -mu));
+        s[nb][i] = p;
+        lsum += p;
+      }
+    l += lsum;
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+      for (int i = 0; i < ACC; ++i) {
+        const int key = nb * MF + acc_row<MF>(i, kg);
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+          o[db] = mma_f32<MF>(Vs[key * C::VST + db * MF + col], s[nb][i], o[db]);
+      }
+  }
+
+  // merge: each wave leaves its rows' reference maximum, sum and unnormalised
+  // output in its region; wave w then combines the value-column blocks
+  // db = w, w + NW, ... of every row
+  const float lt = row_sum<MF>(l);
+  __syncthreads();
+  float* part = lds + w * C::REGION;
+  if (kg == 0) {
+    part[MF * C::DVP + col] = m;
+    part[MF * C::DVP + MF + col] = lt;
+  }
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+    *reinterpret_cast<f32x4*>(&part[col * C::DVP + db * MF + kg * 4]) = o[db];
+  __syncthreads();
+  float mw[NW], M = sink2;
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    mw[u] = lds[u * C::REGION + MF * C::DVP + col];
+    M = fmaxf(M, mw[u]);
+  }
+  float fw[NW], L = 0.0f;
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    fw[u] = mw[u] == -INFINITY ? 0.0f : fast_exp2(mw[u] - M);
+    L += lds[u * C::REGION + MF * C::DVP + MF + col] * fw[u];
+  }
+  if (has_sink && M != -INFINITY) L += fast_exp2(sink2 - M);
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  if (iq >= a.Lq) return;
+  float* op = (float*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq) * DV;
+  for (int db = w; db < C::NDB; db += NW) {
+    const int dv = db * MF + kg * 4;
+    if (dv >= DV) continue;
+    f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < NW; ++u) x += *reinterpret_cast<const f32x4*>(&lds[u * C::REGION + col * C::DVP + dv]) * fw[u];
+    *reinterpret_cast<f32x4*>(op + dv) = x * inv;
+  }
+}
+
+}  // namespace sdpa

@@ -58,27 +58,48 @@ hipError_t launch_zero_fill(void* out, int64_t bytes, hipStream_t stream) {
 
 // Packs the [Lq, Lk] byte mask into bits for the 16-bit prefill kernels: word
 // w of row i holds keys 32w..32w+31, bit j set iff mask[i][32w + j] != 0 (keys
-// past Lk read as 0). One wavefront reads 64 consecutive mask bytes of a row
-// and a ballot turns them into two words; a grid-stride loop covers any size.
+// past Lk read as 0). One thread per output word: it reads the word's 32 mask
+// bytes with two 16-byte loads (global memory is accessed in unaligned mode,
+// so a row may start at any byte) and folds each 4-byte group to 4 bits; the
+// last word of a row reads its bytes one by one. A grid-stride loop covers any
+// size.
+__device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t x) {
+  // each byte's OR of its bits into the byte's low bit, then the four low bits
+  // gathered into bits 24..27 by one multiply (the partial products land on
+  // distinct bit positions, so nothing carries)
+  uint32_t y = x | (x >> 4);
+  y |= y >> 2;
+  y |= y >> 1;
+  y &= 0x01010101u;
+  return (y * 0x01020408u) >> 24;
+}
+
 __global__ void __launch_bounds__(256) mask_bits_kernel(const uint8_t* mask, uint32_t* bits, int64_t Lq,
                                                         int64_t Lk, int64_t nwords) {
-  const int lane = threadIdx.x & 63;
-  const int64_t segs = (Lk + 63) / 64;
-  const int64_t total = Lq * segs;
-  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / 64);
-  for (int64_t wv = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); wv < total; wv += nwaves) {
-    const int64_t row = wv / segs, seg = wv % segs;
-    const int64_t key = seg * 64 + lane;
-    const bool on = key < Lk && mask[row * Lk + key] != 0;
-    const uint64_t word2 = __ballot(on);
-    const int64_t w = seg * 2 + (lane >> 5);
-    if ((lane & 31) == 0 && w < nwords) bits[row * nwords + w] = (uint32_t)(word2 >> (lane & 32));
+  const int64_t total = Lq * nwords;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+    const int64_t row = t / nwords, w = t % nwords;
+    const uint8_t* p = mask + row * Lk + w * 32;
+    uint32_t word = 0u;
+    if (w * 32 + 32 <= Lk) {
+      u32x4_t lo, hi;
+      __builtin_memcpy(&lo, p, 16);
+      __builtin_memcpy(&hi, p + 16, 16);
+      word = nonzero_bytes4(lo[0]) | (nonzero_bytes4(lo[1]) << 4) | (nonzero_bytes4(lo[2]) << 8) |
+             (nonzero_bytes4(lo[3]) << 12) | (nonzero_bytes4(hi[0]) << 16) | (nonzero_bytes4(hi[1]) << 20) |
+             (nonzero_bytes4(hi[2]) << 24) | (nonzero_bytes4(hi[3]) << 28);
+    } else {
+      const int n = (int)(Lk - w * 32);
+      for (int j = 0; j < n; ++j) word |= (p[j] != 0 ? 1u : 0u) << j;
+    }
+    bits[t] = word;
   }
 }
 
 hipError_t launch_mask_bits(const uint8_t* mask, uint32_t* bits, int64_t Lq, int64_t Lk, hipStream_t stream) {
-  const int64_t waves = Lq * ((Lk + 63) / 64);
-  int64_t blocks = (waves + 3) / 4;
+  const int64_t words = Lq * mask_words(Lk);
+  int64_t blocks = (words + 255) / 256;
   if (blocks > (1 << 16)) blocks = 1 << 16;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(mask_bits_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, mask, bits, Lq, Lk,
@@ -258,7 +279,33 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
     const int64_t fbm = (nw / heads) * kFastRows;
     fast = (Hq / heads) * ((Lq + fbm - 1) / fbm) >= kFastMinGridWide;
   }
-  const int rows = fast ? kFastRows : prefill_generic_mf(dtype, (int)D, (int)Dv);
+  int rows = fast ? kFastRows : prefill_generic_mf(dtype, (int)D, (int)Dv);
+  bool ksplit = false;
+  if (dtype == SDPA_F32 && rows == 32) {
+    const int64_t bm32 = (nw / heads) * 32;
+    if ((Hq / heads) * ((Lq + bm32 - 1) / bm32) < kF32SmallGrid) {
+      rows = 16;
+      ksplit = mask_kind != SDPA_MASK_ADDITIVE;
+    }
+  }
+  if (ksplit) {
+    // one workgroup per (batch, head, 16-row query block); its waves split the keys
+    const int64_t nqb = (Lq + 15) / 16;
+    if (B * Hq * nqb > INT_MAX)
+      return fail(SDPA_ERR_UNSUPPORTED, "Lq (%lld) needs more than INT_MAX workgroups in all", (long long)Lq);
+    p.route = SDPA_ROUTE_PREFILL;
+    p.kernels = 1;
+    p.rows_per_wave = 16;
+    p.waves = nw;
+    p.block_n = f32_split_bn((int)D, (int)Dv);
+    p.heads_per_group = 1;
+    p.splits = nw;
+    p.grid[0] = B * Hq * nqb;
+    p.grid[1] = 1;
+    p.grid[2] = 1;
+    *plan = p;
+    return SDPA_OK;
+  }
   const int64_t bm = (nw / heads) * rows;
   const int64_t nqb = (Lq + bm - 1) / bm;
   if ((B * Hq / heads) * nqb > INT_MAX)
@@ -533,7 +580,7 @@ int forward_impl(const Views& x, void* out, int64_t B, int64_t Hq, int64_t Hkv, 
       a.mwords = (int)mask_words(Lk);
     }
     PrefillShape s{p.rows_per_wave, p.waves, p.heads_per_group, p.block_n,
-                   (int)((p.waves / p.heads_per_group) * p.rows_per_wave)};
+                   (int)((p.waves / p.heads_per_group) * p.rows_per_wave), (int)p.splits};
     e = launch_prefill(dtype, (int)D, (int)Dv, s, a, stream, &ok);
   }
   if (!ok) return fail(SDPA_ERR_UNSUPPORTED, "no kernel built for dtype %d, D=%lld, Dv=%lld", dtype, (long long)D,
@@ -739,7 +786,9 @@ int sdpa_paged_forward(const void* q, const void* kcache, const void* vcache, vo
   if (p.route == SDPA_ROUTE_PREFILL) {
     a.head_blocks = (int)(B * Hq / p.heads_per_group);
     a.nqb = (int)(p.grid[0] / a.head_blocks);
-    e = launch_prefill_f32_paged((int)D, (int)Dv, a, stream, &ok);
+    PrefillShape s{p.rows_per_wave, p.waves, p.heads_per_group, p.block_n,
+                   (int)((p.waves / p.heads_per_group) * p.rows_per_wave), (int)p.splits};
+    e = launch_prefill_f32_paged((int)D, (int)Dv, s, a, stream, &ok);
     if (!ok) return fail(SDPA_ERR_UNSUPPORTED, "no kernel built for dtype %d, D=%lld, Dv=%lld", dtype, (long long)D,
                          (long long)Dv);
     if (e != hipSuccess) return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -62,9 +62,30 @@ def test_workload_routes(number, route):
     else:
         assert p["kernels"] == 1 and p["scratch_bytes"] == 0
     if route == "prefill":
-        rows_per_block = p["waves"] // p["heads_per_group"] * p["rows_per_wave"]
+        if p["splits"]:
+            # the waves of a workgroup split the keys of one query block
+            assert w["dtype"] == 0 and p["splits"] == p["waves"] and p["heads_per_group"] == 1
+            rows_per_block = p["rows_per_wave"]
+        else:
+            rows_per_block = p["waves"] // p["heads_per_group"] * p["rows_per_wave"]
         head_blocks = w["B"] * w["Hq"] // p["heads_per_group"]
         assert p["grid"] == (head_blocks * -(-w["Lq"] // rows_per_block), 1, 1)
+
+
+def test_small_f32_calls_split_keys_within_a_workgroup():
+    # workload 1: 8 heads x 128 rows; a 32-row grid would have 8 workgroups
+    p = _plan(B=1, Hq=8, Hkv=8, Lq=128, Lk=128, D=64, Dv=64, mask=1, dtype=0)
+    assert (p["rows_per_wave"], p["splits"], p["heads_per_group"], p["grid"]) == (16, 4, 1, (64, 1, 1))
+    # the rule looks at one batch item, so the batch keeps the tiles
+    q = _plan(B=5, Hq=8, Hkv=8, Lq=128, Lk=128, D=64, Dv=64, mask=1, dtype=0)
+    assert (q["rows_per_wave"], q["splits"], q["grid"]) == (16, 4, (320, 1, 1))
+    # large f32 calls keep the 32-row walk; 16-bit calls never split
+    big = _plan(B=1, Hq=32, Hkv=8, Lq=4096, Lk=4096, D=128, Dv=128, mask=1, dtype=0)
+    assert (big["rows_per_wave"], big["splits"]) == (32, 0)
+    assert _plan(dtype=2)["splits"] == 0
+    # additive masks keep the generic walk at 16 rows
+    add = _plan(B=1, Hq=8, Hkv=8, Lq=128, Lk=128, D=64, Dv=64, mask=3, has_mask=True, dtype=0)
+    assert (add["rows_per_wave"], add["splits"]) == (16, 0)
 
 
 def test_decode_split_size_depends_on_keys_not_batch():

@@ -5,15 +5,18 @@
 //
 //  * each wavefront owns one 32-row MFMA block of query rows and the
 //    workgroup's four wavefronts share every K/V tile (one head each under
-//    grouped queries); the register budget leaves room for two wavefronts
-//    per SIMD, which hide each other's latencies (at 256-wide heads the
-//    32-row output and query fragments take one wavefront's whole register
-//    file, and the software pipeline alone keeps the SIMD busy);
+//    grouped queries). Up to 128-wide heads the kernel fits 168 registers and
+//    48 KB of LDS, so three workgroups share a compute unit and three
+//    wavefronts from different workgroups share each SIMD, hiding each
+//    other's latencies (at 256-wide heads the 32-row output and query
+//    fragments take one wavefront's whole register file, and the software
+//    pipeline alone keeps the SIMD busy);
 //  * K and V tiles go from global memory straight into LDS
 //    (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16 * lane),
-//    four stages, three tiles ahead of the compute, one barrier per tile;
-//    the stages are distinct LDS objects so the compiler can tell the loads
-//    into one stage from the reads of another;
+//    through a ring of three stages, one tile ahead of the step that reads it
+//    (four stages, two ahead, at 256-wide heads), one barrier per tile; the
+//    stages are distinct LDS objects so the compiler can tell the loads into
+//    one stage from the reads of another;
 //  * the loop is software-pipelined inside each wavefront: the QK^T MFMAs of
 //    tile t+1 are issued among the exponentials of tile t, and the PV MFMAs
 //    of tile t among the row maxima of tile t+1, so the matrix cores and the
@@ -54,7 +57,8 @@ struct FastCfg {
   static constexpr int NPV = BN / KW;           // k-steps of PV
   static constexpr int NDB = D / MF;            // 32-column output blocks
   static constexpr int NPK = NSB * ACC / 2;     // packed weight pairs per query block
-  static constexpr int WPE = D <= 128 ? 2 : 1;  // wavefronts per SIMD the registers allow
+  static constexpr int WPE = D <= 128 ? 3 : 1;  // wavefronts per SIMD the registers allow
+  static constexpr int STAGES = D <= 128 ? 3 : 4;  // LDS ring of K/V tiles
   static_assert(D == 64 || D == 128 || D == 256, "fast prefill covers 64-, 128- and 256-wide heads");
   static_assert(LOADS % NW == 0, "loads divide among wavefronts");
 };
@@ -84,7 +88,7 @@ prefill_fast_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[C::STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds3[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds3[C::STAGES == 4 ? C::STAGE_BYTES : 1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -225,18 +229,16 @@ prefill_fast_kernel(FwdArgs a) {
       const int row = nb * MF + col;
       ko[c][nb] = row * C::RB + (((2 * c + kg) ^ swz_k<D>(row)) * 16);
     }
-  uint32_t vo[C::NPV][C::NDB][2];
+  // V^T operands: the providers of every read sit on key rows vk0 + kofs, with
+  // kofs a multiple of 8 fixed per read; the V swizzle depends on the row only
+  // through its residue mod 4 (two rows per 256 bytes at 64-wide heads: mod 4
+  // of row / 2), which kofs leaves unchanged. So each 32-column block takes one
+  // lane offset, and kofs * RB folds into the instruction's offset field.
+  const int vk0 = acc_row<MF>(0, kg) + tr_e;
+  uint32_t vb[C::NDB];
 #pragma unroll
-  for (int t8 = 0; t8 < C::NPV; ++t8) {
-    const int keyA = ((8 * t8) / ACC) * MF + acc_row<MF>((8 * t8) % ACC, kg) + tr_e;
-    const int keyB = ((8 * t8 + 4) / ACC) * MF + acc_row<MF>((8 * t8 + 4) % ACC, kg) + tr_e;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      const int ch = db * 4 + tr_chunk;
-      vo[t8][db][0] = C::TILE_BYTES + keyA * C::RB + tr_half + ((ch ^ swz_v<D>(keyA)) * 16);
-      vo[t8][db][1] = C::TILE_BYTES + keyB * C::RB + tr_half + ((ch ^ swz_v<D>(keyB)) * 16);
-    }
-  }
+  for (int db = 0; db < C::NDB; ++db)
+    vb[db] = C::TILE_BYTES + vk0 * C::RB + tr_half + (((db * 4 + tr_chunk) ^ swz_v<D>(vk0)) * 16);
 
   // S^T = K Q^T for one tile into s (zeroed here)
   auto qk = [&](const uint8_t* Ks, acc_t (&s)[QB][C::NSB]) {
@@ -334,8 +336,10 @@ prefill_fast_kernel(FwdArgs a) {
     for (int t8 = 0; t8 < C::NPV; ++t8) {
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
-        const u32x2 ra = lds_read_tr16((const uint16_t*)(St + vo[t8][db][0]));
-        const u32x2 rb = lds_read_tr16((const uint16_t*)(St + vo[t8][db][1]));
+        const int kA = ((8 * t8) / ACC) * MF + acc_row<MF>((8 * t8) % ACC, 0);
+        const int kB = ((8 * t8 + 4) / ACC) * MF + acc_row<MF>((8 * t8 + 4) % ACC, 0);
+        const u32x2 ra = lds_read_tr16((const uint16_t*)(St + vb[db] + kA * C::RB));
+        const u32x2 rb = lds_read_tr16((const uint16_t*)(St + vb[db] + kB * C::RB));
         const u32x4 va = {ra[0], ra[1], rb[0], rb[1]};
 #pragma unroll
         for (int r = 0; r < QB; ++r) {
@@ -348,7 +352,7 @@ prefill_fast_kernel(FwdArgs a) {
 
   // Pipelined step t: tile t's weights and PV, tile t+1's scores and maxima.
   // Scur holds tile t, Snext tile t+1 and Sload (last read for tile t-1)
-  // receives tile t+3.
+  // receives tile t + STAGES - 1.
   acc_t sa[QB][C::NSB], sb[QB][C::NSB];
   uint32_t pk[QB][C::NPK];
   auto step = [&](int t, acc_t (&scur)[QB][C::NSB], acc_t (&snext)[QB][C::NSB], const uint8_t* Scur,
@@ -360,18 +364,19 @@ prefill_fast_kernel(FwdArgs a) {
         mw_nxt[r] = t + 1 < ntiles ? mbrow[r][tb + t + 1] : 0u;
       }
     }
-    // Tile t+1 has landed: the loads complete in issue order, so waiting
-    // until only tile t+2's are outstanding suffices. The barrier then also
-    // guarantees every wavefront has finished tile t-1 (its LDS reads are
-    // drained before it arrives). A plain s_barrier: the release fence of
-    // __syncthreads would also wait for tile t+2's loads.
-    if (t + 2 < ntiles) {
+    // Tile t+1 has landed: the loads complete in issue order, so with four
+    // stages waiting until only tile t+2's are outstanding suffices (with
+    // three, tile t+1's are the only ones). The barrier then also guarantees
+    // every wavefront has finished tile t-1 (its LDS reads are drained before
+    // it arrives). A plain s_barrier: the release fence of __syncthreads would
+    // also wait for tile t+2's loads.
+    if (C::STAGES == 4 && t + 2 < ntiles) {
       __builtin_amdgcn_s_waitcnt(vmcnt_only(C::LOADS_PER_TILE));
     } else {
       __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     }
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (t + 3 < ntiles) issue_tile((tb + t + 3) * BN, Sload);
+    if (t + C::STAGES - 1 < ntiles) issue_tile((tb + t + C::STAGES - 1) * BN, Sload);
     const int kt = tb + t;  // key tile
     if ((kt + 1) * BN > w_kfull || kt * BN < w_klo) tile_max_masked(kt, scur, mw_cur);
 #pragma unroll
@@ -382,11 +387,11 @@ prefill_fast_kernel(FwdArgs a) {
     tile_max_full(snext);
   };
 
-  // prologue: tiles 0..2 in flight, tile 0's scores and maxima
+  // prologue: tiles 0 .. STAGES-2 in flight, tile 0's scores and maxima
   if (ntiles > 0) issue_tile(tb * BN, lds0);
   if (ntiles > 1) issue_tile((tb + 1) * BN, lds1);
-  if (ntiles > 2) issue_tile((tb + 2) * BN, lds2);
-  if (ntiles > 2) {
+  if (C::STAGES == 4 && ntiles > 2) issue_tile((tb + 2) * BN, lds2);
+  if (C::STAGES == 4 && ntiles > 2) {
     __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * C::LOADS_PER_TILE));
   } else if (ntiles > 1) {
     __builtin_amdgcn_s_waitcnt(vmcnt_only(C::LOADS_PER_TILE));
@@ -398,18 +403,35 @@ prefill_fast_kernel(FwdArgs a) {
     qk(lds0, sa);
     tile_max_full(sa);
   }
-  // Stage of step t is t % 4 and scores alternate between sa (even t) and sb,
-  // so every call has fixed arguments. The last step also scores a next
-  // tile, from a stage holding stale data, and discards the result: one extra
-  // QK^T per workgroup keeps a separate final step out of the loop.
-  for (int t = 0; t < ntiles; t += 4) {
-    step(t, sa, sb, lds0, lds1, lds3);
-    if (t + 1 >= ntiles) break;
-    step(t + 1, sb, sa, lds1, lds2, lds0);
-    if (t + 2 >= ntiles) break;
-    step(t + 2, sa, sb, lds2, lds3, lds1);
-    if (t + 3 >= ntiles) break;
-    step(t + 3, sb, sa, lds3, lds0, lds2);
+  // Stage of step t is t % STAGES and scores alternate between sa (even t)
+  // and sb, so the loop is unrolled by lcm(STAGES, 2) and every call has fixed
+  // arguments. The last step also scores a next tile, from a stage holding
+  // stale data, and discards the result: one extra QK^T per workgroup keeps a
+  // separate final step out of the loop.
+  if constexpr (C::STAGES == 4) {
+    for (int t = 0; t < ntiles; t += 4) {
+      step(t, sa, sb, lds0, lds1, lds3);
+      if (t + 1 >= ntiles) break;
+      step(t + 1, sb, sa, lds1, lds2, lds0);
+      if (t + 2 >= ntiles) break;
+      step(t + 2, sa, sb, lds2, lds3, lds1);
+      if (t + 3 >= ntiles) break;
+      step(t + 3, sb, sa, lds3, lds0, lds2);
+    }
+  } else {
+    for (int t = 0; t < ntiles; t += 6) {
+      step(t, sa, sb, lds0, lds1, lds2);
+      if (t + 1 >= ntiles) break;
+      step(t + 1, sb, sa, lds1, lds2, lds0);
+      if (t + 2 >= ntiles) break;
+      step(t + 2, sa, sb, lds2, lds0, lds1);
+      if (t + 3 >= ntiles) break;
+      step(t + 3, sb, sa, lds0, lds1, lds2);
+      if (t + 4 >= ntiles) break;
+      step(t + 4, sa, sb, lds1, lds2, lds0);
+      if (t + 5 >= ntiles) break;
+      step(t + 5, sb, sa, lds2, lds0, lds1);
+    }
   }
 
   if (!wave_live) return;

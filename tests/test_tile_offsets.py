@@ -91,3 +91,44 @@ def test_every_issued_tile_reads_inside_the_keys(D, mask_kind, window, heads):
                 for rs in strides:
                     check_tile(D, Lk, k0, rs, swz_k)
                     check_tile(D, Lk, k0, rs, swz_v)
+
+
+# --- V^T operand offsets -------------------------------------------------------------------------
+# The pipelined kernel reads the V^T operand of each PV k-step with two transposed
+# LDS reads per 32-column block. Their byte offsets are formed as one lane offset per
+# block plus a key offset folded into the instruction; this replays that form against
+# the direct per-read formula (row * RB + chunk permuted by the V swizzle of that row).
+
+def swz_v_rows(D, row):
+    return swz_v(D, row)
+
+
+def acc_row32(i, kg):
+    # 32x32 MFMA accumulator row of element i in lane group kg (KG = 2)
+    return (i // 4) * 8 + kg * 4 + i % 4
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_v_operand_offsets_fold_the_key_offset(D):
+    MF, ACC, BN = 32, 16, 32
+    RB, TILE = 2 * D, BN * 2 * D
+    NPV, NDB = BN // 16, D // MF
+    for lane in range(64):
+        kg = lane // MF
+        tr_e = (lane & 15) >> 2
+        tr_c = lane & 3
+        tr_chunk = ((lane >> 4) & 1) * 2 + (tr_c >> 1)
+        tr_half = (tr_c & 1) * 8
+        vk0 = acc_row32(0, kg) + tr_e
+        for t8 in range(NPV):
+            for half in (0, 4):
+                i = 8 * t8 + half
+                key = (i // ACC) * MF + acc_row32(i % ACC, kg) + tr_e
+                kofs = (i // ACC) * MF + acc_row32(i % ACC, 0)
+                assert key == vk0 + kofs and kofs % 8 == 0
+                for db in range(NDB):
+                    ch = db * 4 + tr_chunk
+                    direct = TILE + key * RB + tr_half + ((ch ^ swz_v_rows(D, key)) * 16)
+                    folded = TILE + vk0 * RB + tr_half + (((db * 4 + tr_chunk) ^ swz_v_rows(D, vk0)) * 16) + kofs * RB
+                    assert folded == direct, (D, lane, t8, half, db)
+                    assert TILE <= direct < 2 * TILE

@@ -22,7 +22,10 @@ static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_
     // the plan chose the pipelined kernel (32-row tiles) or, at 256-wide
     // heads on a grid too small to fill the chip, the generic one
     if (s.mf == C::MF && s.block_n == C::BN) {
-      hipLaunchKernelGGL((prefill_fast_kernel<E, D>), grid, dim3(C::NW * 64), 0, stream, a);
+      if (a.mask_kind == kMaskBool)
+        hipLaunchKernelGGL((prefill_fast_kernel<E, D, true>), grid, dim3(C::NW * 64), 0, stream, a);
+      else
+        hipLaunchKernelGGL((prefill_fast_kernel<E, D, false>), grid, dim3(C::NW * 64), 0, stream, a);
       return hipGetLastError();
     }
   }

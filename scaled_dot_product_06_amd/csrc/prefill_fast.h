@@ -79,7 +79,9 @@ template <int D> __device__ __forceinline__ int swz_v(int row) {
 // the compiler's own wait tracking sees it.
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <class E, int D>
+// BOOLMASK: the call has a boolean mask (packed into bits); the other
+// instantiation serves causal and unmasked calls without the mask-word code.
+template <class E, int D, bool BOOLMASK>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FastCfg<D>::WPE, FastCfg<D>::WPE)))
 prefill_fast_kernel(FwdArgs a) {
   using C = FastCfg<D>;
@@ -120,7 +122,7 @@ prefill_fast_kernel(FwdArgs a) {
   const int tb = kbeg / BN;
   const int ntiles = max((kend + BN - 1) / BN - tb, 0);
   // keys every row of this wavefront sees: [w_klo, w_kfull)
-  int w_kfull = a.mask_kind == kMaskBool ? 0 : a.Lk;
+  int w_kfull = BOOLMASK ? 0 : a.Lk;
   if (a.mask_kind == kMaskCausal) w_kfull = min(a.Lk, wi0 + shift + 1);
   int w_klo = 0;
   if (a.window > 0) w_klo = min(wi0 + C::ROWS, a.Lq) - 1 + shift - a.window + 1;
@@ -142,7 +144,7 @@ prefill_fast_kernel(FwdArgs a) {
 
   // boolean mask: each lane's row of packed mask words; the word of tile t
   // is fetched one step ahead (before that step's tile loads are issued)
-  const bool bool_mask = a.mask_kind == kMaskBool;
+  constexpr bool bool_mask = BOOLMASK;
   const uint32_t* mbrow[QB];
   uint32_t mw_cur[QB], mw_nxt[QB];
 #pragma unroll
@@ -275,7 +277,7 @@ prefill_fast_kernel(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < QB; ++r) {
       const bool row_ok = iq[r] < a.Lq;
-      if (a.mask_kind == kMaskBool) {
+      if constexpr (BOOLMASK) {
         // the tile's 32 keys are one word of the row's packed mask (zero past
         // Lk); the lane's keys sit at acc_row(i, kg) = acc_row(i, 0) + 4 kg
         static_assert(BN == 32 && C::NSB == 1, "one mask word per tile");
@@ -357,7 +359,7 @@ prefill_fast_kernel(FwdArgs a) {
   uint32_t pk[QB][C::NPK];
   auto step = [&](int t, acc_t (&scur)[QB][C::NSB], acc_t (&snext)[QB][C::NSB], const uint8_t* Scur,
                   const uint8_t* Snext, uint8_t* Sload) {
-    if (bool_mask) {
+    if constexpr (BOOLMASK) {
 #pragma unroll
       for (int r = 0; r < QB; ++r) {
         mw_cur[r] = mw_nxt[r];

@@ -61,7 +61,7 @@ def decode_bytes(p, window: int = 0) -> int:
 # The sources that define each profiled kernel (its code, its argument block and
 # the device helpers it uses); a change to any of them voids its stored traffic.
 KERNEL_SOURCES = {
-    "prefill": ("attn_device.h", "kernels.h", "prefill_fast.h"),
+    "prefill": ("attn_device.h", "kernels.h", "prefill_fast.h", "prefill_f16bf16.hip"),
     "decode": ("attn_device.h", "kernels.h", "decode_impl.h", "decode.hip"),
 }
 

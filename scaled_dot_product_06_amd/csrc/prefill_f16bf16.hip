@@ -1,6 +1,7 @@
 // Prefill kernel instantiations for 16-bit inputs (bf16 and f16).
 #include "prefill_fast.h"
 #include "prefill_impl.h"
+#include "prefill_ksplit.h"
 
 namespace sdpa {
 
@@ -15,6 +16,21 @@ static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_
                        stream, a);
     return hipGetLastError();
   }
+  if constexpr (prefill_can_ksplit(elem, D, DV, kMaskNone)) {
+    using C = KsplitCfg<D>;
+    static_assert(C::MF == kKsplitRows && C::SUB == kKsplitBN && C::KL == kKsplitLanes && C::NWH == kPrefillWaves,
+                  "planner geometry must match the kernel");
+    // the plan chose the key-split kernel (256-wide heads on a small grid)
+    if (s.ksplit > 1) {
+      if (s.ksplit != C::KL || s.mf != C::MF || s.block_n != C::SUB || s.waves != C::NW) return hipErrorInvalidConfiguration;
+      if (a.mask_kind == kMaskBool)
+        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, true>), grid, dim3(C::NW * 64), 0, stream, a);
+      else
+        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, false>), grid, dim3(C::NW * 64), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  if (s.ksplit > 1) return hipErrorInvalidConfiguration;
   if constexpr (prefill_can_fast(elem, D, DV, kMaskNone)) {
     using C = FastCfg<D>;
     static_assert(C::MF == kFastRows && C::ROWS == kFastRows && C::BN == kFastBN && C::NW == kPrefillWaves,

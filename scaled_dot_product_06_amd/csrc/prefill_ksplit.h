@@ -1,0 +1,393 @@
+// Prefill for 16-bit inputs with 256-wide heads on grids too small to fill the
+// chip with 32-row work: the tiled online-softmax walk of lattice-inference
+// "src/attention/flash.rs" (run_tiled_attention_head), with the bottom-right
+// causal alignment of nuvec-core "tests/fast.rs"
+// (attention_fallback_matches_a_direct_formula), laid out for gfx950:
+//
+//  * each wavefront owns 16 query rows of one head (16x16x32 MFMA tiles), so
+//    its query fragment (32 registers) and output (64) leave room for two
+//    wavefronts per SIMD;
+//  * the workgroup's eight wavefronts are four (head, row block) slots times
+//    two key lanes. The workgroup walks the keys in 64-key steps; in each,
+//    key lane j takes keys [32j, 32j + 32) of the step, so every wavefront
+//    keeps its own online-softmax state over half of the keys, and at the end
+//    the two lanes of a slot merge (m, l, O) in LDS with the log-sum-exp
+//    combine. A workgroup thus covers 16 rows of four heads with two
+//    wavefronts on each SIMD, and a 1024-row, 16-head call fills 256 compute
+//    units;
+//  * K and V steps go from global memory straight into LDS
+//    (global_load_lds_dwordx4) through two double-buffered rings (K and V,
+//    32 KB per step each, 128 KB in all): the K of step t+2 and the V of step
+//    t+1 are loaded while step t runs, one barrier per step;
+//  * the walk is software-pipelined inside each wavefront: the QK^T MFMAs of
+//    step t+1 are issued among the exponentials of step t, and the PV MFMAs of
+//    step t among the row maxima of step t+1;
+//  * tiles some row sees only in part (the causal diagonal, a ragged end,
+//    every tile under a boolean mask) have their hidden scores set to -inf and
+//    their row maxima taken again, at the top of their step;
+//  * LDS rows hold their 16-byte chunks permuted by an XOR of the row index,
+//    different for K (16 consecutive rows, one chunk each per read) and V
+//    (16 rows, two adjacent chunks each per transposed read), so reads spread
+//    over all banks.
+#pragma once
+
+#include "attn_device.h"
+#include "kernels.h"
+
+namespace sdpa {
+
+template <int D>
+struct KsplitCfg {
+  static constexpr int MF = 16, KW = 32, ACC = 4, KG = 4;
+  static constexpr int ROWS = 16;              // query rows per wavefront
+  static constexpr int SUB = 32;               // keys per wavefront per step
+  static constexpr int KL = kKsplitLanes;      // key lanes
+  static constexpr int BN = KL * SUB;          // keys per step
+  static constexpr int NWH = kPrefillWaves;    // (head, row block) slots per workgroup
+  static constexpr int NW = NWH * KL;          // wavefronts per workgroup
+  static constexpr int RB = D * 2;             // bytes per row
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int ROWS_PER_KB = 1024 / RB;
+  static constexpr int TILE_BYTES = BN * RB;   // one step of K (or V)
+  static constexpr int LOADS = TILE_BYTES / 1024;
+  static constexpr int LOADS_PER_WAVE = LOADS / NW;
+  static constexpr int NQC = D / KW;           // QK^T k-steps
+  static constexpr int NSB = SUB / MF;         // 16-key blocks per wavefront step
+  static constexpr int NDB = D / MF;           // 16-column output blocks
+  static constexpr int NPK = SUB * MF / 64 / 2;  // packed weight pairs per lane
+  static_assert(D == 256, "the key-split prefill serves 256-wide heads");
+  static_assert(LOADS % NW == 0, "loads divide among wavefronts");
+  static_assert(NSB == 2 && NPK == 4, "two 16-key blocks make one 32-key PV step");
+};
+
+// K: the chunk of row r sits at slot chunk ^ (r % 32); the 16 rows one read
+// touches (r0 .. r0+15, r0 a multiple of 16) land on 16 different slots.
+template <int D> __device__ __forceinline__ int ks_swz_k(int row) { return row % KsplitCfg<D>::CPR; }
+// V: pairs of chunks move together (XOR by an even number), by 2 * (r % 8); the
+// 16 rows of a transposed read put 8 different pairs on each 256-byte line.
+template <int D> __device__ __forceinline__ int ks_swz_v(int row) { return 2 * (row % 8); }
+
+// s_waitcnt immediate: vmcnt(n) only (gfx9 encoding, the other counters left at their maxima)
+constexpr int ks_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// permlane16_swap(x, x) leaves in every lane the values of the two 16-lane rows
+// of its pair: {even row, odd row}; so the pair reduction is over lanes l, l^16.
+__device__ __forceinline__ float max_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <class E, int D, bool BOOLMASK>
+__global__ void __launch_bounds__(KsplitCfg<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_ksplit_kernel(FwdArgs a) {
+  using C = KsplitCfg<D>;
+  constexpr int MF = C::MF, BN = C::BN, SUB = C::SUB;
+  using acc_t = f32x4;
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs1[C::TILE_BYTES];
+  __shared__ float merge_ml[C::NWH][2][MF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kl = w / C::NWH;          // key lane
+  const int ws = w % C::NWH;          // (head, row block) slot
+  const int col = lane % MF;          // query within the wavefront's rows
+  const int kg = lane / MF;           // k-group (4 of them)
+
+  const int heads = a.Hq * a.B / a.head_blocks;
+  const int wph = C::NWH / heads;
+  const int bm = wph * C::ROWS;
+  int hb, qb;
+  prefill_item((int)blockIdx.x, a.head_blocks, a.nqb, a.group / heads, hb, qb);
+  const int groups_per_b = a.Hq / heads;
+  const int b = hb / groups_per_b;
+  const int h0 = (hb % groups_per_b) * heads;
+  const int hkv = h0 / a.group;
+  const int h = h0 + ws / wph;
+  const int wi0 = qb * bm + (ws % wph) * C::ROWS;
+  const int shift = a.Lk - a.Lq;
+
+  // keys the workgroup needs ([kbeg, kend)), in steps tb .. tb + ntiles - 1
+  int kend = a.Lk;
+  if (a.mask_kind == kMaskCausal) kend = min(a.Lk, min(qb * bm + bm, a.Lq) - 1 + shift + 1);
+  if (kend < 0) kend = 0;
+  int kbeg = 0;
+  if (a.window > 0) kbeg = min(max(0, qb * bm + shift - a.window + 1), kend);
+  const int tb = kbeg / BN;
+  const int ntiles = max((kend + BN - 1) / BN - tb, 0);
+  // keys every row of this wavefront sees: [w_klo, w_kfull)
+  int w_kfull = BOOLMASK ? 0 : a.Lk;
+  if (a.mask_kind == kMaskCausal) w_kfull = min(a.Lk, wi0 + shift + 1);
+  int w_klo = 0;
+  if (a.window > 0) w_klo = min(wi0 + C::ROWS, a.Lq) - 1 + shift - a.window + 1;
+
+  const int iq = wi0 + col;
+  u32x4 qop[C::NQC];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + b * a.qs[0] + h * a.qs[1] + (int64_t)iq * a.qs[2];
+#pragma unroll
+    for (int c = 0; c < C::NQC; ++c) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (iq < a.Lq) x = ld_global16(qp + c * C::KW + kg * 8);
+      qop[c] = x ^ a.qsign;
+    }
+  }
+
+  // boolean mask: the lane's row of packed words; its 32 keys of a step are
+  // word 2 * step + kl (none past the row's last word: those keys are past Lk),
+  // fetched one step ahead together with that step's tiles
+  const uint32_t* mbrow = BOOLMASK ? a.mbits + (size_t)min(iq, a.Lq - 1) * a.mwords : nullptr;
+  auto mask_word = [&](int step) -> uint32_t {
+    const int wi = step * C::KL + kl;
+    return wi < a.mwords ? mbrow[wi] : 0u;
+  };
+  uint32_t mw_cur = 0u, mw_nxt = 0u;
+  if (BOOLMASK && ntiles > 0) mw_nxt = mask_word(tb);
+
+  acc_t o[C::NDB];
+#pragma unroll
+  for (int d = 0; d < C::NDB; ++d) o[d] = acc_t{};
+  const bool has_sink = a.sinks != nullptr;
+  const float sink2 = has_sink ? half_to_f32<E>(((const uint16_t*)a.sinks)[h]) * kLog2e : 0.0f;
+  float m = has_sink ? sink2 : -INFINITY;
+  float l = 0.0f, tmax = -INFINITY;
+
+  const uint8_t* kbase = (const uint8_t*)a.k + (b * a.ks[0] + hkv * a.ks[1]) * 2;
+  const uint8_t* vbase = (const uint8_t*)a.v + (b * a.vs[0] + hkv * a.vs[1]) * 2;
+  const uint32_t krs = (uint32_t)(a.ks[2] * 2), vrs = (uint32_t)(a.vs[2] * 2);
+
+  // direct loads: the lane's 16-byte chunk of rows (w + NW*it) * ROWS_PER_KB + lane / CPR
+  const int ld_row = lane / C::CPR;
+  const int ld_slot = lane % C::CPR;
+  uint32_t offk[C::LOADS_PER_WAVE], offv[C::LOADS_PER_WAVE];
+  int ldrow[C::LOADS_PER_WAVE];
+#pragma unroll
+  for (int it = 0; it < C::LOADS_PER_WAVE; ++it) {
+    const int row = (w + C::NW * it) * C::ROWS_PER_KB + ld_row;
+    ldrow[it] = row;
+    offk[it] = row * krs + (ld_slot ^ ks_swz_k<D>(row)) * 16;
+    offv[it] = row * vrs + (ld_slot ^ ks_swz_v<D>(row)) * 16;
+  }
+  // rows past the last key read the last key's row instead (their weights are
+  // zero); a step starts at most at Lk - 1, so the unsigned offsets stay >= 0
+  auto tail_over = [&](int k0, int it) -> uint32_t {
+    return (uint32_t)max(k0 + ldrow[it] - (a.Lk - 1), 0);
+  };
+  auto issue_k = [&](int step, uint8_t* dst) {
+    const int k0 = step * BN;
+    const uint8_t* kt = kbase + (size_t)k0 * krs;
+    const bool tail = k0 + BN > a.Lk;
+#pragma unroll
+    for (int it = 0; it < C::LOADS_PER_WAVE; ++it) {
+      uint32_t ok = offk[it];
+      if (tail) ok -= tail_over(k0, it) * krs;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + ok),
+                                       (__attribute__((address_space(3))) void*)(dst + (w + C::NW * it) * 1024), 16,
+                                       0, 0);
+    }
+  };
+  auto issue_v = [&](int step, uint8_t* dst) {
+    const int k0 = step * BN;
+    const uint8_t* vt = vbase + (size_t)k0 * vrs;
+    const bool tail = k0 + BN > a.Lk;
+#pragma unroll
+    for (int it = 0; it < C::LOADS_PER_WAVE; ++it) {
+      uint32_t ov = offv[it];
+      if (tail) ov -= tail_over(k0, it) * vrs;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt + ov),
+                                       (__attribute__((address_space(3))) void*)(dst + (w + C::NW * it) * 1024), 16,
+                                       0, 0);
+    }
+  };
+
+  // K operand of key block nb, k-step c: row SUB*kl + 16 nb + col, chunk 4c + kg.
+  // With the row's XOR (16 nb + col), the four k-steps c and c + 4 and the two
+  // blocks differ by constants, so four lane offsets serve all sixteen reads.
+  uint32_t kb4[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) kb4[c] = (SUB * kl + col) * C::RB + (((4 * c + kg) ^ col) * 16);
+  auto k_off = [&](int c, int nb) -> uint32_t {
+    return c < 4 ? kb4[c] + nb * (16 * C::RB + 256) : kb4[c - 4] + 256 + nb * (16 * C::RB - 256);
+  };
+  // V^T operand of output block db: transposed reads of keys 4g..4g+3 and
+  // 16+4g..16+4g+3 (g = lane / 16); provider lane l points at row
+  // SUB*kl + l/4 (+16), columns 16 db + 4 (l % 4) .. +3. The V XOR pairs chunk
+  // 2 db with row % 8, so blocks db and db + 8 differ by 256 bytes.
+  const int vr = lane >> 2;
+  uint32_t vb8[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    vb8[db] = (SUB * kl + vr) * C::RB + ((2 * (db ^ (vr % 8)) + ((lane >> 1) & 1)) * 16) + (lane & 1) * 8;
+  auto v_off = [&](int db) -> uint32_t { return db < 8 ? vb8[db] : vb8[db - 8] + 256; };
+
+  // S^T = K Q^T for the wavefront's 32 keys of one step
+  auto qk = [&](const uint8_t* Ks, acc_t (&s)[C::NSB]) {
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb) s[nb] = acc_t{};
+#pragma unroll
+    for (int c = 0; c < C::NQC; ++c)
+#pragma unroll
+      for (int nb = 0; nb < C::NSB; ++nb) {
+        const u32x4 kop = *reinterpret_cast<const u32x4*>(Ks + k_off(c, nb));
+        s[nb] = mma16<E, MF>(kop, qop[c], s[nb]);
+      }
+  };
+  auto row_max16 = [](float x) { return max_xor16(max_xor32(x)); };
+  auto tile_max_full = [&](acc_t (&s)[C::NSB]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+      for (int i = 0; i < C::ACC; ++i) mx = fmaxf(mx, s[nb][i]);
+    tmax = row_max16(mx) * a.c;
+  };
+  // the lane's scores sit at keys k0 + 16 nb + 4 kg + i of the step's sub-tile
+  auto tile_max_masked = [&](int step, acc_t (&s)[C::NSB], uint32_t mw) {
+    const int k0 = step * BN + SUB * kl;
+    const bool row_ok = iq < a.Lq;
+    if constexpr (BOOLMASK) {
+      const uint32_t wsh = row_ok ? (mw >> (4 * kg)) : 0u;
+#pragma unroll
+      for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+        for (int i = 0; i < C::ACC; ++i) s[nb][i] = keep_if_bit(s[nb][i], wsh, 16 * nb + i);
+    } else {
+      const int lim = a.mask_kind == kMaskCausal ? min(iq + shift, a.Lk - 1) : a.Lk - 1;
+      const int lo = a.window > 0 ? iq + shift - a.window : -1;
+#pragma unroll
+      for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+        for (int i = 0; i < C::ACC; ++i) {
+          const int key = k0 + 16 * nb + 4 * kg + i;
+          const bool vis = row_ok & (key <= lim) & (key > lo);
+          s[nb][i] = vis ? s[nb][i] : -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+      for (int i = 0; i < C::ACC; ++i) mx = fmaxf(mx, s[nb][i]);
+    mx = row_max16(mx);
+    tmax = (mx == -INFINITY) ? -INFINITY : mx * a.c;
+  };
+  // weights rounded to 16 bits; the running sum adds the same rounded weights
+  auto weights = [&](acc_t (&s)[C::NSB], uint32_t (&pk)[C::NPK]) {
+    const float mu = (m == -INFINITY) ? 0.0f : m;
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+      for (int i = 0; i < C::ACC; i += 2) {
+        const float p0 = fast_exp2(fmaf(s[nb][i], a.c, -mu));
+        const float p1 = fast_exp2(fmaf(s[nb][i + 1], a.c, -mu));
+        pk[nb * 2 + i / 2] = pack2<E>(p0, p1);
+      }
+    float l0 = pair_sum<E>(pk[0], 0.0f), l1 = pair_sum<E>(pk[1], 0.0f);
+    l0 = pair_sum<E>(pk[2], l0);
+    l1 = pair_sum<E>(pk[3], l1);
+    l += l0 + l1;
+  };
+  // O^T += V^T P^T: MFMA k-slot 8g + e is key 4g + e (e < 4) or 16 + 4g + e - 4
+  auto pv = [&](const uint8_t* Vs, const uint32_t (&pk)[C::NPK]) {
+    const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const u32x2 ra = lds_read_tr16((const uint16_t*)(Vs + v_off(db)));
+      const u32x2 rb = lds_read_tr16((const uint16_t*)(Vs + v_off(db) + 16 * C::RB));
+      o[db] = mma16<E, MF>(u32x4{ra[0], ra[1], rb[0], rb[1]}, pb, o[db]);
+    }
+  };
+
+  acc_t sa[C::NSB], sb[C::NSB];
+  uint32_t pk[C::NPK];
+  // Step t: the loads of step t+1's K and step t's V have landed (they were the
+  // last issued, so vmcnt(0)), and after the barrier every wavefront is done
+  // with step t-1, so K stage t%2 (held K(t), scored in step t-1) and V stage
+  // (t+1)%2 (held V(t-1)) take K(t+2) and V(t+1).
+  auto step = [&](int t, acc_t (&scur)[C::NSB], acc_t (&snext)[C::NSB], const uint8_t* Knext, uint8_t* Kload,
+                  const uint8_t* Vcur, uint8_t* Vload) {
+    __builtin_amdgcn_s_waitcnt(ks_vmcnt(0));
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 2 < ntiles) issue_k(tb + t + 2, Kload);
+    if (t + 1 < ntiles) issue_v(tb + t + 1, Vload);
+    if constexpr (BOOLMASK) {
+      mw_cur = mw_nxt;
+      mw_nxt = t + 1 < ntiles ? mask_word(tb + t + 1) : 0u;
+    }
+    const int kt = tb + t;
+    const int k0 = kt * BN + SUB * kl;
+    if (k0 + SUB > w_kfull || k0 < w_klo) tile_max_masked(kt, scur, mw_cur);
+    softmax_rebase<C::NDB>(tmax, m, l, o);
+    qk(Knext, snext);
+    weights(scur, pk);
+    pv(Vcur, pk);
+    tile_max_full(snext);
+  };
+
+  // prologue: K(0), V(0), K(1) in flight; step 0's scores from K(0)
+  if (ntiles > 0) {
+    issue_k(tb, ks0);
+    issue_v(tb, vs0);
+  }
+  if (ntiles > 1) issue_k(tb + 1, ks1);
+  if (ntiles > 1) {
+    __builtin_amdgcn_s_waitcnt(ks_vmcnt(2 * C::LOADS_PER_WAVE));
+  } else {
+    __builtin_amdgcn_s_waitcnt(ks_vmcnt(0));
+  }
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (ntiles > 0) {
+    qk(ks0, sa);
+    tile_max_full(sa);
+  }
+  // even steps score into sb from K stage 1 and read V stage 0; odd steps the
+  // reverse. The last step also scores a next tile from a stage holding stale
+  // (or never loaded) data and discards it.
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, sa, sb, ks1, ks0, vs0, vs1);
+    if (t + 1 >= ntiles) break;
+    step(t + 1, sb, sa, ks0, ks1, vs1, vs0);
+  }
+
+  // merge the two key lanes of each slot: lane 1 leaves (m, l, O) in LDS (the
+  // K ring, free once every wavefront has passed this barrier), lane 0 combines
+  __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  l = sum_xor16(sum_xor32(l));
+  f32x4* part = reinterpret_cast<f32x4*>(ws < 2 ? ks0 : ks1) + (ws % 2) * (C::NDB * 64);
+  if (kl == 1) {
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) part[db * 64 + lane] = o[db];
+    if (kg == 0) {
+      merge_ml[ws][0][col] = m;
+      merge_ml[ws][1][col] = l;
+    }
+  }
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (kl == 1 || wi0 >= a.Lq) return;
+  const float m1 = merge_ml[ws][0][col], l1 = merge_ml[ws][1][col];
+  const float mm = fmaxf(m, m1);
+  const float f0 = m == -INFINITY ? 0.0f : fast_exp2(m - mm);
+  const float f1 = m1 == -INFINITY ? 0.0f : fast_exp2(m1 - mm);
+  float lt = l * f0 + l1 * f1;
+  if (has_sink) lt += fast_exp2(sink2 - mm);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (iq >= a.Lq) return;
+  const float g0 = f0 * inv, g1 = f1 * inv;
+  uint16_t* op = (uint16_t*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq) * D;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    const f32x4 p = part[db * 64 + lane];
+    const f32x4 r = o[db] * g0 + p * g1;
+    const u32x2 st = {pack2<E>(r[0], r[1]), pack2<E>(r[2], r[3])};
+    st_global8(op + db * MF + kg * 4, st);
+  }
+}
+
+}  // namespace sdpa

@@ -275,9 +275,36 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
   const int nw = prefill_waves(dtype, (int)D, (int)Dv);
   const int64_t heads = gcd64(group, nw);
   bool fast = prefill_can_fast(dtype, (int)D, (int)Dv, mask_kind);
+  bool kspl = false;
   if (fast && prefill_fast_needs_grid((int)D)) {
     const int64_t fbm = (nw / heads) * kFastRows;
     fast = (Hq / heads) * ((Lq + fbm - 1) / fbm) >= kFastMinGridWide;
+    kspl = !fast && prefill_can_ksplit(dtype, (int)D, (int)Dv, mask_kind);
+  }
+  if (kspl) {
+    // 16-row query blocks of `heads` heads per workgroup, two key lanes of wavefronts
+    const int64_t kbm = (nw / heads) * kKsplitRows;
+    const int64_t nqb = (Lq + kbm - 1) / kbm;
+    if ((B * Hq / heads) * nqb > INT_MAX)
+      return fail(SDPA_ERR_UNSUPPORTED, "Lq (%lld) needs more than INT_MAX workgroups in all", (long long)Lq);
+    p.route = SDPA_ROUTE_PREFILL;
+    p.kernels = 1;
+    p.rows_per_wave = kKsplitRows;
+    p.waves = nw * kKsplitLanes;
+    p.block_n = kKsplitBN;
+    p.heads_per_group = (int32_t)heads;
+    p.splits = kKsplitLanes;
+    p.grid[0] = (B * Hq / heads) * nqb;
+    p.grid[1] = 1;
+    p.grid[2] = 1;
+    if (prefill_packs_mask(dtype, mask_kind)) {
+      int64_t sb;
+      if (!mul3(Lq, mask_words(Lk), 4, &sb)) return fail(SDPA_ERR_INVALID, "mask-bit scratch size overflows");
+      p.kernels = 2;
+      p.scratch_bytes = sb;
+    }
+    *plan = p;
+    return SDPA_OK;
   }
   int rows = fast ? kFastRows : prefill_generic_mf(dtype, (int)D, (int)Dv);
   bool ksplit = false;

@@ -62,10 +62,14 @@ def test_workload_routes(number, route):
     else:
         assert p["kernels"] == 1 and p["scratch_bytes"] == 0
     if route == "prefill":
-        if p["splits"]:
+        if p["splits"] and w["dtype"] == 0:
             # the waves of a workgroup split the keys of one query block
-            assert w["dtype"] == 0 and p["splits"] == p["waves"] and p["heads_per_group"] == 1
+            assert p["splits"] == p["waves"] and p["heads_per_group"] == 1
             rows_per_block = p["rows_per_wave"]
+        elif p["splits"]:
+            # 256-wide 16-bit heads on a small grid: two key lanes of wavefronts
+            assert (w["D"], p["splits"], p["rows_per_wave"], p["block_n"]) == (256, 2, 16, 32)
+            rows_per_block = p["waves"] // p["splits"] // p["heads_per_group"] * p["rows_per_wave"]
         else:
             rows_per_block = p["waves"] // p["heads_per_group"] * p["rows_per_wave"]
         head_blocks = w["B"] * w["Hq"] // p["heads_per_group"]
@@ -351,18 +355,25 @@ def test_f32_paged_plans_are_prefill_plans():
 
 def test_wide_heads_plan_the_pipelined_kernel_only_on_full_grids():
     # 256-wide 16-bit heads take the pipelined 32-row kernel when one batch item's grid
-    # has a workgroup per compute unit (256), the generic 16-row kernel below that; the
+    # has a workgroup per compute unit (256), the key-split 16-row kernel below that; the
     # batch size never changes the choice
+    def shape(p):
+        return p["rows_per_wave"], p["block_n"], p["splits"], p["waves"]
     big = sd.sdpa_plan(1, 32, 4, 1040, 1297, 256, 256, 1, False, False, 2)   # 8 x 33 = 264
-    assert (big["rows_per_wave"], big["block_n"], big["grid"][0]) == (32, 32, 8 * 33)
+    assert shape(big) + (big["grid"][0],) == (32, 32, 0, 4, 8 * 33)
     assert sd.sdpa_plan(3, 32, 4, 1040, 1297, 256, 256, 1, False, False, 2)["rows_per_wave"] == 32
     edge = sd.sdpa_plan(1, 32, 4, 1000, 1297, 256, 256, 1, False, False, 2)  # 8 x 32 = 256
-    assert (edge["rows_per_wave"], edge["block_n"]) == (32, 32)
+    assert shape(edge) == (32, 32, 0, 4)
     under = sd.sdpa_plan(1, 32, 4, 992, 1297, 256, 256, 1, False, False, 2)  # 8 x 31 = 248
-    assert (under["rows_per_wave"], under["block_n"]) == (16, 64)
+    assert shape(under) + (under["grid"][0],) == (16, 32, 2, 8, 8 * 62)
     small = sd.sdpa_plan(1, 16, 2, 1024, 1801, 256, 256, 2, True, True, 1)  # workload 4: 4 x 32 = 128
-    assert (small["rows_per_wave"], small["block_n"]) == (16, 64)
+    assert shape(small) + (small["grid"][0], small["kernels"]) == (16, 32, 2, 8, 4 * 64, 2)
     batched = sd.sdpa_plan(8, 16, 2, 1024, 1801, 256, 256, 2, True, True, 1)  # the same per batch item
-    assert (batched["rows_per_wave"], batched["block_n"]) == (16, 64)
-    assert sd.sdpa_plan(1, 64, 8, 1024, 1801, 256, 256, 3, True, True, 1)["rows_per_wave"] == 16  # additive
-    assert sd.sdpa_plan(1, 64, 8, 1024, 1801, 192, 192, 1, False, False, 1)["rows_per_wave"] == 16
+    assert shape(batched) + (batched["grid"][0],) == (16, 32, 2, 8, 8 * 4 * 64)
+    # one or two heads per workgroup: 64 or 32 rows of a head per key lane
+    assert sd.sdpa_plan(1, 4, 4, 100, 300, 256, 256, 0, False, False, 2)["grid"][0] == 4 * 2
+    assert sd.sdpa_plan(1, 4, 2, 100, 300, 256, 256, 0, False, False, 2)["grid"][0] == 2 * 4
+    # additive masks and other head sizes keep the generic 16-row kernel
+    add = sd.sdpa_plan(1, 64, 8, 1024, 1801, 256, 256, 3, True, True, 1)
+    assert shape(add) == (16, 64, 0, 4)
+    assert shape(sd.sdpa_plan(1, 64, 8, 1024, 1801, 192, 192, 1, False, False, 1)) == (16, 64, 0, 4)

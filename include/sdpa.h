@@ -70,9 +70,11 @@ typedef struct sdpa_plan_t {
   int32_t rows_per_wave;  /* query rows one wavefront carries (MFMA tile height). Prefill: 32 on
                              the pipelined kernel (f16/bf16, D == Dv in {64, 128}, and 256 when
                              one batch item's grid has at least 256 workgroups, never with an
-                             additive mask), else the generic kernel's 32 (heads up to 128 wide)
-                             or 16 (wider heads; and f32 calls whose 32-row grid for one batch
-                             item would have fewer than 256 workgroups) */
+                             additive mask); 16 on the key-split kernel (f16/bf16,
+                             D == Dv == 256 on smaller grids, no additive mask); else the
+                             generic kernel's 32 (heads up to 128 wide) or 16 (wider heads;
+                             and f32 calls whose 32-row grid for one batch item would have
+                             fewer than 256 workgroups) */
   int32_t waves;          /* wavefronts per workgroup of the first kernel */
   int32_t block_n;        /* keys per tile */
   int32_t heads_per_group;/* prefill: query heads sharing one workgroup's K/V tiles;
@@ -83,12 +85,16 @@ typedef struct sdpa_plan_t {
                              whose 32-row grid for one batch item would have fewer than 256
                              workgroups (no additive mask), the waves of a workgroup
                              that split the keys of its one 16-row query block and merge their
-                             partial results (heads_per_group is then 1) */
+                             partial results (heads_per_group is then 1); or 2 on the key-split
+                             kernel: two lanes of `waves`/2 wavefronts each take 32 of every
+                             `2 * block_n` keys and merge at the end */
   int64_t grid[3];        /* workgroups of the attention kernel (decode: its first pass) (x, y, z) */
   int64_t scratch_bytes;  /* device scratch the call uses. Decode: per (batch, kv head, split, packed
                              row) a 16-byte {max, sum} slot and Dv f32 partial outputs. Prefill: 0,
-                             except f16/bf16 with a boolean mask, whose mask a first small kernel
-                             packs into Lq x ceil(Lk/32) 32-bit words (bit j of word w: key 32w+j) */
+                             except f16/bf16 with a boolean mask outside the key-split kernel,
+                             whose mask a first small kernel packs into Lq x ceil(Lk/32) 32-bit
+                             words (bit j of word w: key 32w+j); the key-split kernel reads the
+                             mask bytes itself */
 } sdpa_plan_t;
 
 /*

@@ -79,7 +79,8 @@ hipError_t launch_paged_write(void* cache, const void* rows, const int32_t* slot
 hipError_t launch_zero_fill(void* out, int64_t bytes, hipStream_t stream);
 hipError_t launch_mask_bits(const uint8_t* mask, uint32_t* bits, int64_t Lq, int64_t Lk, hipStream_t stream);
 constexpr int64_t mask_words(int64_t Lk) { return (Lk + 31) / 32; }
-// The 16-bit prefill kernels read a boolean mask as packed bits.
+// The pipelined and generic 16-bit prefill kernels read a boolean mask as packed
+// bits, made by a first small kernel; the key-split kernel reads the bytes.
 constexpr bool prefill_packs_mask(int elem, int mask_kind) { return elem != kF32 && mask_kind == kMaskBool; }
 
 // Geometry rules shared by the launchers (template arguments) and the planner.

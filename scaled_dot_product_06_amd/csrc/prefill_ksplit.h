@@ -24,7 +24,10 @@
 //    step t among the row maxima of step t+1;
 //  * tiles some row sees only in part (the causal diagonal, a ragged end,
 //    every tile under a boolean mask) have their hidden scores set to -inf and
-//    their row maxima taken again, at the top of their step;
+//    their row maxima taken again, at the top of their step. A boolean mask is
+//    read as the caller's bytes, staged through a small LDS ring, and enters
+//    the scores as the MFMA accumulators' starting values, 0 or -inf, so
+//    masked steps run the unmasked path;
 //  * LDS rows hold their 16-byte chunks permuted by an XOR of the row index,
 //    different for K (16 consecutive rows, one chunk each per read) and V
 //    (16 rows, two adjacent chunks each per transposed read), so reads spread
@@ -67,8 +70,13 @@ template <int D> __device__ __forceinline__ int ks_swz_k(int row) { return row %
 // 16 rows of a transposed read put 8 different pairs on each 256-byte line.
 template <int D> __device__ __forceinline__ int ks_swz_v(int row) { return 2 * (row % 8); }
 
+// bytes between rows of the boolean-mask ring (64 keys plus padding)
+constexpr int kMaskRow = 80;
+
 // s_waitcnt immediate: vmcnt(n) only (gfx9 encoding, the other counters left at their maxima)
 constexpr int ks_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// s_waitcnt immediate: lgkmcnt(0) only
+constexpr int ks_lgkm0() { return 15 | (3 << 14) | (7 << 4); }
 
 // permlane16_swap(x, x) leaves in every lane the values of the two 16-lane rows
 // of its pair: {even row, odd row}; so the pair reduction is over lanes l, l^16.
@@ -92,6 +100,9 @@ prefill_ksplit_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t vs0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t vs1[C::TILE_BYTES];
   __shared__ float merge_ml[C::NWH][2][MF];
+  // boolean mask ring: up to 64 rows x 64 keys per stage, rows 80 bytes apart so
+  // that the 16 rows x 4 groups one wavefront reads fall on 64 different banks
+  __shared__ __attribute__((aligned(16))) uint8_t mstage[2][BOOLMASK ? C::NWH * 16 * kMaskRow : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -123,7 +134,7 @@ prefill_ksplit_kernel(FwdArgs a) {
   const int tb = kbeg / BN;
   const int ntiles = max((kend + BN - 1) / BN - tb, 0);
   // keys every row of this wavefront sees: [w_klo, w_kfull)
-  int w_kfull = BOOLMASK ? 0 : a.Lk;
+  int w_kfull = a.Lk;
   if (a.mask_kind == kMaskCausal) w_kfull = min(a.Lk, wi0 + shift + 1);
   int w_klo = 0;
   if (a.window > 0) w_klo = min(wi0 + C::ROWS, a.Lq) - 1 + shift - a.window + 1;
@@ -140,16 +151,58 @@ prefill_ksplit_kernel(FwdArgs a) {
     }
   }
 
-  // boolean mask: the lane's row of packed words; its 32 keys of a step are
-  // word 2 * step + kl (none past the row's last word: those keys are past Lk),
-  // fetched one step ahead together with that step's tiles
-  const uint32_t* mbrow = BOOLMASK ? a.mbits + (size_t)min(iq, a.Lq - 1) * a.mwords : nullptr;
-  auto mask_word = [&](int step) -> uint32_t {
-    const int wi = step * C::KL + kl;
-    return wi < a.mwords ? mbrow[wi] : 0u;
+  // Boolean mask, read as the caller's bytes. The workgroup's bm rows x 64 keys
+  // of a step (16 rows per loader wavefront, lane l: row l / 4, keys 16 (l % 4)
+  // .. +15, one 16-byte load; global memory is accessed in unaligned mode, so a
+  // group may start at any byte) go through a two-stage LDS ring: loaded into
+  // registers three steps before the step whose scores use them, written to
+  // the ring at the next step, read after that step's barrier. One load per
+  // loader lane and step keeps the per-step address traffic to a few cache
+  // lines per row. Keys at or past Lk read as hidden.
+  const bool mloader = BOOLMASK && w < wph;
+  const uint8_t* mload_row =
+      mloader ? a.mask + (size_t)min(qb * bm + w * 16 + lane / 4, a.Lq - 1) * a.Lk : nullptr;
+  auto mask_chunk = [&](int step) -> u32x4 {
+    const int key = step * BN + 16 * (lane % 4);
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (key + 16 <= a.Lk) {
+      __builtin_memcpy(&x, mload_row + key, 16);
+    } else {
+      uint32_t wv[4] = {0u, 0u, 0u, 0u};
+      for (int j = 0; j < 16 && key + j < a.Lk; ++j) wv[j / 4] |= (uint32_t)mload_row[key + j] << (8 * (j % 4));
+      x = u32x4{wv[0], wv[1], wv[2], wv[3]};
+    }
+    return x;
   };
-  uint32_t mw_cur = 0u, mw_nxt = 0u;
-  if (BOOLMASK && ntiles > 0) mw_nxt = mask_word(tb);
+  auto mask_store = [&](int stage, u32x4 x) {
+    *reinterpret_cast<u32x4*>(&mstage[stage][(w * 16 + lane / 4) * kMaskRow + (lane % 4) * 16]) = x;
+  };
+  // the lane's bytes of a step: row (slot row block) + col, keys 32 kl + 4 kg (+16)
+  const int mrd = ((ws % wph) * 16 + col) * kMaskRow + SUB * kl + 4 * kg;
+  auto mask_read = [&](int stage) -> u32x2 {
+    return u32x2{*reinterpret_cast<const uint32_t*>(&mstage[stage][mrd]),
+                 *reinterpret_cast<const uint32_t*>(&mstage[stage][mrd + 16])};
+  };
+  // The scores of a step start from its mask: each accumulator starts at 0
+  // (visible) or -inf (hidden), so the MFMAs yield the masked scores and the
+  // step needs no separate masking pass.
+  u32x4 mpend = {0u, 0u, 0u, 0u};   // a loader lane's chunk, waiting for its ring stage
+  auto score_init = [&](acc_t (&s)[C::NSB], u32x2 mb) {
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb) {
+      if constexpr (BOOLMASK) {
+        // bit 8i of y: byte i (key 16 nb + 4 kg + i) is nonzero
+        uint32_t y = mb[nb];
+        y |= y >> 4;
+        y |= y >> 2;
+        y |= y >> 1;
+#pragma unroll
+        for (int i = 0; i < C::ACC; ++i) s[nb][i] = keep_if_bit(0.0f, y, 8 * i);
+      } else {
+        s[nb] = acc_t{};
+      }
+    }
+  };
 
   acc_t o[C::NDB];
 #pragma unroll
@@ -227,17 +280,45 @@ prefill_ksplit_kernel(FwdArgs a) {
     vb8[db] = (SUB * kl + vr) * C::RB + ((2 * (db ^ (vr % 8)) + ((lane >> 1) & 1)) * 16) + (lane & 1) * 8;
   auto v_off = [&](int db) -> uint32_t { return db < 8 ? vb8[db] : vb8[db - 8] + 256; };
 
-  // S^T = K Q^T for the wavefront's 32 keys of one step
+  // LDS operands go through two register buffers of eight 16-byte groups: the
+  // reads of one group are issued before the MFMAs of the previous one, and an
+  // explicit wait for all LDS reads follows those MFMAs. (With direct-to-LDS loads
+  // in flight every LDS wait is a wait for all reads, so this keeps each wait
+  // behind a group of MFMAs instead of in front of each one.)
+  auto read_k = [&](const uint8_t* Ks, int c0, u32x4 (&buf)[8]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int nb = 0; nb < C::NSB; ++nb) buf[c * 2 + nb] = *reinterpret_cast<const u32x4*>(Ks + k_off(c0 + c, nb));
+  };
+  auto mma_qk = [&](int c0, const u32x4 (&buf)[8], acc_t (&s)[C::NSB]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int nb = 0; nb < C::NSB; ++nb) s[nb] = mma16<E, MF>(buf[c * 2 + nb], qop[c0 + c], s[nb]);
+  };
+  auto read_v = [&](const uint8_t* Vs, int db0, u32x4 (&buf)[8]) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const u32x2 ra = lds_read_tr16((const uint16_t*)(Vs + v_off(db0 + d)));
+      const u32x2 rb = lds_read_tr16((const uint16_t*)(Vs + v_off(db0 + d) + 16 * C::RB));
+      buf[d] = u32x4{ra[0], ra[1], rb[0], rb[1]};
+    }
+  };
+  auto lds_wait = [] { __builtin_amdgcn_s_waitcnt(ks_lgkm0()); };
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  // S^T = K Q^T for the wavefront's 32 keys of one step (not pipelined: the prologue)
   auto qk = [&](const uint8_t* Ks, acc_t (&s)[C::NSB]) {
-#pragma unroll
-    for (int nb = 0; nb < C::NSB; ++nb) s[nb] = acc_t{};
-#pragma unroll
-    for (int c = 0; c < C::NQC; ++c)
-#pragma unroll
-      for (int nb = 0; nb < C::NSB; ++nb) {
-        const u32x4 kop = *reinterpret_cast<const u32x4*>(Ks + k_off(c, nb));
-        s[nb] = mma16<E, MF>(kop, qop[c], s[nb]);
-      }
+    u32x4 ba[8], bb[8];
+    u32x2 mb = {0u, 0u};
+    if constexpr (BOOLMASK) mb = mask_read(0);
+    read_k(Ks, 0, ba);
+    lds_wait();
+    score_init(s, mb);
+    read_k(Ks, 4, bb);
+    lds_wait();
+    mma_qk(0, ba, s);
+    mma_qk(4, bb, s);
   };
   auto row_max16 = [](float x) { return max_xor16(max_xor32(x)); };
   auto tile_max_full = [&](acc_t (&s)[C::NSB]) {
@@ -249,27 +330,20 @@ prefill_ksplit_kernel(FwdArgs a) {
     tmax = row_max16(mx) * a.c;
   };
   // the lane's scores sit at keys k0 + 16 nb + 4 kg + i of the step's sub-tile
-  auto tile_max_masked = [&](int step, acc_t (&s)[C::NSB], uint32_t mw) {
+  // (causal and window limits, and keys past Lk; a boolean mask is already in the scores)
+  auto tile_max_masked = [&](int step, acc_t (&s)[C::NSB]) {
     const int k0 = step * BN + SUB * kl;
     const bool row_ok = iq < a.Lq;
-    if constexpr (BOOLMASK) {
-      const uint32_t wsh = row_ok ? (mw >> (4 * kg)) : 0u;
+    const int lim = a.mask_kind == kMaskCausal ? min(iq + shift, a.Lk - 1) : a.Lk - 1;
+    const int lo = a.window > 0 ? iq + shift - a.window : -1;
 #pragma unroll
-      for (int nb = 0; nb < C::NSB; ++nb)
+    for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
-        for (int i = 0; i < C::ACC; ++i) s[nb][i] = keep_if_bit(s[nb][i], wsh, 16 * nb + i);
-    } else {
-      const int lim = a.mask_kind == kMaskCausal ? min(iq + shift, a.Lk - 1) : a.Lk - 1;
-      const int lo = a.window > 0 ? iq + shift - a.window : -1;
-#pragma unroll
-      for (int nb = 0; nb < C::NSB; ++nb)
-#pragma unroll
-        for (int i = 0; i < C::ACC; ++i) {
-          const int key = k0 + 16 * nb + 4 * kg + i;
-          const bool vis = row_ok & (key <= lim) & (key > lo);
-          s[nb][i] = vis ? s[nb][i] : -INFINITY;
-        }
-    }
+      for (int i = 0; i < C::ACC; ++i) {
+        const int key = k0 + 16 * nb + 4 * kg + i;
+        const bool vis = row_ok & (key <= lim) & (key > lo);
+        s[nb][i] = vis ? s[nb][i] : -INFINITY;
+      }
     float mx = -INFINITY;
 #pragma unroll
     for (int nb = 0; nb < C::NSB; ++nb)
@@ -295,14 +369,10 @@ prefill_ksplit_kernel(FwdArgs a) {
     l += l0 + l1;
   };
   // O^T += V^T P^T: MFMA k-slot 8g + e is key 4g + e (e < 4) or 16 + 4g + e - 4
-  auto pv = [&](const uint8_t* Vs, const uint32_t (&pk)[C::NPK]) {
+  auto mma_pv = [&](int db0, const u32x4 (&buf)[8], const uint32_t (&pk)[C::NPK]) {
     const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      const u32x2 ra = lds_read_tr16((const uint16_t*)(Vs + v_off(db)));
-      const u32x2 rb = lds_read_tr16((const uint16_t*)(Vs + v_off(db) + 16 * C::RB));
-      o[db] = mma16<E, MF>(u32x4{ra[0], ra[1], rb[0], rb[1]}, pb, o[db]);
-    }
+    for (int d = 0; d < 8; ++d) o[db0 + d] = mma16<E, MF>(buf[d], pb, o[db0 + d]);
   };
 
   acc_t sa[C::NSB], sb[C::NSB];
@@ -315,23 +385,53 @@ prefill_ksplit_kernel(FwdArgs a) {
                   const uint8_t* Vcur, uint8_t* Vload) {
     __builtin_amdgcn_s_waitcnt(ks_vmcnt(0));
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // the mask of step t + 2 into ring stage t % 2 (last read for step t's scores)
+    if (mloader) mask_store(t & 1, mpend);
     if (t + 2 < ntiles) issue_k(tb + t + 2, Kload);
     if (t + 1 < ntiles) issue_v(tb + t + 1, Vload);
-    if constexpr (BOOLMASK) {
-      mw_cur = mw_nxt;
-      mw_nxt = t + 1 < ntiles ? mask_word(tb + t + 1) : 0u;
-    }
+    if (mloader && t + 3 < ntiles) mpend = mask_chunk(tb + t + 3);
     const int kt = tb + t;
     const int k0 = kt * BN + SUB * kl;
-    if (k0 + SUB > w_kfull || k0 < w_klo) tile_max_masked(kt, scur, mw_cur);
+    if (k0 + SUB > w_kfull || k0 < w_klo) tile_max_masked(kt, scur);
     softmax_rebase<C::NDB>(tmax, m, l, o);
-    qk(Knext, snext);
+    u32x4 ba[8], bb[8];
+    u32x2 mb = {0u, 0u};
+    fence();
+    if constexpr (BOOLMASK) mb = mask_read((t + 1) & 1);
+    read_k(Knext, 0, ba);
     weights(scur, pk);
-    pv(Vcur, pk);
+    fence();
+    lds_wait();
+    read_k(Knext, 4, bb);
+    score_init(snext, mb);
+    fence();
+    mma_qk(0, ba, snext);
+    fence();
+    lds_wait();
+    read_v(Vcur, 0, ba);
+    fence();
+    mma_qk(4, bb, snext);
+    fence();
+    lds_wait();
+    read_v(Vcur, 8, bb);
+    fence();
+    mma_pv(0, ba, pk);
+    fence();
+    lds_wait();
+    mma_pv(8, bb, pk);
+    fence();
     tile_max_full(snext);
   };
 
-  // prologue: K(0), V(0), K(1) in flight; step 0's scores from K(0)
+  // prologue: the mask of steps 0 and 1 into the ring and step 2's in registers;
+  // K(0), V(0), K(1) in flight; step 0's scores from K(0)
+  if (mloader) {
+    const u32x4 m0 = ntiles > 0 ? mask_chunk(tb) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 m1 = ntiles > 1 ? mask_chunk(tb + 1) : u32x4{0u, 0u, 0u, 0u};
+    if (ntiles > 2) mpend = mask_chunk(tb + 2);
+    mask_store(0, m0);
+    mask_store(1, m1);
+  }
   if (ntiles > 0) {
     issue_k(tb, ks0);
     issue_v(tb, vs0);

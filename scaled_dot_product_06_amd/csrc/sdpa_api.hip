@@ -297,12 +297,7 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
     p.grid[0] = (B * Hq / heads) * nqb;
     p.grid[1] = 1;
     p.grid[2] = 1;
-    if (prefill_packs_mask(dtype, mask_kind)) {
-      int64_t sb;
-      if (!mul3(Lq, mask_words(Lk), 4, &sb)) return fail(SDPA_ERR_INVALID, "mask-bit scratch size overflows");
-      p.kernels = 2;
-      p.scratch_bytes = sb;
-    }
+    // the kernel reads a boolean mask's bytes itself: one kernel, no scratch
     *plan = p;
     return SDPA_OK;
   }
@@ -598,7 +593,9 @@ int forward_impl(const Views& x, void* out, int64_t B, int64_t Hq, int64_t Hkv, 
   } else {
     a.head_blocks = (int)(B * Hq / p.heads_per_group);
     a.nqb = (int)(p.grid[0] / a.head_blocks);
-    if (prefill_packs_mask(dtype, mask_kind)) {
+    // the plan gives the packing kernel scratch for the mask bits; the key-split
+    // kernel reads the bytes itself
+    if (prefill_packs_mask(dtype, mask_kind) && p.scratch_bytes > 0) {
       void* bits = nullptr;
       if ((rc = call_scratch(scratch_source, stream, (size_t)p.scratch_bytes, &bits)) != SDPA_OK) return rc;
       e = launch_mask_bits((const uint8_t*)x.mask, (uint32_t*)bits, Lq, Lk, stream);

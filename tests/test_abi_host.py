@@ -56,7 +56,7 @@ def test_workload_routes(number, route):
         assert p["splits"] * p["keys_per_split"] >= w["Lk"] > (p["splits"] - 1) * p["keys_per_split"]
         assert p["scratch_bytes"] == w["B"] * w["Hkv"] * p["splits"] * rows * (w["Dv"] + 4) * 4
         assert p["grid"] == (p["splits"], w["Hkv"], w["B"])
-    elif w["mask_kind"] == 2 and w["dtype"] != 0:
+    elif w["mask_kind"] == 2 and w["dtype"] != 0 and p["splits"] != 2:
         # 16-bit prefill with a boolean mask: the mask is first packed into bits
         assert p["kernels"] == 2 and p["scratch_bytes"] == w["Lq"] * -(-w["Lk"] // 32) * 4
     else:
@@ -367,7 +367,11 @@ def test_wide_heads_plan_the_pipelined_kernel_only_on_full_grids():
     under = sd.sdpa_plan(1, 32, 4, 992, 1297, 256, 256, 1, False, False, 2)  # 8 x 31 = 248
     assert shape(under) + (under["grid"][0],) == (16, 32, 2, 8, 8 * 62)
     small = sd.sdpa_plan(1, 16, 2, 1024, 1801, 256, 256, 2, True, True, 1)  # workload 4: 4 x 32 = 128
-    assert shape(small) + (small["grid"][0], small["kernels"]) == (16, 32, 2, 8, 4 * 64, 2)
+    # the key-split kernel reads the boolean mask's bytes: one kernel, no scratch
+    assert shape(small) + (small["grid"][0], small["kernels"], small["scratch_bytes"]) == (16, 32, 2, 8, 4 * 64, 1, 0)
+    # the pipelined kernel packs it first
+    packed = sd.sdpa_plan(1, 16, 2, 1024, 1801, 128, 128, 2, True, True, 1)
+    assert (packed["kernels"], packed["scratch_bytes"]) == (2, 1024 * 57 * 4)
     batched = sd.sdpa_plan(8, 16, 2, 1024, 1801, 256, 256, 2, True, True, 1)  # the same per batch item
     assert shape(batched) + (batched["grid"][0],) == (16, 32, 2, 8, 8 * 4 * 64)
     # one or two heads per workgroup: 64 or 32 rows of a head per key lane

@@ -51,7 +51,9 @@ def _call(kind, B, Hq, Hkv, Lq, Lk, D, dtype):
 
 CASES = [
     (1, 2, 8, 2, 300, 300, 128, BF16),      # pipelined prefill
-    (2, 1, 8, 2, 100, 257, 256, F16),       # mask packing + generic prefill (two kernels, scratch)
+    (2, 1, 8, 2, 100, 257, 128, F16),       # mask packing + pipelined prefill (two kernels, scratch)
+    (2, 1, 16, 2, 100, 300, 256, F16),      # key-split prefill reading the mask bytes
+    (0, 1, 8, 2, 77, 150, 192, BF16),       # generic prefill
     (1, 1, 4, 2, 40, 70, 64, F32),          # f32 prefill
     (0, 2, 16, 2, 1, 9000, 256, BF16),      # decode split + reduce (scratch)
     (1, 1, 8, 2, 5, 0, 128, BF16),          # no keys: the fill kernel
@@ -96,9 +98,9 @@ def test_concurrent_streams_and_threads():
     import threading
 
     import torch
-    cases = [_call(0, 2, 16, 2, 1, 9000, 256, BF16), _call(2, 1, 8, 2, 100, 257, 256, F16),
+    cases = [_call(0, 2, 16, 2, 1, 9000, 256, BF16), _call(2, 1, 8, 2, 100, 257, 128, F16),
              _call("window", 1, 8, 2, 3, 2000, 128, BF16), _call("paged", 2, 8, 2, 1, 3000, 128, BF16)]
-    shapes = [(2, 16, 1, 256, torch.bfloat16), (1, 8, 100, 256, torch.float16), (1, 8, 3, 128, torch.bfloat16),
+    shapes = [(2, 16, 1, 256, torch.bfloat16), (1, 8, 100, 128, torch.float16), (1, 8, 3, 128, torch.bfloat16),
               (2, 8, 1, 128, torch.bfloat16)]
     wants = []
     for call, (B, H, L, D, dt) in zip(cases, shapes):

@@ -1,4 +1,5 @@
-"""CPU check of the pipelined prefill's tile-load addresses (csrc/prefill_fast.h).
+"""CPU check of the tile-load addresses of the pipelined prefill (csrc/prefill_fast.h)
+and the key-split prefill (csrc/prefill_ksplit.h).
 
 Each lane of each wavefront issues direct-to-LDS loads of one 16-byte chunk of
 a K and a V row per tile. Its offset within the tile is kept as a 32-bit
@@ -50,9 +51,9 @@ def issued_tiles(Lq, Lk, qb, mask_kind, window, heads=4):
     return [(tb + t) * BN for t in range(ntiles)]
 
 
-def check_tile(D, Lk, k0, rs, swz):
+def check_tile(D, Lk, k0, rs, swz, BN=BN, NW=NW):
     """Every lane's load of the tile at key k0 with row stride rs bytes."""
-    c = cfg(D)
+    c = dict(cfg(D), LPW=(BN * 2 * D // 1024) // NW)
     for w, it, lane in itertools.product(range(NW), range(c["LPW"]), range(64)):
         row = (w + NW * it) * c["ROWS_PER_KB"] + lane // c["CPR"]
         slot = lane % c["CPR"]
@@ -132,3 +133,72 @@ def test_v_operand_offsets_fold_the_key_offset(D):
                     folded = TILE + vk0 * RB + tr_half + (((db * 4 + tr_chunk) ^ swz_v_rows(D, vk0)) * 16) + kofs * RB
                     assert folded == direct, (D, lane, t8, half, db)
                     assert TILE <= direct < 2 * TILE
+
+
+# --- the key-split prefill: 64-key steps loaded by eight wavefronts ---------------------------
+# (256-wide heads; 16 query rows per (head, row block) slot, so a workgroup's query block is
+# 16, 32 or 64 rows for four, two or one heads per workgroup)
+
+def ks_swz_k(D, row):
+    return row % (D // 8)
+
+
+def ks_swz_v(D, row):
+    return 2 * (row % 8)
+
+
+@pytest.mark.parametrize("heads", [1, 2, 4])
+@pytest.mark.parametrize("mask_kind,window", [(0, 0), (1, 0), (1, 7), (1, 300), (2, 0)])
+def test_key_split_steps_read_inside_the_keys(mask_kind, window, heads):
+    D, KBN, KNW = 256, 64, 8
+    bm = (4 // heads) * 16
+    strides = [2 * D, 2 * D * 3 + 16 * 5, (1 << 26) - 16]
+    for Lq, Lk in CALLS:
+        shift = Lk - Lq
+        for qb in range(-(-Lq // bm)):
+            kend = Lk
+            if mask_kind == 1:
+                kend = min(Lk, min(qb * bm + bm, Lq) - 1 + shift + 1)
+            kend = max(kend, 0)
+            kbeg = min(max(0, qb * bm + shift - window + 1), kend) if window > 0 else 0
+            tb = kbeg // KBN
+            steps = [(tb + t) * KBN for t in range(max((kend + KBN - 1) // KBN - tb, 0))]
+            for k0 in steps:
+                assert k0 <= Lk - 1, "a step starts past the last key"
+            for k0 in [t for t in steps if t + KBN > Lk] + steps[:1]:
+                for rs in strides:
+                    check_tile(D, Lk, k0, rs, ks_swz_k, KBN, KNW)
+                    check_tile(D, Lk, k0, rs, ks_swz_v, KBN, KNW)
+
+
+def test_key_split_lds_operand_offsets():
+    # K operand reads fold four lane offsets plus constants; V^T transposed reads fold
+    # eight lane offsets plus 256 bytes for the upper eight output blocks and 16 rows for
+    # the second read. Both against the direct row * RB + swizzled chunk formula.
+    D, RB, SUB = 256, 512, 32
+    for kl in (0, 1):
+        for lane in range(64):
+            col, kg = lane % 16, lane // 16
+            kb4 = [(SUB * kl + col) * RB + (((4 * c + kg) ^ col) * 16) for c in range(4)]
+            for c in range(8):
+                for nb in range(2):
+                    folded = (kb4[c] + nb * (16 * RB + 256) if c < 4
+                              else kb4[c - 4] + 256 + nb * (16 * RB - 256))
+                    row = SUB * kl + 16 * nb + col
+                    chunk = (4 * c + kg) ^ ks_swz_k(D, row)
+                    assert chunk < D // 8
+                    assert folded == row * RB + chunk * 16, (kl, lane, c, nb)
+            vr = lane >> 2
+            vb8 = [(SUB * kl + vr) * RB + ((2 * (d ^ (vr % 8)) + ((lane >> 1) & 1)) * 16) + (lane & 1) * 8
+                   for d in range(8)]
+            for db in range(16):
+                folded = vb8[db % 8] + (256 if db >= 8 else 0)
+                for second in (0, 1):
+                    row = SUB * kl + vr + 16 * second
+                    # provider lane 4e + c of its 16-lane group: row 4g + e, columns 16 db + 4c
+                    assert row - SUB * kl - 16 * second == 4 * (lane // 16) + (lane % 16) // 4
+                    byte = 2 * (16 * db + 4 * (lane % 4))
+                    slot = (byte // 16) ^ ks_swz_v(D, row)
+                    direct = row * RB + slot * 16 + byte % 16
+                    assert folded + 16 * RB * second == direct, (kl, lane, db, second)
+                    assert 0 <= direct and direct + 8 <= 64 * RB

@@ -56,6 +56,7 @@ CASES = [
     (0, 1, 8, 2, 77, 150, 192, BF16),       # generic prefill
     (1, 1, 4, 2, 40, 70, 64, F32),          # f32 prefill
     (0, 2, 16, 2, 1, 9000, 256, BF16),      # decode split + reduce (scratch)
+    (1, 1, 32, 4, 1, 8193, 128, BF16),      # the 8193-key decode: split + reduce
     (1, 1, 8, 2, 5, 0, 128, BF16),          # no keys: the fill kernel
     ("window", 1, 8, 2, 3, 2000, 128, BF16),
     ("additive", 1, 8, 2, 70, 257, 128, BF16),

@@ -182,6 +182,11 @@ OTHER_WORKLOADS = (1, 2, 4)   # timed and reported; not the headline metric
 WINDOWED_WORKLOADS = ((5, 4096), (3, 1024))
 
 
+# caps on the reported-only workloads' timing batches (--other-calls, --other-rounds):
+# profiling runs shorten them
+OTHER_CAPS = {"calls": 1 << 30, "rounds": 1 << 30}
+
+
 def measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, rounds=5):
     """Per-call kernel time (HIP events on the library's stream, median of
     `rounds` batches of `calls`) of the f32 causal prefill, the 8193-key bf16
@@ -189,6 +194,8 @@ def measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, 
     calls on the headline shapes, each against its own roofline (windowed work
     counts only the keys in the band). Decode K/V rotates over copies whose
     windows together span > 2x the 256 MB MALL, so every call streams from HBM."""
+    calls = max(1, min(calls, OTHER_CAPS["calls"]))
+    rounds = max(1, min(rounds, OTHER_CAPS["rounds"]))
     import numpy as np
     res = {}
     for num, window in [(n, 0) for n in OTHER_WORKLOADS] + list(WINDOWED_WORKLOADS):
@@ -284,6 +291,8 @@ def measure_paged_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, 
     workload's K/V copied into blocks of 16 positions at shuffled places (three
     spare blocks), every sequence at its full length, with and without a sliding
     window. Counted bytes are the K/V rows the call reads (block ids excluded)."""
+    calls = max(1, min(calls, OTHER_CAPS["calls"]))
+    rounds = max(1, min(rounds, OTHER_CAPS["rounds"]))
     import numpy as np
     res = {}
     for num, bs, window in PAGED_WORKLOADS:
@@ -332,6 +341,8 @@ def measure_paged_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, 
 
 def _time_calls(torch, stream, call, calls=50, rounds=5):
     """Median per-call time (us) over `rounds` batches of `calls`, HIP events on `stream`."""
+    calls = max(1, min(calls, OTHER_CAPS["calls"]))
+    rounds = max(1, min(rounds, OTHER_CAPS["rounds"]))
     for _ in range(20):
         call()
     torch.cuda.synchronize()
@@ -402,7 +413,15 @@ def main() -> int:
     ap.add_argument("--no-others", action="store_true", help="skip the reported-only workloads (f32 prefill, "
                     "8193-key decode, f16 masked prefill with sinks, sliding windows, paged decode, "
                     "strided views, additive mask, 256-wide prefill)")
+    ap.add_argument("--other-calls", type=int, default=None,
+                    help="at most this many calls per timed batch of a reported-only workload (profiling runs)")
+    ap.add_argument("--other-rounds", type=int, default=None,
+                    help="at most this many timed batches per reported-only workload (profiling runs)")
     args = ap.parse_args()
+    if args.other_calls:
+        OTHER_CAPS["calls"] = args.other_calls
+    if args.other_rounds:
+        OTHER_CAPS["rounds"] = args.other_rounds
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
               f"multi-GPU path)", file=sys.stderr)

@@ -105,12 +105,13 @@ constexpr int kFastRows = 32, kFastBN = 32;
 // (and gives the same bits) alone or within a batch.
 constexpr int kFastMinGridWide = 256;
 constexpr bool prefill_fast_needs_grid(int D) { return D > 128; }
-// Below that grid, 256-wide heads (16-bit, no additive mask) run the key-split
-// kernel: 16-row tiles, and the workgroup's wavefronts in two key lanes that
-// each take 32 keys of every 64-key step, so each SIMD holds two wavefronts.
+// Below that grid, and with an additive mask on any grid, 256-wide 16-bit heads
+// run the key-split kernel: 16-row tiles, and the workgroup's wavefronts in two
+// key lanes that each take 32 keys of every 64-key step, so each SIMD holds two
+// wavefronts.
 constexpr int kKsplitLanes = 2, kKsplitRows = 16, kKsplitBN = 32;
 constexpr bool prefill_can_ksplit(int elem, int D, int Dv, int mask_kind) {
-  return elem != kF32 && D == Dv && D == 256 && mask_kind != kMaskAdditive;
+  return elem != kF32 && D == Dv && D == 256;
 }
 // Generic kernel: 32x32 MFMA tiles (32 query rows per wavefront) up to
 // 128-wide heads; 16x16 tiles above, where a 32-row output accumulator would

@@ -11,11 +11,6 @@ static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_
   constexpr int MF = prefill_generic_mf(elem, D, DV);
   constexpr int BN = prefill_generic_bn(elem, D, DV);
   dim3 grid(a.head_blocks * a.nqb, 1, 1);
-  if (a.mask_kind == kMaskAdditive) {
-    hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves, true>), grid, dim3(kPrefillWaves * 64), 0,
-                       stream, a);
-    return hipGetLastError();
-  }
   if constexpr (prefill_can_ksplit(elem, D, DV, kMaskNone)) {
     using C = KsplitCfg<D>;
     static_assert(C::MF == kKsplitRows && C::SUB == kKsplitBN && C::KL == kKsplitLanes && C::NWH == kPrefillWaves,
@@ -24,13 +19,20 @@ static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_
     if (s.ksplit > 1) {
       if (s.ksplit != C::KL || s.mf != C::MF || s.block_n != C::SUB || s.waves != C::NW) return hipErrorInvalidConfiguration;
       if (a.mask_kind == kMaskBool)
-        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, true>), grid, dim3(C::NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, kKsBool>), grid, dim3(C::NW * 64), 0, stream, a);
+      else if (a.mask_kind == kMaskAdditive)
+        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, kKsAdd>), grid, dim3(C::NW * 64), 0, stream, a);
       else
-        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, false>), grid, dim3(C::NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, kKsPlain>), grid, dim3(C::NW * 64), 0, stream, a);
       return hipGetLastError();
     }
   }
   if (s.ksplit > 1) return hipErrorInvalidConfiguration;
+  if (a.mask_kind == kMaskAdditive) {
+    hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves, true>), grid, dim3(kPrefillWaves * 64), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
   if constexpr (prefill_can_fast(elem, D, DV, kMaskNone)) {
     using C = FastCfg<D>;
     static_assert(C::MF == kFastRows && C::ROWS == kFastRows && C::BN == kFastBN && C::NW == kPrefillWaves,

@@ -27,7 +27,9 @@
 //    their row maxima taken again, at the top of their step. A boolean mask is
 //    read as the caller's bytes, staged through a small LDS ring, and enters
 //    the scores as the MFMA accumulators' starting values, 0 or -inf, so
-//    masked steps run the unmasked path;
+//    masked steps run the unmasked path. An additive mask goes through a ring
+//    of its own in the order the lanes read it and is added as the scores are
+//    scaled, once per step;
 //  * LDS rows hold their 16-byte chunks permuted by an XOR of the row index,
 //    different for K (16 consecutive rows, one chunk each per read) and V
 //    (16 rows, two adjacent chunks each per transposed read), so reads spread
@@ -72,6 +74,8 @@ template <int D> __device__ __forceinline__ int ks_swz_v(int row) { return 2 * (
 
 // bytes between rows of the boolean-mask ring (64 keys plus padding)
 constexpr int kMaskRow = 80;
+// mask modes of the kernel
+constexpr int kKsPlain = 0, kKsBool = 1, kKsAdd = 2;
 
 // s_waitcnt immediate: vmcnt(n) only (gfx9 encoding, the other counters left at their maxima)
 constexpr int ks_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -89,7 +93,9 @@ __device__ __forceinline__ float sum_xor16(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <class E, int D, bool BOOLMASK>
+// MK: kKsPlain (no mask or causal), kKsBool (boolean mask bytes) or kKsAdd
+// (additive mask values)
+template <class E, int D, int MK>
 __global__ void __launch_bounds__(KsplitCfg<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_ksplit_kernel(FwdArgs a) {
   using C = KsplitCfg<D>;
@@ -102,7 +108,11 @@ prefill_ksplit_kernel(FwdArgs a) {
   __shared__ float merge_ml[C::NWH][2][MF];
   // boolean mask ring: up to 64 rows x 64 keys per stage, rows 80 bytes apart so
   // that the 16 rows x 4 groups one wavefront reads fall on 64 different banks
+  constexpr bool BOOLMASK = MK == kKsBool, ADDMASK = MK == kKsAdd;
   __shared__ __attribute__((aligned(16))) uint8_t mstage[2][BOOLMASK ? C::NWH * 16 * kMaskRow : 16];
+  // additive mask ring: per (slot, key lane) 64 lanes x 8 values, in the order
+  // each lane reads them (one 16-byte read per lane and step)
+  __shared__ __attribute__((aligned(16))) uint8_t astage[2][ADDMASK ? C::NWH * C::KL * 1024 : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -187,6 +197,61 @@ prefill_ksplit_kernel(FwdArgs a) {
   // (visible) or -inf (hidden), so the MFMAs yield the masked scores and the
   // step needs no separate masking pass.
   u32x4 mpend = {0u, 0u, 0u, 0u};   // a loader lane's chunk, waiting for its ring stage
+
+  // Additive mask: key lane 0's wavefront of each slot loads the slot's 16 rows x
+  // 64 keys of a step (two 16-byte loads per lane: 8 keys of one row each) three
+  // steps ahead, and writes them to the ring at the next step in the order the
+  // readers take them: lane (col, kg) of key lane kl gets keys 4 kg .. 4 kg + 3 and
+  // 16 + 4 kg .. of its 32. Keys at or past Lk read as -inf. The scores are then
+  // scaled once with the mask added, in base 2, and used unscaled after that.
+  const bool aloader = ADDMASK && kl == 0;
+  const uint16_t* arow[2] = {nullptr, nullptr};
+  if (aloader) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int rq = (lane + 64 * j) / 8;   // row of the slot's 16
+      arow[j] = (const uint16_t*)a.amask + b * a.ms[0] + h * a.ms[1] + (int64_t)min(wi0 + rq, a.Lq - 1) * a.ms[2];
+    }
+  }
+  auto add_chunk = [&](int step, int j) -> u32x4 {
+    const int key = step * BN + 8 * ((lane + 64 * j) % 8);
+    u32x4 x;
+    if (key + 8 <= a.Lk) {
+      __builtin_memcpy(&x, arow[j] + key, 16);
+    } else {
+      uint32_t hv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = key + e < a.Lk ? arow[j][key + e] : neg_inf_bits<E>();
+      x = u32x4{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16)};
+    }
+    return x;
+  };
+  // 8-key group g of a row (keys 8g .. 8g+7 of the step): key lane g / 4, block
+  // nb = (g % 4) / 2, halves to the lanes of k-groups 2 (g % 2) and 2 (g % 2) + 1
+  auto add_store = [&](int stage, int j, u32x4 x) {
+    const int q = lane + 64 * j, row = q / 8, g = q % 8;
+    const int kk = g / 4, nb = (g % 4) / 2, kg0 = 2 * (g % 2);
+    uint8_t* base = &astage[stage][(ws * C::KL + kk) * 1024 + nb * 8];
+    *reinterpret_cast<u32x2*>(base + (kg0 * 16 + row) * 16) = u32x2{x[0], x[1]};
+    *reinterpret_cast<u32x2*>(base + ((kg0 + 1) * 16 + row) * 16) = u32x2{x[2], x[3]};
+  };
+  auto add_read = [&](int stage) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(&astage[stage][((ws * C::KL + kl) * 64 + lane) * 16]);
+  };
+  // scores scaled once, mask added: s = c s + mask log2(e)
+  auto add_apply = [&](acc_t (&s)[C::NSB], u32x4 mv) {
+#pragma unroll
+    for (int nb = 0; nb < C::NSB; ++nb)
+#pragma unroll
+      for (int i = 0; i < C::ACC; ++i) {
+        const uint32_t wv = mv[nb * 2 + i / 2];
+        const float add = half_to_f32<E>((uint16_t)((i & 1) ? (wv >> 16) : (wv & 0xFFFFu))) * kLog2e;
+        s[nb][i] = fmaf(s[nb][i], a.c, add);
+      }
+  };
+  u32x4 apend[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+  // scale applied to the scores from here on (1 once the additive mask's pass scaled them)
+  const float cs = ADDMASK ? 1.0f : a.c;
   auto score_init = [&](acc_t (&s)[C::NSB], u32x2 mb) {
 #pragma unroll
     for (int nb = 0; nb < C::NSB; ++nb) {
@@ -327,7 +392,7 @@ prefill_ksplit_kernel(FwdArgs a) {
     for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
       for (int i = 0; i < C::ACC; ++i) mx = fmaxf(mx, s[nb][i]);
-    tmax = row_max16(mx) * a.c;
+    tmax = row_max16(mx) * cs;
   };
   // the lane's scores sit at keys k0 + 16 nb + 4 kg + i of the step's sub-tile
   // (causal and window limits, and keys past Lk; a boolean mask is already in the scores)
@@ -350,7 +415,7 @@ prefill_ksplit_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < C::ACC; ++i) mx = fmaxf(mx, s[nb][i]);
     mx = row_max16(mx);
-    tmax = (mx == -INFINITY) ? -INFINITY : mx * a.c;
+    tmax = (mx == -INFINITY) ? -INFINITY : mx * cs;
   };
   // weights rounded to 16 bits; the running sum adds the same rounded weights
   auto weights = [&](acc_t (&s)[C::NSB], uint32_t (&pk)[C::NPK]) {
@@ -359,8 +424,8 @@ prefill_ksplit_kernel(FwdArgs a) {
     for (int nb = 0; nb < C::NSB; ++nb)
 #pragma unroll
       for (int i = 0; i < C::ACC; i += 2) {
-        const float p0 = fast_exp2(fmaf(s[nb][i], a.c, -mu));
-        const float p1 = fast_exp2(fmaf(s[nb][i + 1], a.c, -mu));
+        const float p0 = fast_exp2(fmaf(s[nb][i], cs, -mu));
+        const float p1 = fast_exp2(fmaf(s[nb][i + 1], cs, -mu));
         pk[nb * 2 + i / 2] = pack2<E>(p0, p1);
       }
     float l0 = pair_sum<E>(pk[0], 0.0f), l1 = pair_sum<E>(pk[1], 0.0f);
@@ -390,14 +455,26 @@ prefill_ksplit_kernel(FwdArgs a) {
     if (t + 2 < ntiles) issue_k(tb + t + 2, Kload);
     if (t + 1 < ntiles) issue_v(tb + t + 1, Vload);
     if (mloader && t + 3 < ntiles) mpend = mask_chunk(tb + t + 3);
+    if constexpr (ADDMASK) {
+      if (aloader) {
+        add_store(t & 1, 0, apend[0]);
+        add_store(t & 1, 1, apend[1]);
+        if (t + 3 < ntiles) {
+          apend[0] = add_chunk(tb + t + 3, 0);
+          apend[1] = add_chunk(tb + t + 3, 1);
+        }
+      }
+    }
     const int kt = tb + t;
     const int k0 = kt * BN + SUB * kl;
     if (k0 + SUB > w_kfull || k0 < w_klo) tile_max_masked(kt, scur);
     softmax_rebase<C::NDB>(tmax, m, l, o);
     u32x4 ba[8], bb[8];
     u32x2 mb = {0u, 0u};
+    u32x4 mv = {0u, 0u, 0u, 0u};
     fence();
     if constexpr (BOOLMASK) mb = mask_read((t + 1) & 1);
+    if constexpr (ADDMASK) mv = add_read((t + 1) & 1);
     read_k(Knext, 0, ba);
     weights(scur, pk);
     fence();
@@ -420,6 +497,7 @@ prefill_ksplit_kernel(FwdArgs a) {
     lds_wait();
     mma_pv(8, bb, pk);
     fence();
+    if constexpr (ADDMASK) add_apply(snext, mv);
     tile_max_full(snext);
   };
 
@@ -431,6 +509,18 @@ prefill_ksplit_kernel(FwdArgs a) {
     if (ntiles > 2) mpend = mask_chunk(tb + 2);
     mask_store(0, m0);
     mask_store(1, m1);
+  }
+  if constexpr (ADDMASK) {
+    if (aloader) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 a0 = ntiles > 0 ? add_chunk(tb, j) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 a1 = ntiles > 1 ? add_chunk(tb + 1, j) : u32x4{0u, 0u, 0u, 0u};
+        if (ntiles > 2) apend[j] = add_chunk(tb + 2, j);
+        add_store(0, j, a0);
+        add_store(1, j, a1);
+      }
+    }
   }
   if (ntiles > 0) {
     issue_k(tb, ks0);
@@ -445,6 +535,7 @@ prefill_ksplit_kernel(FwdArgs a) {
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   if (ntiles > 0) {
     qk(ks0, sa);
+    if constexpr (ADDMASK) add_apply(sa, add_read(0));
     tile_max_full(sa);
   }
   // even steps score into sb from K stage 1 and read V stage 0; odd steps the

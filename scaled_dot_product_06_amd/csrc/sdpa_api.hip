@@ -276,10 +276,14 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
   const int64_t heads = gcd64(group, nw);
   bool fast = prefill_can_fast(dtype, (int)D, (int)Dv, mask_kind);
   bool kspl = false;
-  if (fast && prefill_fast_needs_grid((int)D)) {
+  if (prefill_can_ksplit(dtype, (int)D, (int)Dv, mask_kind)) {
+    // 256-wide heads: the pipelined kernel when one batch item's 32-row grid fills
+    // the chip (and no additive mask), else the key-split kernel
     const int64_t fbm = (nw / heads) * kFastRows;
-    fast = (Hq / heads) * ((Lq + fbm - 1) / fbm) >= kFastMinGridWide;
-    kspl = !fast && prefill_can_ksplit(dtype, (int)D, (int)Dv, mask_kind);
+    fast = fast && (Hq / heads) * ((Lq + fbm - 1) / fbm) >= kFastMinGridWide;
+    kspl = !fast;
+  } else if (fast && prefill_fast_needs_grid((int)D)) {
+    fast = false;
   }
   if (kspl) {
     // 16-row query blocks of `heads` heads per workgroup, two key lanes of wavefronts

@@ -377,7 +377,11 @@ def test_wide_heads_plan_the_pipelined_kernel_only_on_full_grids():
     # one or two heads per workgroup: 64 or 32 rows of a head per key lane
     assert sd.sdpa_plan(1, 4, 4, 100, 300, 256, 256, 0, False, False, 2)["grid"][0] == 4 * 2
     assert sd.sdpa_plan(1, 4, 2, 100, 300, 256, 256, 0, False, False, 2)["grid"][0] == 2 * 4
-    # additive masks and other head sizes keep the generic 16-row kernel
+    # additive masks take the key-split kernel at 256-wide heads on any grid (the
+    # pipelined kernel reads no additive mask); other head sizes keep the generic kernel
     add = sd.sdpa_plan(1, 64, 8, 1024, 1801, 256, 256, 3, True, True, 1)
-    assert shape(add) == (16, 64, 0, 4)
+    assert shape(add) + (add["kernels"], add["scratch_bytes"]) == (16, 32, 2, 8, 1, 0)
+    big_add = sd.sdpa_plan(1, 32, 4, 1040, 1297, 256, 256, 3, True, False, 2)
+    assert shape(big_add) == (16, 32, 2, 8)
+    assert shape(sd.sdpa_plan(1, 16, 2, 1024, 1801, 128, 128, 3, True, True, 1)) == (32, 64, 0, 4)
     assert shape(sd.sdpa_plan(1, 64, 8, 1024, 1801, 192, 192, 1, False, False, 1)) == (16, 64, 0, 4)

@@ -5,7 +5,8 @@ The kernel's workgroup holds 16 query rows of up to four heads and splits each
 64-key step between two lanes of wavefronts, which merge at the end. The cases
 cover one, two and four heads per workgroup (64, 32 and 16 rows of a head),
 key counts on both sides of the 32-key lane and 64-key step edges, causal calls
-whose early rows see no key, windows, boolean masks, sinks, and batches."""
+whose early rows see no key, windows, boolean and additive masks, sinks, and
+batches."""
 import numpy as np
 import pytest
 
@@ -101,3 +102,81 @@ def test_batch_items_equal_each_item_alone():
                          p.k[b:b + 1], p.v[b:b + 1], p.mask, p.sinks)
         alone = from_device(run_gpu(pb), BF16)
         assert np.array_equal(whole[b:b + 1], alone), f"batch item {b} differs"
+
+
+# --- additive masks (always the key-split kernel at 256-wide heads) -------------------------
+
+def _additive_call(p, add, sinks, offset=0):
+    """Run with `add` (any broadcast shape) as an additive mask, `offset` elements into its buffer."""
+    import torch
+    from scaled_dot_product_06_amd import attention
+    from tests.gpu_util import to_device
+    flat = np.concatenate([np.zeros(offset, dtype=add.dtype), add.ravel()])
+    dmask = to_device(flat, p.dtype)[offset:].view(add.shape)
+    dq, dk, dv = (to_device(a, p.dtype) for a in (p.q, p.k, p.v))
+    ds = None if sinks is None else to_device(sinks, p.dtype)
+    got = attention(dq, dk, dv, p.scale, 3, dmask, ds)
+    torch.cuda.synchronize()
+    return from_device(got, p.dtype)
+
+
+def _additive_plan(p):
+    import scaled_dot_product_06_amd as sd
+    plan = sd.sdpa_plan(*p.shape_args(), 3, True, True, p.dtype)
+    assert (plan["rows_per_wave"], plan["splits"], plan["waves"]) == (16, 2, 8), plan
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("Lq,Lk", [(9, 300), (45, 1), (45, 63), (70, 257), (100, 1801)])
+def test_additive_mask_layouts(Lq, Lk, dtype):
+    # full, per-head, per-batch and 2-D masks; a buffer starting one element in
+    # (unaligned rows); -inf holes and one row hidden entirely (zeros, sinks or not)
+    B, Hq, Hkv, D = 2, 8, 2, 256
+    dt = DT[dtype]
+    seed = 8700 + Lq + Lk
+    p = gen.make_problem(seed, B, Hq, Hkv, Lq, Lk, D, D, dt, 0, sinks=True)
+    _additive_plan(p)
+    q, k, v, _, s = p.widened()
+    for shape in [(B, Hq, Lq, Lk), (1, Hq, Lq, Lk), (B, 1, Lq, Lk), (Lq, Lk)]:
+        add = gen.additive_mask(seed + len(shape), shape, dt, holes=0.2)
+        add[..., Lq // 2, :] = gen.NEG_INF_BITS[dt]
+        for offset, sinks in ((0, p.sinks), (1, None)):
+            got = _additive_call(p, add, sinks, offset)
+            want = orc.sdpa(q, k, v, p.scale, 3, gen.widen(add, dt), None if sinks is None else s)
+            assert not got[:, :, Lq // 2].any()
+            assert_parity(p, got, want, f"additive {shape} offset {offset} sinks={sinks is not None}")
+
+
+@pytest.mark.parametrize("shape", HEAD_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_additive_mask_heads_per_workgroup(shape):
+    B, Hq, Hkv, Lq = shape
+    p = gen.make_problem(8800 + Hq + Lq, B, Hq, Hkv, Lq, 333, 256, 256, F16, 0, sinks=True, scale=1.0)
+    _additive_plan(p)
+    add = gen.additive_mask(8801, (B, Hq, Lq, 333), F16, holes=0.1)
+    got = _additive_call(p, add, p.sinks)
+    q, k, v, _, s = p.widened()
+    want = orc.sdpa(q, k, v, p.scale, 3, gen.widen(add, F16), s)
+    assert_parity(p, got, want, "additive, peaked scores")
+
+
+def test_additive_mask_with_zero_scale():
+    # scale 0: the scores are the mask values alone
+    p = gen.make_problem(8900, 1, 8, 2, 40, 200, 256, 256, BF16, 0, sinks=True, scale=0.0)
+    add = gen.additive_mask(8901, (1, 8, 40, 200), BF16, holes=0.3)
+    got = _additive_call(p, add, p.sinks)
+    q, k, v, _, s = p.widened()
+    want = orc.sdpa(q, k, v, 0.0, 3, gen.widen(add, BF16), s)
+    assert_parity(p, got, want, "additive, scale 0")
+
+
+def test_additive_mask_on_a_full_grid_sampled_rows():
+    # 32 heads x 1040 rows: a grid the pipelined kernel would fill, which has no additive path
+    from tests.gpu_util import sample_rows
+    p = gen.make_problem(8950, 1, 32, 4, 1040, 1297, 256, 256, BF16, 0, sinks=True)
+    _additive_plan(p)
+    add = gen.additive_mask(8951, (1, 32, 1040, 1297), BF16, holes=0.1)
+    got = _additive_call(p, add, p.sinks)
+    rows = sample_rows(p, 160, seed=3)
+    q, k, v, _, s = p.widened()
+    want = orc.sdpa(q, k, v, p.scale, 3, gen.widen(add, BF16), s, rows=rows)
+    assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want, "additive, full grid, sampled rows")

@@ -613,3 +613,63 @@ def test_additive_mask_rejects_a_window():
     q, k, v, add = _additive_case(np.random.default_rng(1306))
     with pytest.raises(ValueError):
         orc.sdpa(q, k, v, 0.4, orc.MASK_ADDITIVE, add, window=3)
+
+
+def test_paged_clamp_equals_a_hand_gathered_sequence():
+    # the clamp reading checked against an independent construction: each sequence's
+    # keys gathered by hand, position by position (length clamped to [0, capacity], table
+    # entries to [0, blocks - 1]), then the plain contiguous definition with the causal
+    # alignment to that length
+    rng = np.random.default_rng(1204)
+    blocks, hkv, bs, d = 5, 2, 8, 4
+    kc, vc = _rand(rng, blocks, hkv, bs, d), _rand(rng, blocks, hkv, bs, d)
+    q = _rand(rng, 2, 4, 3, d)
+    table = np.array([[0, 1005, -5, 2**31 - 1], [4, -1, 3, 7]], dtype=np.int64)
+    lengths = np.array([4 * bs + 1, 19], dtype=np.int64)
+    got = pgd.paged_sdpa(q, kc, vc, table, lengths, 0.125, 1)
+    cap = table.shape[1] * bs
+    for b in range(2):
+        n = min(max(int(lengths[b]), 0), cap)
+        ks = np.zeros((1, hkv, n, d))
+        vs = np.zeros((1, hkv, n, d))
+        for j in range(n):
+            entry = int(table[b][j // bs])
+            blk = 0 if entry < 0 else (blocks - 1 if entry > blocks - 1 else entry)
+            ks[0, :, j] = kc[blk, :, j % bs]
+            vs[0, :, j] = vc[blk, :, j % bs]
+        want = orc.sdpa(q[b:b + 1], ks, vs, 0.125, orc.MASK_CAUSAL)
+        assert np.allclose(got[b:b + 1], want, rtol=0, atol=1e-14), b
+
+
+def _softmax_in_float32(q, k, v, scale, sinks):
+    """The causal definition computed in float32 throughout (scores, exponentials,
+    sums, the divide): what float32 arithmetic alone gives, for the tolerance reading."""
+    q, k, v = (x.astype(np.float32) for x in (q, k, v))
+    Lq, Lk = q.shape[2], k.shape[2]
+    g = q.shape[1] // k.shape[1]
+    out = np.zeros(q.shape[:3] + (v.shape[-1],), np.float32)
+    vis = np.arange(Lk)[None, :] <= np.arange(Lq)[:, None] + Lk - Lq
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            s = np.where(vis, (q[b, h] @ k[b, h // g].T) * np.float32(scale), -np.inf).astype(np.float32)
+            sk = np.float32(sinks[h])
+            m = np.maximum(s.max(1, keepdims=True), sk)
+            p = np.exp(s - m).astype(np.float32)
+            den = p.sum(1, keepdims=True, dtype=np.float32) + np.exp(sk - m).astype(np.float32)
+            out[b, h] = (p @ v[b, h // g]) / den
+    return out
+
+
+def test_float32_arithmetic_alone_reaches_the_f32_bound_at_wide_scores():
+    from scaled_dot_product_06_amd import inputs as gen
+    # reading O16: the f32 wide-score GPU test runs at scores of std ~8 (scale 1.0)
+    # because float32 arithmetic by itself, against the float64 definition, exceeds the
+    # pages' 2e-5 bound at std ~16 (scale 2.0) on this input, and meets it at std ~8
+    worst = {}
+    for scale in (1.0, 2.0):
+        p = gen.make_problem(80 + 96, 1, 4, 1, 96, 2000, 64, 64, gen.F32, 1, scale=scale, sinks=True)
+        q, k, v, _, s = p.widened()
+        want = orc.sdpa(q, k, v, p.scale, orc.MASK_CAUSAL, None, s)
+        got = _softmax_in_float32(q, k, v, p.scale, s)
+        worst[scale] = float(np.max(np.abs(got - want) / np.maximum(np.abs(want), 1.0)))
+    assert worst[2.0] > 2e-5 > worst[1.0], worst

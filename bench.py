@@ -183,8 +183,9 @@ WINDOWED_WORKLOADS = ((5, 4096), (3, 1024))
 
 
 # caps on the reported-only workloads' timing batches (--other-calls, --other-rounds):
-# profiling runs shorten them
-OTHER_CAPS = {"calls": 1 << 30, "rounds": 1 << 30}
+# profiling runs shorten them; "settle" is the untimed load (seconds) before each
+# workload's batches (at most --settle)
+OTHER_CAPS = {"calls": 1 << 30, "rounds": 1 << 30, "settle": 0.25}
 
 
 def measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, rounds=5):
@@ -194,8 +195,6 @@ def measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, 
     calls on the headline shapes, each against its own roofline (windowed work
     counts only the keys in the band). Decode K/V rotates over copies whose
     windows together span > 2x the 256 MB MALL, so every call streams from HBM."""
-    calls = max(1, min(calls, OTHER_CAPS["calls"]))
-    rounds = max(1, min(rounds, OTHER_CAPS["rounds"]))
     import numpy as np
     res = {}
     for num, window in [(n, 0) for n in OTHER_WORKLOADS] + list(WINDOWED_WORKLOADS):
@@ -221,19 +220,7 @@ def measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, 
             sd.attention(q, ks[i % copies], vs[i % copies], p.scale, p.mask_kind, mask, sinks, out=out,
                          stream=stream.cuda_stream, window=window or None)
 
-        for i in range(20):
-            call(i)
-        torch.cuda.synchronize()
-        times = []
-        for r in range(rounds):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(calls):
-                call(r * calls + i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1) / calls * 1e3)
-        us = sorted(times)[len(times) // 2]
+        us = _time_calls(torch, stream, call, calls, rounds)
         rec = {"workload": p.name, "us_per_call": round(us, 2)}
         if window:
             rec["window"] = window
@@ -264,12 +251,9 @@ def measure_wide_workloads(torch, sd, gen, dev, to_dev, stream, log):
     out = torch.empty((p.B, p.Hq, p.Lq, p.Dv), dtype=q.dtype, device=dev)
     plan = sd.sdpa_plan(p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.D, p.Dv, 1, False, False, p.dtype)
 
-    def call():
+    def call(i):
         sd.attention(q, k, v, p.scale, 1, out=out, stream=stream.cuda_stream)
 
-    for _ in range(5):
-        call()
-    torch.cuda.synchronize()
     us = _time_calls(torch, stream, call, calls=10, rounds=5)
     flop = prefill_flop(p)
     tf = flop / us / 1e6
@@ -291,8 +275,6 @@ def measure_paged_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, 
     workload's K/V copied into blocks of 16 positions at shuffled places (three
     spare blocks), every sequence at its full length, with and without a sliding
     window. Counted bytes are the K/V rows the call reads (block ids excluded)."""
-    calls = max(1, min(calls, OTHER_CAPS["calls"]))
-    rounds = max(1, min(rounds, OTHER_CAPS["rounds"]))
     import numpy as np
     res = {}
     for num, bs, window in PAGED_WORKLOADS:
@@ -311,22 +293,10 @@ def measure_paged_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, 
         nbytes = decode_bytes(p, window)
         mask_kind = 1 if window else p.mask_kind
 
-        def call():
+        def call(i):
             sd.paged_attention(q, kd, vd, td, ld, p.scale, mask_kind, window, out=out, stream=stream.cuda_stream)
 
-        for _ in range(20):
-            call()
-        torch.cuda.synchronize()
-        times = []
-        for _ in range(rounds):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(calls):
-                call()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1) / calls * 1e3)
-        us = sorted(times)[len(times) // 2]
+        us = _time_calls(torch, stream, call, calls, rounds)
         gbps = nbytes / us / 1e3
         name = f"{p.name} paged bs={bs}" + (f" window {window}" if window else "")
         res[f"{num}p{bs}" + (f"w{window}" if window else "")] = {
@@ -340,18 +310,29 @@ def measure_paged_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, 
 
 
 def _time_calls(torch, stream, call, calls=50, rounds=5):
-    """Median per-call time (us) over `rounds` batches of `calls`, HIP events on `stream`."""
+    """Median per-call time (us) over `rounds` batches of `calls`, HIP events on
+    `stream`. `call(i)` makes the i-th call. Untimed calls for OTHER_CAPS["settle"]
+    seconds (at least 20) come first: the clocks fall while the host builds a
+    workload's inputs, and a few ms of calls after such a pause run up to 15 %
+    slow."""
     calls = max(1, min(calls, OTHER_CAPS["calls"]))
     rounds = max(1, min(rounds, OTHER_CAPS["rounds"]))
-    for _ in range(20):
-        call()
-    torch.cuda.synchronize()
+    n = 0
+    t_end = time.perf_counter() + OTHER_CAPS["settle"]
+    while True:
+        for _ in range(20):
+            call(n)
+            n += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            break
     times = []
     for _ in range(rounds):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(calls):
-            call()
+            call(n)
+            n += 1
         e1.record(stream)
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) / calls * 1e3)
@@ -371,8 +352,8 @@ def measure_strided_workloads(torch, sd, gen, dev, to_dev, stream, log):
     tv = lambda a: to_dev(np.ascontiguousarray(a.transpose(0, 2, 1, 3)), p.dtype).transpose(1, 2)
     q, k, v = tv(p.q), tv(p.k), tv(p.v)
     out = torch.empty((p.B, p.Hq, p.Lq, p.Dv), dtype=q.dtype, device=dev)
-    us = _time_calls(torch, stream, lambda: sd.attention(q, k, v, p.scale, p.mask_kind, out=out,
-                                                         stream=stream.cuda_stream))
+    us = _time_calls(torch, stream, lambda i: sd.attention(q, k, v, p.scale, p.mask_kind, out=out,
+                                                           stream=stream.cuda_stream))
     flop = prefill_flop(p)
     tf = flop / us / 1e6
     res["3v"] = {"workload": p.name + ", q/k/v as transposed [B,L,H,D] views", "us_per_call": round(us, 2),
@@ -385,8 +366,8 @@ def measure_strided_workloads(torch, sd, gen, dev, to_dev, stream, log):
     q, k, v = (to_dev(a, p.dtype) for a in (p.q, p.k, p.v))
     m, s = to_dev(add, p.dtype), to_dev(p.sinks, p.dtype)
     out = torch.empty((p.B, p.Hq, p.Lq, p.Dv), dtype=q.dtype, device=dev)
-    us = _time_calls(torch, stream, lambda: sd.attention(q, k, v, p.scale, 3, m, s, out=out,
-                                                         stream=stream.cuda_stream))
+    us = _time_calls(torch, stream, lambda i: sd.attention(q, k, v, p.scale, 3, m, s, out=out,
+                                                           stream=stream.cuda_stream))
     flop = p.B * p.Hq * p.Lq * p.Lk * 2 * (p.D + p.Dv)
     tf = flop / us / 1e6
     mbytes = add.size * add.itemsize
@@ -422,6 +403,7 @@ def main() -> int:
         OTHER_CAPS["calls"] = args.other_calls
     if args.other_rounds:
         OTHER_CAPS["rounds"] = args.other_rounds
+    OTHER_CAPS["settle"] = max(0.0, min(OTHER_CAPS["settle"], args.settle))
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
               f"multi-GPU path)", file=sys.stderr)

@@ -22,12 +22,12 @@
 //  * the walk is software-pipelined inside each wavefront: the QK^T MFMAs of
 //    step t+1 are issued among the exponentials of step t, and the PV MFMAs of
 //    step t among the row maxima of step t+1;
-//  * tiles some row sees only in part (the causal diagonal, a ragged end,
-//    every tile under a boolean mask) have their hidden scores set to -inf and
-//    their row maxima taken again, at the top of their step. A boolean mask is
-//    read as the caller's bytes, staged through a small LDS ring, and enters
-//    the scores as the MFMA accumulators' starting values, 0 or -inf, so
-//    masked steps run the unmasked path. An additive mask goes through a ring
+//  * tiles some row sees only in part (the causal diagonal, a window's edge, a
+//    ragged end) have their hidden scores set to -inf and their row maxima
+//    taken again, at the top of their step. A boolean mask is read as the
+//    caller's bytes, staged through a small LDS ring, and enters the scores as
+//    the MFMA accumulators' starting values, 0 or -inf, so its steps need no
+//    masking pass. An additive mask goes through a ring
 //    of its own in the order the lanes read it and is added as the scores are
 //    scaled, once per step;
 //  * LDS rows hold their 16-byte chunks permuted by an XOR of the row index,

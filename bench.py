@@ -243,8 +243,8 @@ def measure_other_workloads(torch, sd, gen, dev, to_dev, stream, log, calls=50, 
 
 def measure_wide_workloads(torch, sd, gen, dev, to_dev, stream, log):
     """The headline prefill shape at 256-wide heads (bf16, causal; seed 31), which
-    plans the pipelined 32-row kernel: per-call kernel time against the bf16
-    MFMA peak (reported)."""
+    runs the key-split kernel: per-call kernel time against the bf16 MFMA peak
+    (reported)."""
     p = gen.make_problem(31, 2, 32, 8, 4096, 4096, 256, 256, gen.BF16, 1,
                          name="bf16 GQA causal prefill B2 H32/8 L4096x4096 D256")
     q, k, v = (to_dev(a, p.dtype) for a in (p.q, p.k, p.v))
@@ -263,7 +263,7 @@ def measure_wide_workloads(torch, sd, gen, dev, to_dev, stream, log):
     return {"3d256": {"workload": p.name, "us_per_call": round(us, 2), "flop_per_call": flop,
                       "TFLOP/s": round(tf, 2), "peak_TFLOP/s": PEAK_BF16_TFLOPS,
                       "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4), "rows_per_wave": plan["rows_per_wave"],
-                      "block_n": plan["block_n"]}}
+                      "block_n": plan["block_n"], "key_lanes": plan["splits"]}}
 
 
 # paged-cache decode on the long-context decode shape (reported): (workload, block size, window)

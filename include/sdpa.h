@@ -68,13 +68,11 @@ typedef struct sdpa_plan_t {
   int32_t route;          /* SDPA_ROUTE_* */
   int32_t kernels;        /* kernel launches the call enqueues */
   int32_t rows_per_wave;  /* query rows one wavefront carries (MFMA tile height). Prefill: 32 on
-                             the pipelined kernel (f16/bf16, D == Dv in {64, 128}, and 256 when
-                             one batch item's grid has at least 256 workgroups, never with an
-                             additive mask); 16 on the key-split kernel (f16/bf16,
-                             D == Dv == 256 on smaller grids, no additive mask); else the
-                             generic kernel's 32 (heads up to 128 wide) or 16 (wider heads;
-                             and f32 calls whose 32-row grid for one batch item would have
-                             fewer than 256 workgroups) */
+                             the pipelined kernel (f16/bf16, D == Dv in {64, 128}, no additive
+                             mask); 16 on the key-split kernel (f16/bf16, D == Dv == 256, every
+                             mask kind); else the generic kernel's 32 (heads up to 128 wide) or
+                             16 (wider heads; and f32 calls whose 32-row grid for one batch item
+                             would have fewer than 256 workgroups) */
   int32_t waves;          /* wavefronts per workgroup of the first kernel */
   int32_t block_n;        /* keys per tile */
   int32_t heads_per_group;/* prefill: query heads sharing one workgroup's K/V tiles;

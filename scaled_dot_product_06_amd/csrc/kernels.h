@@ -90,25 +90,17 @@ constexpr int kDecodeBN = 32;       // keys per decode tile
 // value columns per decode-reduce workgroup: 32 when they divide Dv, else 16
 constexpr int reduce_cols(int DV) { return DV % 32 == 0 ? 32 : 16; }
 constexpr int head_max(int D, int Dv) { return D > Dv ? D : Dv; }
-// The 64/128/256-wide 16-bit prefill shapes can run the pipelined direct-load
+// The 64- and 128-wide 16-bit prefill shapes run the pipelined direct-load
 // kernel (32-row tiles, 32-key steps), except with an additive mask (the
 // generic kernel reads it).
 constexpr bool prefill_can_fast(int elem, int D, int Dv, int mask_kind) {
-  return elem != kF32 && D == Dv && (D == 64 || D == 128 || D == 256) && mask_kind != kMaskAdditive;
+  return elem != kF32 && D == Dv && (D == 64 || D == 128) && mask_kind != kMaskAdditive;
 }
 constexpr int kFastRows = 32, kFastBN = 32;
-// At 256-wide heads the pipelined kernel holds one wavefront per SIMD and one
-// workgroup per compute unit, so it runs only when one batch item's grid has
-// at least this many workgroups (MI355X's compute units); smaller calls keep
-// the generic kernel's 16-row tiles, which put twice as many wavefronts on the
-// chip. The rule ignores the batch size, so a batch item takes the same kernel
-// (and gives the same bits) alone or within a batch.
-constexpr int kFastMinGridWide = 256;
-constexpr bool prefill_fast_needs_grid(int D) { return D > 128; }
-// Below that grid, and with an additive mask on any grid, 256-wide 16-bit heads
-// run the key-split kernel: 16-row tiles, and the workgroup's wavefronts in two
-// key lanes that each take 32 keys of every 64-key step, so each SIMD holds two
-// wavefronts.
+// 256-wide 16-bit heads run the key-split kernel on every grid and with every
+// mask: 16-row tiles, and the workgroup's wavefronts in two key lanes that each
+// take 32 keys of every 64-key step, so each SIMD holds two wavefronts (a
+// 32-row tile of these heads leaves room for one).
 constexpr int kKsplitLanes = 2, kKsplitRows = 16, kKsplitBN = 32;
 constexpr bool prefill_can_ksplit(int elem, int D, int Dv, int mask_kind) {
   return elem != kF32 && D == Dv && D == 256;

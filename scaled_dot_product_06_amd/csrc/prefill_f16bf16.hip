@@ -8,51 +8,46 @@ namespace sdpa {
 template <class E, int D, int DV>
 static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_t stream) {
   constexpr int elem = std::is_same<E, ElemBF16>::value ? kBF16 : kF16;
-  constexpr int MF = prefill_generic_mf(elem, D, DV);
-  constexpr int BN = prefill_generic_bn(elem, D, DV);
   dim3 grid(a.head_blocks * a.nqb, 1, 1);
   if constexpr (prefill_can_ksplit(elem, D, DV, kMaskNone)) {
+    // 256-wide heads: the key-split kernel, whatever the mask
     using C = KsplitCfg<D>;
     static_assert(C::MF == kKsplitRows && C::SUB == kKsplitBN && C::KL == kKsplitLanes && C::NWH == kPrefillWaves,
                   "planner geometry must match the kernel");
-    // the plan chose the key-split kernel (256-wide heads on a small grid)
-    if (s.ksplit > 1) {
-      if (s.ksplit != C::KL || s.mf != C::MF || s.block_n != C::SUB || s.waves != C::NW) return hipErrorInvalidConfiguration;
-      if (a.mask_kind == kMaskBool)
-        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, kKsBool>), grid, dim3(C::NW * 64), 0, stream, a);
-      else if (a.mask_kind == kMaskAdditive)
-        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, kKsAdd>), grid, dim3(C::NW * 64), 0, stream, a);
-      else
-        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, kKsPlain>), grid, dim3(C::NW * 64), 0, stream, a);
+    if (s.ksplit != C::KL || s.mf != C::MF || s.block_n != C::SUB || s.waves != C::NW) return hipErrorInvalidConfiguration;
+    if (a.mask_kind == kMaskBool)
+      hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, kKsBool>), grid, dim3(C::NW * 64), 0, stream, a);
+    else if (a.mask_kind == kMaskAdditive)
+      hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, kKsAdd>), grid, dim3(C::NW * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, kKsPlain>), grid, dim3(C::NW * 64), 0, stream, a);
+    return hipGetLastError();
+  } else {
+    constexpr int MF = prefill_generic_mf(elem, D, DV);
+    constexpr int BN = prefill_generic_bn(elem, D, DV);
+    if (s.ksplit > 1) return hipErrorInvalidConfiguration;
+    if (a.mask_kind == kMaskAdditive) {
+      hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves, true>), grid, dim3(kPrefillWaves * 64), 0,
+                         stream, a);
       return hipGetLastError();
     }
-  }
-  if (s.ksplit > 1) return hipErrorInvalidConfiguration;
-  if (a.mask_kind == kMaskAdditive) {
-    hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves, true>), grid, dim3(kPrefillWaves * 64), 0,
-                       stream, a);
-    return hipGetLastError();
-  }
-  if constexpr (prefill_can_fast(elem, D, DV, kMaskNone)) {
-    using C = FastCfg<D>;
-    static_assert(C::MF == kFastRows && C::ROWS == kFastRows && C::BN == kFastBN && C::NW == kPrefillWaves,
-                  "planner geometry must match the kernel");
-    // the plan chose the pipelined kernel (32-row tiles) or, at 256-wide
-    // heads on a grid too small to fill the chip, the generic one
-    if (s.mf == C::MF && s.block_n == C::BN) {
+    if constexpr (prefill_can_fast(elem, D, DV, kMaskNone)) {
+      // the pipelined kernel (32-row tiles)
+      using C = FastCfg<D>;
+      static_assert(C::MF == kFastRows && C::ROWS == kFastRows && C::BN == kFastBN && C::NW == kPrefillWaves,
+                    "planner geometry must match the kernel");
+      if (s.mf != C::MF || s.block_n != C::BN) return hipErrorInvalidConfiguration;
       if (a.mask_kind == kMaskBool)
         hipLaunchKernelGGL((prefill_fast_kernel<E, D, true>), grid, dim3(C::NW * 64), 0, stream, a);
       else
         hipLaunchKernelGGL((prefill_fast_kernel<E, D, false>), grid, dim3(C::NW * 64), 0, stream, a);
       return hipGetLastError();
+    } else {
+      hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves, false>), grid, dim3(kPrefillWaves * 64), 0,
+                         stream, a);
+      return hipGetLastError();
     }
   }
-  if constexpr (!prefill_can_fast(elem, D, DV, kMaskNone) || prefill_fast_needs_grid(D)) {
-    hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves, false>), grid, dim3(kPrefillWaves * 64), 0,
-                       stream, a);
-    return hipGetLastError();
-  }
-  return hipErrorInvalidConfiguration;
 }
 
 hipError_t launch_prefill_16(int elem, int D, int Dv, const PrefillShape& s, const FwdArgs& a,

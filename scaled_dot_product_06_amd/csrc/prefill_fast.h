@@ -1,20 +1,17 @@
-// Prefill for 16-bit inputs with D = Dv in {64, 128, 256}: the tiled online-softmax
+// Prefill for 16-bit inputs with D = Dv in {64, 128}: the tiled online-softmax
 // walk of lattice-inference "src/attention/flash.rs" (run_tiled_attention_head)
 // with the bottom-right causal alignment of nuvec-core "tests/fast.rs"
 // (attention_fallback_matches_a_direct_formula), laid out for gfx950:
 //
 //  * each wavefront owns one 32-row MFMA block of query rows and the
 //    workgroup's four wavefronts share every K/V tile (one head each under
-//    grouped queries). Up to 128-wide heads the kernel fits 168 registers and
-//    48 KB of LDS, so three workgroups share a compute unit and three
-//    wavefronts from different workgroups share each SIMD, hiding each
-//    other's latencies (at 256-wide heads the 32-row output and query
-//    fragments take one wavefront's whole register file, and the software
-//    pipeline alone keeps the SIMD busy);
+//    grouped queries). The kernel fits 168 registers and 48 KB of LDS, so
+//    three workgroups share a compute unit and three wavefronts from
+//    different workgroups share each SIMD, hiding each other's latencies;
 //  * K and V tiles go from global memory straight into LDS
 //    (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16 * lane),
-//    through a ring of three stages, one tile ahead of the step that reads it
-//    (four stages, two ahead, at 256-wide heads), one barrier per tile; the
+//    through a ring of three stages, one tile ahead of the step that reads it,
+//    one barrier per tile; the
 //    stages are distinct LDS objects so the compiler can tell the loads into
 //    one stage from the reads of another;
 //  * the loop is software-pipelined inside each wavefront: the QK^T MFMAs of
@@ -57,9 +54,9 @@ struct FastCfg {
   static constexpr int NPV = BN / KW;           // k-steps of PV
   static constexpr int NDB = D / MF;            // 32-column output blocks
   static constexpr int NPK = NSB * ACC / 2;     // packed weight pairs per query block
-  static constexpr int WPE = D <= 128 ? 3 : 1;  // wavefronts per SIMD the registers allow
-  static constexpr int STAGES = D <= 128 ? 3 : 4;  // LDS ring of K/V tiles
-  static_assert(D == 64 || D == 128 || D == 256, "fast prefill covers 64-, 128- and 256-wide heads");
+  static constexpr int WPE = 3;                 // wavefronts per SIMD the registers allow
+  static constexpr int STAGES = 3;              // LDS ring of K/V tiles
+  static_assert(D == 64 || D == 128, "fast prefill covers 64- and 128-wide heads");
   static_assert(LOADS % NW == 0, "loads divide among wavefronts");
 };
 
@@ -90,7 +87,6 @@ prefill_fast_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[C::STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds3[C::STAGES == 4 ? C::STAGE_BYTES : 1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -366,17 +362,12 @@ prefill_fast_kernel(FwdArgs a) {
         mw_nxt[r] = t + 1 < ntiles ? mbrow[r][tb + t + 1] : 0u;
       }
     }
-    // Tile t+1 has landed: the loads complete in issue order, so with four
-    // stages waiting until only tile t+2's are outstanding suffices (with
-    // three, tile t+1's are the only ones). The barrier then also guarantees
-    // every wavefront has finished tile t-1 (its LDS reads are drained before
-    // it arrives). A plain s_barrier: the release fence of __syncthreads would
-    // also wait for tile t+2's loads.
-    if (C::STAGES == 4 && t + 2 < ntiles) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(C::LOADS_PER_TILE));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-    }
+    // Tile t+1 has landed: its loads are the only ones outstanding. The
+    // barrier then also guarantees every wavefront has finished tile t-1 (its
+    // LDS reads are drained before it arrives), whose stage the next issue
+    // refills. A plain s_barrier: the release fence of __syncthreads would
+    // also wait for the vector-memory counter.
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (t + C::STAGES - 1 < ntiles) issue_tile((tb + t + C::STAGES - 1) * BN, Sload);
     const int kt = tb + t;  // key tile
@@ -392,10 +383,7 @@ prefill_fast_kernel(FwdArgs a) {
   // prologue: tiles 0 .. STAGES-2 in flight, tile 0's scores and maxima
   if (ntiles > 0) issue_tile(tb * BN, lds0);
   if (ntiles > 1) issue_tile((tb + 1) * BN, lds1);
-  if (C::STAGES == 4 && ntiles > 2) issue_tile((tb + 2) * BN, lds2);
-  if (C::STAGES == 4 && ntiles > 2) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * C::LOADS_PER_TILE));
-  } else if (ntiles > 1) {
+  if (ntiles > 1) {
     __builtin_amdgcn_s_waitcnt(vmcnt_only(C::LOADS_PER_TILE));
   } else {
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
@@ -410,30 +398,18 @@ prefill_fast_kernel(FwdArgs a) {
   // arguments. The last step also scores a next tile, from a stage holding
   // stale data, and discards the result: one extra QK^T per workgroup keeps a
   // separate final step out of the loop.
-  if constexpr (C::STAGES == 4) {
-    for (int t = 0; t < ntiles; t += 4) {
-      step(t, sa, sb, lds0, lds1, lds3);
-      if (t + 1 >= ntiles) break;
-      step(t + 1, sb, sa, lds1, lds2, lds0);
-      if (t + 2 >= ntiles) break;
-      step(t + 2, sa, sb, lds2, lds3, lds1);
-      if (t + 3 >= ntiles) break;
-      step(t + 3, sb, sa, lds3, lds0, lds2);
-    }
-  } else {
-    for (int t = 0; t < ntiles; t += 6) {
-      step(t, sa, sb, lds0, lds1, lds2);
-      if (t + 1 >= ntiles) break;
-      step(t + 1, sb, sa, lds1, lds2, lds0);
-      if (t + 2 >= ntiles) break;
-      step(t + 2, sa, sb, lds2, lds0, lds1);
-      if (t + 3 >= ntiles) break;
-      step(t + 3, sb, sa, lds0, lds1, lds2);
-      if (t + 4 >= ntiles) break;
-      step(t + 4, sa, sb, lds1, lds2, lds0);
-      if (t + 5 >= ntiles) break;
-      step(t + 5, sb, sa, lds2, lds0, lds1);
-    }
+  for (int t = 0; t < ntiles; t += 6) {
+    step(t, sa, sb, lds0, lds1, lds2);
+    if (t + 1 >= ntiles) break;
+    step(t + 1, sb, sa, lds1, lds2, lds0);
+    if (t + 2 >= ntiles) break;
+    step(t + 2, sa, sb, lds2, lds0, lds1);
+    if (t + 3 >= ntiles) break;
+    step(t + 3, sb, sa, lds0, lds1, lds2);
+    if (t + 4 >= ntiles) break;
+    step(t + 4, sa, sb, lds1, lds2, lds0);
+    if (t + 5 >= ntiles) break;
+    step(t + 5, sb, sa, lds2, lds0, lds1);
   }
 
   if (!wave_live) return;

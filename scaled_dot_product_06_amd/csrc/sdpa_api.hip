@@ -269,22 +269,12 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
     *plan = p;
     return SDPA_OK;
   }
-  // pipelined kernel (32-row tiles) where it applies and, at 256-wide heads,
-  // where one batch item's grid fills the chip; else the generic kernel's
-  // geometry
+  // the key-split kernel at 256-wide 16-bit heads, the pipelined kernel (32-row
+  // tiles) where it applies, else the generic kernel's geometry
   const int nw = prefill_waves(dtype, (int)D, (int)Dv);
   const int64_t heads = gcd64(group, nw);
-  bool fast = prefill_can_fast(dtype, (int)D, (int)Dv, mask_kind);
-  bool kspl = false;
-  if (prefill_can_ksplit(dtype, (int)D, (int)Dv, mask_kind)) {
-    // 256-wide heads: the pipelined kernel when one batch item's 32-row grid fills
-    // the chip (and no additive mask), else the key-split kernel
-    const int64_t fbm = (nw / heads) * kFastRows;
-    fast = fast && (Hq / heads) * ((Lq + fbm - 1) / fbm) >= kFastMinGridWide;
-    kspl = !fast;
-  } else if (fast && prefill_fast_needs_grid((int)D)) {
-    fast = false;
-  }
+  const bool kspl = prefill_can_ksplit(dtype, (int)D, (int)Dv, mask_kind);
+  const bool fast = !kspl && prefill_can_fast(dtype, (int)D, (int)Dv, mask_kind);
   if (kspl) {
     // 16-row query blocks of `heads` heads per workgroup, two key lanes of wavefronts
     const int64_t kbm = (nw / heads) * kKsplitRows;

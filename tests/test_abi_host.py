@@ -67,7 +67,7 @@ def test_workload_routes(number, route):
             assert p["splits"] == p["waves"] and p["heads_per_group"] == 1
             rows_per_block = p["rows_per_wave"]
         elif p["splits"]:
-            # 256-wide 16-bit heads on a small grid: two key lanes of wavefronts
+            # 256-wide 16-bit heads: two key lanes of wavefronts
             assert (w["D"], p["splits"], p["rows_per_wave"], p["block_n"]) == (256, 2, 16, 32)
             rows_per_block = p["waves"] // p["splits"] // p["heads_per_group"] * p["rows_per_wave"]
         else:
@@ -353,23 +353,21 @@ def test_f32_paged_plans_are_prefill_plans():
         assert p == sd.sdpa_plan(2, 8, 2, Lq, 20 * 16, 128, 128, 1, False, False, 0)
 
 
-def test_wide_heads_plan_the_pipelined_kernel_only_on_full_grids():
-    # 256-wide 16-bit heads take the pipelined 32-row kernel when one batch item's grid
-    # has a workgroup per compute unit (256), the key-split 16-row kernel below that; the
-    # batch size never changes the choice
+def test_wide_heads_plan_the_key_split_kernel_on_every_grid():
+    # 256-wide 16-bit heads take the key-split 16-row kernel whatever the grid (it
+    # measured faster than 32-row tiles, one wavefront per SIMD, on full grids too);
+    # the batch size never changes the geometry
     def shape(p):
         return p["rows_per_wave"], p["block_n"], p["splits"], p["waves"]
-    big = sd.sdpa_plan(1, 32, 4, 1040, 1297, 256, 256, 1, False, False, 2)   # 8 x 33 = 264
-    assert shape(big) + (big["grid"][0],) == (32, 32, 0, 4, 8 * 33)
-    assert sd.sdpa_plan(3, 32, 4, 1040, 1297, 256, 256, 1, False, False, 2)["rows_per_wave"] == 32
-    edge = sd.sdpa_plan(1, 32, 4, 1000, 1297, 256, 256, 1, False, False, 2)  # 8 x 32 = 256
-    assert shape(edge) == (32, 32, 0, 4)
-    under = sd.sdpa_plan(1, 32, 4, 992, 1297, 256, 256, 1, False, False, 2)  # 8 x 31 = 248
+    big = sd.sdpa_plan(1, 32, 4, 1040, 1297, 256, 256, 1, False, False, 2)   # 8 x 65 workgroups
+    assert shape(big) + (big["grid"][0],) == (16, 32, 2, 8, 8 * 65)
+    assert shape(sd.sdpa_plan(3, 32, 4, 1040, 1297, 256, 256, 1, False, False, 2)) == (16, 32, 2, 8)
+    under = sd.sdpa_plan(1, 32, 4, 992, 1297, 256, 256, 1, False, False, 2)  # 8 x 62
     assert shape(under) + (under["grid"][0],) == (16, 32, 2, 8, 8 * 62)
-    small = sd.sdpa_plan(1, 16, 2, 1024, 1801, 256, 256, 2, True, True, 1)  # workload 4: 4 x 32 = 128
+    small = sd.sdpa_plan(1, 16, 2, 1024, 1801, 256, 256, 2, True, True, 1)  # workload 4: 4 x 64
     # the key-split kernel reads the boolean mask's bytes: one kernel, no scratch
     assert shape(small) + (small["grid"][0], small["kernels"], small["scratch_bytes"]) == (16, 32, 2, 8, 4 * 64, 1, 0)
-    # the pipelined kernel packs it first
+    # the pipelined kernel (128-wide heads) packs it first
     packed = sd.sdpa_plan(1, 16, 2, 1024, 1801, 128, 128, 2, True, True, 1)
     assert (packed["kernels"], packed["scratch_bytes"]) == (2, 1024 * 57 * 4)
     batched = sd.sdpa_plan(8, 16, 2, 1024, 1801, 256, 256, 2, True, True, 1)  # the same per batch item
@@ -377,8 +375,8 @@ def test_wide_heads_plan_the_pipelined_kernel_only_on_full_grids():
     # one or two heads per workgroup: 64 or 32 rows of a head per key lane
     assert sd.sdpa_plan(1, 4, 4, 100, 300, 256, 256, 0, False, False, 2)["grid"][0] == 4 * 2
     assert sd.sdpa_plan(1, 4, 2, 100, 300, 256, 256, 0, False, False, 2)["grid"][0] == 2 * 4
-    # additive masks take the key-split kernel at 256-wide heads on any grid (the
-    # pipelined kernel reads no additive mask); other head sizes keep the generic kernel
+    # additive masks take the key-split kernel at 256-wide heads too; other head sizes
+    # keep the generic kernel (the pipelined kernel reads no additive mask)
     add = sd.sdpa_plan(1, 64, 8, 1024, 1801, 256, 256, 3, True, True, 1)
     assert shape(add) + (add["kernels"], add["scratch_bytes"]) == (16, 32, 2, 8, 1, 0)
     big_add = sd.sdpa_plan(1, 32, 4, 1040, 1297, 256, 256, 3, True, False, 2)

@@ -1,5 +1,5 @@
-"""GPU parity of the key-split prefill (256-wide 16-bit heads on grids too small
-for 32-row tiles) against the CPU float64 oracle, every output element.
+"""GPU parity of the key-split prefill (every 256-wide 16-bit call) against the
+CPU float64 oracle, every output element.
 
 The kernel's workgroup holds 16 query rows of up to four heads and splits each
 64-key step between two lanes of wavefronts, which merge at the end. The cases
@@ -170,7 +170,7 @@ def test_additive_mask_with_zero_scale():
 
 
 def test_additive_mask_on_a_full_grid_sampled_rows():
-    # 32 heads x 1040 rows: a grid the pipelined kernel would fill, which has no additive path
+    # 32 heads x 1040 rows: 520 workgroups, two per compute unit and more
     from tests.gpu_util import sample_rows
     p = gen.make_problem(8950, 1, 32, 4, 1040, 1297, 256, 256, BF16, 0, sinks=True)
     _additive_plan(p)

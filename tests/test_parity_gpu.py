@@ -128,34 +128,34 @@ def test_prefill_bool_mask_word_edges(D, Lk):
             _full_check(p, f"bool mask {name} D={D} Lk={Lk}")
 
 
-# --- 256-wide heads on the pipelined kernel -------------------------------------------------
-# A batch item's grid of at least one workgroup per compute unit routes 256-wide 16-bit heads
-# to the pipelined 32-row kernel (smaller calls keep the generic 16-row one, as workload 4
-# does). Ragged on both axes: 1040 query rows (33 blocks of 32) over 1297 keys (40.5 tiles).
+# --- 256-wide heads on a full grid ------------------------------------------------------------
+# 256-wide 16-bit heads run the key-split kernel on every grid; here 520 workgroups (two
+# batch items of 32 heads), ragged on both axes: 1040 query rows (65 blocks of 16) over
+# 1297 keys (20.3 steps of 64).
 
 WIDE = dict(B=2, Hq=32, Hkv=4, Lq=1040, Lk=1297, D=256)
 
 
 @pytest.mark.parametrize("mask_kind,sinks", [(0, False), (1, False), (1, True), (2, True)])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_wide_heads_pipelined_sampled_rows(mask_kind, sinks, dtype):
+def test_wide_heads_full_grid_sampled_rows(mask_kind, sinks, dtype):
     w = WIDE
     p = gen.make_problem(1700 + 10 * mask_kind + sinks, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], w["D"],
                          w["D"], DT[dtype], mask_kind, sinks=sinks)
-    say(f"wide pipelined: {p!r}")
+    say(f"wide, full grid: {p!r}")
     got = from_device(run_gpu(p), p.dtype)
     assert np.all(np.isfinite(got))
     rows = sample_rows(p, 120, seed=17 + mask_kind)
     want = oracle_rows(p, rows)
     assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want,
-                  f"256-wide pipelined mask {mask_kind} sinks {sinks}, sampled rows")
+                  f"256-wide full grid mask {mask_kind} sinks {sinks}, sampled rows")
 
 
-def test_wide_heads_pipelined_batch_items_equal_each_item_alone():
+def test_wide_heads_full_grid_batch_items_equal_each_item_alone():
     w = WIDE
     p = gen.make_problem(1795, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], w["D"], w["D"], BF16, 1, sinks=True)
     import scaled_dot_product_06_amd as sd
-    assert sd.sdpa_plan(*p.shape_args(), 1, False, True, BF16)["rows_per_wave"] == 32
+    assert sd.sdpa_plan(*p.shape_args(), 1, False, True, BF16)["splits"] == 2
     whole = from_device(run_gpu(p), BF16)
     for b in range(w["B"]):
         pb = gen.Problem(1, w["Hq"], w["Hkv"], w["Lq"], w["Lk"], w["D"], w["D"], BF16, 1, p.scale, p.q[b:b + 1],
@@ -164,7 +164,7 @@ def test_wide_heads_pipelined_batch_items_equal_each_item_alone():
         assert np.array_equal(whole[b:b + 1], alone), f"batch item {b} differs"
 
 
-def test_wide_heads_pipelined_window_sampled_rows():
+def test_wide_heads_full_grid_window_sampled_rows():
     from scaled_dot_product_06_amd import attention
     import torch
     w = WIDE
@@ -175,7 +175,7 @@ def test_wide_heads_pipelined_window_sampled_rows():
     rows = sample_rows(p, 96, seed=23)
     qq, kk, vv, _, ss = p.widened()
     want = orc.sdpa(qq, kk, vv, p.scale, 1, None, ss, window=300, rows=rows)
-    assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want, "256-wide pipelined window 300")
+    assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want, "256-wide full grid window 300")
 
 
 # --- sliding windows (nuvec-core tests/fast.rs, windowed-kernel tests) -------------------------

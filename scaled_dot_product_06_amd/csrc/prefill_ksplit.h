@@ -1,12 +1,12 @@
-// Prefill for 16-bit inputs with 256-wide heads on grids too small to fill the
-// chip with 32-row work: the tiled online-softmax walk of lattice-inference
+// Prefill for 16-bit inputs with 256-wide heads (every grid, every mask kind):
+// the tiled online-softmax walk of lattice-inference
 // "src/attention/flash.rs" (run_tiled_attention_head), with the bottom-right
 // causal alignment of nuvec-core "tests/fast.rs"
 // (attention_fallback_matches_a_direct_formula), laid out for gfx950:
 //
 //  * each wavefront owns 16 query rows of one head (16x16x32 MFMA tiles), so
 //    its query fragment (32 registers) and output (64) leave room for two
-//    wavefronts per SIMD;
+//    wavefronts per SIMD, where a 32-row wavefront would hold its SIMD alone;
 //  * the workgroup's eight wavefronts are four (head, row block) slots times
 //    two key lanes. The workgroup walks the keys in 64-key steps; in each,
 //    key lane j takes keys [32j, 32j + 32) of the step, so every wavefront

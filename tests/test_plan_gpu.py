@@ -133,7 +133,7 @@ def _case(kind, B, Hq, Hkv, Lq, Lk, D, Dv, dtype, window=0, bs=16):
 # (kind, B, Hq, Hkv, Lq, Lk, D, Dv, dtype[, window]): every route and launch count
 CASES = [
     (1, 2, 8, 2, 300, 300, 128, 128, BF16),        # pipelined prefill
-    (0, 1, 8, 2, 77, 150, 256, 256, F16),          # key-split prefill (256-wide heads, small grid)
+    (0, 1, 8, 2, 77, 150, 256, 256, F16),          # key-split prefill (256-wide heads)
     (2, 1, 16, 2, 100, 300, 256, 256, BF16),       # key-split prefill reading the mask bytes: one kernel
     (0, 1, 8, 2, 77, 150, 192, 192, F16),          # generic prefill
     (2, 1, 8, 2, 200, 333, 64, 64, F16),           # mask packing + prefill

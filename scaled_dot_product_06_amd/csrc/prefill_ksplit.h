@@ -482,6 +482,9 @@ prefill_ksplit_kernel(FwdArgs a) {
     read_k(Knext, 4, bb);
     score_init(snext, mb);
     fence();
+    // the MFMA groups at raised wave priority: of the two wavefronts on a SIMD,
+    // which leave each barrier together, the one in its MFMA groups issues first
+    __builtin_amdgcn_s_setprio(1);
     mma_qk(0, ba, snext);
     fence();
     lds_wait();
@@ -497,6 +500,7 @@ prefill_ksplit_kernel(FwdArgs a) {
     lds_wait();
     mma_pv(8, bb, pk);
     fence();
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (ADDMASK) add_apply(snext, mv);
     tile_max_full(snext);
   };

@@ -67,9 +67,18 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(FwdArgs a) {
   const int col = lane % MF;
   const int kg = lane / MF;
 
-  const int split = blockIdx.x;
-  const int hkv = blockIdx.y;
-  const int b = blockIdx.z;
+  // Dispatch order: splits 0 .. nsplit-2 of each (kv head, batch item) pair,
+  // pair after pair, then the last split of every pair. The last split is the
+  // shortest, so when the grid overflows the compute units by a few
+  // workgroups (260 for 256 at 8193 keys and four kv heads) the overflow is
+  // made of short splits rather than full ones (12.7 -> 11.8 us there).
+  const int64_t lin = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+  const int64_t per = a.nsplit > 1 ? a.nsplit - 1 : 1;   // splits before the last one
+  const int64_t nbulk = (int64_t)a.Hkv * a.B * (a.nsplit - 1);
+  const int64_t pair = lin < nbulk ? lin / per : lin - nbulk;
+  const int split = lin < nbulk ? (int)(lin % per) : a.nsplit - 1;
+  const int hkv = (int)(pair % a.Hkv);
+  const int b = (int)(pair / a.Hkv);
   // the keys this batch item holds: all Lk, or the sequence's clamped length
   int Lk = a.Lk, koff = a.koff;
   if constexpr (PAGED) {

@@ -67,12 +67,14 @@ enum {
 typedef struct sdpa_plan_t {
   int32_t route;          /* SDPA_ROUTE_* */
   int32_t kernels;        /* kernel launches the call enqueues */
-  int32_t rows_per_wave;  /* query rows one wavefront carries (MFMA tile height). Prefill: 32 on
-                             the pipelined kernel (f16/bf16, D == Dv in {64, 128}, no additive
-                             mask); 16 on the key-split kernel (f16/bf16, D == Dv == 256, every
-                             mask kind); else the generic kernel's 32 (heads up to 128 wide) or
-                             16 (wider heads; and f32 calls whose 32-row grid for one batch item
-                             would have fewer than 256 workgroups) */
+  int32_t rows_per_wave;  /* query rows one wavefront carries (MFMA tile height). Prefill: 16 on
+                             the key-split kernel (f16/bf16, D == Dv == 256 with every mask kind,
+                             and D == Dv == 128 when the pipelined kernel's grid for one batch item
+                             would have fewer than 256 workgroups); 32 on the pipelined kernel
+                             (other f16/bf16 calls with D == Dv in {64, 128}, no additive mask);
+                             else the generic kernel's 32 (heads up to 128 wide) or 16 (wider
+                             heads; and f32 calls whose 32-row grid for one batch item would have
+                             fewer than 256 workgroups) */
   int32_t waves;          /* wavefronts per workgroup of the first kernel */
   int32_t block_n;        /* keys per tile */
   int32_t heads_per_group;/* prefill: query heads sharing one workgroup's K/V tiles;

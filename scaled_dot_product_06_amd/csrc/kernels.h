@@ -97,13 +97,17 @@ constexpr bool prefill_can_fast(int elem, int D, int Dv, int mask_kind) {
   return elem != kF32 && D == Dv && (D == 64 || D == 128) && mask_kind != kMaskAdditive;
 }
 constexpr int kFastRows = 32, kFastBN = 32;
-// 256-wide 16-bit heads run the key-split kernel on every grid and with every
-// mask: 16-row tiles, and the workgroup's wavefronts in two key lanes that each
-// take 32 keys of every 64-key step, so each SIMD holds two wavefronts (a
-// 32-row tile of these heads leaves room for one).
+// The key-split kernel: 16-row tiles, and the workgroup's wavefronts in two key
+// lanes that each take 32 keys of every 64-key step, so each SIMD holds two
+// wavefronts. 256-wide 16-bit heads run it on every grid and with every mask (a
+// 32-row tile of these heads leaves room for one wavefront per SIMD);
+// 128-wide heads run it when the pipelined kernel's grid for one batch item
+// would have fewer than kKsplitGrid128 workgroups (the rule ignores the batch
+// size, so a batch item takes the same kernel alone or within a batch).
 constexpr int kKsplitLanes = 2, kKsplitRows = 16, kKsplitBN = 32;
-constexpr bool prefill_can_ksplit(int elem, int D, int Dv, int mask_kind) {
-  return elem != kF32 && D == Dv && D == 256;
+constexpr int kKsplitGrid128 = 256;
+constexpr bool prefill_can_ksplit(int elem, int D, int Dv) {
+  return elem != kF32 && D == Dv && (D == 128 || D == 256);
 }
 // Generic kernel: 32x32 MFMA tiles (32 query rows per wavefront) up to
 // 128-wide heads; 16x16 tiles above, where a 32-row output accumulator would

@@ -1,5 +1,6 @@
-// Prefill for 16-bit inputs with 256-wide heads (every grid, every mask kind):
-// the tiled online-softmax walk of lattice-inference
+// Prefill for 16-bit inputs with 256-wide heads (every grid, every mask kind)
+// and 128-wide heads on grids too small for the pipelined 32-row kernel: the
+// tiled online-softmax walk of lattice-inference
 // "src/attention/flash.rs" (run_tiled_attention_head), with the bottom-right
 // causal alignment of nuvec-core "tests/fast.rs"
 // (attention_fallback_matches_a_direct_formula), laid out for gfx950:
@@ -17,7 +18,8 @@
 //    units;
 //  * K and V steps go from global memory straight into LDS
 //    (global_load_lds_dwordx4) through two double-buffered rings (K and V,
-//    32 KB per step each, 128 KB in all): the K of step t+2 and the V of step
+//    32 KB per step each at 256-wide heads, 128 KB in all; half that at 128):
+//    the K of step t+2 and the V of step
 //    t+1 are loaded while step t runs, one barrier per step;
 //  * the walk is software-pipelined inside each wavefront: the QK^T MFMAs of
 //    step t+1 are issued among the exponentials of step t, and the PV MFMAs of
@@ -60,16 +62,18 @@ struct KsplitCfg {
   static constexpr int NSB = SUB / MF;         // 16-key blocks per wavefront step
   static constexpr int NDB = D / MF;           // 16-column output blocks
   static constexpr int NPK = SUB * MF / 64 / 2;  // packed weight pairs per lane
-  static_assert(D == 256, "the key-split prefill serves 256-wide heads");
+  static_assert(D == 128 || D == 256, "the key-split prefill serves 128- and 256-wide heads");
   static_assert(LOADS % NW == 0, "loads divide among wavefronts");
   static_assert(NSB == 2 && NPK == 4, "two 16-key blocks make one 32-key PV step");
 };
 
-// K: the chunk of row r sits at slot chunk ^ (r % 32); the 16 rows one read
-// touches (r0 .. r0+15, r0 a multiple of 16) land on 16 different slots.
+// K: the chunk of row r sits at slot chunk ^ (r % CPR) (CPR = 32 chunks per row at
+// 256-wide heads, 16 at 128); the 16 rows one read touches (r0 .. r0+15, r0 a
+// multiple of 16) land on 16 different slots.
 template <int D> __device__ __forceinline__ int ks_swz_k(int row) { return row % KsplitCfg<D>::CPR; }
-// V: pairs of chunks move together (XOR by an even number), by 2 * (r % 8); the
-// 16 rows of a transposed read put 8 different pairs on each 256-byte line.
+// V: pairs of chunks move together (XOR by an even number), by 2 * (r % 8); each
+// half-wavefront of a transposed read covers 8 consecutive rows, whose 8
+// different pairs fill one 256-byte line of banks.
 template <int D> __device__ __forceinline__ int ks_swz_v(int row) { return 2 * (row % 8); }
 
 // bytes between rows of the boolean-mask ring (64 keys plus padding)
@@ -331,19 +335,22 @@ prefill_ksplit_kernel(FwdArgs a) {
   uint32_t kb4[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) kb4[c] = (SUB * kl + col) * C::RB + (((4 * c + kg) ^ col) * 16);
+  // (at 128-wide heads the XOR of row 16 nb + col is col's alone: blocks differ by 16 rows)
   auto k_off = [&](int c, int nb) -> uint32_t {
+    if constexpr (D == 128) return kb4[c] + nb * (16 * C::RB);
     return c < 4 ? kb4[c] + nb * (16 * C::RB + 256) : kb4[c - 4] + 256 + nb * (16 * C::RB - 256);
   };
   // V^T operand of output block db: transposed reads of keys 4g..4g+3 and
   // 16+4g..16+4g+3 (g = lane / 16); provider lane l points at row
   // SUB*kl + l/4 (+16), columns 16 db + 4 (l % 4) .. +3. The V XOR pairs chunk
-  // 2 db with row % 8, so blocks db and db + 8 differ by 256 bytes.
+  // 2 db with row % 8, so blocks db and db + 8 (256-wide heads) differ by 256 bytes.
   const int vr = lane >> 2;
   uint32_t vb8[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db)
     vb8[db] = (SUB * kl + vr) * C::RB + ((2 * (db ^ (vr % 8)) + ((lane >> 1) & 1)) * 16) + (lane & 1) * 8;
   auto v_off = [&](int db) -> uint32_t { return db < 8 ? vb8[db] : vb8[db - 8] + 256; };
+  static_assert(C::NQC % 4 == 0 && C::NDB % 8 == 0, "LDS operands come in groups of four k-steps and eight blocks");
 
   // LDS operands go through two register buffers of eight 16-byte groups: the
   // reads of one group are issued before the MFMAs of the previous one, and an
@@ -380,10 +387,12 @@ prefill_ksplit_kernel(FwdArgs a) {
     read_k(Ks, 0, ba);
     lds_wait();
     score_init(s, mb);
-    read_k(Ks, 4, bb);
-    lds_wait();
+    if constexpr (C::NQC == 8) {
+      read_k(Ks, 4, bb);
+      lds_wait();
+    }
     mma_qk(0, ba, s);
-    mma_qk(4, bb, s);
+    if constexpr (C::NQC == 8) mma_qk(4, bb, s);
   };
   auto row_max16 = [](float x) { return max_xor16(max_xor32(x)); };
   auto tile_max_full = [&](acc_t (&s)[C::NSB]) {
@@ -479,27 +488,42 @@ prefill_ksplit_kernel(FwdArgs a) {
     weights(scur, pk);
     fence();
     lds_wait();
-    read_k(Knext, 4, bb);
-    score_init(snext, mb);
-    fence();
-    // the MFMA groups at raised wave priority: of the two wavefronts on a SIMD,
-    // which leave each barrier together, the one in its MFMA groups issues first
-    __builtin_amdgcn_s_setprio(1);
-    mma_qk(0, ba, snext);
-    fence();
-    lds_wait();
-    read_v(Vcur, 0, ba);
-    fence();
-    mma_qk(4, bb, snext);
-    fence();
-    lds_wait();
-    read_v(Vcur, 8, bb);
-    fence();
-    mma_pv(0, ba, pk);
-    fence();
-    lds_wait();
-    mma_pv(8, bb, pk);
-    fence();
+    if constexpr (C::NQC == 8) {
+      // 256-wide heads: two groups of K operands and two of V, each group's
+      // reads issued before the MFMAs of the previous one
+      read_k(Knext, 4, bb);
+      score_init(snext, mb);
+      fence();
+      // the MFMA groups at raised wave priority: of the two wavefronts on a SIMD,
+      // which leave each barrier together, the one in its MFMA groups issues first
+      __builtin_amdgcn_s_setprio(1);
+      mma_qk(0, ba, snext);
+      fence();
+      lds_wait();
+      read_v(Vcur, 0, ba);
+      fence();
+      mma_qk(4, bb, snext);
+      fence();
+      lds_wait();
+      read_v(Vcur, 8, bb);
+      fence();
+      mma_pv(0, ba, pk);
+      fence();
+      lds_wait();
+      mma_pv(8, bb, pk);
+      fence();
+    } else {
+      // 128-wide heads: one group of K operands and one of V
+      read_v(Vcur, 0, bb);
+      score_init(snext, mb);
+      fence();
+      __builtin_amdgcn_s_setprio(1);
+      mma_qk(0, ba, snext);
+      fence();
+      lds_wait();
+      mma_pv(0, bb, pk);
+      fence();
+    }
     __builtin_amdgcn_s_setprio(0);
     if constexpr (ADDMASK) add_apply(snext, mv);
     tile_max_full(snext);

@@ -83,10 +83,13 @@ def test_small_f32_calls_split_keys_within_a_workgroup():
     # the rule looks at one batch item, so the batch keeps the tiles
     q = _plan(B=5, Hq=8, Hkv=8, Lq=128, Lk=128, D=64, Dv=64, mask=1, dtype=0)
     assert (q["rows_per_wave"], q["splits"], q["grid"]) == (16, 4, (320, 1, 1))
-    # large f32 calls keep the 32-row walk; 16-bit calls never split
+    # large f32 calls keep the 32-row walk; 16-bit calls never take this split (a small
+    # 128-wide bf16 grid takes the key-split kernel's two key lanes of eight waves instead,
+    # 64-wide heads the pipelined kernel)
     big = _plan(B=1, Hq=32, Hkv=8, Lq=4096, Lk=4096, D=128, Dv=128, mask=1, dtype=0)
     assert (big["rows_per_wave"], big["splits"]) == (32, 0)
-    assert _plan(dtype=2)["splits"] == 0
+    assert (_plan(dtype=2)["splits"], _plan(dtype=2)["waves"]) == (2, 8)
+    assert _plan(D=64, Dv=64, dtype=2)["splits"] == 0
     # additive masks keep the generic walk at 16 rows
     add = _plan(B=1, Hq=8, Hkv=8, Lq=128, Lk=128, D=64, Dv=64, mask=3, has_mask=True, dtype=0)
     assert (add["rows_per_wave"], add["splits"]) == (16, 0)
@@ -311,10 +314,15 @@ def _strided(q=(16, 4 * 5 * 64, 5 * 64, 64), k=(16, 2 * 9 * 64, 9 * 64, 64), v=(
 
 
 def test_additive_masks_plan_on_the_generic_prefill_kernel():
-    fast = sd.sdpa_plan(1, 8, 2, 300, 300, 128, 128, 0, False, False, 2)
-    add = sd.sdpa_plan(1, 8, 2, 300, 300, 128, 128, 3, True, False, 2)
+    # a grid the pipelined kernel fills (32 heads x 4096 rows at 128-wide heads): it
+    # reads no additive mask, so those calls take the generic kernel
+    fast = sd.sdpa_plan(1, 32, 8, 4096, 4096, 128, 128, 0, False, False, 2)
+    add = sd.sdpa_plan(1, 32, 8, 4096, 4096, 128, 128, 3, True, False, 2)
     assert fast["route"] == add["route"] == "prefill"
     assert (fast["block_n"], add["block_n"]) == (32, 64)
+    # on a small grid both take the key-split kernel
+    small = sd.sdpa_plan(1, 8, 2, 300, 300, 128, 128, 3, True, False, 2)
+    assert (small["splits"], small["rows_per_wave"]) == (2, 16)
     dec = sd.sdpa_plan(1, 8, 2, 1, 3000, 128, 128, 3, True, False, 2)
     assert dec["route"] == "decode"
     assert sd.sdpa_plan(1, 8, 2, 1, 3000, 128, 128, 3, False, False, 2, check=False) == -1
@@ -353,7 +361,7 @@ def test_f32_paged_plans_are_prefill_plans():
         assert p == sd.sdpa_plan(2, 8, 2, Lq, 20 * 16, 128, 128, 1, False, False, 0)
 
 
-def test_wide_heads_plan_the_key_split_kernel_on_every_grid():
+def test_key_split_plans_for_wide_heads_and_small_128_wide_grids():
     # 256-wide 16-bit heads take the key-split 16-row kernel whatever the grid (it
     # measured faster than 32-row tiles, one wavefront per SIMD, on full grids too);
     # the batch size never changes the geometry
@@ -367,19 +375,28 @@ def test_wide_heads_plan_the_key_split_kernel_on_every_grid():
     small = sd.sdpa_plan(1, 16, 2, 1024, 1801, 256, 256, 2, True, True, 1)  # workload 4: 4 x 64
     # the key-split kernel reads the boolean mask's bytes: one kernel, no scratch
     assert shape(small) + (small["grid"][0], small["kernels"], small["scratch_bytes"]) == (16, 32, 2, 8, 4 * 64, 1, 0)
-    # the pipelined kernel (128-wide heads) packs it first
-    packed = sd.sdpa_plan(1, 16, 2, 1024, 1801, 128, 128, 2, True, True, 1)
+    # the pipelined kernel (128-wide heads on a grid it fills) packs it first
+    packed = sd.sdpa_plan(1, 64, 8, 1024, 1801, 128, 128, 2, True, True, 1)   # 16 x 32 workgroups
     assert (packed["kernels"], packed["scratch_bytes"]) == (2, 1024 * 57 * 4)
+    # 128-wide heads on a small grid: the key-split kernel, which reads the bytes itself
+    small128 = sd.sdpa_plan(1, 16, 2, 1024, 1801, 128, 128, 2, True, True, 1)  # 4 x 32 for the pipelined kernel
+    assert shape(small128) + (small128["kernels"], small128["scratch_bytes"]) == (16, 32, 2, 8, 1, 0)
+    # the threshold: 256 pipelined workgroups per batch item keep the pipelined kernel
+    assert shape(sd.sdpa_plan(1, 32, 4, 1024, 1024, 128, 128, 1, False, False, 2)) == (32, 32, 0, 4)   # 8 x 32
+    assert shape(sd.sdpa_plan(1, 32, 4, 992, 1024, 128, 128, 1, False, False, 2)) == (16, 32, 2, 8)    # 8 x 31
+    assert shape(sd.sdpa_plan(4, 32, 4, 992, 1024, 128, 128, 1, False, False, 2)) == (16, 32, 2, 8)    # per item
     batched = sd.sdpa_plan(8, 16, 2, 1024, 1801, 256, 256, 2, True, True, 1)  # the same per batch item
     assert shape(batched) + (batched["grid"][0],) == (16, 32, 2, 8, 8 * 4 * 64)
     # one or two heads per workgroup: 64 or 32 rows of a head per key lane
     assert sd.sdpa_plan(1, 4, 4, 100, 300, 256, 256, 0, False, False, 2)["grid"][0] == 4 * 2
     assert sd.sdpa_plan(1, 4, 2, 100, 300, 256, 256, 0, False, False, 2)["grid"][0] == 2 * 4
-    # additive masks take the key-split kernel at 256-wide heads too; other head sizes
-    # keep the generic kernel (the pipelined kernel reads no additive mask)
+    # additive masks take the key-split kernel at 256-wide heads too, and at 128-wide
+    # heads on small grids; other calls keep the generic kernel (the pipelined kernel
+    # reads no additive mask)
     add = sd.sdpa_plan(1, 64, 8, 1024, 1801, 256, 256, 3, True, True, 1)
     assert shape(add) + (add["kernels"], add["scratch_bytes"]) == (16, 32, 2, 8, 1, 0)
     big_add = sd.sdpa_plan(1, 32, 4, 1040, 1297, 256, 256, 3, True, False, 2)
     assert shape(big_add) == (16, 32, 2, 8)
-    assert shape(sd.sdpa_plan(1, 16, 2, 1024, 1801, 128, 128, 3, True, True, 1)) == (32, 64, 0, 4)
+    assert shape(sd.sdpa_plan(1, 64, 8, 1024, 1801, 128, 128, 3, True, True, 1)) == (32, 64, 0, 4)
+    assert shape(sd.sdpa_plan(1, 16, 2, 1024, 1801, 128, 128, 3, True, True, 1)) == (16, 32, 2, 8)
     assert shape(sd.sdpa_plan(1, 64, 8, 1024, 1801, 192, 192, 1, False, False, 1)) == (16, 64, 0, 4)

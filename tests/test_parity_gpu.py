@@ -128,54 +128,67 @@ def test_prefill_bool_mask_word_edges(D, Lk):
             _full_check(p, f"bool mask {name} D={D} Lk={Lk}")
 
 
-# --- 256-wide heads on a full grid ------------------------------------------------------------
-# 256-wide 16-bit heads run the key-split kernel on every grid; here 520 workgroups (two
-# batch items of 32 heads), ragged on both axes: 1040 query rows (65 blocks of 16) over
-# 1297 keys (20.3 steps of 64).
+# --- full grids at 128- and 256-wide heads -----------------------------------------------------
+# Two batch items of 32 heads, ragged on both axes: 1040 query rows over 1297 keys. At
+# 256-wide heads the key-split kernel (520 workgroups of 16-row blocks); at 128-wide heads
+# the pipelined kernel, whose grid here (264 workgroups of 32-row blocks per batch item)
+# is large enough that the plan keeps it (the small-grid tests of 128-wide heads run the
+# key-split kernel).
 
-WIDE = dict(B=2, Hq=32, Hkv=4, Lq=1040, Lk=1297, D=256)
+WIDE = dict(B=2, Hq=32, Hkv=4, Lq=1040, Lk=1297)
+WIDE_KERNEL = {128: 0, 256: 2}   # the plan's key lanes: 0 = pipelined kernel, 2 = key-split
 
 
+def _wide_plan_check(p):
+    import scaled_dot_product_06_amd as sd
+    plan = sd.sdpa_plan(*p.shape_args(), p.mask_kind, p.mask is not None, p.sinks is not None, p.dtype)
+    assert plan["splits"] == WIDE_KERNEL[p.D], plan
+
+
+@pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("mask_kind,sinks", [(0, False), (1, False), (1, True), (2, True)])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_wide_heads_full_grid_sampled_rows(mask_kind, sinks, dtype):
+def test_wide_heads_full_grid_sampled_rows(mask_kind, sinks, dtype, D):
     w = WIDE
-    p = gen.make_problem(1700 + 10 * mask_kind + sinks, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], w["D"],
-                         w["D"], DT[dtype], mask_kind, sinks=sinks)
-    say(f"wide, full grid: {p!r}")
+    p = gen.make_problem(1700 + 10 * mask_kind + sinks + D, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], D, D,
+                         DT[dtype], mask_kind, sinks=sinks)
+    _wide_plan_check(p)
+    say(f"full grid: {p!r}")
     got = from_device(run_gpu(p), p.dtype)
     assert np.all(np.isfinite(got))
     rows = sample_rows(p, 120, seed=17 + mask_kind)
     want = oracle_rows(p, rows)
     assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want,
-                  f"256-wide full grid mask {mask_kind} sinks {sinks}, sampled rows")
+                  f"{D}-wide full grid mask {mask_kind} sinks {sinks}, sampled rows")
 
 
-def test_wide_heads_full_grid_batch_items_equal_each_item_alone():
+@pytest.mark.parametrize("D", [128, 256])
+def test_wide_heads_full_grid_batch_items_equal_each_item_alone(D):
     w = WIDE
-    p = gen.make_problem(1795, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], w["D"], w["D"], BF16, 1, sinks=True)
-    import scaled_dot_product_06_amd as sd
-    assert sd.sdpa_plan(*p.shape_args(), 1, False, True, BF16)["splits"] == 2
+    p = gen.make_problem(1795 + D, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], D, D, BF16, 1, sinks=True)
+    _wide_plan_check(p)
     whole = from_device(run_gpu(p), BF16)
     for b in range(w["B"]):
-        pb = gen.Problem(1, w["Hq"], w["Hkv"], w["Lq"], w["Lk"], w["D"], w["D"], BF16, 1, p.scale, p.q[b:b + 1],
+        pb = gen.Problem(1, w["Hq"], w["Hkv"], w["Lq"], w["Lk"], D, D, BF16, 1, p.scale, p.q[b:b + 1],
                          p.k[b:b + 1], p.v[b:b + 1], None, p.sinks)
         alone = from_device(run_gpu(pb), BF16)
         assert np.array_equal(whole[b:b + 1], alone), f"batch item {b} differs"
 
 
-def test_wide_heads_full_grid_window_sampled_rows():
+@pytest.mark.parametrize("D", [128, 256])
+def test_wide_heads_full_grid_window_sampled_rows(D):
     from scaled_dot_product_06_amd import attention
     import torch
     w = WIDE
-    p = gen.make_problem(1790, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], w["D"], w["D"], BF16, 1, sinks=True)
+    p = gen.make_problem(1790 + D, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], D, D, BF16, 1, sinks=True)
+    _wide_plan_check(p)
     q, k, v, _, sinks = device_inputs(p)
     got = from_device(attention(q, k, v, p.scale, 1, None, sinks, window=300), p.dtype)
     torch.cuda.synchronize()
     rows = sample_rows(p, 96, seed=23)
     qq, kk, vv, _, ss = p.widened()
     want = orc.sdpa(qq, kk, vv, p.scale, 1, None, ss, window=300, rows=rows)
-    assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want, "256-wide full grid window 300")
+    assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want, f"{D}-wide full grid window 300")
 
 
 # --- sliding windows (nuvec-core tests/fast.rs, windowed-kernel tests) -------------------------

@@ -50,9 +50,10 @@ PAIRS = [
     # decode split + reduce: 65,537 keys at 256-wide heads (4.3 MB of partials), then 8,193 keys
     (dict(seed=5, B=4, Hq=16, Hkv=2, Lq=1, Lk=65537, D=256, Dv=256, dtype=BF16, mask_kind=0),
      dict(seed=2, B=1, Hq=32, Hkv=4, Lq=1, Lk=8193, D=128, Dv=128, dtype=BF16, mask_kind=1)),
-    # boolean-mask prefill (packed mask bits), then a smaller one
-    (dict(seed=4, B=1, Hq=16, Hkv=2, Lq=1024, Lk=1801, D=128, Dv=128, dtype=F16, mask_kind=2, sinks=True),
-     dict(seed=41, B=1, Hq=8, Hkv=2, Lq=100, Lk=257, D=128, Dv=128, dtype=F16, mask_kind=2, sinks=True)),
+    # boolean-mask prefill on grids the pipelined kernel fills (packed mask bits), then
+    # a smaller one
+    (dict(seed=4, B=1, Hq=64, Hkv=8, Lq=1024, Lk=1801, D=128, Dv=128, dtype=F16, mask_kind=2, sinks=True),
+     dict(seed=41, B=1, Hq=64, Hkv=8, Lq=512, Lk=257, D=128, Dv=128, dtype=F16, mask_kind=2, sinks=True)),
 ]
 
 

@@ -101,13 +101,14 @@ constexpr int kFastRows = 32, kFastBN = 32;
 // lanes that each take 32 keys of every 64-key step, so each SIMD holds two
 // wavefronts. 256-wide 16-bit heads run it on every grid and with every mask (a
 // 32-row tile of these heads leaves room for one wavefront per SIMD);
-// 128-wide heads run it when the pipelined kernel's grid for one batch item
-// would have fewer than kKsplitGrid128 workgroups (the rule ignores the batch
-// size, so a batch item takes the same kernel alone or within a batch).
+// 64- and 128-wide heads run it when the pipelined kernel's whole grid (every
+// batch item) would have fewer than kKsplitSmallGrid workgroups: at one workgroup
+// per compute unit or less, the twice as many 16-row workgroups and the halved key
+// chain of each win; on fuller grids the 32-row pipelined tiles do.
 constexpr int kKsplitLanes = 2, kKsplitRows = 16, kKsplitBN = 32;
-constexpr int kKsplitGrid128 = 256;
+constexpr int kKsplitSmallGrid = 256;
 constexpr bool prefill_can_ksplit(int elem, int D, int Dv) {
-  return elem != kF32 && D == Dv && (D == 128 || D == 256);
+  return elem != kF32 && D == Dv && (D == 64 || D == 128 || D == 256);
 }
 // Generic kernel: 32x32 MFMA tiles (32 query rows per wavefront) up to
 // 128-wide heads; 16x16 tiles above, where a 32-row output accumulator would

@@ -1,5 +1,5 @@
 // Prefill for 16-bit inputs with 256-wide heads (every grid, every mask kind)
-// and 128-wide heads on grids too small for the pipelined 32-row kernel: the
+// and 64- and 128-wide heads on grids too small for the pipelined 32-row kernel: the
 // tiled online-softmax walk of lattice-inference
 // "src/attention/flash.rs" (run_tiled_attention_head), with the bottom-right
 // causal alignment of nuvec-core "tests/fast.rs"
@@ -62,19 +62,26 @@ struct KsplitCfg {
   static constexpr int NSB = SUB / MF;         // 16-key blocks per wavefront step
   static constexpr int NDB = D / MF;           // 16-column output blocks
   static constexpr int NPK = SUB * MF / 64 / 2;  // packed weight pairs per lane
-  static_assert(D == 128 || D == 256, "the key-split prefill serves 128- and 256-wide heads");
+  static_assert(D == 64 || D == 128 || D == 256, "the key-split prefill serves 64-, 128- and 256-wide heads");
   static_assert(LOADS % NW == 0, "loads divide among wavefronts");
   static_assert(NSB == 2 && NPK == 4, "two 16-key blocks make one 32-key PV step");
 };
 
 // K: the chunk of row r sits at slot chunk ^ (r % CPR) (CPR = 32 chunks per row at
 // 256-wide heads, 16 at 128); the 16 rows one read touches (r0 .. r0+15, r0 a
-// multiple of 16) land on 16 different slots.
-template <int D> __device__ __forceinline__ int ks_swz_k(int row) { return row % KsplitCfg<D>::CPR; }
+// multiple of 16) land on 16 different slots. At 64-wide heads two 128-byte rows
+// share a 256-byte line of banks, so the XOR is (r / 2) % 8: the 16 rows take the
+// two halves of the line times 8 different slots.
+template <int D> __device__ __forceinline__ int ks_swz_k(int row) {
+  return D == 64 ? (row >> 1) % 8 : row % KsplitCfg<D>::CPR;
+}
 // V: pairs of chunks move together (XOR by an even number), by 2 * (r % 8); each
 // half-wavefront of a transposed read covers 8 consecutive rows, whose 8
-// different pairs fill one 256-byte line of banks.
-template <int D> __device__ __forceinline__ int ks_swz_v(int row) { return 2 * (row % 8); }
+// different pairs fill one 256-byte line of banks. At 64-wide heads (four pairs
+// per row, two rows per line) by 2 * ((r / 2) % 4): 2 row halves times 4 pairs.
+template <int D> __device__ __forceinline__ int ks_swz_v(int row) {
+  return D == 64 ? 2 * ((row >> 1) % 4) : 2 * (row % 8);
+}
 
 // bytes between rows of the boolean-mask ring (64 keys plus padding)
 constexpr int kMaskRow = 80;
@@ -332,12 +339,14 @@ prefill_ksplit_kernel(FwdArgs a) {
   // K operand of key block nb, k-step c: row SUB*kl + 16 nb + col, chunk 4c + kg.
   // With the row's XOR (16 nb + col), the four k-steps c and c + 4 and the two
   // blocks differ by constants, so four lane offsets serve all sixteen reads.
-  uint32_t kb4[4];
+  constexpr int KC = C::NQC < 4 ? C::NQC : 4;   // k-steps per group of K operand reads
+  uint32_t kb4[KC];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) kb4[c] = (SUB * kl + col) * C::RB + (((4 * c + kg) ^ col) * 16);
-  // (at 128-wide heads the XOR of row 16 nb + col is col's alone: blocks differ by 16 rows)
+  for (int c = 0; c < KC; ++c) kb4[c] = (SUB * kl + col) * C::RB + (((4 * c + kg) ^ ks_swz_k<D>(SUB * kl + col)) * 16);
+  // (at 64- and 128-wide heads the XOR of row 16 nb + col does not depend on nb:
+  // the blocks differ by 16 rows)
   auto k_off = [&](int c, int nb) -> uint32_t {
-    if constexpr (D == 128) return kb4[c] + nb * (16 * C::RB);
+    if constexpr (D <= 128) return kb4[c] + nb * (16 * C::RB);
     return c < 4 ? kb4[c] + nb * (16 * C::RB + 256) : kb4[c - 4] + 256 + nb * (16 * C::RB - 256);
   };
   // V^T operand of output block db: transposed reads of keys 4g..4g+3 and
@@ -345,12 +354,15 @@ prefill_ksplit_kernel(FwdArgs a) {
   // SUB*kl + l/4 (+16), columns 16 db + 4 (l % 4) .. +3. The V XOR pairs chunk
   // 2 db with row % 8, so blocks db and db + 8 (256-wide heads) differ by 256 bytes.
   const int vr = lane >> 2;
-  uint32_t vb8[8];
+  constexpr int VB = C::NDB < 8 ? C::NDB : 8;   // output blocks per group of V^T reads
+  uint32_t vb8[VB];
+  const int vsw = ks_swz_v<D>(SUB * kl + vr) / 2;   // the row's pair XOR (the same 16 rows on)
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
-    vb8[db] = (SUB * kl + vr) * C::RB + ((2 * (db ^ (vr % 8)) + ((lane >> 1) & 1)) * 16) + (lane & 1) * 8;
-  auto v_off = [&](int db) -> uint32_t { return db < 8 ? vb8[db] : vb8[db - 8] + 256; };
-  static_assert(C::NQC % 4 == 0 && C::NDB % 8 == 0, "LDS operands come in groups of four k-steps and eight blocks");
+  for (int db = 0; db < VB; ++db)
+    vb8[db] = (SUB * kl + vr) * C::RB + ((2 * (db ^ vsw) + ((lane >> 1) & 1)) * 16) + (lane & 1) * 8;
+  auto v_off = [&](int db) -> uint32_t { return db < VB ? vb8[db] : vb8[db - VB] + 256; };
+  static_assert((C::NQC <= 4 || C::NQC % 4 == 0) && (C::NDB <= 8 || C::NDB % 8 == 0),
+                "LDS operands come in groups of up to four k-steps and eight blocks");
 
   // LDS operands go through two register buffers of eight 16-byte groups: the
   // reads of one group are issued before the MFMAs of the previous one, and an
@@ -359,19 +371,19 @@ prefill_ksplit_kernel(FwdArgs a) {
   // behind a group of MFMAs instead of in front of each one.)
   auto read_k = [&](const uint8_t* Ks, int c0, u32x4 (&buf)[8]) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < KC; ++c)
 #pragma unroll
       for (int nb = 0; nb < C::NSB; ++nb) buf[c * 2 + nb] = *reinterpret_cast<const u32x4*>(Ks + k_off(c0 + c, nb));
   };
   auto mma_qk = [&](int c0, const u32x4 (&buf)[8], acc_t (&s)[C::NSB]) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < KC; ++c)
 #pragma unroll
       for (int nb = 0; nb < C::NSB; ++nb) s[nb] = mma16<E, MF>(buf[c * 2 + nb], qop[c0 + c], s[nb]);
   };
   auto read_v = [&](const uint8_t* Vs, int db0, u32x4 (&buf)[8]) {
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
+    for (int d = 0; d < VB; ++d) {
       const u32x2 ra = lds_read_tr16((const uint16_t*)(Vs + v_off(db0 + d)));
       const u32x2 rb = lds_read_tr16((const uint16_t*)(Vs + v_off(db0 + d) + 16 * C::RB));
       buf[d] = u32x4{ra[0], ra[1], rb[0], rb[1]};
@@ -446,7 +458,7 @@ prefill_ksplit_kernel(FwdArgs a) {
   auto mma_pv = [&](int db0, const u32x4 (&buf)[8], const uint32_t (&pk)[C::NPK]) {
     const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
 #pragma unroll
-    for (int d = 0; d < 8; ++d) o[db0 + d] = mma16<E, MF>(buf[d], pb, o[db0 + d]);
+    for (int d = 0; d < VB; ++d) o[db0 + d] = mma16<E, MF>(buf[d], pb, o[db0 + d]);
   };
 
   acc_t sa[C::NSB], sb[C::NSB];
@@ -513,7 +525,7 @@ prefill_ksplit_kernel(FwdArgs a) {
       mma_pv(8, bb, pk);
       fence();
     } else {
-      // 128-wide heads: one group of K operands and one of V
+      // 64- and 128-wide heads: one group of K operands and one of V
       read_v(Vcur, 0, bb);
       score_init(snext, mb);
       fence();

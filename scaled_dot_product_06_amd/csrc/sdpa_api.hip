@@ -269,15 +269,15 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
     *plan = p;
     return SDPA_OK;
   }
-  // the key-split kernel at 256-wide 16-bit heads and at 128-wide ones on small
-  // grids, the pipelined kernel (32-row tiles) where it applies, else the
+  // the key-split kernel at 256-wide 16-bit heads and at 64/128-wide ones on
+  // small grids, the pipelined kernel (32-row tiles) where it applies, else the
   // generic kernel's geometry
   const int nw = prefill_waves(dtype, (int)D, (int)Dv);
   const int64_t heads = gcd64(group, nw);
   bool kspl = false;
   if (prefill_can_ksplit(dtype, (int)D, (int)Dv)) {
     const int64_t fbm = (nw / heads) * kFastRows;   // a pipelined workgroup's query rows per head
-    kspl = D == 256 || (Hq / heads) * ((Lq + fbm - 1) / fbm) < kKsplitGrid128;
+    kspl = D == 256 || (B * Hq / heads) * ((Lq + fbm - 1) / fbm) < kKsplitSmallGrid;
   }
   const bool fast = !kspl && prefill_can_fast(dtype, (int)D, (int)Dv, mask_kind);
   if (kspl) {

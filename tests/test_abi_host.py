@@ -83,13 +83,14 @@ def test_small_f32_calls_split_keys_within_a_workgroup():
     # the rule looks at one batch item, so the batch keeps the tiles
     q = _plan(B=5, Hq=8, Hkv=8, Lq=128, Lk=128, D=64, Dv=64, mask=1, dtype=0)
     assert (q["rows_per_wave"], q["splits"], q["grid"]) == (16, 4, (320, 1, 1))
-    # large f32 calls keep the 32-row walk; 16-bit calls never take this split (a small
-    # 128-wide bf16 grid takes the key-split kernel's two key lanes of eight waves instead,
-    # 64-wide heads the pipelined kernel)
+    # large f32 calls keep the 32-row walk; 16-bit calls never take this split (small
+    # 64/128-wide 16-bit grids take the key-split kernel's two key lanes of eight waves
+    # instead, large ones the pipelined kernel)
     big = _plan(B=1, Hq=32, Hkv=8, Lq=4096, Lk=4096, D=128, Dv=128, mask=1, dtype=0)
     assert (big["rows_per_wave"], big["splits"]) == (32, 0)
     assert (_plan(dtype=2)["splits"], _plan(dtype=2)["waves"]) == (2, 8)
-    assert _plan(D=64, Dv=64, dtype=2)["splits"] == 0
+    assert _plan(D=64, Dv=64, dtype=2)["splits"] == 2
+    assert _plan(B=1, Hq=64, Hkv=8, Lq=1024, Lk=1024, D=64, Dv=64, dtype=2)["splits"] == 0
     # additive masks keep the generic walk at 16 rows
     add = _plan(B=1, Hq=8, Hkv=8, Lq=128, Lk=128, D=64, Dv=64, mask=3, has_mask=True, dtype=0)
     assert (add["rows_per_wave"], add["splits"]) == (16, 0)
@@ -361,7 +362,7 @@ def test_f32_paged_plans_are_prefill_plans():
         assert p == sd.sdpa_plan(2, 8, 2, Lq, 20 * 16, 128, 128, 1, False, False, 0)
 
 
-def test_key_split_plans_for_wide_heads_and_small_128_wide_grids():
+def test_key_split_plans_for_wide_heads_and_small_64_and_128_wide_grids():
     # 256-wide 16-bit heads take the key-split 16-row kernel whatever the grid (it
     # measured faster than 32-row tiles, one wavefront per SIMD, on full grids too);
     # the batch size never changes the geometry
@@ -381,18 +382,22 @@ def test_key_split_plans_for_wide_heads_and_small_128_wide_grids():
     # 128-wide heads on a small grid: the key-split kernel, which reads the bytes itself
     small128 = sd.sdpa_plan(1, 16, 2, 1024, 1801, 128, 128, 2, True, True, 1)  # 4 x 32 for the pipelined kernel
     assert shape(small128) + (small128["kernels"], small128["scratch_bytes"]) == (16, 32, 2, 8, 1, 0)
-    # the threshold: 256 pipelined workgroups per batch item keep the pipelined kernel
-    assert shape(sd.sdpa_plan(1, 32, 4, 1024, 1024, 128, 128, 1, False, False, 2)) == (32, 32, 0, 4)   # 8 x 32
-    assert shape(sd.sdpa_plan(1, 32, 4, 992, 1024, 128, 128, 1, False, False, 2)) == (16, 32, 2, 8)    # 8 x 31
-    assert shape(sd.sdpa_plan(4, 32, 4, 992, 1024, 128, 128, 1, False, False, 2)) == (16, 32, 2, 8)    # per item
+    # the threshold: a pipelined grid of 256 workgroups (all batch items) keeps the
+    # pipelined kernel, at 64-wide heads as at 128-wide ones
+    for d in (64, 128):
+        assert shape(sd.sdpa_plan(1, 32, 4, 1024, 1024, d, d, 1, False, False, 2)) == (32, 32, 0, 4)   # 8 x 32
+        assert shape(sd.sdpa_plan(1, 32, 4, 992, 1024, d, d, 1, False, False, 2)) == (16, 32, 2, 8)    # 8 x 31
+        assert shape(sd.sdpa_plan(4, 32, 4, 992, 1024, d, d, 1, False, False, 2)) == (32, 32, 0, 4)    # 4 x 8 x 31
+        assert shape(sd.sdpa_plan(2, 32, 4, 480, 1024, d, d, 1, False, False, 2)) == (16, 32, 2, 8)    # 2 x 8 x 15
+        assert shape(sd.sdpa_plan(2, 32, 4, 512, 1024, d, d, 1, False, False, 2)) == (32, 32, 0, 4)    # 2 x 8 x 16
     batched = sd.sdpa_plan(8, 16, 2, 1024, 1801, 256, 256, 2, True, True, 1)  # the same per batch item
     assert shape(batched) + (batched["grid"][0],) == (16, 32, 2, 8, 8 * 4 * 64)
     # one or two heads per workgroup: 64 or 32 rows of a head per key lane
     assert sd.sdpa_plan(1, 4, 4, 100, 300, 256, 256, 0, False, False, 2)["grid"][0] == 4 * 2
     assert sd.sdpa_plan(1, 4, 2, 100, 300, 256, 256, 0, False, False, 2)["grid"][0] == 2 * 4
-    # additive masks take the key-split kernel at 256-wide heads too, and at 128-wide
-    # heads on small grids; other calls keep the generic kernel (the pipelined kernel
-    # reads no additive mask)
+    # additive masks take the key-split kernel at 256-wide heads too, and at 64- and
+    # 128-wide heads on small grids; other calls keep the generic kernel (the pipelined
+    # kernel reads no additive mask)
     add = sd.sdpa_plan(1, 64, 8, 1024, 1801, 256, 256, 3, True, True, 1)
     assert shape(add) + (add["kernels"], add["scratch_bytes"]) == (16, 32, 2, 8, 1, 0)
     big_add = sd.sdpa_plan(1, 32, 4, 1040, 1297, 256, 256, 3, True, False, 2)

@@ -1,5 +1,5 @@
-"""GPU parity of the key-split prefill (every 256-wide 16-bit call, and 128-wide
-calls on small grids) against the CPU float64 oracle, every output element.
+"""GPU parity of the key-split prefill (every 256-wide 16-bit call, and 64- and
+128-wide calls on small grids) against the CPU float64 oracle, every output element.
 
 The kernel's workgroup holds 16 query rows of up to four heads and splits each
 64-key step between two lanes of wavefronts, which merge at the end. The cases
@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 F16, BF16 = gen.F16, gen.BF16
 DT = {"f16": F16, "bf16": BF16}
-WIDTHS = [128, 256]   # head sizes (D = Dv) the key-split kernel is built for
+WIDTHS = [64, 128, 256]   # head sizes (D = Dv) the key-split kernel is built for
 
 
 def _plan(p, window=0):
@@ -111,7 +111,7 @@ def test_batch_items_equal_each_item_alone(D):
         assert np.array_equal(whole[b:b + 1], alone), f"batch item {b} differs"
 
 
-# --- additive masks (the key-split path: every 256-wide call, 128-wide ones on small grids) ---
+# --- additive masks (the key-split path: every 256-wide call, 64/128-wide ones on small grids)
 
 def _additive_call(p, add, sinks, offset=0):
     """Run with `add` (any broadcast shape) as an additive mask, `offset` elements into its buffer."""

@@ -128,15 +128,15 @@ def test_prefill_bool_mask_word_edges(D, Lk):
             _full_check(p, f"bool mask {name} D={D} Lk={Lk}")
 
 
-# --- full grids at 128- and 256-wide heads -----------------------------------------------------
+# --- full grids at 64-, 128- and 256-wide heads ------------------------------------------------
 # Two batch items of 32 heads, ragged on both axes: 1040 query rows over 1297 keys. At
-# 256-wide heads the key-split kernel (520 workgroups of 16-row blocks); at 128-wide heads
-# the pipelined kernel, whose grid here (264 workgroups of 32-row blocks per batch item)
-# is large enough that the plan keeps it (the small-grid tests of 128-wide heads run the
-# key-split kernel).
+# 256-wide heads the key-split kernel (520 workgroups of 16-row blocks); at 64- and
+# 128-wide heads the pipelined kernel, whose grid here (264 workgroups of 32-row blocks per
+# batch item) is large enough that the plan keeps it (the small-grid tests of those
+# widths run the key-split kernel).
 
 WIDE = dict(B=2, Hq=32, Hkv=4, Lq=1040, Lk=1297)
-WIDE_KERNEL = {128: 0, 256: 2}   # the plan's key lanes: 0 = pipelined kernel, 2 = key-split
+WIDE_KERNEL = {64: 0, 128: 0, 256: 2}   # the plan's key lanes: 0 = pipelined kernel, 2 = key-split
 
 
 def _wide_plan_check(p):
@@ -145,7 +145,7 @@ def _wide_plan_check(p):
     assert plan["splits"] == WIDE_KERNEL[p.D], plan
 
 
-@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("mask_kind,sinks", [(0, False), (1, False), (1, True), (2, True)])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_wide_heads_full_grid_sampled_rows(mask_kind, sinks, dtype, D):
@@ -162,7 +162,7 @@ def test_wide_heads_full_grid_sampled_rows(mask_kind, sinks, dtype, D):
                   f"{D}-wide full grid mask {mask_kind} sinks {sinks}, sampled rows")
 
 
-@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_wide_heads_full_grid_batch_items_equal_each_item_alone(D):
     w = WIDE
     p = gen.make_problem(1795 + D, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], D, D, BF16, 1, sinks=True)
@@ -175,7 +175,7 @@ def test_wide_heads_full_grid_batch_items_equal_each_item_alone(D):
         assert np.array_equal(whole[b:b + 1], alone), f"batch item {b} differs"
 
 
-@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_wide_heads_full_grid_window_sampled_rows(D):
     from scaled_dot_product_06_amd import attention
     import torch

@@ -138,7 +138,8 @@ CASES = [
     (0, 1, 8, 2, 77, 150, 256, 256, F16),          # key-split prefill (256-wide heads)
     (2, 1, 16, 2, 100, 300, 256, 256, BF16),       # key-split prefill reading the mask bytes: one kernel
     (0, 1, 8, 2, 77, 150, 192, 192, F16),          # generic prefill
-    (2, 1, 8, 2, 200, 333, 64, 64, F16),           # mask packing + prefill
+    (2, 1, 8, 2, 200, 333, 64, 64, F16),           # key-split prefill (64-wide heads, small grid), byte mask
+    (2, 1, 64, 8, 512, 333, 64, 64, F16),          # mask packing + pipelined prefill (64-wide heads)
     (2, 1, 4, 2, 70, 90, 128, 128, F32),           # f32 prefill, byte mask
     (3, 1, 64, 8, 512, 257, 128, 128, BF16),       # additive mask: generic prefill (a large grid)
     (3, 1, 8, 2, 100, 257, 128, 128, BF16),        # additive mask: key-split prefill (small grid)

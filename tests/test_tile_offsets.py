@@ -136,18 +136,18 @@ def test_v_operand_offsets_fold_the_key_offset(D):
 
 
 # --- the key-split prefill: 64-key steps loaded by eight wavefronts ---------------------------
-# (128- and 256-wide heads; 16 query rows per (head, row block) slot, so a workgroup's query
-# block is 16, 32 or 64 rows for four, two or one heads per workgroup)
+# (64-, 128- and 256-wide heads; 16 query rows per (head, row block) slot, so a workgroup's
+# query block is 16, 32 or 64 rows for four, two or one heads per workgroup)
 
 def ks_swz_k(D, row):
-    return row % (D // 8)
+    return (row >> 1) % 8 if D == 64 else row % (D // 8)
 
 
 def ks_swz_v(D, row):
-    return 2 * (row % 8)
+    return 2 * ((row >> 1) % 4) if D == 64 else 2 * (row % 8)
 
 
-@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("heads", [1, 2, 4])
 @pytest.mark.parametrize("mask_kind,window", [(0, 0), (1, 0), (1, 7), (1, 300), (2, 0)])
 def test_key_split_steps_read_inside_the_keys(mask_kind, window, heads, D):
@@ -172,7 +172,7 @@ def test_key_split_steps_read_inside_the_keys(mask_kind, window, heads, D):
                     check_tile(D, Lk, k0, rs, ks_swz_v, KBN, KNW)
 
 
-@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_key_split_lds_operand_offsets(D):
     # K operand reads fold four lane offsets plus constants; V^T transposed reads fold
     # eight lane offsets plus 256 bytes for the upper eight output blocks (256-wide
@@ -182,10 +182,10 @@ def test_key_split_lds_operand_offsets(D):
     for kl in (0, 1):
         for lane in range(64):
             col, kg = lane % 16, lane // 16
-            kb4 = [(SUB * kl + col) * RB + (((4 * c + kg) ^ col) * 16) for c in range(4)]
+            kb4 = [(SUB * kl + col) * RB + (((4 * c + kg) ^ ks_swz_k(D, SUB * kl + col)) * 16) for c in range(4)]
             for c in range(D // 32):
                 for nb in range(2):
-                    if D == 128:
+                    if D <= 128:
                         folded = kb4[c] + nb * (16 * RB)
                     else:
                         folded = (kb4[c] + nb * (16 * RB + 256) if c < 4
@@ -195,7 +195,8 @@ def test_key_split_lds_operand_offsets(D):
                     assert chunk < D // 8
                     assert folded == row * RB + chunk * 16, (kl, lane, c, nb)
             vr = lane >> 2
-            vb8 = [(SUB * kl + vr) * RB + ((2 * (d ^ (vr % 8)) + ((lane >> 1) & 1)) * 16) + (lane & 1) * 8
+            vsw = ks_swz_v(D, SUB * kl + vr) // 2
+            vb8 = [(SUB * kl + vr) * RB + ((2 * (d ^ vsw) + ((lane >> 1) & 1)) * 16) + (lane & 1) * 8
                    for d in range(8)]
             for db in range(D // 16):
                 folded = vb8[db % 8] + (256 if db >= 8 else 0)

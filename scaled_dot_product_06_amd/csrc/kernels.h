@@ -90,11 +90,12 @@ constexpr int kDecodeBN = 32;       // keys per decode tile
 // value columns per decode-reduce workgroup: 32 when they divide Dv, else 16
 constexpr int reduce_cols(int DV) { return DV % 32 == 0 ? 32 : 16; }
 constexpr int head_max(int D, int Dv) { return D > Dv ? D : Dv; }
-// The 64- and 128-wide 16-bit prefill shapes run the pipelined direct-load
-// kernel (32-row tiles, 32-key steps), except with an additive mask (the
-// generic kernel reads it).
+// The 16-bit prefill shapes with heads up to 128 wide, (64,64), (80,80), (96,96),
+// (128,128) and (96,64), run the pipelined direct-load kernel (32-row tiles,
+// 32-key steps), except with an additive mask (the generic kernel reads it).
 constexpr bool prefill_can_fast(int elem, int D, int Dv, int mask_kind) {
-  return elem != kF32 && D == Dv && (D == 64 || D == 128) && mask_kind != kMaskAdditive;
+  return elem != kF32 && mask_kind != kMaskAdditive &&
+         ((D == Dv && (D == 64 || D == 80 || D == 96 || D == 128)) || (D == 96 && Dv == 64));
 }
 constexpr int kFastRows = 32, kFastBN = 32;
 // The key-split kernel: 16-row tiles, and the workgroup's wavefronts in two key

@@ -39,14 +39,14 @@ static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_
     }
     if constexpr (prefill_can_fast(elem, D, DV, kMaskNone)) {
       // the pipelined kernel (32-row tiles)
-      using C = FastCfg<D>;
+      using C = FastCfg<D, DV>;
       static_assert(C::MF == kFastRows && C::ROWS == kFastRows && C::BN == kFastBN && C::NW == kPrefillWaves,
                     "planner geometry must match the kernel");
       if (s.mf != C::MF || s.block_n != C::BN) return hipErrorInvalidConfiguration;
       if (a.mask_kind == kMaskBool)
-        hipLaunchKernelGGL((prefill_fast_kernel<E, D, true>), grid, dim3(C::NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((prefill_fast_kernel<E, D, DV, true>), grid, dim3(C::NW * 64), 0, stream, a);
       else
-        hipLaunchKernelGGL((prefill_fast_kernel<E, D, false>), grid, dim3(C::NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((prefill_fast_kernel<E, D, DV, false>), grid, dim3(C::NW * 64), 0, stream, a);
       return hipGetLastError();
     } else {
       hipLaunchKernelGGL((prefill_kernel<E, MF, D, DV, BN, kPrefillWaves, false>), grid, dim3(kPrefillWaves * 64), 0,

@@ -1,4 +1,5 @@
-// Prefill for 16-bit inputs with D = Dv in {64, 128}: the tiled online-softmax
+// Prefill for 16-bit inputs with (D, Dv) in {(64, 64), (80, 80), (96, 96), (128, 128),
+// (96, 64)}: the tiled online-softmax
 // walk of lattice-inference "src/attention/flash.rs" (run_tiled_attention_head)
 // with the bottom-right causal alignment of nuvec-core "tests/fast.rs"
 // (attention_fallback_matches_a_direct_formula), laid out for gfx950:
@@ -25,7 +26,12 @@
 //  * each LDS row holds its 16-byte chunks permuted by an XOR of the row index
 //    (different for K and V), so the K-operand reads (16 consecutive rows, one
 //    chunk each) and the V transpose reads (8 consecutive rows, four chunks
-//    each) touch every bank equally.
+//    each) touch every bank equally;
+//  * 80- and 96-wide rows sit in the 128-wide LDS layout: the QK^T k-steps and
+//    the PV output blocks cover the real columns (an 80-wide output's third
+//    32-column block computes 16 spare columns that are never stored), and the
+//    lanes whose layout slot falls past a row's real chunks load a real chunk
+//    again, so every LDS byte an operand read touches holds input data.
 #pragma once
 
 #include "attn_device.h"
@@ -33,7 +39,7 @@
 
 namespace sdpa {
 
-template <int D>
+template <int D, int DV>
 struct FastCfg {
   static constexpr int MF = 32, KW = 16, ACC = 16, KG = 2;
   static constexpr int QB = 1;                  // 32-row query blocks per wavefront
@@ -41,8 +47,10 @@ struct FastCfg {
   static constexpr int BN = 32;                 // keys per tile
   static constexpr int NW = 4;                  // wavefronts per workgroup
   static constexpr int NT = NW * 64;
-  static constexpr int RB = D * 2;              // bytes per row
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int LW = D <= 64 && DV <= 64 ? 64 : 128;  // LDS row width (elements)
+  static constexpr int RB = LW * 2;             // bytes per LDS row
+  static constexpr int CPR = LW / 8;            // 16-byte chunks per LDS row
+  static constexpr int KCH = D / 8, VCH = DV / 8;  // real chunks of a K and a V row
   static constexpr int ROWS_PER_KB = 1024 / RB; // rows filled by one direct-load instruction
   static constexpr int TILE_BYTES = BN * RB;    // one K or V tile
   static constexpr int LOADS = TILE_BYTES / 1024;  // direct-load instructions per tile and tensor
@@ -52,22 +60,30 @@ struct FastCfg {
   static constexpr int NQC = D / KW;            // k-steps of QK^T
   static constexpr int NSB = BN / MF;           // 32-key blocks per tile
   static constexpr int NPV = BN / KW;           // k-steps of PV
-  static constexpr int NDB = D / MF;            // 32-column output blocks
+  static constexpr int NDB = (DV + MF - 1) / MF;  // 32-column output blocks
   static constexpr int NPK = NSB * ACC / 2;     // packed weight pairs per query block
   static constexpr int WPE = 3;                 // wavefronts per SIMD the registers allow
   static constexpr int STAGES = 3;              // LDS ring of K/V tiles
-  static_assert(D == 64 || D == 128, "fast prefill covers 64- and 128-wide heads");
+  static_assert((D == DV && (D == 64 || D == 80 || D == 96 || D == 128)) || (D == 96 && DV == 64),
+                "the pipelined prefill covers (64,64), (80,80), (96,96), (128,128) and (96,64)");
+  static_assert(D % KW == 0 && DV % 8 == 0, "whole k-steps and 8-column store groups");
   static_assert(LOADS % NW == 0, "loads divide among wavefronts");
 };
 
-// chunk permutations (XOR masks) for the K and V tiles
-template <int D> __device__ __forceinline__ int swz_k(int row) { return row % FastCfg<D>::CPR; }
+// chunk permutations (XOR masks) for the K and V tiles of an LW-wide LDS layout
+template <int LW> __device__ __forceinline__ int swz_k(int row) { return row % (LW / 8); }
 // (V: the row's place among the rows sharing one 256-byte line of banks;
 // rows of 256 bytes or more start on the same bank, so consecutive rows differ)
-template <int D> __device__ __forceinline__ int swz_v(int row) {
-  constexpr int RPL = FastCfg<D>::RB >= 256 ? 1 : 256 / FastCfg<D>::RB;  // rows per 256-byte line
-  constexpr int NX = FastCfg<D>::CPR / 4 < 4 ? FastCfg<D>::CPR / 4 : 4;
+template <int LW> __device__ __forceinline__ int swz_v(int row) {
+  constexpr int RPL = LW * 2 >= 256 ? 1 : 256 / (LW * 2);  // rows per 256-byte line
+  constexpr int NX = LW / 32 < 4 ? LW / 32 : 4;
   return 4 * ((row / RPL) % NX);
+}
+// the chunk a lane loads into layout slot `slot` of a row with `real` chunks:
+// slots past the real ones take a real chunk again
+template <int CPR, int REAL> __device__ __forceinline__ int fast_src_chunk(int slot) {
+  if constexpr (REAL < CPR) return slot < REAL ? slot : slot - REAL;
+  return slot;
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations
@@ -78,10 +94,10 @@ constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 
 // BOOLMASK: the call has a boolean mask (packed into bits); the other
 // instantiation serves causal and unmasked calls without the mask-word code.
-template <class E, int D, bool BOOLMASK>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FastCfg<D>::WPE, FastCfg<D>::WPE)))
+template <class E, int D, int DV, bool BOOLMASK>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FastCfg<D, DV>::WPE, FastCfg<D, DV>::WPE)))
 prefill_fast_kernel(FwdArgs a) {
-  using C = FastCfg<D>;
+  using C = FastCfg<D, DV>;
   constexpr int MF = C::MF, ACC = C::ACC, BN = C::BN, QB = C::QB;
   using acc_t = f32x16;
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::STAGE_BYTES];
@@ -182,8 +198,8 @@ prefill_fast_kernel(FwdArgs a) {
   for (int it = 0; it < C::LOADS_PER_WAVE; ++it) {
     const int row = (w + C::NW * it) * C::ROWS_PER_KB + ld_row;
     ldrow[it] = row;
-    offk[it] = row * krs + (ld_slot ^ swz_k<D>(row)) * 16;
-    offv[it] = row * vrs + (ld_slot ^ swz_v<D>(row)) * 16;
+    offk[it] = row * krs + fast_src_chunk<C::CPR, C::KCH>(ld_slot ^ swz_k<C::LW>(row)) * 16;
+    offv[it] = row * vrs + fast_src_chunk<C::CPR, C::VCH>(ld_slot ^ swz_v<C::LW>(row)) * 16;
   }
   auto issue_tile = [&](int k0, uint8_t* sbase) {
     const uint8_t* kt = kbase + (size_t)k0 * krs;
@@ -225,7 +241,7 @@ prefill_fast_kernel(FwdArgs a) {
 #pragma unroll
     for (int nb = 0; nb < C::NSB; ++nb) {
       const int row = nb * MF + col;
-      ko[c][nb] = row * C::RB + (((2 * c + kg) ^ swz_k<D>(row)) * 16);
+      ko[c][nb] = row * C::RB + (((2 * c + kg) ^ swz_k<C::LW>(row)) * 16);
     }
   // V^T operands: the providers of every read sit on key rows vk0 + kofs, with
   // kofs a multiple of 8 fixed per read; the V swizzle depends on the row only
@@ -236,7 +252,7 @@ prefill_fast_kernel(FwdArgs a) {
   uint32_t vb[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
-    vb[db] = C::TILE_BYTES + vk0 * C::RB + tr_half + (((db * 4 + tr_chunk) ^ swz_v<D>(vk0)) * 16);
+    vb[db] = C::TILE_BYTES + vk0 * C::RB + tr_half + (((db * 4 + tr_chunk) ^ swz_v<C::LW>(vk0)) * 16);
 
   // S^T = K Q^T for one tile into s (zeroed here)
   auto qk = [&](const uint8_t* Ks, acc_t (&s)[QB][C::NSB]) {
@@ -419,11 +435,12 @@ prefill_fast_kernel(FwdArgs a) {
     if (has_sink) lt += fast_exp2(sink2 - m[r]);
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     if (iq[r] >= a.Lq) continue;
-    uint16_t* op = (uint16_t*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq[r]) * D;
+    uint16_t* op = (uint16_t*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq[r]) * DV;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < ACC / 4; ++g4) {
+        if (db * MF + g4 * 4 * C::KG >= DV) continue;   // spare columns of the last block
         const int dv = db * MF + g4 * 4 * C::KG + kg * 4;
         const u32x2 st = {pack2<E>(o[r][db][g4 * 4 + 0] * inv, o[r][db][g4 * 4 + 1] * inv),
                           pack2<E>(o[r][db][g4 * 4 + 2] * inv, o[r][db][g4 * 4 + 3] * inv)};

@@ -53,6 +53,7 @@ CASES = [
     (1, 1, 64, 8, 512, 300, 128, BF16),     # pipelined prefill (a grid it fills: 256 workgroups)
     (2, 1, 64, 8, 512, 257, 128, F16),      # mask packing + pipelined prefill (two kernels, scratch)
     (1, 2, 8, 2, 300, 300, 128, BF16),      # key-split prefill (128-wide heads, small grid)
+    (2, 1, 8, 2, 300, 300, 64, F16),        # key-split prefill (64-wide heads, small grid), mask bytes
     (2, 1, 16, 2, 100, 300, 256, F16),      # key-split prefill reading the mask bytes
     (0, 1, 8, 2, 77, 150, 192, BF16),       # generic prefill
     (1, 1, 4, 2, 40, 70, 64, F32),          # f32 prefill

@@ -11,10 +11,11 @@ again here independently of the C planner:
     and Dv floats per (batch, kv head, split, packed row) of scratch;
   * otherwise "prefill" on one of four kernels: the key-split kernel for
     16-bit 256-wide heads and for 16-bit 64/128-wide heads whose pipelined
-    grid (all batch items) is under 256 workgroups, the pipelined kernel for other
-    16-bit 64/128-wide calls without an additive mask, the f32 key-split kernel for f32 calls whose
+    grid (all batch items) is under 256 workgroups; the pipelined kernel for
+    other 16-bit calls at (64,64), (80,80), (96,96), (128,128) or (96,64)
+    without an additive mask; the f32 key-split kernel for f32 calls whose
     32-row grid for one batch item is under 256 workgroups (no additive
-    mask), else the generic kernel; 16-bit boolean masks outside the
+    mask); else the generic kernel. 16-bit boolean masks outside the
     key-split kernel are packed into Lq x ceil(Lk/32) words first.
 """
 import math
@@ -62,7 +63,7 @@ def expected_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, dtype, window=0):
         bm = (WAVES // heads) * 16
         return dict(base, route="prefill", kernels=1, rows_per_wave=16, waves=2 * WAVES, block_n=32,
                     heads_per_group=heads, splits=2, grid=(B * Hq // heads * -(-Lq // bm), 1, 1))
-    pipelined = dtype != F32 and D == Dv and D in (64, 128) and mask_kind != 3
+    pipelined = dtype != F32 and (D, Dv) in ((64, 64), (80, 80), (96, 96), (128, 128), (96, 64)) and mask_kind != 3
     rows = 32 if pipelined or hmax <= 128 else 16
     if dtype == F32 and rows == 32 and (Hq // heads) * -(-Lq // ((WAVES // heads) * 32)) < 256:
         rows = 16

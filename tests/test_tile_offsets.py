@@ -9,6 +9,10 @@ offset. This replays that arithmetic, modulo 2^32 as the kernel does it, for
 every tile a workgroup issues, over ragged key counts, causal, windowed and
 unmasked calls and strided rows, and checks that every load reads a key row in
 [0, Lk) and a chunk inside the row, i.e. the unsigned offset never wraps.
+
+80- and 96-wide rows (and the 64-wide V rows of the (96, 64) pair) sit in the
+pipelined kernel's 128-wide LDS layout; a lane whose layout slot falls past the
+row's real chunks loads a real chunk again, which the replay checks too.
 """
 import itertools
 
@@ -18,20 +22,33 @@ BN, NW, ROWS = 32, 4, 32
 U32 = 1 << 32
 
 
-def cfg(D):
-    rb = 2 * D
-    return dict(RB=rb, CPR=D // 8, ROWS_PER_KB=1024 // rb, LPW=(BN * rb // 1024) // NW)
+FAST_PAIRS = [(64, 64), (80, 80), (96, 96), (128, 128), (96, 64)]   # the pipelined kernel's head pairs
 
 
-def swz_k(D, row):
-    return row % (D // 8)
+def layout(D, Dv):
+    """LDS row width (elements) of the pipelined kernel for a head pair."""
+    return 64 if D <= 64 and Dv <= 64 else 128
 
 
-def swz_v(D, row):
-    c = cfg(D)
+def cfg(LW):
+    rb = 2 * LW
+    return dict(RB=rb, CPR=LW // 8, ROWS_PER_KB=1024 // rb)
+
+
+def swz_k(LW, row):
+    return row % (LW // 8)
+
+
+def swz_v(LW, row):
+    c = cfg(LW)
     rpl = 1 if c["RB"] >= 256 else 256 // c["RB"]
     nx = min(c["CPR"] // 4, 4)
     return 4 * ((row // rpl) % nx)
+
+
+def src_chunk(slot, real):
+    """The chunk a lane loads into layout slot `slot` of a row with `real` chunks."""
+    return slot if slot < real else slot - real
 
 
 def issued_tiles(Lq, Lk, qb, mask_kind, window, heads=4):
@@ -51,13 +68,17 @@ def issued_tiles(Lq, Lk, qb, mask_kind, window, heads=4):
     return [(tb + t) * BN for t in range(ntiles)]
 
 
-def check_tile(D, Lk, k0, rs, swz, BN=BN, NW=NW):
-    """Every lane's load of the tile at key k0 with row stride rs bytes."""
-    c = dict(cfg(D), LPW=(BN * 2 * D // 1024) // NW)
-    for w, it, lane in itertools.product(range(NW), range(c["LPW"]), range(64)):
+def check_tile(LW, Lk, k0, rs, swz, BN=BN, NW=NW, real=None):
+    """Every lane's load of the tile at key k0 with row stride rs bytes, in an LDS
+    layout of LW-wide rows holding `real` 16-byte chunks of each row (all of them
+    by default)."""
+    c = cfg(LW)
+    real = c["CPR"] if real is None else real
+    lpw = (BN * c["RB"] // 1024) // NW
+    for w, it, lane in itertools.product(range(NW), range(lpw), range(64)):
         row = (w + NW * it) * c["ROWS_PER_KB"] + lane // c["CPR"]
         slot = lane % c["CPR"]
-        chunk = (slot ^ swz(D, row)) * 16
+        chunk = src_chunk(slot ^ swz(LW, row), real) * 16
         off = (row * rs + chunk) % U32
         if k0 + BN > Lk:
             over = max(k0 + row - (Lk - 1), 0)
@@ -65,10 +86,10 @@ def check_tile(D, Lk, k0, rs, swz, BN=BN, NW=NW):
         else:
             over = 0
         exact = (row - over) * rs + chunk          # what the offset must be, as a signed value
-        assert off == exact, (D, Lk, k0, rs, row, over)
+        assert off == exact, (LW, Lk, k0, rs, row, over)
         key = k0 + row - over
-        assert 0 <= key <= Lk - 1, (D, Lk, k0, row, key)
-        assert 0 <= chunk < c["RB"]
+        assert 0 <= key <= Lk - 1, (LW, Lk, k0, row, key)
+        assert 0 <= chunk < 16 * real
 
 
 CALLS = [(1, 1), (5, 31), (40, 32), (40, 33), (97, 700), (130, 130), (333, 1297), (64, 96), (1040, 1297),
@@ -76,11 +97,11 @@ CALLS = [(1, 1), (5, 31), (40, 32), (40, 33), (97, 700), (130, 130), (333, 1297)
 
 
 @pytest.mark.parametrize("heads", [1, 4])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D,Dv", FAST_PAIRS)
 @pytest.mark.parametrize("mask_kind,window", [(0, 0), (1, 0), (1, 7), (1, 300), (2, 0)])
-def test_every_issued_tile_reads_inside_the_keys(D, mask_kind, window, heads):
+def test_every_issued_tile_reads_inside_the_keys(D, Dv, mask_kind, window, heads):
     # heads: query heads sharing a workgroup (4 under grouped queries; 1 gives 128-row blocks)
-    strides = [2 * D, 2 * D * 3 + 16 * 5, (1 << 26) - 16]   # contiguous, odd, the largest allowed
+    LW = layout(D, Dv)
     for Lq, Lk in CALLS:
         nqb = -(-Lq // (ROWS * NW // heads))
         for qb in range(nqb):
@@ -89,9 +110,11 @@ def test_every_issued_tile_reads_inside_the_keys(D, mask_kind, window, heads):
                 assert k0 <= Lk - 1, "a tile starts past the last key"
             # the ragged last tile is the one that pulls rows back
             for k0 in [t for t in tiles if t + BN > Lk] + tiles[:1]:
-                for rs in strides:
-                    check_tile(D, Lk, k0, rs, swz_k)
-                    check_tile(D, Lk, k0, rs, swz_v)
+                # K and V rows: contiguous, odd and the largest allowed strides
+                for rs in [2 * D, 2 * D * 3 + 16 * 5, (1 << 26) - 16]:
+                    check_tile(LW, Lk, k0, rs, swz_k, real=D // 8)
+                for rs in [2 * Dv, 2 * Dv * 3 + 16 * 5, (1 << 26) - 16]:
+                    check_tile(LW, Lk, k0, rs, swz_v, real=Dv // 8)
 
 
 # --- V^T operand offsets -------------------------------------------------------------------------
@@ -100,8 +123,8 @@ def test_every_issued_tile_reads_inside_the_keys(D, mask_kind, window, heads):
 # block plus a key offset folded into the instruction; this replays that form against
 # the direct per-read formula (row * RB + chunk permuted by the V swizzle of that row).
 
-def swz_v_rows(D, row):
-    return swz_v(D, row)
+def swz_v_rows(LW, row):
+    return swz_v(LW, row)
 
 
 def acc_row32(i, kg):
@@ -109,11 +132,12 @@ def acc_row32(i, kg):
     return (i // 4) * 8 + kg * 4 + i % 4
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_v_operand_offsets_fold_the_key_offset(D):
+@pytest.mark.parametrize("D,Dv", FAST_PAIRS)
+def test_v_operand_offsets_fold_the_key_offset(D, Dv):
     MF, ACC, BN = 32, 16, 32
-    RB, TILE = 2 * D, BN * 2 * D
-    NPV, NDB = BN // 16, D // MF
+    LW = layout(D, Dv)
+    RB, TILE = 2 * LW, BN * 2 * LW
+    NPV, NDB = BN // 16, -(-Dv // MF)
     for lane in range(64):
         kg = lane // MF
         tr_e = (lane & 15) >> 2
@@ -129,10 +153,35 @@ def test_v_operand_offsets_fold_the_key_offset(D):
                 assert key == vk0 + kofs and kofs % 8 == 0
                 for db in range(NDB):
                     ch = db * 4 + tr_chunk
-                    direct = TILE + key * RB + tr_half + ((ch ^ swz_v_rows(D, key)) * 16)
-                    folded = TILE + vk0 * RB + tr_half + (((db * 4 + tr_chunk) ^ swz_v_rows(D, vk0)) * 16) + kofs * RB
+                    direct = TILE + key * RB + tr_half + ((ch ^ swz_v_rows(LW, key)) * 16)
+                    folded = TILE + vk0 * RB + tr_half + (((db * 4 + tr_chunk) ^ swz_v_rows(LW, vk0)) * 16) + kofs * RB
                     assert folded == direct, (D, lane, t8, half, db)
                     assert TILE <= direct < 2 * TILE
+                    # the slot read holds, as loaded, chunk src_chunk(slot ^ swizzle): for
+                    # a real chunk that is the chunk itself (spare chunks feed columns at or
+                    # past Dv, which are not stored)
+                    held = src_chunk((ch ^ swz_v_rows(LW, key)) ^ swz_v_rows(LW, key), Dv // 8)
+                    assert held == ch if ch < Dv // 8 else 8 * ch >= Dv
+
+
+@pytest.mark.parametrize("D,Dv", FAST_PAIRS)
+def test_k_operands_and_query_loads_stay_in_the_real_columns(D, Dv):
+    # QK^T k-steps read chunks 2c + kg of K rows and elements 16c + 8kg .. +7 of
+    # the query row, c < D / 16; output stores cover 8-column groups below Dv
+    KW, MF = 16, 32
+    for c in range(D // KW):
+        for kg in (0, 1):
+            assert 2 * c + kg < D // 8 and 16 * c + 8 * kg + 8 <= D
+    stored = set()
+    for db in range(-(-Dv // MF)):
+        for g4 in range(4):
+            if db * MF + g4 * 8 >= Dv:
+                continue
+            for kg in (0, 1):
+                dv = db * MF + g4 * 8 + kg * 4
+                assert dv + 4 <= Dv
+                stored.update(range(dv, dv + 4))
+    assert stored == set(range(Dv))
 
 
 # --- the key-split prefill: 64-key steps loaded by eight wavefronts ---------------------------

@@ -10,25 +10,26 @@ static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_
   constexpr int elem = std::is_same<E, ElemBF16>::value ? kBF16 : kF16;
   dim3 grid(a.head_blocks * a.nqb, 1, 1);
   if constexpr (prefill_can_ksplit(elem, D, DV)) {
-    using C = KsplitCfg<D>;
+    using C = KsplitCfg<D, DV>;
     static_assert(C::MF == kKsplitRows && C::SUB == kKsplitBN && C::KL == kKsplitLanes && C::NWH == kPrefillWaves,
                   "planner geometry must match the kernel");
-    // the plan chose the key-split kernel (every 256-wide call; 128-wide calls on small grids)
+    // the plan chose the key-split kernel (every call with heads of 192 columns or
+    // more; 64- and 128-wide calls on small grids)
     if (s.ksplit > 1) {
       if (s.ksplit != C::KL || s.mf != C::MF || s.block_n != C::SUB || s.waves != C::NW)
         return hipErrorInvalidConfiguration;
       if (a.mask_kind == kMaskBool)
-        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, kKsBool>), grid, dim3(C::NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, DV, kKsBool>), grid, dim3(C::NW * 64), 0, stream, a);
       else if (a.mask_kind == kMaskAdditive)
-        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, kKsAdd>), grid, dim3(C::NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, DV, kKsAdd>), grid, dim3(C::NW * 64), 0, stream, a);
       else
-        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, kKsPlain>), grid, dim3(C::NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((prefill_ksplit_kernel<E, D, DV, kKsPlain>), grid, dim3(C::NW * 64), 0, stream, a);
       return hipGetLastError();
     }
   }
   if (s.ksplit > 1) return hipErrorInvalidConfiguration;
-  if constexpr (D == 256 && DV == 256) {
-    return hipErrorInvalidConfiguration;   // 256-wide 16-bit heads run the key-split kernel only
+  if constexpr (prefill_can_ksplit(elem, D, DV) && prefill_ksplit_always(D, DV)) {
+    return hipErrorInvalidConfiguration;   // these 16-bit heads run the key-split kernel only
   } else {
     constexpr int MF = prefill_generic_mf(elem, D, DV);
     constexpr int BN = prefill_generic_bn(elem, D, DV);

@@ -1,5 +1,6 @@
-// Prefill for 16-bit inputs with 256-wide heads (every grid, every mask kind)
-// and 64- and 128-wide heads on grids too small for the pipelined 32-row kernel: the
+// Prefill for 16-bit inputs with heads of 192 or 256 columns, (192,192), (192,128)
+// and (256,256) (every grid, every mask kind), and 64- and 128-wide heads on grids
+// too small for the pipelined 32-row kernel: the
 // tiled online-softmax walk of lattice-inference
 // "src/attention/flash.rs" (run_tiled_attention_head), with the bottom-right
 // causal alignment of nuvec-core "tests/fast.rs"
@@ -18,7 +19,9 @@
 //    units;
 //  * K and V steps go from global memory straight into LDS
 //    (global_load_lds_dwordx4) through two double-buffered rings (K and V,
-//    32 KB per step each at 256-wide heads, 128 KB in all; half that at 128):
+//    32 KB per step each at 256-wide heads, 128 KB in all; half that at 128;
+//    192-wide rows sit in 256-wide ones, whose spare slots take a real chunk
+//    of the row again, so every byte an operand read touches holds input data):
 //    the K of step t+2 and the V of step
 //    t+1 are loaded while step t runs, one barrier per step;
 //  * the walk is software-pipelined inside each wavefront: the QK^T MFMAs of
@@ -43,7 +46,7 @@
 
 namespace sdpa {
 
-template <int D>
+template <int D, int DV>
 struct KsplitCfg {
   static constexpr int MF = 16, KW = 32, ACC = 4, KG = 4;
   static constexpr int ROWS = 16;              // query rows per wavefront
@@ -52,35 +55,47 @@ struct KsplitCfg {
   static constexpr int BN = KL * SUB;          // keys per step
   static constexpr int NWH = kPrefillWaves;    // (head, row block) slots per workgroup
   static constexpr int NW = NWH * KL;          // wavefronts per workgroup
-  static constexpr int RB = D * 2;             // bytes per row
-  static constexpr int CPR = D / 8;            // 16-byte chunks per row
-  static constexpr int ROWS_PER_KB = 1024 / RB;
-  static constexpr int TILE_BYTES = BN * RB;   // one step of K (or V)
-  static constexpr int LOADS = TILE_BYTES / 1024;
-  static constexpr int LOADS_PER_WAVE = LOADS / NW;
+  // LDS row widths (elements) of K and of V: 192-wide rows sit in 256-wide ones
+  static constexpr int LW = D <= 64 ? 64 : D <= 128 ? 128 : 256;       // K
+  static constexpr int LWV = DV <= 64 ? 64 : DV <= 128 ? 128 : 256;   // V
+  static constexpr int RB = LW * 2, RBV = LWV * 2;      // bytes per LDS row
+  static constexpr int CPR = LW / 8, CPRV = LWV / 8;    // 16-byte chunks per LDS row
+  static constexpr int KCH = D / 8, VCH = DV / 8;       // real chunks of a K and a V row
+  static constexpr int ROWS_PER_KB = 1024 / RB, ROWS_PER_KB_V = 1024 / RBV;
+  static constexpr int TILE_BYTES = BN * RB, TILE_BYTES_V = BN * RBV;   // one step of K, of V
+  static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / NW;       // direct loads per step
+  static constexpr int LOADS_PER_WAVE_V = TILE_BYTES_V / 1024 / NW;
   static constexpr int NQC = D / KW;           // QK^T k-steps
   static constexpr int NSB = SUB / MF;         // 16-key blocks per wavefront step
-  static constexpr int NDB = D / MF;           // 16-column output blocks
+  static constexpr int NDB = DV / MF;          // 16-column output blocks
   static constexpr int NPK = SUB * MF / 64 / 2;  // packed weight pairs per lane
-  static_assert(D == 64 || D == 128 || D == 256, "the key-split prefill serves 64-, 128- and 256-wide heads");
-  static_assert(LOADS % NW == 0, "loads divide among wavefronts");
+  static_assert((D == DV && (D == 64 || D == 128 || D == 192 || D == 256)) || (D == 192 && DV == 128),
+                "the key-split prefill serves (64,64), (128,128), (192,192), (256,256) and (192,128)");
+  static_assert(2 * NDB * 64 * 16 <= TILE_BYTES, "two slots' merge partials fit one K stage");
+  static_assert(TILE_BYTES_V % (1024 * NW) == 0, "loads divide among wavefronts");
   static_assert(NSB == 2 && NPK == 4, "two 16-key blocks make one 32-key PV step");
 };
 
-// K: the chunk of row r sits at slot chunk ^ (r % CPR) (CPR = 32 chunks per row at
-// 256-wide heads, 16 at 128); the 16 rows one read touches (r0 .. r0+15, r0 a
+// K: the chunk of row r sits at slot chunk ^ (r % CPR) (CPR = 32 chunks per row in
+// the 256-wide layout, 16 in the 128-wide one); the 16 rows one read touches (r0 .. r0+15, r0 a
 // multiple of 16) land on 16 different slots. At 64-wide heads two 128-byte rows
 // share a 256-byte line of banks, so the XOR is (r / 2) % 8: the 16 rows take the
 // two halves of the line times 8 different slots.
-template <int D> __device__ __forceinline__ int ks_swz_k(int row) {
-  return D == 64 ? (row >> 1) % 8 : row % KsplitCfg<D>::CPR;
+template <int LW> __device__ __forceinline__ int ks_swz_k(int row) {
+  return LW == 64 ? (row >> 1) % 8 : row % (LW / 8);
 }
 // V: pairs of chunks move together (XOR by an even number), by 2 * (r % 8); each
 // half-wavefront of a transposed read covers 8 consecutive rows, whose 8
 // different pairs fill one 256-byte line of banks. At 64-wide heads (four pairs
 // per row, two rows per line) by 2 * ((r / 2) % 4): 2 row halves times 4 pairs.
-template <int D> __device__ __forceinline__ int ks_swz_v(int row) {
-  return D == 64 ? 2 * ((row >> 1) % 4) : 2 * (row % 8);
+template <int LW> __device__ __forceinline__ int ks_swz_v(int row) {
+  return LW == 64 ? 2 * ((row >> 1) % 4) : 2 * (row % 8);
+}
+// the chunk a lane loads into layout slot `slot` of a row with REAL chunks (a
+// row narrower than its layout): slots past the real ones take a real chunk again
+template <int CPR, int REAL> __device__ __forceinline__ int ks_src_chunk(int slot) {
+  if constexpr (REAL < CPR) return slot < REAL ? slot : slot - REAL;
+  return slot;
 }
 
 // bytes between rows of the boolean-mask ring (64 keys plus padding)
@@ -106,16 +121,16 @@ __device__ __forceinline__ float sum_xor16(float x) {
 
 // MK: kKsPlain (no mask or causal), kKsBool (boolean mask bytes) or kKsAdd
 // (additive mask values)
-template <class E, int D, int MK>
-__global__ void __launch_bounds__(KsplitCfg<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <class E, int D, int DV, int MK>
+__global__ void __launch_bounds__((KsplitCfg<D, DV>::NW * 64)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_ksplit_kernel(FwdArgs a) {
-  using C = KsplitCfg<D>;
+  using C = KsplitCfg<D, DV>;
   constexpr int MF = C::MF, BN = C::BN, SUB = C::SUB;
   using acc_t = f32x4;
   __shared__ __attribute__((aligned(1024))) uint8_t ks0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t ks1[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs0[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[C::TILE_BYTES_V];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs1[C::TILE_BYTES_V];
   __shared__ float merge_ml[C::NWH][2][MF];
   // boolean mask ring: up to 64 rows x 64 keys per stage, rows 80 bytes apart so
   // that the 16 rows x 4 groups one wavefront reads fall on 64 different banks
@@ -293,22 +308,23 @@ prefill_ksplit_kernel(FwdArgs a) {
   const uint32_t krs = (uint32_t)(a.ks[2] * 2), vrs = (uint32_t)(a.vs[2] * 2);
 
   // direct loads: the lane's 16-byte chunk of rows (w + NW*it) * ROWS_PER_KB + lane / CPR
-  const int ld_row = lane / C::CPR;
-  const int ld_slot = lane % C::CPR;
-  uint32_t offk[C::LOADS_PER_WAVE], offv[C::LOADS_PER_WAVE];
-  int ldrow[C::LOADS_PER_WAVE];
+  uint32_t offk[C::LOADS_PER_WAVE], offv[C::LOADS_PER_WAVE_V];
+  int ldrow[C::LOADS_PER_WAVE], ldrowv[C::LOADS_PER_WAVE_V];
 #pragma unroll
   for (int it = 0; it < C::LOADS_PER_WAVE; ++it) {
-    const int row = (w + C::NW * it) * C::ROWS_PER_KB + ld_row;
+    const int row = (w + C::NW * it) * C::ROWS_PER_KB + lane / C::CPR;
     ldrow[it] = row;
-    offk[it] = row * krs + (ld_slot ^ ks_swz_k<D>(row)) * 16;
-    offv[it] = row * vrs + (ld_slot ^ ks_swz_v<D>(row)) * 16;
+    offk[it] = row * krs + ks_src_chunk<C::CPR, C::KCH>((lane % C::CPR) ^ ks_swz_k<C::LW>(row)) * 16;
+  }
+#pragma unroll
+  for (int it = 0; it < C::LOADS_PER_WAVE_V; ++it) {
+    const int row = (w + C::NW * it) * C::ROWS_PER_KB_V + lane / C::CPRV;
+    ldrowv[it] = row;
+    offv[it] = row * vrs + ks_src_chunk<C::CPRV, C::VCH>((lane % C::CPRV) ^ ks_swz_v<C::LWV>(row)) * 16;
   }
   // rows past the last key read the last key's row instead (their weights are
   // zero); a step starts at most at Lk - 1, so the unsigned offsets stay >= 0
-  auto tail_over = [&](int k0, int it) -> uint32_t {
-    return (uint32_t)max(k0 + ldrow[it] - (a.Lk - 1), 0);
-  };
+  auto tail_over = [&](int k0, int row) -> uint32_t { return (uint32_t)max(k0 + row - (a.Lk - 1), 0); };
   auto issue_k = [&](int step, uint8_t* dst) {
     const int k0 = step * BN;
     const uint8_t* kt = kbase + (size_t)k0 * krs;
@@ -316,7 +332,7 @@ prefill_ksplit_kernel(FwdArgs a) {
 #pragma unroll
     for (int it = 0; it < C::LOADS_PER_WAVE; ++it) {
       uint32_t ok = offk[it];
-      if (tail) ok -= tail_over(k0, it) * krs;
+      if (tail) ok -= tail_over(k0, ldrow[it]) * krs;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + ok),
                                        (__attribute__((address_space(3))) void*)(dst + (w + C::NW * it) * 1024), 16,
                                        0, 0);
@@ -327,9 +343,9 @@ prefill_ksplit_kernel(FwdArgs a) {
     const uint8_t* vt = vbase + (size_t)k0 * vrs;
     const bool tail = k0 + BN > a.Lk;
 #pragma unroll
-    for (int it = 0; it < C::LOADS_PER_WAVE; ++it) {
+    for (int it = 0; it < C::LOADS_PER_WAVE_V; ++it) {
       uint32_t ov = offv[it];
-      if (tail) ov -= tail_over(k0, it) * vrs;
+      if (tail) ov -= tail_over(k0, ldrowv[it]) * vrs;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt + ov),
                                        (__attribute__((address_space(3))) void*)(dst + (w + C::NW * it) * 1024), 16,
                                        0, 0);
@@ -342,11 +358,12 @@ prefill_ksplit_kernel(FwdArgs a) {
   constexpr int KC = C::NQC < 4 ? C::NQC : 4;   // k-steps per group of K operand reads
   uint32_t kb4[KC];
 #pragma unroll
-  for (int c = 0; c < KC; ++c) kb4[c] = (SUB * kl + col) * C::RB + (((4 * c + kg) ^ ks_swz_k<D>(SUB * kl + col)) * 16);
+  for (int c = 0; c < KC; ++c)
+    kb4[c] = (SUB * kl + col) * C::RB + (((4 * c + kg) ^ ks_swz_k<C::LW>(SUB * kl + col)) * 16);
   // (at 64- and 128-wide heads the XOR of row 16 nb + col does not depend on nb:
   // the blocks differ by 16 rows)
   auto k_off = [&](int c, int nb) -> uint32_t {
-    if constexpr (D <= 128) return kb4[c] + nb * (16 * C::RB);
+    if constexpr (C::LW <= 128) return kb4[c] + nb * (16 * C::RB);
     return c < 4 ? kb4[c] + nb * (16 * C::RB + 256) : kb4[c - 4] + 256 + nb * (16 * C::RB - 256);
   };
   // V^T operand of output block db: transposed reads of keys 4g..4g+3 and
@@ -356,36 +373,41 @@ prefill_ksplit_kernel(FwdArgs a) {
   const int vr = lane >> 2;
   constexpr int VB = C::NDB < 8 ? C::NDB : 8;   // output blocks per group of V^T reads
   uint32_t vb8[VB];
-  const int vsw = ks_swz_v<D>(SUB * kl + vr) / 2;   // the row's pair XOR (the same 16 rows on)
+  const int vsw = ks_swz_v<C::LWV>(SUB * kl + vr) / 2;   // the row's pair XOR (the same 16 rows on)
 #pragma unroll
   for (int db = 0; db < VB; ++db)
-    vb8[db] = (SUB * kl + vr) * C::RB + ((2 * (db ^ vsw) + ((lane >> 1) & 1)) * 16) + (lane & 1) * 8;
+    vb8[db] = (SUB * kl + vr) * C::RBV + ((2 * (db ^ vsw) + ((lane >> 1) & 1)) * 16) + (lane & 1) * 8;
   auto v_off = [&](int db) -> uint32_t { return db < VB ? vb8[db] : vb8[db - VB] + 256; };
-  static_assert((C::NQC <= 4 || C::NQC % 4 == 0) && (C::NDB <= 8 || C::NDB % 8 == 0),
-                "LDS operands come in groups of up to four k-steps and eight blocks");
+  static_assert(C::NQC <= 8 && C::NDB <= 16 && (C::LW == 256 || C::NQC <= 4) && (C::LWV == 256 || C::NDB <= 8),
+                "LDS operands come in up to two groups of up to four k-steps and eight blocks");
 
   // LDS operands go through two register buffers of eight 16-byte groups: the
   // reads of one group are issued before the MFMAs of the previous one, and an
   // explicit wait for all LDS reads follows those MFMAs. (With direct-to-LDS loads
   // in flight every LDS wait is a wait for all reads, so this keeps each wait
   // behind a group of MFMAs instead of in front of each one.)
+  // (a group stops at the last k-step or block: 192-wide heads take a second K group
+  // of two k-steps, 192-wide values a second V group of four blocks)
   auto read_k = [&](const uint8_t* Ks, int c0, u32x4 (&buf)[8]) {
 #pragma unroll
     for (int c = 0; c < KC; ++c)
+      if (c0 + c < C::NQC)
 #pragma unroll
-      for (int nb = 0; nb < C::NSB; ++nb) buf[c * 2 + nb] = *reinterpret_cast<const u32x4*>(Ks + k_off(c0 + c, nb));
+        for (int nb = 0; nb < C::NSB; ++nb) buf[c * 2 + nb] = *reinterpret_cast<const u32x4*>(Ks + k_off(c0 + c, nb));
   };
   auto mma_qk = [&](int c0, const u32x4 (&buf)[8], acc_t (&s)[C::NSB]) {
 #pragma unroll
     for (int c = 0; c < KC; ++c)
+      if (c0 + c < C::NQC)
 #pragma unroll
-      for (int nb = 0; nb < C::NSB; ++nb) s[nb] = mma16<E, MF>(buf[c * 2 + nb], qop[c0 + c], s[nb]);
+        for (int nb = 0; nb < C::NSB; ++nb) s[nb] = mma16<E, MF>(buf[c * 2 + nb], qop[c0 + c], s[nb]);
   };
   auto read_v = [&](const uint8_t* Vs, int db0, u32x4 (&buf)[8]) {
 #pragma unroll
     for (int d = 0; d < VB; ++d) {
+      if (db0 + d >= C::NDB) continue;
       const u32x2 ra = lds_read_tr16((const uint16_t*)(Vs + v_off(db0 + d)));
-      const u32x2 rb = lds_read_tr16((const uint16_t*)(Vs + v_off(db0 + d) + 16 * C::RB));
+      const u32x2 rb = lds_read_tr16((const uint16_t*)(Vs + v_off(db0 + d) + 16 * C::RBV));
       buf[d] = u32x4{ra[0], ra[1], rb[0], rb[1]};
     }
   };
@@ -399,12 +421,12 @@ prefill_ksplit_kernel(FwdArgs a) {
     read_k(Ks, 0, ba);
     lds_wait();
     score_init(s, mb);
-    if constexpr (C::NQC == 8) {
+    if constexpr (C::NQC > 4) {
       read_k(Ks, 4, bb);
       lds_wait();
     }
     mma_qk(0, ba, s);
-    if constexpr (C::NQC == 8) mma_qk(4, bb, s);
+    if constexpr (C::NQC > 4) mma_qk(4, bb, s);
   };
   auto row_max16 = [](float x) { return max_xor16(max_xor32(x)); };
   auto tile_max_full = [&](acc_t (&s)[C::NSB]) {
@@ -458,7 +480,8 @@ prefill_ksplit_kernel(FwdArgs a) {
   auto mma_pv = [&](int db0, const u32x4 (&buf)[8], const uint32_t (&pk)[C::NPK]) {
     const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
 #pragma unroll
-    for (int d = 0; d < VB; ++d) o[db0 + d] = mma16<E, MF>(buf[d], pb, o[db0 + d]);
+    for (int d = 0; d < VB; ++d)
+      if (db0 + d < C::NDB) o[db0 + d] = mma16<E, MF>(buf[d], pb, o[db0 + d]);
   };
 
   acc_t sa[C::NSB], sb[C::NSB];
@@ -500,9 +523,9 @@ prefill_ksplit_kernel(FwdArgs a) {
     weights(scur, pk);
     fence();
     lds_wait();
-    if constexpr (C::NQC == 8) {
-      // 256-wide heads: two groups of K operands and two of V, each group's
-      // reads issued before the MFMAs of the previous one
+    if constexpr (C::NQC > 4) {
+      // 192- and 256-wide heads: two groups of K operands and up to two of V,
+      // each group's reads issued before the MFMAs of the previous one
       read_k(Knext, 4, bb);
       score_init(snext, mb);
       fence();
@@ -568,7 +591,7 @@ prefill_ksplit_kernel(FwdArgs a) {
   }
   if (ntiles > 1) issue_k(tb + 1, ks1);
   if (ntiles > 1) {
-    __builtin_amdgcn_s_waitcnt(ks_vmcnt(2 * C::LOADS_PER_WAVE));
+    __builtin_amdgcn_s_waitcnt(ks_vmcnt(C::LOADS_PER_WAVE + C::LOADS_PER_WAVE_V));
   } else {
     __builtin_amdgcn_s_waitcnt(ks_vmcnt(0));
   }
@@ -611,7 +634,7 @@ prefill_ksplit_kernel(FwdArgs a) {
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (iq >= a.Lq) return;
   const float g0 = f0 * inv, g1 = f1 * inv;
-  uint16_t* op = (uint16_t*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq) * D;
+  uint16_t* op = (uint16_t*)a.out + ((size_t)(b * a.Hq + h) * a.Lq + iq) * DV;
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) {
     const f32x4 p = part[db * 64 + lane];

@@ -404,4 +404,8 @@ def test_key_split_plans_for_wide_heads_and_small_64_and_128_wide_grids():
     assert shape(big_add) == (16, 32, 2, 8)
     assert shape(sd.sdpa_plan(1, 64, 8, 1024, 1801, 128, 128, 3, True, True, 1)) == (32, 64, 0, 4)
     assert shape(sd.sdpa_plan(1, 16, 2, 1024, 1801, 128, 128, 3, True, True, 1)) == (16, 32, 2, 8)
-    assert shape(sd.sdpa_plan(1, 64, 8, 1024, 1801, 192, 192, 1, False, False, 1)) == (16, 64, 0, 4)
+    # heads of 192 columns take the key-split kernel on every grid, with every mask kind
+    for dv in (192, 128):
+        for mk in (0, 1, 2, 3):
+            big192 = sd.sdpa_plan(1, 64, 8, 1024, 1801, 192, dv, mk, mk >= 2, True, 1)
+            assert shape(big192) + (big192["kernels"], big192["scratch_bytes"]) == (16, 32, 2, 8, 1, 0)

@@ -128,29 +128,31 @@ def test_prefill_bool_mask_word_edges(D, Lk):
             _full_check(p, f"bool mask {name} D={D} Lk={Lk}")
 
 
-# --- full grids at 64-, 128- and 256-wide heads ------------------------------------------------
+# --- full grids at 64- to 256-wide heads -------------------------------------------------------
 # Two batch items of 32 heads, ragged on both axes: 1040 query rows over 1297 keys. At
-# 256-wide heads the key-split kernel (520 workgroups of 16-row blocks); at 64- and
-# 128-wide heads the pipelined kernel, whose grid here (264 workgroups of 32-row blocks per
-# batch item) is large enough that the plan keeps it (the small-grid tests of those
-# widths run the key-split kernel).
+# heads of 192 and 256 columns the key-split kernel (520 workgroups of 16-row blocks per
+# batch item); at 64-, 96- and 128-wide heads the pipelined kernel, whose grid here (264
+# workgroups of 32-row blocks per batch item) is large enough that the plan keeps it (the
+# small-grid tests of the 64- and 128-wide heads run the key-split kernel).
 
 WIDE = dict(B=2, Hq=32, Hkv=4, Lq=1040, Lk=1297)
-WIDE_KERNEL = {64: 0, 128: 0, 256: 2}   # the plan's key lanes: 0 = pipelined kernel, 2 = key-split
+WIDE_PAIRS = [(64, 64), (96, 96), (128, 128), (192, 192), (192, 128), (256, 256)]
+WIDE_IDS = ["x".join(map(str, w)) for w in WIDE_PAIRS]
 
 
 def _wide_plan_check(p):
     import scaled_dot_product_06_amd as sd
     plan = sd.sdpa_plan(*p.shape_args(), p.mask_kind, p.mask is not None, p.sinks is not None, p.dtype)
-    assert plan["splits"] == WIDE_KERNEL[p.D], plan
+    # the plan's key lanes: 0 = pipelined kernel, 2 = key-split
+    assert plan["splits"] == (2 if p.D >= 192 else 0), plan
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D,Dv", WIDE_PAIRS, ids=WIDE_IDS)
 @pytest.mark.parametrize("mask_kind,sinks", [(0, False), (1, False), (1, True), (2, True)])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_wide_heads_full_grid_sampled_rows(mask_kind, sinks, dtype, D):
+def test_wide_heads_full_grid_sampled_rows(mask_kind, sinks, dtype, D, Dv):
     w = WIDE
-    p = gen.make_problem(1700 + 10 * mask_kind + sinks + D, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], D, D,
+    p = gen.make_problem(1700 + 10 * mask_kind + sinks + D, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], D, Dv,
                          DT[dtype], mask_kind, sinks=sinks)
     _wide_plan_check(p)
     say(f"full grid: {p!r}")
@@ -159,28 +161,28 @@ def test_wide_heads_full_grid_sampled_rows(mask_kind, sinks, dtype, D):
     rows = sample_rows(p, 120, seed=17 + mask_kind)
     want = oracle_rows(p, rows)
     assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want,
-                  f"{D}-wide full grid mask {mask_kind} sinks {sinks}, sampled rows")
+                  f"({D},{Dv}) full grid mask {mask_kind} sinks {sinks}, sampled rows")
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
-def test_wide_heads_full_grid_batch_items_equal_each_item_alone(D):
+@pytest.mark.parametrize("D,Dv", WIDE_PAIRS, ids=WIDE_IDS)
+def test_wide_heads_full_grid_batch_items_equal_each_item_alone(D, Dv):
     w = WIDE
-    p = gen.make_problem(1795 + D, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], D, D, BF16, 1, sinks=True)
+    p = gen.make_problem(1795 + D, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], D, Dv, BF16, 1, sinks=True)
     _wide_plan_check(p)
     whole = from_device(run_gpu(p), BF16)
     for b in range(w["B"]):
-        pb = gen.Problem(1, w["Hq"], w["Hkv"], w["Lq"], w["Lk"], D, D, BF16, 1, p.scale, p.q[b:b + 1],
+        pb = gen.Problem(1, w["Hq"], w["Hkv"], w["Lq"], w["Lk"], D, Dv, BF16, 1, p.scale, p.q[b:b + 1],
                          p.k[b:b + 1], p.v[b:b + 1], None, p.sinks)
         alone = from_device(run_gpu(pb), BF16)
         assert np.array_equal(whole[b:b + 1], alone), f"batch item {b} differs"
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
-def test_wide_heads_full_grid_window_sampled_rows(D):
+@pytest.mark.parametrize("D,Dv", WIDE_PAIRS, ids=WIDE_IDS)
+def test_wide_heads_full_grid_window_sampled_rows(D, Dv):
     from scaled_dot_product_06_amd import attention
     import torch
     w = WIDE
-    p = gen.make_problem(1790 + D, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], D, D, BF16, 1, sinks=True)
+    p = gen.make_problem(1790 + D, w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], D, Dv, BF16, 1, sinks=True)
     _wide_plan_check(p)
     q, k, v, _, sinks = device_inputs(p)
     got = from_device(attention(q, k, v, p.scale, 1, None, sinks, window=300), p.dtype)
@@ -188,7 +190,7 @@ def test_wide_heads_full_grid_window_sampled_rows(D):
     rows = sample_rows(p, 96, seed=23)
     qq, kk, vv, _, ss = p.widened()
     want = orc.sdpa(qq, kk, vv, p.scale, 1, None, ss, window=300, rows=rows)
-    assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want, f"{D}-wide full grid window 300")
+    assert_parity(p, np.stack([got[b, h, i] for b, h, i in rows]), want, f"({D},{Dv}) full grid window 300")
 
 
 # --- sliding windows (nuvec-core tests/fast.rs, windowed-kernel tests) -------------------------

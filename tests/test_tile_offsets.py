@@ -185,24 +185,32 @@ def test_k_operands_and_query_loads_stay_in_the_real_columns(D, Dv):
 
 
 # --- the key-split prefill: 64-key steps loaded by eight wavefronts ---------------------------
-# (64-, 128- and 256-wide heads; 16 query rows per (head, row block) slot, so a workgroup's
+# (head pairs (64,64), (128,128), (192,192), (192,128) and (256,256); 16 query rows per (head, row block) slot, so a workgroup's
 # query block is 16, 32 or 64 rows for four, two or one heads per workgroup)
 
-def ks_swz_k(D, row):
-    return (row >> 1) % 8 if D == 64 else row % (D // 8)
+KS_PAIRS = [(64, 64), (128, 128), (192, 192), (192, 128), (256, 256)]   # the key-split kernel's head pairs
 
 
-def ks_swz_v(D, row):
-    return 2 * ((row >> 1) % 4) if D == 64 else 2 * (row % 8)
+def ks_layout(width):
+    # LDS row width of a K or V row: 192-wide rows sit in 256-wide ones
+    return 64 if width <= 64 else 128 if width <= 128 else 256
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+def ks_swz_k(LW, row):
+    return (row >> 1) % 8 if LW == 64 else row % (LW // 8)
+
+
+def ks_swz_v(LW, row):
+    return 2 * ((row >> 1) % 4) if LW == 64 else 2 * (row % 8)
+
+
+@pytest.mark.parametrize("D,Dv", KS_PAIRS)
 @pytest.mark.parametrize("heads", [1, 2, 4])
 @pytest.mark.parametrize("mask_kind,window", [(0, 0), (1, 0), (1, 7), (1, 300), (2, 0)])
-def test_key_split_steps_read_inside_the_keys(mask_kind, window, heads, D):
+def test_key_split_steps_read_inside_the_keys(mask_kind, window, heads, D, Dv):
     KBN, KNW = 64, 8
+    LW, LWV = ks_layout(D), ks_layout(Dv)
     bm = (4 // heads) * 16
-    strides = [2 * D, 2 * D * 3 + 16 * 5, (1 << 26) - 16]
     for Lq, Lk in CALLS:
         shift = Lk - Lq
         for qb in range(-(-Lq // bm)):
@@ -216,45 +224,50 @@ def test_key_split_steps_read_inside_the_keys(mask_kind, window, heads, D):
             for k0 in steps:
                 assert k0 <= Lk - 1, "a step starts past the last key"
             for k0 in [t for t in steps if t + KBN > Lk] + steps[:1]:
-                for rs in strides:
-                    check_tile(D, Lk, k0, rs, ks_swz_k, KBN, KNW)
-                    check_tile(D, Lk, k0, rs, ks_swz_v, KBN, KNW)
+                for rs in [2 * D, 2 * D * 3 + 16 * 5, (1 << 26) - 16]:
+                    check_tile(LW, Lk, k0, rs, ks_swz_k, KBN, KNW, real=D // 8)
+                for rs in [2 * Dv, 2 * Dv * 3 + 16 * 5, (1 << 26) - 16]:
+                    check_tile(LWV, Lk, k0, rs, ks_swz_v, KBN, KNW, real=Dv // 8)
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
-def test_key_split_lds_operand_offsets(D):
+@pytest.mark.parametrize("D,Dv", KS_PAIRS)
+def test_key_split_lds_operand_offsets(D, Dv):
     # K operand reads fold four lane offsets plus constants; V^T transposed reads fold
-    # eight lane offsets plus 256 bytes for the upper eight output blocks (256-wide
-    # heads) and 16 rows for the second read. Both against the direct
-    # row * RB + swizzled chunk formula.
-    RB, SUB = 2 * D, 32
+    # eight lane offsets plus 256 bytes for the upper output blocks (256-wide layout)
+    # and 16 rows for the second read. Both against the direct row * RB + swizzled
+    # chunk formula, and each read lands on a slot that holds the real chunk it wants.
+    LW, LWV = ks_layout(D), ks_layout(Dv)
+    RB, RBV, SUB = 2 * LW, 2 * LWV, 32
     for kl in (0, 1):
         for lane in range(64):
             col, kg = lane % 16, lane // 16
-            kb4 = [(SUB * kl + col) * RB + (((4 * c + kg) ^ ks_swz_k(D, SUB * kl + col)) * 16) for c in range(4)]
+            kb4 = [(SUB * kl + col) * RB + (((4 * c + kg) ^ ks_swz_k(LW, SUB * kl + col)) * 16) for c in range(4)]
             for c in range(D // 32):
                 for nb in range(2):
-                    if D <= 128:
+                    if LW <= 128:
                         folded = kb4[c] + nb * (16 * RB)
                     else:
                         folded = (kb4[c] + nb * (16 * RB + 256) if c < 4
                                   else kb4[c - 4] + 256 + nb * (16 * RB - 256))
                     row = SUB * kl + 16 * nb + col
-                    chunk = (4 * c + kg) ^ ks_swz_k(D, row)
-                    assert chunk < D // 8
-                    assert folded == row * RB + chunk * 16, (kl, lane, c, nb)
+                    slot = (4 * c + kg) ^ ks_swz_k(LW, row)
+                    assert slot < LW // 8 and 4 * c + kg < D // 8
+                    # the slot holds, as loaded, the chunk it is read for
+                    assert src_chunk(slot ^ ks_swz_k(LW, row), D // 8) == 4 * c + kg
+                    assert folded == row * RB + slot * 16, (kl, lane, c, nb)
             vr = lane >> 2
-            vsw = ks_swz_v(D, SUB * kl + vr) // 2
-            vb8 = [(SUB * kl + vr) * RB + ((2 * (d ^ vsw) + ((lane >> 1) & 1)) * 16) + (lane & 1) * 8
+            vsw = ks_swz_v(LWV, SUB * kl + vr) // 2
+            vb8 = [(SUB * kl + vr) * RBV + ((2 * (d ^ vsw) + ((lane >> 1) & 1)) * 16) + (lane & 1) * 8
                    for d in range(8)]
-            for db in range(D // 16):
+            for db in range(Dv // 16):
                 folded = vb8[db % 8] + (256 if db >= 8 else 0)
                 for second in (0, 1):
                     row = SUB * kl + vr + 16 * second
                     # provider lane 4e + c of its 16-lane group: row 4g + e, columns 16 db + 4c
                     assert row - SUB * kl - 16 * second == 4 * (lane // 16) + (lane % 16) // 4
                     byte = 2 * (16 * db + 4 * (lane % 4))
-                    slot = (byte // 16) ^ ks_swz_v(D, row)
-                    direct = row * RB + slot * 16 + byte % 16
-                    assert folded + 16 * RB * second == direct, (kl, lane, db, second)
-                    assert 0 <= direct and direct + 8 <= 64 * RB
+                    slot = (byte // 16) ^ ks_swz_v(LWV, row)
+                    assert src_chunk(slot ^ ks_swz_v(LWV, row), Dv // 8) == byte // 16 < Dv // 8
+                    direct = row * RBV + slot * 16 + byte % 16
+                    assert folded + 16 * RBV * second == direct, (kl, lane, db, second)
+                    assert 0 <= direct and direct + 8 <= 64 * RBV

@@ -102,7 +102,8 @@ constexpr int kFastRows = 32, kFastBN = 32;
 // lanes that each take 32 keys of every 64-key step, so each SIMD holds two
 // wavefronts. 16-bit heads of 192 columns or more, (192,192), (192,128) and
 // (256,256), run it on every grid and with every mask (a 32-row tile of these
-// heads leaves room for one wavefront per SIMD);
+// heads leaves room for one wavefront per SIMD), and so do 128-wide heads with an
+// additive mask;
 // 64- and 128-wide heads run it when the pipelined kernel's whole grid (every
 // batch item) would have fewer than kKsplitSmallGrid workgroups: at one workgroup
 // per compute unit or less, the twice as many 16-row workgroups and the halved key
@@ -112,7 +113,12 @@ constexpr int kKsplitSmallGrid = 256;
 constexpr bool prefill_can_ksplit(int elem, int D, int Dv) {
   return elem != kF32 && ((D == Dv && (D == 64 || D == 128 || D == 192 || D == 256)) || (D == 192 && Dv == 128));
 }
-constexpr bool prefill_ksplit_always(int D, int Dv) { return D >= 192 && Dv >= 128; }
+// Calls that take it on every grid: heads of 192 columns or more, and 128-wide
+// heads with an additive mask (the pipelined kernel reads none, and the generic
+// kernel measured slower on every grid).
+constexpr bool prefill_ksplit_always(int D, int Dv, int mask_kind) {
+  return (D >= 192 && Dv >= 128) || (D == 128 && Dv == 128 && mask_kind == kMaskAdditive);
+}
 // Generic kernel: 32x32 MFMA tiles (32 query rows per wavefront) up to
 // 128-wide heads; 16x16 tiles above, where a 32-row output accumulator would
 // leave too few registers for its staging.

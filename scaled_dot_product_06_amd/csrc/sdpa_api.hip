@@ -269,15 +269,16 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
     *plan = p;
     return SDPA_OK;
   }
-  // the key-split kernel at 16-bit heads of 192 columns or more and at 64/128-wide
-  // ones on small grids, the pipelined kernel (32-row tiles) where it applies, else
-  // the generic kernel's geometry
+  // the key-split kernel at 16-bit heads of 192 columns or more, 128-wide ones with
+  // an additive mask, and 64/128-wide ones on small grids; the pipelined kernel
+  // (32-row tiles) where it applies; else the generic kernel's geometry
   const int nw = prefill_waves(dtype, (int)D, (int)Dv);
   const int64_t heads = gcd64(group, nw);
   bool kspl = false;
   if (prefill_can_ksplit(dtype, (int)D, (int)Dv)) {
     const int64_t fbm = (nw / heads) * kFastRows;   // a pipelined workgroup's query rows per head
-    kspl = prefill_ksplit_always((int)D, (int)Dv) || (B * Hq / heads) * ((Lq + fbm - 1) / fbm) < kKsplitSmallGrid;
+    kspl = prefill_ksplit_always((int)D, (int)Dv, mask_kind) ||
+           (B * Hq / heads) * ((Lq + fbm - 1) / fbm) < kKsplitSmallGrid;
   }
   const bool fast = !kspl && prefill_can_fast(dtype, (int)D, (int)Dv, mask_kind);
   if (kspl) {

@@ -314,14 +314,18 @@ def _strided(q=(16, 4 * 5 * 64, 5 * 64, 64), k=(16, 2 * 9 * 64, 9 * 64, 64), v=(
                                    dtype, None, check=False)
 
 
-def test_additive_masks_plan_on_the_generic_prefill_kernel():
-    # a grid the pipelined kernel fills (32 heads x 4096 rows at 128-wide heads): it
-    # reads no additive mask, so those calls take the generic kernel
+def test_additive_masks_plan_off_the_pipelined_kernel():
+    # the pipelined kernel reads no additive mask: on a grid it fills (32 heads x 4096
+    # rows), 128-wide heads with an additive mask take the key-split kernel and
+    # 64- and 96-wide ones the generic kernel
     fast = sd.sdpa_plan(1, 32, 8, 4096, 4096, 128, 128, 0, False, False, 2)
     add = sd.sdpa_plan(1, 32, 8, 4096, 4096, 128, 128, 3, True, False, 2)
     assert fast["route"] == add["route"] == "prefill"
-    assert (fast["block_n"], add["block_n"]) == (32, 64)
-    # on a small grid both take the key-split kernel
+    assert (fast["block_n"], fast["splits"], add["block_n"], add["splits"]) == (32, 0, 32, 2)
+    for d in (64, 96):
+        gen_add = sd.sdpa_plan(1, 32, 8, 4096, 4096, d, d, 3, True, False, 2)
+        assert (gen_add["rows_per_wave"], gen_add["block_n"], gen_add["splits"]) == (32, 64, 0)
+    # on a small grid 64- and 128-wide heads take the key-split kernel
     small = sd.sdpa_plan(1, 8, 2, 300, 300, 128, 128, 3, True, False, 2)
     assert (small["splits"], small["rows_per_wave"]) == (2, 16)
     dec = sd.sdpa_plan(1, 8, 2, 1, 3000, 128, 128, 3, True, False, 2)
@@ -395,14 +399,15 @@ def test_key_split_plans_for_wide_heads_and_small_64_and_128_wide_grids():
     # one or two heads per workgroup: 64 or 32 rows of a head per key lane
     assert sd.sdpa_plan(1, 4, 4, 100, 300, 256, 256, 0, False, False, 2)["grid"][0] == 4 * 2
     assert sd.sdpa_plan(1, 4, 2, 100, 300, 256, 256, 0, False, False, 2)["grid"][0] == 2 * 4
-    # additive masks take the key-split kernel at 256-wide heads too, and at 64- and
-    # 128-wide heads on small grids; other calls keep the generic kernel (the pipelined
-    # kernel reads no additive mask)
+    # additive masks take the key-split kernel at 192- and 256-wide heads too, at
+    # 128-wide heads on every grid and at 64-wide heads on small grids; other calls
+    # keep the generic kernel (the pipelined kernel reads no additive mask)
     add = sd.sdpa_plan(1, 64, 8, 1024, 1801, 256, 256, 3, True, True, 1)
     assert shape(add) + (add["kernels"], add["scratch_bytes"]) == (16, 32, 2, 8, 1, 0)
     big_add = sd.sdpa_plan(1, 32, 4, 1040, 1297, 256, 256, 3, True, False, 2)
     assert shape(big_add) == (16, 32, 2, 8)
-    assert shape(sd.sdpa_plan(1, 64, 8, 1024, 1801, 128, 128, 3, True, True, 1)) == (32, 64, 0, 4)
+    assert shape(sd.sdpa_plan(1, 64, 8, 1024, 1801, 128, 128, 3, True, True, 1)) == (16, 32, 2, 8)
+    assert shape(sd.sdpa_plan(1, 64, 8, 1024, 1801, 64, 64, 3, True, True, 1)) == (32, 64, 0, 4)
     assert shape(sd.sdpa_plan(1, 16, 2, 1024, 1801, 128, 128, 3, True, True, 1)) == (16, 32, 2, 8)
     # heads of 192 columns take the key-split kernel on every grid, with every mask kind
     for dv in (192, 128):

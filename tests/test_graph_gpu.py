@@ -55,7 +55,7 @@ CASES = [
     (1, 2, 8, 2, 300, 300, 128, BF16),      # key-split prefill (128-wide heads, small grid)
     (2, 1, 8, 2, 300, 300, 64, F16),        # key-split prefill (64-wide heads, small grid), mask bytes
     (2, 1, 16, 2, 100, 300, 256, F16),      # key-split prefill reading the mask bytes
-    (0, 1, 8, 2, 77, 150, 192, BF16),       # generic prefill
+    (0, 1, 8, 2, 77, 150, 512, BF16),       # generic prefill (512-wide heads)
     (1, 1, 4, 2, 40, 70, 64, F32),          # f32 prefill
     (0, 2, 16, 2, 1, 9000, 256, BF16),      # decode split + reduce (scratch)
     (1, 1, 32, 4, 1, 8193, 128, BF16),      # the 8193-key decode: split + reduce

@@ -137,11 +137,14 @@ CASES = [
     (1, 2, 8, 2, 300, 300, 128, 128, BF16),        # key-split prefill (128-wide heads, small grid)
     (0, 1, 8, 2, 77, 150, 256, 256, F16),          # key-split prefill (256-wide heads)
     (2, 1, 16, 2, 100, 300, 256, 256, BF16),       # key-split prefill reading the mask bytes: one kernel
-    (0, 1, 8, 2, 77, 150, 192, 192, F16),          # generic prefill
+    (0, 1, 8, 2, 77, 150, 192, 128, F16),          # key-split prefill (192-wide K, 128-wide V)
+    (0, 1, 8, 2, 77, 150, 512, 512, F16),          # generic prefill (512-wide heads)
+    (1, 1, 64, 8, 512, 300, 96, 96, BF16),         # pipelined prefill (96-wide heads in the 128-wide layout)
     (2, 1, 8, 2, 200, 333, 64, 64, F16),           # key-split prefill (64-wide heads, small grid), byte mask
     (2, 1, 64, 8, 512, 333, 64, 64, F16),          # mask packing + pipelined prefill (64-wide heads)
     (2, 1, 4, 2, 70, 90, 128, 128, F32),           # f32 prefill, byte mask
-    (3, 1, 64, 8, 512, 257, 128, 128, BF16),       # additive mask: generic prefill (a large grid)
+    (3, 1, 64, 8, 512, 257, 128, 128, BF16),       # additive mask: key-split prefill (128-wide heads, a large grid)
+    (3, 1, 64, 8, 512, 257, 64, 64, BF16),         # additive mask: generic prefill (64-wide heads, a large grid)
     (3, 1, 8, 2, 100, 257, 128, 128, BF16),        # additive mask: key-split prefill (small grid)
     (1, 2, 16, 2, 1, 65537, 256, 256, BF16),       # long decode: split + reduce
     (2, 1, 32, 4, 1, 8193, 128, 128, BF16),        # decode with a byte mask

@@ -104,17 +104,18 @@ def test_every_issued_tile_reads_inside_the_keys(D, Dv, mask_kind, window, heads
     LW = layout(D, Dv)
     for Lq, Lk in CALLS:
         nqb = -(-Lq // (ROWS * NW // heads))
+        starts = set()   # the ragged last tile (the one that pulls rows back) and the first, per block
         for qb in range(nqb):
             tiles = issued_tiles(Lq, Lk, qb, mask_kind, window, heads)
             for k0 in tiles:
                 assert k0 <= Lk - 1, "a tile starts past the last key"
-            # the ragged last tile is the one that pulls rows back
-            for k0 in [t for t in tiles if t + BN > Lk] + tiles[:1]:
-                # K and V rows: contiguous, odd and the largest allowed strides
-                for rs in [2 * D, 2 * D * 3 + 16 * 5, (1 << 26) - 16]:
-                    check_tile(LW, Lk, k0, rs, swz_k, real=D // 8)
-                for rs in [2 * Dv, 2 * Dv * 3 + 16 * 5, (1 << 26) - 16]:
-                    check_tile(LW, Lk, k0, rs, swz_v, real=Dv // 8)
+            starts.update([t for t in tiles if t + BN > Lk] + tiles[:1])
+        for k0 in sorted(starts):
+            # K and V rows: contiguous, odd and the largest allowed strides
+            for rs in [2 * D, 2 * D * 3 + 16 * 5, (1 << 26) - 16]:
+                check_tile(LW, Lk, k0, rs, swz_k, real=D // 8)
+            for rs in [2 * Dv, 2 * Dv * 3 + 16 * 5, (1 << 26) - 16]:
+                check_tile(LW, Lk, k0, rs, swz_v, real=Dv // 8)
 
 
 # --- V^T operand offsets -------------------------------------------------------------------------
@@ -213,6 +214,7 @@ def test_key_split_steps_read_inside_the_keys(mask_kind, window, heads, D, Dv):
     bm = (4 // heads) * 16
     for Lq, Lk in CALLS:
         shift = Lk - Lq
+        starts = set()   # the ragged last step and the first, per query block
         for qb in range(-(-Lq // bm)):
             kend = Lk
             if mask_kind == 1:
@@ -223,11 +225,12 @@ def test_key_split_steps_read_inside_the_keys(mask_kind, window, heads, D, Dv):
             steps = [(tb + t) * KBN for t in range(max((kend + KBN - 1) // KBN - tb, 0))]
             for k0 in steps:
                 assert k0 <= Lk - 1, "a step starts past the last key"
-            for k0 in [t for t in steps if t + KBN > Lk] + steps[:1]:
-                for rs in [2 * D, 2 * D * 3 + 16 * 5, (1 << 26) - 16]:
-                    check_tile(LW, Lk, k0, rs, ks_swz_k, KBN, KNW, real=D // 8)
-                for rs in [2 * Dv, 2 * Dv * 3 + 16 * 5, (1 << 26) - 16]:
-                    check_tile(LWV, Lk, k0, rs, ks_swz_v, KBN, KNW, real=Dv // 8)
+            starts.update([t for t in steps if t + KBN > Lk] + steps[:1])
+        for k0 in sorted(starts):
+            for rs in [2 * D, 2 * D * 3 + 16 * 5, (1 << 26) - 16]:
+                check_tile(LW, Lk, k0, rs, ks_swz_k, KBN, KNW, real=D // 8)
+            for rs in [2 * Dv, 2 * Dv * 3 + 16 * 5, (1 << 26) - 16]:
+                check_tile(LWV, Lk, k0, rs, ks_swz_v, KBN, KNW, real=Dv // 8)
 
 
 @pytest.mark.parametrize("D,Dv", KS_PAIRS)

@@ -70,7 +70,7 @@ typedef struct sdpa_plan_t {
   int32_t rows_per_wave;  /* query rows one wavefront carries (MFMA tile height). Prefill: 16 on
                              the key-split kernel (f16/bf16, (D, Dv) in {(192,192), (192,128),
                              (256,256)} with every mask kind, (128,128) with an additive mask,
-                             and D == Dv in {64, 128} when the
+                             and (D, Dv) in {(64,64), (80,80), (96,96), (128,128), (96,64)} when the
                              pipelined kernel's grid, all batch items together, would have fewer
                              than 256 workgroups); 32 on the pipelined kernel (other f16/bf16
                              calls with (D, Dv) in {(64,64), (80,80), (96,96), (128,128), (96,64)},

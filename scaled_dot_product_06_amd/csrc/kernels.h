@@ -104,14 +104,16 @@ constexpr int kFastRows = 32, kFastBN = 32;
 // (256,256), run it on every grid and with every mask (a 32-row tile of these
 // heads leaves room for one wavefront per SIMD), and so do 128-wide heads with an
 // additive mask;
-// 64- and 128-wide heads run it when the pipelined kernel's whole grid (every
-// batch item) would have fewer than kKsplitSmallGrid workgroups: at one workgroup
-// per compute unit or less, the twice as many 16-row workgroups and the halved key
-// chain of each win; on fuller grids the 32-row pipelined tiles do.
+// narrower heads ((64,64), (80,80), (96,96), (128,128), (96,64)) run it when the
+// pipelined kernel's whole grid (every batch item) would have fewer than
+// kKsplitSmallGrid workgroups: at one workgroup per compute unit or less, the
+// twice as many 16-row workgroups and the halved key chain of each win; on
+// fuller grids the 32-row pipelined tiles do.
 constexpr int kKsplitLanes = 2, kKsplitRows = 16, kKsplitBN = 32;
 constexpr int kKsplitSmallGrid = 256;
 constexpr bool prefill_can_ksplit(int elem, int D, int Dv) {
-  return elem != kF32 && ((D == Dv && (D == 64 || D == 128 || D == 192 || D == 256)) || (D == 192 && Dv == 128));
+  return elem != kF32 && ((D == Dv && (D == 64 || D == 80 || D == 96 || D == 128 || D == 192 || D == 256)) ||
+                          (D == 96 && Dv == 64) || (D == 192 && Dv == 128));
 }
 // Calls that take it on every grid: heads of 192 columns or more, and 128-wide
 // heads with an additive mask (the pipelined kernel reads none, and the generic

@@ -1,6 +1,7 @@
 // Prefill for 16-bit inputs with heads of 192 or 256 columns, (192,192), (192,128)
-// and (256,256) (every grid, every mask kind), and 64- and 128-wide heads on grids
-// too small for the pipelined 32-row kernel: the
+// and (256,256) (every grid, every mask kind), and heads up to 128 wide, (64,64),
+// (80,80), (96,96), (128,128) and (96,64), on grids too small for the pipelined
+// 32-row kernel (128-wide heads with an additive mask on every grid): the
 // tiled online-softmax walk of lattice-inference
 // "src/attention/flash.rs" (run_tiled_attention_head), with the bottom-right
 // causal alignment of nuvec-core "tests/fast.rs"
@@ -65,12 +66,15 @@ struct KsplitCfg {
   static constexpr int TILE_BYTES = BN * RB, TILE_BYTES_V = BN * RBV;   // one step of K, of V
   static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / NW;       // direct loads per step
   static constexpr int LOADS_PER_WAVE_V = TILE_BYTES_V / 1024 / NW;
-  static constexpr int NQC = D / KW;           // QK^T k-steps
+  static constexpr int NQC = (D + KW - 1) / KW;  // QK^T k-steps (an 80-wide query is zero past 80)
   static constexpr int NSB = SUB / MF;         // 16-key blocks per wavefront step
   static constexpr int NDB = DV / MF;          // 16-column output blocks
   static constexpr int NPK = SUB * MF / 64 / 2;  // packed weight pairs per lane
-  static_assert((D == DV && (D == 64 || D == 128 || D == 192 || D == 256)) || (D == 192 && DV == 128),
-                "the key-split prefill serves (64,64), (128,128), (192,192), (256,256) and (192,128)");
+  static_assert((D == DV && (D == 64 || D == 80 || D == 96 || D == 128 || D == 192 || D == 256)) ||
+                    (D == 96 && DV == 64) || (D == 192 && DV == 128),
+                "the key-split prefill serves (64,64), (80,80), (96,96), (128,128), (192,192), (256,256), "
+                "(96,64) and (192,128)");
+  static_assert(D % 8 == 0 && DV % MF == 0, "whole 16-byte query groups and 16-column output blocks");
   static_assert(2 * NDB * 64 * 16 <= TILE_BYTES, "two slots' merge partials fit one K stage");
   static_assert(TILE_BYTES_V % (1024 * NW) == 0, "loads divide among wavefronts");
   static_assert(NSB == 2 && NPK == 4, "two 16-key blocks make one 32-key PV step");
@@ -182,7 +186,11 @@ prefill_ksplit_kernel(FwdArgs a) {
 #pragma unroll
     for (int c = 0; c < C::NQC; ++c) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (iq < a.Lq) x = ld_global16(qp + c * C::KW + kg * 8);
+      bool in = iq < a.Lq;
+      // (the k-step past an 80-wide query's end reads zeros: its K operands are
+      // real chunks loaded again, so it adds nothing to the scores)
+      if constexpr (D % C::KW != 0) in = in && c * C::KW + kg * 8 < D;
+      if (in) x = ld_global16(qp + c * C::KW + kg * 8);
       qop[c] = x ^ a.qsign;
     }
   }

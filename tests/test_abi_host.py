@@ -84,7 +84,7 @@ def test_small_f32_calls_split_keys_within_a_workgroup():
     q = _plan(B=5, Hq=8, Hkv=8, Lq=128, Lk=128, D=64, Dv=64, mask=1, dtype=0)
     assert (q["rows_per_wave"], q["splits"], q["grid"]) == (16, 4, (320, 1, 1))
     # large f32 calls keep the 32-row walk; 16-bit calls never take this split (small
-    # 64/128-wide 16-bit grids take the key-split kernel's two key lanes of eight waves
+    # 16-bit grids of heads up to 128 wide take the key-split kernel's two key lanes of eight waves
     # instead, large ones the pipelined kernel)
     big = _plan(B=1, Hq=32, Hkv=8, Lq=4096, Lk=4096, D=128, Dv=128, mask=1, dtype=0)
     assert (big["rows_per_wave"], big["splits"]) == (32, 0)
@@ -325,9 +325,12 @@ def test_additive_masks_plan_off_the_pipelined_kernel():
     for d in (64, 96):
         gen_add = sd.sdpa_plan(1, 32, 8, 4096, 4096, d, d, 3, True, False, 2)
         assert (gen_add["rows_per_wave"], gen_add["block_n"], gen_add["splits"]) == (32, 64, 0)
-    # on a small grid 64- and 128-wide heads take the key-split kernel
+    # on a small grid heads up to 128 wide take the key-split kernel
     small = sd.sdpa_plan(1, 8, 2, 300, 300, 128, 128, 3, True, False, 2)
     assert (small["splits"], small["rows_per_wave"]) == (2, 16)
+    for d, dv in ((64, 64), (80, 80), (96, 96), (96, 64)):
+        small = sd.sdpa_plan(1, 8, 2, 300, 300, d, dv, 3, True, False, 2)
+        assert (small["splits"], small["rows_per_wave"], small["block_n"]) == (2, 16, 32)
     dec = sd.sdpa_plan(1, 8, 2, 1, 3000, 128, 128, 3, True, False, 2)
     assert dec["route"] == "decode"
     assert sd.sdpa_plan(1, 8, 2, 1, 3000, 128, 128, 3, False, False, 2, check=False) == -1
@@ -400,7 +403,7 @@ def test_key_split_plans_for_wide_heads_and_small_64_and_128_wide_grids():
     assert sd.sdpa_plan(1, 4, 4, 100, 300, 256, 256, 0, False, False, 2)["grid"][0] == 4 * 2
     assert sd.sdpa_plan(1, 4, 2, 100, 300, 256, 256, 0, False, False, 2)["grid"][0] == 2 * 4
     # additive masks take the key-split kernel at 192- and 256-wide heads too, at
-    # 128-wide heads on every grid and at 64-wide heads on small grids; other calls
+    # 128-wide heads on every grid and at 64-, 80- and 96-wide heads on small grids; other calls
     # keep the generic kernel (the pipelined kernel reads no additive mask)
     add = sd.sdpa_plan(1, 64, 8, 1024, 1801, 256, 256, 3, True, True, 1)
     assert shape(add) + (add["kernels"], add["scratch_bytes"]) == (16, 32, 2, 8, 1, 0)

@@ -1,5 +1,6 @@
 """GPU parity of the key-split prefill (every 16-bit call with heads of 192 or 256
-columns, (192,192), (192,128) and (256,256), and 64- and 128-wide calls on small
+columns, (192,192), (192,128) and (256,256); 128-wide calls with an additive mask;
+calls with narrower heads, (64,64), (80,80), (96,96), (128,128) and (96,64), on small
 grids) against the CPU float64 oracle, every output element.
 
 The kernel's workgroup holds 16 query rows of up to four heads and splits each
@@ -20,7 +21,7 @@ pytestmark = pytest.mark.gpu
 F16, BF16 = gen.F16, gen.BF16
 DT = {"f16": F16, "bf16": BF16}
 # head pairs (D, Dv) the key-split kernel is built for
-WIDTHS = [(64, 64), (128, 128), (192, 192), (192, 128), (256, 256)]
+WIDTHS = [(64, 64), (80, 80), (96, 96), (128, 128), (96, 64), (192, 192), (192, 128), (256, 256)]
 PAIR_IDS = ["x".join(map(str, w)) for w in WIDTHS]
 
 

@@ -11,8 +11,9 @@ again here independently of the C planner:
     and Dv floats per (batch, kv head, split, packed row) of scratch;
   * otherwise "prefill" on one of four kernels: the key-split kernel for
     16-bit (192,192), (192,128) and (256,256) heads, for 16-bit 128-wide heads
-    with an additive mask, and for 16-bit 64/128-wide heads whose pipelined
-    grid (all batch items) is under 256 workgroups; the pipelined kernel for
+    with an additive mask, and for 16-bit (64,64), (80,80), (96,96), (128,128)
+    and (96,64) heads whose pipelined grid (all batch items) is under 256
+    workgroups; the pipelined kernel for
     other 16-bit calls at (64,64), (80,80), (96,96), (128,128) or (96,64)
     without an additive mask; the f32 key-split kernel for f32 calls whose
     32-row grid for one batch item is under 256 workgroups (no additive
@@ -62,7 +63,8 @@ def expected_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, dtype, window=0):
     pipelined_grid = B * (Hq // heads) * -(-Lq // ((WAVES // heads) * 32))   # every batch item
     if dtype != F32 and ((D, Dv) in ((192, 192), (192, 128), (256, 256))
                          or ((D, Dv) == (128, 128) and mask_kind == 3)
-                         or (D == Dv and D in (64, 128) and pipelined_grid < 256)):
+                         or ((D, Dv) in ((64, 64), (80, 80), (96, 96), (128, 128), (96, 64))
+                             and pipelined_grid < 256)):
         bm = (WAVES // heads) * 16
         return dict(base, route="prefill", kernels=1, rows_per_wave=16, waves=2 * WAVES, block_n=32,
                     heads_per_group=heads, splits=2, grid=(B * Hq // heads * -(-Lq // bm), 1, 1))

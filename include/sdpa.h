@@ -128,7 +128,7 @@ typedef struct sdpa_plan_t {
  * enqueued; a launch failure returns SDPA_ERR_HIP. A given plan gives the
  * same bits run to run, and each batch item's bits depend on B only through
  * the plan: B joins the choice between the pipelined and key-split kernels
- * for f16/bf16 calls with D == Dv in {64, 128} (rows_per_wave 32 or 16), and
+ * for f16/bf16 calls with heads up to 128 wide (rows_per_wave 32 or 16), and
  * calls that take the same kernel give each batch item the same bits.
  * Scratch (decode partials, packed mask bits; sdpa_plan's scratch_bytes)
  * comes from a per-(device, stream) buffer that the library allocates with

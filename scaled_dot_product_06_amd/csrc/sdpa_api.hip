@@ -270,7 +270,7 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
     return SDPA_OK;
   }
   // the key-split kernel at 16-bit heads of 192 columns or more, 128-wide ones with
-  // an additive mask, and 64/128-wide ones on small grids; the pipelined kernel
+  // an additive mask, and narrower ones on small grids; the pipelined kernel
   // (32-row tiles) where it applies; else the generic kernel's geometry
   const int nw = prefill_waves(dtype, (int)D, (int)Dv);
   const int64_t heads = gcd64(group, nw);

@@ -115,7 +115,8 @@ def test_batch_items_equal_each_item_alone(D, Dv):
         assert np.array_equal(whole[b:b + 1], alone), f"batch item {b} differs"
 
 
-# --- additive masks (the key-split path: every 256-wide call, 64/128-wide ones on small grids)
+# --- additive masks (the key-split path: heads of 192 or more and 128-wide ones on every grid,
+# narrower ones on small grids)
 
 def _additive_call(p, add, sinks, offset=0):
     """Run with `add` (any broadcast shape) as an additive mask, `offset` elements into its buffer."""

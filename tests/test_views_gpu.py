@@ -113,6 +113,9 @@ def test_query_view_and_kv_cache_slices(Lq, Lk, D, Hq, Hkv, w, dtype):
     ("bf16", (2, 8, 2, 300, 300, 128, 128), 1),   # key-split 16-bit prefill (128-wide heads, small grid)
     ("f16", (1, 8, 2, 200, 333, 64, 64), 2),      # key-split 16-bit prefill (64-wide heads, small grid)
     ("bf16", (1, 64, 8, 512, 300, 64, 64), 0),    # pipelined 16-bit prefill (64-wide heads)
+    ("f16", (1, 64, 8, 512, 300, 96, 64), 1),     # pipelined 16-bit prefill, (96,64) in the 128-wide layout
+    ("bf16", (1, 64, 8, 512, 300, 80, 80), 2),    # pipelined 16-bit prefill, 80-wide heads, byte mask
+    ("bf16", (1, 32, 8, 300, 333, 192, 128), 1),  # key-split 16-bit prefill, (192,128)
     ("bf16", (1, 4, 2, 100, 250, 256, 256), 1),   # key-split 16-bit prefill (256-wide heads)
     ("f32", (1, 4, 2, 70, 90, 128, 128), 1),      # f32 prefill
     ("bf16", (2, 16, 2, 1, 5000, 256, 256), 0),   # decode

@@ -71,8 +71,8 @@ typedef struct sdpa_plan_t {
                              the key-split kernel (f16/bf16, (D, Dv) in {(192,192), (192,128),
                              (256,256)} with every mask kind, (128,128) with an additive mask,
                              and (D, Dv) in {(64,64), (80,80), (96,96), (128,128), (96,64)} when the
-                             pipelined kernel's grid, all batch items together, would have fewer
-                             than 256 workgroups); 32 on the pipelined kernel (other f16/bf16
+                             pipelined kernel's grid for one batch item would have fewer than 256
+                             workgroups); 32 on the pipelined kernel (other f16/bf16
                              calls with (D, Dv) in {(64,64), (80,80), (96,96), (128,128), (96,64)},
                              no additive mask);
                              else the generic kernel's 32 (heads up to 128 wide) or 16 (wider
@@ -126,10 +126,7 @@ typedef struct sdpa_plan_t {
  * Empty cases: B*Hq*Lq == 0 or Dv == 0 enqueue nothing; Lk == 0 writes zeros.
  * The call is asynchronous: validation errors return before anything is
  * enqueued; a launch failure returns SDPA_ERR_HIP. A given plan gives the
- * same bits run to run, and each batch item's bits depend on B only through
- * the plan: B joins the choice between the pipelined and key-split kernels
- * for f16/bf16 calls with heads up to 128 wide (rows_per_wave 32 or 16), and
- * calls that take the same kernel give each batch item the same bits.
+ * same bits run to run, and each batch item's bits do not depend on B.
  * Scratch (decode partials, packed mask bits; sdpa_plan's scratch_bytes)
  * comes from a per-(device, stream) buffer that the library allocates with
  * hipMallocAsync on the stream's first call that needs it. A later call that

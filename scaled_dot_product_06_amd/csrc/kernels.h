@@ -105,10 +105,12 @@ constexpr int kFastRows = 32, kFastBN = 32;
 // heads leaves room for one wavefront per SIMD), and so do 128-wide heads with an
 // additive mask;
 // narrower heads ((64,64), (80,80), (96,96), (128,128), (96,64)) run it when the
-// pipelined kernel's whole grid (every batch item) would have fewer than
+// pipelined kernel's grid for one batch item would have fewer than
 // kKsplitSmallGrid workgroups: at one workgroup per compute unit or less, the
 // twice as many 16-row workgroups and the halved key chain of each win; on
-// fuller grids the 32-row pipelined tiles do.
+// fuller grids the 32-row pipelined tiles do. The rule leaves the batch size out,
+// so a batch item takes the same kernel, and gives the same bits, alone or
+// within a batch.
 constexpr int kKsplitLanes = 2, kKsplitRows = 16, kKsplitBN = 32;
 constexpr int kKsplitSmallGrid = 256;
 constexpr bool prefill_can_ksplit(int elem, int D, int Dv) {

@@ -277,8 +277,7 @@ int validate_and_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
   bool kspl = false;
   if (prefill_can_ksplit(dtype, (int)D, (int)Dv)) {
     const int64_t fbm = (nw / heads) * kFastRows;   // a pipelined workgroup's query rows per head
-    kspl = prefill_ksplit_always((int)D, (int)Dv, mask_kind) ||
-           (B * Hq / heads) * ((Lq + fbm - 1) / fbm) < kKsplitSmallGrid;
+    kspl = prefill_ksplit_always((int)D, (int)Dv, mask_kind) || (Hq / heads) * ((Lq + fbm - 1) / fbm) < kKsplitSmallGrid;
   }
   const bool fast = !kspl && prefill_can_fast(dtype, (int)D, (int)Dv, mask_kind);
   if (kspl) {

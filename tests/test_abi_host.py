@@ -389,14 +389,13 @@ def test_key_split_plans_for_wide_heads_and_small_64_and_128_wide_grids():
     # 128-wide heads on a small grid: the key-split kernel, which reads the bytes itself
     small128 = sd.sdpa_plan(1, 16, 2, 1024, 1801, 128, 128, 2, True, True, 1)  # 4 x 32 for the pipelined kernel
     assert shape(small128) + (small128["kernels"], small128["scratch_bytes"]) == (16, 32, 2, 8, 1, 0)
-    # the threshold: a pipelined grid of 256 workgroups (all batch items) keeps the
-    # pipelined kernel, at 64-wide heads as at 128-wide ones
-    for d in (64, 128):
-        assert shape(sd.sdpa_plan(1, 32, 4, 1024, 1024, d, d, 1, False, False, 2)) == (32, 32, 0, 4)   # 8 x 32
-        assert shape(sd.sdpa_plan(1, 32, 4, 992, 1024, d, d, 1, False, False, 2)) == (16, 32, 2, 8)    # 8 x 31
-        assert shape(sd.sdpa_plan(4, 32, 4, 992, 1024, d, d, 1, False, False, 2)) == (32, 32, 0, 4)    # 4 x 8 x 31
-        assert shape(sd.sdpa_plan(2, 32, 4, 480, 1024, d, d, 1, False, False, 2)) == (16, 32, 2, 8)    # 2 x 8 x 15
-        assert shape(sd.sdpa_plan(2, 32, 4, 512, 1024, d, d, 1, False, False, 2)) == (32, 32, 0, 4)    # 2 x 8 x 16
+    # the threshold: 256 pipelined workgroups per batch item keep the pipelined kernel,
+    # at every head pair up to 128 wide; the batch size never changes the kernel
+    for d, dv in ((64, 64), (80, 80), (96, 96), (128, 128), (96, 64)):
+        assert shape(sd.sdpa_plan(1, 32, 4, 1024, 1024, d, dv, 1, False, False, 2)) == (32, 32, 0, 4)   # 8 x 32
+        assert shape(sd.sdpa_plan(1, 32, 4, 992, 1024, d, dv, 1, False, False, 2)) == (16, 32, 2, 8)    # 8 x 31
+        assert shape(sd.sdpa_plan(4, 32, 4, 992, 1024, d, dv, 1, False, False, 2)) == (16, 32, 2, 8)    # per item
+        assert shape(sd.sdpa_plan(9, 32, 4, 1024, 1024, d, dv, 1, False, False, 2)) == (32, 32, 0, 4)   # per item
     batched = sd.sdpa_plan(8, 16, 2, 1024, 1801, 256, 256, 2, True, True, 1)  # the same per batch item
     assert shape(batched) + (batched["grid"][0],) == (16, 32, 2, 8, 8 * 4 * 64)
     # one or two heads per workgroup: 64 or 32 rows of a head per key lane

@@ -12,7 +12,7 @@ again here independently of the C planner:
   * otherwise "prefill" on one of four kernels: the key-split kernel for
     16-bit (192,192), (192,128) and (256,256) heads, for 16-bit 128-wide heads
     with an additive mask, and for 16-bit (64,64), (80,80), (96,96), (128,128)
-    and (96,64) heads whose pipelined grid (all batch items) is under 256
+    and (96,64) heads whose pipelined grid for one batch item is under 256
     workgroups; the pipelined kernel for
     other 16-bit calls at (64,64), (80,80), (96,96), (128,128) or (96,64)
     without an additive mask; the f32 key-split kernel for f32 calls whose
@@ -60,7 +60,7 @@ def expected_plan(B, Hq, Hkv, Lq, Lk, D, Dv, mask_kind, dtype, window=0):
                     grid=(splits, Hkv, B), scratch_bytes=B * Hkv * splits * rows * (Dv + 4) * 4)
     heads = math.gcd(g, WAVES)
     hmax = max(D, Dv)
-    pipelined_grid = B * (Hq // heads) * -(-Lq // ((WAVES // heads) * 32))   # every batch item
+    pipelined_grid = (Hq // heads) * -(-Lq // ((WAVES // heads) * 32))   # per batch item
     if dtype != F32 and ((D, Dv) in ((192, 192), (192, 128), (256, 256))
                          or ((D, Dv) == (128, 128) and mask_kind == 3)
                          or ((D, Dv) in ((64, 64), (80, 80), (96, 96), (128, 128), (96, 64))

@@ -115,6 +115,26 @@ def test_batch_items_equal_each_item_alone(D, Dv):
         assert np.array_equal(whole[b:b + 1], alone), f"batch item {b} differs"
 
 
+@pytest.mark.parametrize("D,Dv", [(64, 64), (128, 128), (96, 64)], ids=["64x64", "128x128", "96x64"])
+def test_a_full_batch_of_small_items_keeps_each_items_bits(D, Dv):
+    # 8 items of 32 heads x 256 rows: each item's pipelined grid is 64 workgroups, the
+    # whole batch's 512. The plan looks at one item, so the batch runs the key-split
+    # kernel like each item alone, and every item's bits equal its bits alone.
+    p = gen.make_problem(8650 + D + Dv, 8, 32, 8, 256, 256, D, Dv, BF16, 1, sinks=True)
+    plan = _plan(p)
+    assert (plan["rows_per_wave"], plan["splits"]) == (16, 2), plan
+    whole = from_device(run_gpu(p), BF16)
+    for b in (0, 3, 7):
+        pb = gen.Problem(1, p.Hq, p.Hkv, p.Lq, p.Lk, p.D, p.Dv, BF16, p.mask_kind, p.scale, p.q[b:b + 1],
+                         p.k[b:b + 1], p.v[b:b + 1], p.mask, p.sinks)
+        assert _plan(pb)["splits"] == 2
+        alone = from_device(run_gpu(pb), BF16)
+        assert np.array_equal(whole[b:b + 1], alone), f"batch item {b} differs"
+    from tests.gpu_util import sample_rows
+    rows = sample_rows(p, 64, seed=5)
+    assert_parity(p, np.stack([whole[b, h, i] for b, h, i in rows]), oracle_rows(p, rows), "full batch, sampled rows")
+
+
 # --- additive masks (the key-split path: heads of 192 or more and 128-wide ones on every grid,
 # narrower ones on small grids)
 

@@ -14,7 +14,7 @@ static hipError_t launch_one(const PrefillShape& s, const FwdArgs& a, hipStream_
     static_assert(C::MF == kKsplitRows && C::SUB == kKsplitBN && C::KL == kKsplitLanes && C::NWH == kPrefillWaves,
                   "planner geometry must match the kernel");
     // the plan chose the key-split kernel (every call with heads of 192 columns or
-    // more, 128-wide calls with an additive mask, 64- and 128-wide calls on small grids)
+    // more, 128-wide calls with an additive mask, narrower heads on small grids)
     if (s.ksplit > 1) {
       if (s.ksplit != C::KL || s.mf != C::MF || s.block_n != C::SUB || s.waves != C::NW)
         return hipErrorInvalidConfiguration;
